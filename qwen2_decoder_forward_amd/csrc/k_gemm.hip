@@ -1,0 +1,220 @@
+// MFMA GEMM of the prefill and batched-decode projections:
+//   C[M, N] = A[M, K] * W[N, K]^T,  A and W binary16, f32 accumulation,
+// on v_mfma_f32_32x32x16_f16.  Block tile 128 x 128 x 32, four wavefronts in
+// a 2 x 2 arrangement, each owning 64 x 64 (2 x 2 MFMA tiles).  The next K
+// slice is fetched into registers while the current one is multiplied out of
+// LDS.  Epilogues are fused:
+//   QKV    bias + RoPE + q write / K,V cache store (pair partner via lane^1)
+//   RESID  h += C                (WO, down)
+//   SWIGLU a = silu(gate) * up   (pair-packed gate/up rows, f16 out)
+//   LMHEAD logits + per-row greedy argmax
+// MFMA 32x32 layout: lane l supplies A[l%32][8*(l/32)..+8] and
+// B[8*(l/32)..+8][l%32]; it receives D[8*(r/4) + 4*(l/32) + r%4][l%32].
+#include "q2_device.h"
+
+namespace q2 {
+
+enum { G_QKV = 0, G_RESID = 1, G_SWIGLU = 2, G_LMHEAD = 3 };
+
+constexpr int BM = 128, BN = 128, BK = 32, LDT = BK + 8;
+
+struct GemmP {
+  const _Float16 *A;
+  int lda, M;
+  const _Float16 *W;
+  int N, K;
+  Dims d;
+  QkvEpi qkv;
+  float *h;
+  int ldh;
+  _Float16 *a16;
+  int ld_a;
+  ArgmaxEpi am;
+};
+
+template <int EPI>
+__global__ __launch_bounds__(256) void k_gemm(GemmP p) {
+  __shared__ __attribute__((aligned(16))) _Float16 sA[BM * LDT];
+  __shared__ __attribute__((aligned(16))) _Float16 sW[BN * LDT];
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int wm = wave >> 1, wn = wave & 1;
+  const int m0 = blockIdx.y * BM, n0 = blockIdx.x * BN;
+  const int M = p.M, N = p.N, K = p.K;
+  const int hi = lane >> 5, l32 = lane & 31;
+
+  // each thread moves two 16-byte chunks of A and two of W per K slice
+  const int cr0 = tid >> 2, cr1 = (tid + 256) >> 2, ck = (tid & 3) * 8;
+  const bool a0ok = m0 + cr0 < M, a1ok = m0 + cr1 < M;
+  const bool w0ok = n0 + cr0 < N, w1ok = n0 + cr1 < N;
+  const _Float16 *Ap0 = p.A + (size_t)(a0ok ? m0 + cr0 : 0) * p.lda + ck;
+  const _Float16 *Ap1 = p.A + (size_t)(a1ok ? m0 + cr1 : 0) * p.lda + ck;
+  const _Float16 *Wp0 = p.W + (size_t)(w0ok ? n0 + cr0 : 0) * K + ck;
+  const _Float16 *Wp1 = p.W + (size_t)(w1ok ? n0 + cr1 : 0) * K + ck;
+  const h8 zero = {0, 0, 0, 0, 0, 0, 0, 0};
+
+  h8 ra0 = a0ok ? *(const h8 *)Ap0 : zero, ra1 = a1ok ? *(const h8 *)Ap1 : zero;
+  h8 rw0 = w0ok ? *(const h8 *)Wp0 : zero, rw1 = w1ok ? *(const h8 *)Wp1 : zero;
+
+  f16x acc[2][2];
+#pragma unroll
+  for (int i = 0; i < 2; ++i)
+#pragma unroll
+    for (int j = 0; j < 2; ++j)
+#pragma unroll
+      for (int r = 0; r < 16; ++r) acc[i][j][r] = 0.f;
+
+  const int nk = K / BK;
+  for (int kt = 0; kt < nk; ++kt) {
+    *(h8 *)(sA + cr0 * LDT + ck) = ra0;
+    *(h8 *)(sA + cr1 * LDT + ck) = ra1;
+    *(h8 *)(sW + cr0 * LDT + ck) = rw0;
+    *(h8 *)(sW + cr1 * LDT + ck) = rw1;
+    __syncthreads();
+    if (kt + 1 < nk) {
+      const int ko = (kt + 1) * BK;
+      ra0 = a0ok ? *(const h8 *)(Ap0 + ko) : zero;
+      ra1 = a1ok ? *(const h8 *)(Ap1 + ko) : zero;
+      rw0 = w0ok ? *(const h8 *)(Wp0 + ko) : zero;
+      rw1 = w1ok ? *(const h8 *)(Wp1 + ko) : zero;
+    }
+#pragma unroll
+    for (int s = 0; s < 2; ++s) {
+      h8 af[2], bf[2];
+#pragma unroll
+      for (int i = 0; i < 2; ++i)
+        af[i] = *(const h8 *)(sA + (wm * 64 + i * 32 + l32) * LDT + s * 16 + hi * 8);
+#pragma unroll
+      for (int j = 0; j < 2; ++j)
+        bf[j] = *(const h8 *)(sW + (wn * 64 + j * 32 + l32) * LDT + s * 16 + hi * 8);
+#pragma unroll
+      for (int i = 0; i < 2; ++i)
+#pragma unroll
+        for (int j = 0; j < 2; ++j)
+          acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_f16(af[i], bf[j], acc[i][j], 0, 0, 0);
+    }
+    __syncthreads();
+  }
+
+  // ---------------------------------------------------------------- epilogue
+  if (EPI == G_LMHEAD) {
+    __shared__ unsigned long long sBest[2][BM];
+    __shared__ int s_last;
+    unsigned long long kb[2][16];
+#pragma unroll
+    for (int i = 0; i < 2; ++i)
+#pragma unroll
+      for (int r = 0; r < 16; ++r) {
+        const int m = m0 + wm * 64 + i * 32 + 8 * (r >> 2) + 4 * hi + (r & 3);
+        unsigned long long b = 0ull;
+#pragma unroll
+        for (int j = 0; j < 2; ++j) {
+          const int n = n0 + wn * 64 + j * 32 + l32;
+          if (m < M && n < N) {
+            const float v = acc[i][j][r];
+            if (p.am.logits) p.am.logits[(size_t)m * N + n] = v;
+            const unsigned long long key = argmax_key(v, n);
+            b = key > b ? key : b;
+          }
+        }
+#pragma unroll
+        for (int o = 1; o < 32; o <<= 1) {
+          const unsigned long long x = shfl_xor_u64(b, o);
+          b = x > b ? x : b;
+        }
+        kb[i][r] = b;
+      }
+    if (l32 == 0) {
+#pragma unroll
+      for (int i = 0; i < 2; ++i)
+#pragma unroll
+        for (int r = 0; r < 16; ++r) sBest[wn][wm * 64 + i * 32 + 8 * (r >> 2) + 4 * hi + (r & 3)] = kb[i][r];
+    }
+    __syncthreads();
+    if (tid < BM && m0 + tid < M) {
+      const unsigned long long b = sBest[0][tid] > sBest[1][tid] ? sBest[0][tid] : sBest[1][tid];
+      atomicMax(&p.am.best[m0 + tid], b);
+    }
+    __threadfence();
+    __syncthreads();
+    if (tid == 0) s_last = (atomicAdd(p.am.counter, 1u) == gridDim.x * gridDim.y - 1);
+    __syncthreads();
+    if (s_last) {
+      __threadfence();
+      for (int m = tid; m < M; m += 256) {
+        const unsigned long long b = atomicExch(&p.am.best[m], 0ull);
+        if (p.am.out) p.am.out[m] = argmax_index(b);
+      }
+      if (tid == 0) atomicExch(p.am.counter, 0u);
+    }
+    return;
+  }
+
+#pragma unroll
+  for (int i = 0; i < 2; ++i)
+#pragma unroll
+    for (int j = 0; j < 2; ++j) {
+      const int n = n0 + wn * 64 + j * 32 + l32;
+#pragma unroll
+      for (int r = 0; r < 16; ++r) {
+        const int m = m0 + wm * 64 + i * 32 + 8 * (r >> 2) + 4 * hi + (r & 3);
+        const float v = acc[i][j][r];
+        if (EPI == G_RESID) {
+          if (m < M && n < N) p.h[(size_t)m * p.ldh + n] += v;
+        } else {
+          const float partner = __shfl_xor(v, 1, 64);
+          if ((n & 1) == 0 && m < M && n < N) {
+            if (EPI == G_QKV)
+              qkv_store_pair(p.d, p.qkv, m, n, v, partner);
+            else
+              p.a16[(size_t)m * p.ld_a + (n >> 1)] = (_Float16)(silu(v) * partner);
+          }
+        }
+      }
+    }
+}
+
+static dim3 grid_for(int M, int N) { return dim3((N + BN - 1) / BN, (M + BM - 1) / BM); }
+
+static GemmP base(const _Float16 *A, int lda, int M, const uint16_t *W, int N, int K) {
+  GemmP p{};
+  p.A = A;
+  p.lda = lda;
+  p.M = M;
+  p.W = (const _Float16 *)W;
+  p.N = N;
+  p.K = K;
+  return p;
+}
+
+void gemm_qkv(const Dims &d, const LayerW &w, const _Float16 *x, int lda, int M,
+              const QkvEpi &e, hipStream_t st) {
+  GemmP p = base(x, lda, M, w.wqkv, d.nqkv, d.H);
+  p.d = d;
+  p.qkv = e;
+  hipLaunchKernelGGL(k_gemm<G_QKV>, grid_for(M, p.N), dim3(256), 0, st, p);
+}
+
+void gemm_resid(const uint16_t *W, int N, int K, const _Float16 *x, int lda, int M, float *h,
+                int ldh, hipStream_t st) {
+  GemmP p = base(x, lda, M, W, N, K);
+  p.h = h;
+  p.ldh = ldh;
+  hipLaunchKernelGGL(k_gemm<G_RESID>, grid_for(M, N), dim3(256), 0, st, p);
+}
+
+void gemm_swiglu(const Dims &d, const LayerW &w, const _Float16 *x, int lda, int M,
+                 _Float16 *a, int ld_a, hipStream_t st) {
+  GemmP p = base(x, lda, M, w.wgu, 2 * d.I_pad, d.H);
+  p.a16 = a;
+  p.ld_a = ld_a;
+  hipLaunchKernelGGL(k_gemm<G_SWIGLU>, grid_for(M, p.N), dim3(256), 0, st, p);
+}
+
+void gemm_lmhead(const Dims &d, const uint16_t *W, const _Float16 *x, int lda, int M,
+                 const ArgmaxEpi &e, hipStream_t st) {
+  GemmP p = base(x, lda, M, W, d.V, d.H);
+  p.am = e;
+  hipLaunchKernelGGL(k_gemm<G_LMHEAD>, grid_for(M, d.V), dim3(256), 0, st, p);
+}
+
+}  // namespace q2

@@ -1,0 +1,64 @@
+// Embedding gather and row RMSNorm.
+#include "q2_device.h"
+
+namespace q2 {
+
+// h[m] = f32(E[tokens[m]]): the embedding output enters the first layer
+// unscaled.  An id outside [0, V) cannot be rejected on the host when the
+// tokens live on the device; it reads row 0 and latches *bad.
+__global__ __launch_bounds__(256) void k_embed(const uint16_t *E, int H, int V, const int *tokens,
+                                               float *h, unsigned int *bad) {
+  const int m = blockIdx.x;
+  int t = tokens[m];
+  if (t < 0 || t >= V) {
+    if (threadIdx.x == 0) *bad = 1u;
+    t = 0;
+  }
+  const _Float16 *row = (const _Float16 *)E + (size_t)t * H;
+  for (int k = threadIdx.x * 8; k < H; k += 256 * 8) {
+    const h8 v = *(const h8 *)(row + k);
+    f4 a = {(float)v[0], (float)v[1], (float)v[2], (float)v[3]};
+    f4 b = {(float)v[4], (float)v[5], (float)v[6], (float)v[7]};
+    *(f4 *)(h + (size_t)m * H + k) = a;
+    *(f4 *)(h + (size_t)m * H + k + 4) = b;
+  }
+}
+
+void embed_rows(const uint16_t *E, int H, int V, const int *tokens, int M, float *h,
+                unsigned int *bad_flag, hipStream_t st) {
+  hipLaunchKernelGGL(k_embed, dim3(M), dim3(256), 0, st, E, H, V, tokens, h, bad_flag);
+}
+
+// One wavefront per row: y = w * x / sqrt(mean(x^2) + eps), stored as f16
+// (MFMA operand) and optionally f32.
+__global__ __launch_bounds__(256) void k_rmsnorm_rows(const float *h, int ldh, const float *w,
+                                                      int H, int M, float eps, _Float16 *x,
+                                                      int ldx, float *y32) {
+  const int lane = threadIdx.x & 63;
+  const int m = blockIdx.x * 4 + (threadIdx.x >> 6);
+  if (m >= M) return;
+  const float *row = h + (size_t)m * ldh;
+  float ss = 0.f;
+  for (int k = lane * 4; k < H; k += 256) {
+    const f4 v = *(const f4 *)(row + k);
+    ss += v.x * v.x + v.y * v.y + v.z * v.z + v.w * v.w;
+  }
+  ss = wave_sum(ss);
+  const float inv = 1.0f / sqrtf(ss / (float)H + eps);
+  for (int k = lane * 4; k < H; k += 256) {
+    const f4 v = *(const f4 *)(row + k);
+    const f4 g = *(const f4 *)(w + k);
+    const f4 y = v * inv * g;
+    h4 yh = {(_Float16)y.x, (_Float16)y.y, (_Float16)y.z, (_Float16)y.w};
+    *(h4 *)(x + (size_t)m * ldx + k) = yh;
+    if (y32) *(f4 *)(y32 + (size_t)m * H + k) = y;
+  }
+}
+
+void rmsnorm_rows_f16(const float *h, int ldh, const float *w, int H, int M, float eps,
+                      _Float16 *x, int ldx, float *y32, hipStream_t st) {
+  hipLaunchKernelGGL(k_rmsnorm_rows, dim3((M + 3) / 4), dim3(256), 0, st, h, ldh, w, H, M, eps,
+                     x, ldx, y32);
+}
+
+}  // namespace q2

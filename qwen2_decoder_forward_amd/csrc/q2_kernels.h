@@ -1,0 +1,114 @@
+// Internal interface between the host runtime (qwen2_abi.cpp) and the HIP
+// kernels (k_*.hip).  Not part of the public C ABI.
+#pragma once
+#include <hip/hip_runtime.h>
+#include <stddef.h>
+#include <stdint.h>
+
+namespace q2 {
+
+// Model dimensions as the kernels see them.
+struct Dims {
+  int L, H, nh, nkv, hd, group, I, I_pad, V, n_ctx, n_seq;
+  int nqkv;  // (nh + 2 * nkv) * hd rows of the fused QKV matrix
+};
+
+// Device weight store of one layer (repacked at load time).
+//  wqkv [nqkv, H]: rows [q heads | k heads | v heads]; inside every head the
+//       rows are pair-interleaved: packed rows (2j, 2j+1) hold the natural
+//       rows (j, j + hd/2), the two halves RoPE rotates together.
+//  bqkv [nqkv] in the same packed order.
+//  wgu  [2 * I_pad, H]: packed row 2i = gate row i, 2i+1 = up row i; rows of
+//       i >= I are zero.
+//  wd   [H, I_pad]: columns >= I are zero.
+struct LayerW {
+  const float *attn_norm, *ffn_norm, *bqkv;
+  const uint16_t *wqkv, *wo, *wgu, *wd;
+};
+
+// Where rows of the current call live and where K/V go.
+struct RowInfo {
+  const int *pos;  // [M] position of each row
+  const int *seq;  // [M] sequence slot of each row
+};
+
+struct KVCache {
+  float *k, *v;  // [L][n_seq][nkv][n_ctx][hd] each
+  __host__ __device__ size_t off(const Dims &d, int l, int s, int g, int p) const {
+    return ((((size_t)l * d.n_seq + s) * d.nkv + g) * d.n_ctx + p) * (size_t)d.hd;
+  }
+};
+
+struct RopeTable {
+  const float *cos, *sin;  // [n_ctx][hd/2]
+};
+
+// Epilogue of the fused QKV projection: bias, RoPE on q/k, K/V store.
+struct QkvEpi {
+  const float *bias;  // packed order
+  float *q;           // [M, nh*hd] rotated queries (f32)
+  int ldq;
+  KVCache kv;
+  int layer;
+  RowInfo rows;
+  RopeTable rope;
+};
+
+// Greedy readout: packed (ordered-key, ~index) 64-bit maxima per row, a
+// block counter and the int32 result.  `best` and `counter` are zero between
+// calls (the last block resets them).
+struct ArgmaxEpi {
+  float *logits;            // [M, V] or null
+  unsigned long long *best;  // [M]
+  unsigned int *counter;     // [1]
+  int *out;                  // [M] or null
+};
+
+// ---------------------------------------------------------------- launchers
+// GEMV family (rows M <= 8, f32 activations, f16 weights streamed once).
+// y[m, n] = sum_k x'[m, k] W[n, k] with x' = x, or RMSNorm(x) * norm_w when
+// norm_w is given (then K must equal the normed width).
+void gemv_qkv(const Dims &d, const LayerW &w, const float *h, int M, const QkvEpi &e,
+              float eps, hipStream_t st);
+void gemv_resid(const uint16_t *W, int N, int K, const float *x, int ldx, int M, float *h,
+                int ldh, hipStream_t st);
+void gemv_swiglu(const Dims &d, const LayerW &w, const float *h, int M, float *a, int lda,
+                 float eps, hipStream_t st);
+void gemv_lmhead(const Dims &d, const uint16_t *W, const float *norm_w, const float *h, int M,
+                 float *normed_out, const ArgmaxEpi &e, float eps, hipStream_t st);
+
+// MFMA GEMM family (rows M > 8): A f16 [M, lda], W f16 [N, K], K % 32 == 0.
+void gemm_qkv(const Dims &d, const LayerW &w, const _Float16 *x, int lda, int M,
+              const QkvEpi &e, hipStream_t st);
+void gemm_resid(const uint16_t *W, int N, int K, const _Float16 *x, int lda, int M, float *h,
+                int ldh, hipStream_t st);
+void gemm_swiglu(const Dims &d, const LayerW &w, const _Float16 *x, int lda, int M,
+                 _Float16 *a, int ld_a, hipStream_t st);
+void gemm_lmhead(const Dims &d, const uint16_t *W, const _Float16 *x, int lda, int M,
+                 const ArgmaxEpi &e, hipStream_t st);
+
+// RMSNorm of rows into an f16 copy (the MFMA A operand) and, when y32 is
+// given, also into f32 [M, H].
+void rmsnorm_rows_f16(const float *h, int ldh, const float *w, int H, int M, float eps,
+                      _Float16 *x, int ldx, float *y32, hipStream_t st);
+// Embedding gather h[m] = f32(E[tokens[m]]) without scaling; an id outside
+// [0, V) reads row 0 and sets *bad_flag to 1.
+void embed_rows(const uint16_t *E, int H, int V, const int *tokens, int M, float *h,
+                unsigned int *bad_flag, hipStream_t st);
+
+// Attention.
+struct AttnPartials {
+  float *buf;              // [rows][nkv][n_chunks][group][hd + 2]
+  unsigned int *counters;  // [rows][nkv], zero between calls
+  int n_chunks;
+};
+// Split-KV attention, one row per query token (decode and short prefills).
+void attn_decode(const Dims &d, int layer, const KVCache &kv, const float *q, int ldq,
+                 RowInfo rows, int M, const AttnPartials &p, float *o32, _Float16 *o16,
+                 int ldo, hipStream_t st);
+// Causal flash attention over MFMA for one prefill pass of M rows of one
+// sequence (positions strictly increasing).
+void attn_prefill(const Dims &d, int layer, const KVCache &kv, const float *q, int ldq,
+                  RowInfo rows, int M, _Float16 *o16, int ldo, hipStream_t st);
+
+}  // namespace q2

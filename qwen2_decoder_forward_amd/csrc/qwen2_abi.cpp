@@ -1,0 +1,562 @@
+// C ABI of the MI355X Qwen2 decoder forward pass: context, device weight
+// store, KV cache, scratch and the per-call launch sequence.
+#include <hip/hip_runtime.h>
+#include <math.h>
+#include <stdio.h>
+#include <string.h>
+
+#include <algorithm>
+#include <string>
+#include <vector>
+
+#include "../../include/qwen2.h"
+#include "q2_kernels.h"
+#include "validate.h"
+
+using q2::Dims;
+using q2::LayerW;
+
+namespace {
+
+constexpr int kRing = 4;          // pinned staging slots for per-call row data
+constexpr int kGemvRows = 8;      // rows up to this use the f32 GEMV path
+constexpr int kMaxPassRows = 4096;  // rows per prefill pass
+
+thread_local std::string g_load_error;
+
+size_t align256(size_t x) { return (x + 255) & ~(size_t)255; }
+
+}  // namespace
+
+struct qwen2_ctx {
+  qwen2_hparams hp{};
+  Dims d{};
+  int device = 0;
+  // weight store
+  char *warena = nullptr;
+  size_t warena_bytes = 0;
+  const uint16_t *tok_embd = nullptr, *lm_head = nullptr;
+  const float *out_norm = nullptr;
+  std::vector<LayerW> layers;
+  uint64_t w_f16 = 0, w_f32 = 0;
+  // KV cache and RoPE table
+  float *kc = nullptr, *vc = nullptr;
+  size_t kv_elems = 0;
+  float *rope_cos = nullptr, *rope_sin = nullptr;
+  // scratch
+  char *sarena = nullptr;
+  size_t sarena_bytes = 0;
+  int max_rows = 0;   // rows per prefill pass
+  int rows_cap = 0;   // rows of the activation buffers: max(max_rows, n_seq)
+  int dec_rows = 0;   // rows of the GEMV / decode-attention buffers: max(n_seq, 8)
+  float *h = nullptr, *q32 = nullptr, *o32 = nullptr, *a32 = nullptr, *normed = nullptr;
+  _Float16 *x16 = nullptr, *a16 = nullptr;
+  int *io = nullptr;  // device copy of the per-call rows: tokens | positions | seqs
+  size_t io_cap = 0;  // entries per field
+  q2::AttnPartials part{};
+  unsigned long long *best = nullptr;
+  unsigned int *best_cnt = nullptr;
+  unsigned int *bad_flag = nullptr;
+  // pinned staging ring
+  int32_t *pinned = nullptr;
+  hipEvent_t ev[kRing] = {};
+  int ring = 0;
+  // last read-out rows
+  const float *last_h = nullptr;
+  int last_rows = 0;
+  std::string err;
+};
+
+namespace {
+
+int set_err(qwen2_ctx *c, int code, const std::string &m) {
+  if (c) c->err = m;
+  else g_load_error = m;
+  return code;
+}
+
+#define HIP_TRY(ctx, expr)                                                                \
+  do {                                                                                    \
+    hipError_t e_ = (expr);                                                               \
+    if (e_ != hipSuccess)                                                                 \
+      return set_err(ctx, e_ == hipErrorOutOfMemory ? QWEN2_E_OOM : QWEN2_E_HIP,          \
+                     std::string(#expr) + ": " + hipGetErrorString(e_));                  \
+  } while (0)
+
+void release(qwen2_ctx *c) {
+  if (!c) return;
+  hipDeviceSynchronize();
+  if (c->warena) hipFree(c->warena);
+  if (c->kc) hipFree(c->kc);
+  if (c->vc) hipFree(c->vc);
+  if (c->rope_cos) hipFree(c->rope_cos);
+  if (c->sarena) hipFree(c->sarena);
+  if (c->pinned) hipHostFree(c->pinned);
+  for (auto &e : c->ev)
+    if (e) hipEventDestroy(e);
+  delete c;
+}
+
+// Packs the fused QKV rows: for every head of [q | k | v], packed rows
+// (2j, 2j+1) = natural rows (j, j + hd/2).
+template <typename T>
+void pack_qkv(const qwen2_hparams &hp, const T *q, const T *k, const T *v, size_t rowlen,
+              std::vector<T> &out) {
+  const int hd = hp.head_dim, half = hd / 2;
+  const int nh = hp.n_head, nkv = hp.n_head_kv;
+  out.assign((size_t)(nh + 2 * nkv) * hd * rowlen, T(0));
+  size_t dst_row = 0;
+  auto put_heads = [&](const T *src, int heads) {
+    for (int hh = 0; hh < heads; ++hh)
+      for (int j = 0; j < half; ++j) {
+        for (int part = 0; part < 2; ++part) {
+          const size_t srow = (size_t)hh * hd + j + part * half;
+          memcpy(&out[dst_row * rowlen], src + srow * rowlen, rowlen * sizeof(T));
+          ++dst_row;
+        }
+      }
+  };
+  put_heads(q, nh);
+  put_heads(k, nkv);
+  put_heads(v, nkv);
+}
+
+}  // namespace
+
+extern "C" {
+
+int qwen2_load(const qwen2_hparams *hp, const qwen2_weights *w, void *stream, qwen2_ctx **out) {
+  if (!out) return set_err(nullptr, QWEN2_E_ARG, "null output pointer");
+  *out = nullptr;
+  std::string msg;
+  int rc = q2::check_hparams(hp, &msg);
+  if (rc) return set_err(nullptr, rc, msg);
+  if (!w || !w->tok_embd || !w->out_norm || !w->layers || (!hp->tied && !w->lm_head))
+    return set_err(nullptr, QWEN2_E_ARG, "missing weight pointer");
+  for (int l = 0; l < hp->n_layer; ++l) {
+    const qwen2_layer_weights &L = w->layers[l];
+    if (!L.attn_norm || !L.bq || !L.bk || !L.bv || !L.ffn_norm || !L.wq || !L.wk || !L.wv ||
+        !L.wo || !L.w_gate || !L.w_up || !L.w_down)
+      return set_err(nullptr, QWEN2_E_ARG, "missing weight pointer in layer " + std::to_string(l));
+  }
+  hipStream_t st = (hipStream_t)stream;
+
+  qwen2_ctx *c = new qwen2_ctx();
+  c->hp = *hp;
+  Dims &d = c->d;
+  d.L = hp->n_layer;
+  d.H = hp->n_embd;
+  d.nh = hp->n_head;
+  d.nkv = hp->n_head_kv;
+  d.hd = hp->head_dim;
+  d.group = d.nh / d.nkv;
+  d.I = hp->n_ff;
+  d.I_pad = (d.I + 63) / 64 * 64;
+  d.V = hp->n_vocab;
+  d.n_ctx = hp->n_ctx;
+  d.n_seq = hp->n_seq;
+  d.nqkv = (d.nh + 2 * d.nkv) * d.hd;
+
+  auto fail = [&](int code) {
+    std::string m = c->err;
+    release(c);
+    return set_err(nullptr, code, m);
+  };
+#define LTRY(expr)                    \
+  do {                                \
+    int r_ = (expr);                  \
+    if (r_) return fail(r_);          \
+  } while (0)
+
+  LTRY([&]() -> int { HIP_TRY(c, hipGetDevice(&c->device)); return 0; }());
+
+  // ---- weight store layout
+  const size_t H = d.H, V = d.V, I = d.I, Ip = d.I_pad, nq = d.nqkv, nhd = (size_t)d.nh * d.hd;
+  struct Slot { size_t off, bytes; };
+  size_t cur = 0;
+  auto take = [&](size_t bytes) { Slot s{cur, bytes}; cur = align256(cur + bytes); return s; };
+  Slot s_emb = take(V * H * 2);
+  Slot s_lm = hp->tied ? s_emb : take(V * H * 2);
+  Slot s_onorm = take(H * 4);
+  std::vector<Slot> s_l(7 * d.L);
+  for (int l = 0; l < d.L; ++l) {
+    s_l[7 * l + 0] = take(H * 4);        // attn_norm
+    s_l[7 * l + 1] = take(H * 4);        // ffn_norm
+    s_l[7 * l + 2] = take(nq * 4);       // bqkv
+    s_l[7 * l + 3] = take(nq * H * 2);   // wqkv
+    s_l[7 * l + 4] = take(H * nhd * 2);  // wo
+    s_l[7 * l + 5] = take(2 * Ip * H * 2);  // wgu
+    s_l[7 * l + 6] = take(H * Ip * 2);   // wd
+  }
+  c->warena_bytes = cur;
+  c->w_f16 = (uint64_t)(V * H * (hp->tied ? 1 : 2) +
+                        d.L * (nq * H + H * nhd + 3 * I * H)) * 2;
+  c->w_f32 = (uint64_t)(H + d.L * (2 * H + nq)) * 4;
+  LTRY([&]() -> int { HIP_TRY(c, hipMalloc(&c->warena, c->warena_bytes)); return 0; }());
+  char *A = c->warena;
+  auto put = [&](const Slot &s, const void *src) -> int {
+    HIP_TRY(c, hipMemcpy(A + s.off, src, s.bytes, hipMemcpyHostToDevice));
+    return 0;
+  };
+  LTRY(put(s_emb, w->tok_embd));
+  if (!hp->tied) LTRY(put(s_lm, w->lm_head));
+  LTRY(put(s_onorm, w->out_norm));
+  c->tok_embd = (const uint16_t *)(A + s_emb.off);
+  c->lm_head = (const uint16_t *)(A + s_lm.off);
+  c->out_norm = (const float *)(A + s_onorm.off);
+  {
+    std::vector<uint16_t> tmp16;
+    std::vector<float> tmp32;
+    for (int l = 0; l < d.L; ++l) {
+      const qwen2_layer_weights &L = w->layers[l];
+      const Slot *s = &s_l[7 * l];
+      LTRY(put(s[0], L.attn_norm));
+      LTRY(put(s[1], L.ffn_norm));
+      pack_qkv<float>(*hp, L.bq, L.bk, L.bv, 1, tmp32);
+      LTRY(put(s[2], tmp32.data()));
+      pack_qkv<uint16_t>(*hp, L.wq, L.wk, L.wv, H, tmp16);
+      LTRY(put(s[3], tmp16.data()));
+      LTRY(put(s[4], L.wo));
+      tmp16.assign(2 * Ip * H, 0);
+      for (size_t i = 0; i < I; ++i) {
+        memcpy(&tmp16[(2 * i) * H], L.w_gate + i * H, H * 2);
+        memcpy(&tmp16[(2 * i + 1) * H], L.w_up + i * H, H * 2);
+      }
+      LTRY(put(s[5], tmp16.data()));
+      tmp16.assign(H * Ip, 0);
+      for (size_t r = 0; r < H; ++r) memcpy(&tmp16[r * Ip], L.w_down + r * I, I * 2);
+      LTRY(put(s[6], tmp16.data()));
+      LayerW lw;
+      lw.attn_norm = (const float *)(A + s[0].off);
+      lw.ffn_norm = (const float *)(A + s[1].off);
+      lw.bqkv = (const float *)(A + s[2].off);
+      lw.wqkv = (const uint16_t *)(A + s[3].off);
+      lw.wo = (const uint16_t *)(A + s[4].off);
+      lw.wgu = (const uint16_t *)(A + s[5].off);
+      lw.wd = (const uint16_t *)(A + s[6].off);
+      c->layers.push_back(lw);
+    }
+  }
+
+  // ---- KV cache (zero-filled: slots never written read as zero)
+  c->kv_elems = (size_t)d.L * d.n_seq * d.nkv * d.n_ctx * d.hd;
+  LTRY([&]() -> int {
+    HIP_TRY(c, hipMalloc(&c->kc, c->kv_elems * 4));
+    HIP_TRY(c, hipMalloc(&c->vc, c->kv_elems * 4));
+    HIP_TRY(c, hipMemset(c->kc, 0, c->kv_elems * 4));
+    HIP_TRY(c, hipMemset(c->vc, 0, c->kv_elems * 4));
+    return 0;
+  }());
+
+  // ---- RoPE table: angle = pos * freq_scale * theta^(-2j/hd), computed in
+  // double and rounded to float once.
+  {
+    const int half = d.hd / 2;
+    std::vector<float> cs((size_t)d.n_ctx * half), sn((size_t)d.n_ctx * half);
+    for (int p = 0; p < d.n_ctx; ++p)
+      for (int j = 0; j < half; ++j) {
+        const double inv = pow((double)hp->rope_theta, -2.0 * j / d.hd);
+        const double ang = (double)p * (double)hp->rope_freq_scale * inv;
+        cs[(size_t)p * half + j] = (float)cos(ang);
+        sn[(size_t)p * half + j] = (float)sin(ang);
+      }
+    LTRY([&]() -> int {
+      HIP_TRY(c, hipMalloc(&c->rope_cos, 2 * cs.size() * 4));
+      c->rope_sin = c->rope_cos + cs.size();
+      HIP_TRY(c, hipMemcpy(c->rope_cos, cs.data(), cs.size() * 4, hipMemcpyHostToDevice));
+      HIP_TRY(c, hipMemcpy(c->rope_sin, sn.data(), sn.size() * 4, hipMemcpyHostToDevice));
+      return 0;
+    }());
+  }
+
+  // ---- scratch
+  c->max_rows = std::min(d.n_ctx, kMaxPassRows);
+  c->rows_cap = std::max(c->max_rows, d.n_seq);
+  c->dec_rows = std::max(d.n_seq, kGemvRows);
+  c->part.n_chunks = (d.n_ctx + 63) / 64;
+  c->io_cap = (size_t)std::max(d.n_ctx, d.n_seq);
+  {
+    const size_t R = c->rows_cap, D = c->dec_rows;
+    cur = 0;
+    Slot s_h = take(R * H * 4), s_q = take(R * nhd * 4), s_x16 = take(R * H * 2),
+         s_a16 = take(R * Ip * 2), s_o32 = take(D * nhd * 4), s_a32 = take(D * Ip * 4),
+         s_norm = take(D * H * 4), s_io = take(3 * c->io_cap * 4),
+         s_part = take((size_t)D * d.nkv * c->part.n_chunks * d.group * (d.hd + 2) * 4),
+         s_pcnt = take((size_t)D * d.nkv * 4), s_best = take(D * 8), s_bcnt = take(4),
+         s_bad = take(4);
+    c->sarena_bytes = cur;
+    LTRY([&]() -> int {
+      HIP_TRY(c, hipMalloc(&c->sarena, c->sarena_bytes));
+      HIP_TRY(c, hipMemset(c->sarena, 0, c->sarena_bytes));
+      return 0;
+    }());
+    char *S = c->sarena;
+    c->h = (float *)(S + s_h.off);
+    c->q32 = (float *)(S + s_q.off);
+    c->x16 = (_Float16 *)(S + s_x16.off);
+    c->a16 = (_Float16 *)(S + s_a16.off);
+    c->o32 = (float *)(S + s_o32.off);
+    c->a32 = (float *)(S + s_a32.off);
+    c->normed = (float *)(S + s_norm.off);
+    c->io = (int *)(S + s_io.off);
+    c->part.buf = (float *)(S + s_part.off);
+    c->part.counters = (unsigned *)(S + s_pcnt.off);
+    c->best = (unsigned long long *)(S + s_best.off);
+    c->best_cnt = (unsigned *)(S + s_bcnt.off);
+    c->bad_flag = (unsigned *)(S + s_bad.off);
+  }
+  LTRY([&]() -> int {
+    HIP_TRY(c, hipHostMalloc((void **)&c->pinned, kRing * 3 * c->io_cap * 4, hipHostMallocDefault));
+    for (auto &e : c->ev) HIP_TRY(c, hipEventCreateWithFlags(&e, hipEventDisableTiming));
+    HIP_TRY(c, hipStreamSynchronize(st));
+    HIP_TRY(c, hipDeviceSynchronize());
+    return 0;
+  }());
+#undef LTRY
+  *out = c;
+  return QWEN2_OK;
+}
+
+}  // extern "C"
+
+namespace {
+
+// Copies `nf` fields of n int32 each to the device row buffer through the
+// pinned ring; returns device pointers to the fields.
+int stage_rows(qwen2_ctx *c, hipStream_t st, int n, const int32_t *f0, const int32_t *f1,
+               const int32_t *f2_or_null, int32_t seq_fill, int **d0, int **d1, int **d2) {
+  const int slot = c->ring;
+  c->ring = (c->ring + 1) % kRing;
+  HIP_TRY(c, hipEventSynchronize(c->ev[slot]));
+  int32_t *hbuf = c->pinned + (size_t)slot * 3 * c->io_cap;
+  memcpy(hbuf, f0, n * 4);
+  memcpy(hbuf + n, f1, n * 4);
+  if (f2_or_null) memcpy(hbuf + 2 * n, f2_or_null, n * 4);
+  else
+    for (int i = 0; i < n; ++i) hbuf[2 * n + i] = seq_fill;
+  HIP_TRY(c, hipMemcpyAsync(c->io, hbuf, (size_t)3 * n * 4, hipMemcpyHostToDevice, st));
+  HIP_TRY(c, hipEventRecord(c->ev[slot], st));
+  *d0 = c->io;
+  *d1 = c->io + n;
+  *d2 = c->io + 2 * n;
+  return QWEN2_OK;
+}
+
+q2::QkvEpi qkv_epi(qwen2_ctx *c, int l, const int *pos, const int *seq) {
+  q2::QkvEpi e;
+  e.bias = c->layers[l].bqkv;
+  e.q = c->q32;
+  e.ldq = c->d.nh * c->d.hd;
+  e.kv = q2::KVCache{c->kc, c->vc};
+  e.layer = l;
+  e.rows = q2::RowInfo{pos, seq};
+  e.rope = q2::RopeTable{c->rope_cos, c->rope_sin};
+  return e;
+}
+
+// The last layer of a prefill pass after its K/V are stored: only the last
+// row goes on (attention, WO, FFN, final norm, lm_head, argmax).
+void tail_row(qwen2_ctx *c, int r, const int *pos, const int *seq, float *logits, int *argmax,
+              hipStream_t st) {
+  const Dims &d = c->d;
+  const int l = d.L - 1;
+  const LayerW &w = c->layers[l];
+  const int nhd = d.nh * d.hd;
+  float *hr = c->h + (size_t)r * d.H;
+  q2::attn_decode(d, l, q2::KVCache{c->kc, c->vc}, c->q32 + (size_t)r * nhd, nhd,
+                  q2::RowInfo{pos + r, seq + r}, 1, c->part, c->o32, nullptr, nhd, st);
+  q2::gemv_resid(w.wo, d.H, nhd, c->o32, nhd, 1, hr, d.H, st);
+  q2::gemv_swiglu(d, w, hr, 1, c->a32, d.I_pad, c->hp.rms_eps, st);
+  q2::gemv_resid(w.wd, d.H, d.I_pad, c->a32, d.I_pad, 1, hr, d.H, st);
+  q2::ArgmaxEpi am{logits, c->best, c->best_cnt, argmax};
+  q2::gemv_lmhead(d, c->lm_head, c->out_norm, hr, 1, c->normed, am, c->hp.rms_eps, st);
+  c->last_h = hr;
+  c->last_rows = 1;
+}
+
+// One pass of at most max_rows rows; `last` marks the pass that reads out.
+void prefill_pass(qwen2_ctx *c, int M, const int *tok, const int *pos, const int *seq, bool last,
+                  float *logits, int *argmax, hipStream_t st) {
+  const Dims &d = c->d;
+  const float eps = c->hp.rms_eps;
+  const int nhd = d.nh * d.hd;
+  const q2::KVCache kv{c->kc, c->vc};
+  const q2::RowInfo rows{pos, seq};
+  q2::embed_rows(c->tok_embd, d.H, d.V, tok, M, c->h, c->bad_flag, st);
+  const bool gemv = M <= kGemvRows;
+  for (int l = 0; l < d.L; ++l) {
+    const LayerW &w = c->layers[l];
+    const q2::QkvEpi e = qkv_epi(c, l, pos, seq);
+    if (gemv) {
+      q2::gemv_qkv(d, w, c->h, M, e, eps, st);
+    } else {
+      q2::rmsnorm_rows_f16(c->h, d.H, w.attn_norm, d.H, M, eps, c->x16, d.H, nullptr, st);
+      q2::gemm_qkv(d, w, c->x16, d.H, M, e, st);
+    }
+    if (l == d.L - 1) break;  // the last layer continues on the last row only
+    if (gemv) {
+      q2::attn_decode(d, l, kv, c->q32, nhd, rows, M, c->part, c->o32, nullptr, nhd, st);
+      q2::gemv_resid(w.wo, d.H, nhd, c->o32, nhd, M, c->h, d.H, st);
+      q2::gemv_swiglu(d, w, c->h, M, c->a32, d.I_pad, eps, st);
+      q2::gemv_resid(w.wd, d.H, d.I_pad, c->a32, d.I_pad, M, c->h, d.H, st);
+    } else {
+      q2::attn_prefill(d, l, kv, c->q32, nhd, rows, M, c->x16, nhd, st);
+      q2::gemm_resid(w.wo, d.H, nhd, c->x16, nhd, M, c->h, d.H, st);
+      q2::rmsnorm_rows_f16(c->h, d.H, w.ffn_norm, d.H, M, eps, c->x16, d.H, nullptr, st);
+      q2::gemm_swiglu(d, w, c->x16, d.H, M, c->a16, d.I_pad, st);
+      q2::gemm_resid(w.wd, d.H, d.I_pad, c->a16, d.I_pad, M, c->h, d.H, st);
+    }
+  }
+  if (last) tail_row(c, M - 1, pos, seq, logits, argmax, st);
+}
+
+}  // namespace
+
+extern "C" {
+
+int qwen2_prefill(qwen2_ctx *c, int32_t seq, const int32_t *tokens, const int32_t *positions,
+                  int32_t n, float *logits_dev, int32_t *argmax_dev, void *stream) {
+  if (!c) return QWEN2_E_ARG;
+  std::string msg;
+  int rc = q2::check_prefill(&c->hp, seq, tokens, positions, n, &msg);
+  if (rc) return set_err(c, rc, msg);
+  hipStream_t st = (hipStream_t)stream;
+  int *dtok, *dpos, *dseq;
+  rc = stage_rows(c, st, n, tokens, positions, nullptr, seq, &dtok, &dpos, &dseq);
+  if (rc) return rc;
+  for (int off = 0; off < n; off += c->max_rows) {
+    const int M = std::min(c->max_rows, n - off);
+    prefill_pass(c, M, dtok + off, dpos + off, dseq + off, off + M == n, logits_dev, argmax_dev, st);
+  }
+  HIP_TRY(c, hipGetLastError());
+  return QWEN2_OK;
+}
+
+int qwen2_decode(qwen2_ctx *c, int32_t B, const int32_t *seq_ids, const int32_t *tokens_dev,
+                 const int32_t *positions, float *logits_dev, int32_t *argmax_dev, void *stream) {
+  if (!c) return QWEN2_E_ARG;
+  std::string msg;
+  int rc = q2::check_decode(&c->hp, B, seq_ids, positions, &msg);
+  if (rc) return set_err(c, rc, msg);
+  if (!tokens_dev) return set_err(c, QWEN2_E_ARG, "null tokens_dev");
+  hipStream_t st = (hipStream_t)stream;
+  int *dpos, *dseq, *dunused;
+  rc = stage_rows(c, st, B, positions, seq_ids, positions, 0, &dpos, &dseq, &dunused);
+  if (rc) return rc;
+  const Dims &d = c->d;
+  const float eps = c->hp.rms_eps;
+  const int nhd = d.nh * d.hd;
+  const q2::KVCache kv{c->kc, c->vc};
+  const q2::RowInfo rows{dpos, dseq};
+  q2::embed_rows(c->tok_embd, d.H, d.V, tokens_dev, B, c->h, c->bad_flag, st);
+  const bool gemv = B <= kGemvRows;
+  for (int l = 0; l < d.L; ++l) {
+    const LayerW &w = c->layers[l];
+    const q2::QkvEpi e = qkv_epi(c, l, dpos, dseq);
+    if (gemv) {
+      q2::gemv_qkv(d, w, c->h, B, e, eps, st);
+      q2::attn_decode(d, l, kv, c->q32, nhd, rows, B, c->part, c->o32, nullptr, nhd, st);
+      q2::gemv_resid(w.wo, d.H, nhd, c->o32, nhd, B, c->h, d.H, st);
+      q2::gemv_swiglu(d, w, c->h, B, c->a32, d.I_pad, eps, st);
+      q2::gemv_resid(w.wd, d.H, d.I_pad, c->a32, d.I_pad, B, c->h, d.H, st);
+    } else {
+      q2::rmsnorm_rows_f16(c->h, d.H, w.attn_norm, d.H, B, eps, c->x16, d.H, nullptr, st);
+      q2::gemm_qkv(d, w, c->x16, d.H, B, e, st);
+      q2::attn_decode(d, l, kv, c->q32, nhd, rows, B, c->part, nullptr, c->x16, nhd, st);
+      q2::gemm_resid(w.wo, d.H, nhd, c->x16, nhd, B, c->h, d.H, st);
+      q2::rmsnorm_rows_f16(c->h, d.H, w.ffn_norm, d.H, B, eps, c->x16, d.H, nullptr, st);
+      q2::gemm_swiglu(d, w, c->x16, d.H, B, c->a16, d.I_pad, st);
+      q2::gemm_resid(w.wd, d.H, d.I_pad, c->a16, d.I_pad, B, c->h, d.H, st);
+    }
+  }
+  q2::ArgmaxEpi am{logits_dev, c->best, c->best_cnt, argmax_dev};
+  if (gemv) {
+    q2::gemv_lmhead(d, c->lm_head, c->out_norm, c->h, B, c->normed, am, eps, st);
+  } else {
+    q2::rmsnorm_rows_f16(c->h, d.H, c->out_norm, d.H, B, eps, c->x16, d.H, c->normed, st);
+    q2::gemm_lmhead(d, c->lm_head, c->x16, d.H, B, am, st);
+  }
+  c->last_h = c->h;
+  c->last_rows = B;
+  HIP_TRY(c, hipGetLastError());
+  return QWEN2_OK;
+}
+
+int qwen2_read_hidden(qwen2_ctx *c, int32_t which, float *out_dev, void *stream) {
+  if (!c || !out_dev || (which != 0 && which != 1)) return set_err(c, QWEN2_E_ARG, "bad argument");
+  if (!c->last_rows) return set_err(c, QWEN2_E_ARG, "no prefill or decode has run yet");
+  const float *src = which == 0 ? c->last_h : c->normed;
+  HIP_TRY(c, hipMemcpyAsync(out_dev, src, (size_t)c->last_rows * c->d.H * 4,
+                            hipMemcpyDeviceToDevice, (hipStream_t)stream));
+  return QWEN2_OK;
+}
+
+static int kv_copy(qwen2_ctx *c, int32_t layer, int32_t seq, int32_t pos0, int32_t n, float *k,
+                   float *v, void *stream, bool to_cache) {
+  if (!c || !k || !v || n <= 0 || layer < 0 || layer >= c->d.L)
+    return set_err(c, QWEN2_E_ARG, "bad kv copy argument");
+  if (seq < 0 || seq >= c->d.n_seq) return set_err(c, QWEN2_E_SEQ, "bad sequence slot");
+  if (pos0 < 0 || (long long)pos0 + n > c->d.n_ctx)
+    return set_err(c, QWEN2_E_POS, "kv range outside [0, n_ctx)");
+  const q2::KVCache kv{c->kc, c->vc};
+  const size_t bytes = (size_t)n * c->d.hd * 4;
+  for (int g = 0; g < c->d.nkv; ++g) {
+    float *ck = c->kc + kv.off(c->d, layer, seq, g, pos0);
+    float *cv = c->vc + kv.off(c->d, layer, seq, g, pos0);
+    float *bk = k + (size_t)g * n * c->d.hd, *bv = v + (size_t)g * n * c->d.hd;
+    hipStream_t st = (hipStream_t)stream;
+    if (to_cache) {
+      HIP_TRY(c, hipMemcpyAsync(ck, bk, bytes, hipMemcpyDeviceToDevice, st));
+      HIP_TRY(c, hipMemcpyAsync(cv, bv, bytes, hipMemcpyDeviceToDevice, st));
+    } else {
+      HIP_TRY(c, hipMemcpyAsync(bk, ck, bytes, hipMemcpyDeviceToDevice, st));
+      HIP_TRY(c, hipMemcpyAsync(bv, cv, bytes, hipMemcpyDeviceToDevice, st));
+    }
+  }
+  return QWEN2_OK;
+}
+
+int qwen2_kv_read(qwen2_ctx *c, int32_t layer, int32_t seq, int32_t pos0, int32_t n, float *k_dev,
+                  float *v_dev, void *stream) {
+  return kv_copy(c, layer, seq, pos0, n, k_dev, v_dev, stream, false);
+}
+
+int qwen2_kv_write(qwen2_ctx *c, int32_t layer, int32_t seq, int32_t pos0, int32_t n,
+                   const float *k_dev, const float *v_dev, void *stream) {
+  return kv_copy(c, layer, seq, pos0, n, (float *)k_dev, (float *)v_dev, stream, true);
+}
+
+int qwen2_sync_status(qwen2_ctx *c, void *stream) {
+  if (!c) return QWEN2_E_ARG;
+  HIP_TRY(c, hipStreamSynchronize((hipStream_t)stream));
+  unsigned flag = 0;
+  HIP_TRY(c, hipMemcpy(&flag, c->bad_flag, 4, hipMemcpyDeviceToHost));
+  if (flag) {
+    HIP_TRY(c, hipMemset(c->bad_flag, 0, 4));
+    return set_err(c, QWEN2_E_TOKEN, "a device-side token id was outside [0, n_vocab)");
+  }
+  return QWEN2_OK;
+}
+
+int qwen2_info(const qwen2_ctx *c, qwen2_info_t *o) {
+  if (!c || !o) return QWEN2_E_ARG;
+  memset(o, 0, sizeof *o);
+  o->weight_bytes_f16 = c->w_f16;
+  o->weight_bytes_f32 = c->w_f32;
+  o->weight_bytes_alloc = c->warena_bytes;
+  o->kv_bytes_per_pos = (uint64_t)c->d.L * 2 * c->d.nkv * c->d.hd * 4;
+  o->kv_bytes = (uint64_t)c->kv_elems * 2 * 4;
+  o->scratch_bytes = c->sarena_bytes;
+  o->n_ctx = c->d.n_ctx;
+  o->n_seq = c->d.n_seq;
+  o->max_rows = c->max_rows;
+  return QWEN2_OK;
+}
+
+const char *qwen2_last_error(const qwen2_ctx *c) {
+  return c ? c->err.c_str() : g_load_error.c_str();
+}
+
+void qwen2_free(qwen2_ctx *c) { release(c); }
+
+}  // extern "C"

@@ -1,0 +1,118 @@
+"""CPU checks of the C ABI: the library loads, exports every entry point the
+header declares, and its host-side validation (which runs before anything is
+enqueued) agrees with the oracle's error codes.  No GPU call is made."""
+import dataclasses
+import os
+import re
+
+import numpy as np
+import pytest
+
+import qwen2_synth as syn
+from oracle import qwen2_oracle as O
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "qwen2.h")
+
+q = pytest.importorskip("qwen2_decoder_forward_amd")
+if not os.path.exists(q.LIB_PATH):
+    pytest.skip("library not built", allow_module_level=True)
+
+
+def declared():
+    text = open(HEADER).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    return sorted(set(re.findall(r"\b(qwen2_[a-z_0-9]+)\s*\(", text)))
+
+
+def test_every_declared_symbol_is_exported():
+    L = q.lib()
+    names = declared()
+    assert len(names) >= 14, names
+    for n in names:
+        assert hasattr(L, n), n
+
+
+def test_struct_sizes_match_header_layout():
+    import ctypes
+    assert ctypes.sizeof(q.Hparams) == 11 * 4 + 3 * 4
+    assert ctypes.sizeof(q.LayerWeights) == 12 * 8
+    assert ctypes.sizeof(q.Weights) == 4 * 8
+
+
+def test_strerror_names():
+    for code, name in q.CODES.items():
+        assert q.qwen2_strerror(code)
+    assert "n_ctx" in q.qwen2_strerror(-3)
+
+
+def hp_for(shape, n_ctx=16, n_seq=2):
+    return q.make_hparams(shape, n_ctx, n_seq)
+
+
+def oracle_code(fn):
+    try:
+        fn()
+    except O.OracleError as e:
+        return e.code
+    return "OK"
+
+
+def test_validation_matches_oracle():
+    shape = syn.MODELS["tiny"]
+    hp = hp_for(shape)
+    ohp = O.hparams_for(shape, 16, 2)
+    orc = O.Qwen2Oracle(ohp, syn.make_weights(shape))
+    V = shape.n_vocab
+    prefill_cases = [
+        (0, [1, 2], [0, 1]), (0, [1, 2], [3, 16]), (0, [4], [-1]), (0, [4, V], [3, 4]),
+        (0, [-1], [0]), (2, [4], [3]), (-1, [4], [3]), (0, [4, 5, 6], [3, 5, 4]),
+        (0, [4, 5], [3, 3]), (0, [], []), (1, [V, 1], [99, 0]),  # token checked before position
+        (0, list(range(16)), list(range(16))),
+    ]
+    for seq, toks, pos in prefill_cases:
+        got = q.CODES[q.qwen2_check_prefill(hp, seq, toks, pos)]
+        want = oracle_code(lambda: orc._validate([seq] * len(toks), toks, pos, prefill=True)
+                           if toks else orc.prefill(seq, toks, pos))
+        assert got == want, (seq, toks, pos, got, want)
+    decode_cases = [
+        ([0, 1], [3, 4]), ([0, 0], [3, 4]), ([0, 2], [3, 4]), ([1], [16]), ([1], [-5]),
+        ([1, 0], [15, 0]), ([], []),
+    ]
+    for seqs, pos in decode_cases:
+        got = q.CODES[q.qwen2_check_decode(hp, seqs, pos)]
+        want = oracle_code(lambda: orc._validate(seqs, [0] * len(seqs), pos, prefill=False))
+        assert got == want, (seqs, pos, got, want)
+
+
+@pytest.mark.parametrize("change,ok", [
+    ({}, True),
+    ({"n_head_kv": 3}, False),             # n_head % n_head_kv
+    ({"head_dim": 32, "n_embd": 128}, False),  # head_dim not in {16, 64, 128}
+    ({"n_embd": 80, "n_head": 5}, False),  # n_embd % 64
+    ({"n_embd": 128}, False),              # n_embd != n_head * head_dim
+    ({"n_head": 36, "n_head_kv": 4, "n_embd": 576}, False),  # group 9 > 8
+    ({"n_head_kv": 4}, True),              # MHA
+    ({"n_head_kv": 1}, True),              # MQA, group 4
+])
+def test_hparams_checks(change, ok):
+    shape = dataclasses.replace(syn.MODELS["tiny"], **change)
+    hp = hp_for(shape)
+    assert (q.qwen2_check_hparams(hp) == 0) == ok
+
+
+def test_rope_style_and_bad_scalars_rejected():
+    hp = hp_for(syn.MODELS["tiny"])
+    hp.rope_style = 1
+    assert q.CODES[q.qwen2_check_hparams(hp)] == "E_HPARAMS"
+    hp = hp_for(syn.MODELS["tiny"])
+    hp.rope_theta = 0.0
+    assert q.CODES[q.qwen2_check_hparams(hp)] == "E_HPARAMS"
+    hp = hp_for(syn.MODELS["tiny"])
+    hp.n_ctx = 0
+    assert q.CODES[q.qwen2_check_hparams(hp)] == "E_HPARAMS"
+
+
+def test_real_shapes_are_accepted():
+    for name in syn.MODELS:
+        assert q.qwen2_check_hparams(hp_for(syn.MODELS[name], 4096, 1)) == 0, name

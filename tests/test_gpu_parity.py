@@ -1,0 +1,167 @@
+"""GPU parity: the HIP path through the C ABI against the CPU oracle.
+
+Bars: max-abs error <= 1e-4 * max|ref| on the tiny (f32-activation) path,
+<= 1e-2 * max|ref| for hidden states and logits elsewhere, greedy ids
+bit-exact wherever the oracle's top-2 logit margin exceeds 1e-2 (teacher
+forcing: both sides are fed the oracle's id).
+"""
+import dataclasses
+
+import numpy as np
+import pytest
+
+torch = pytest.importorskip("torch")
+if not torch.cuda.is_available():
+    pytest.skip("no GPU", allow_module_level=True)
+
+import qwen2_synth as syn  # noqa: E402
+from gpu_common import DEV, Pair, check, check_id, run_chain, say  # noqa: E402
+
+pytestmark = pytest.mark.gpu
+
+TINY = syn.MODELS["tiny"]
+TOL_F32 = 1e-4
+TOL = 1e-2
+
+
+@pytest.fixture(scope="module")
+def tiny_w():
+    return syn.make_weights(TINY)
+
+
+def test_tiny_prefill_and_greedy_decode(tiny_w):
+    """The tiny configuration: prompt 8 (GEMV path), 8 greedy steps, n_ctx 64."""
+    p = Pair(TINY, tiny_w, n_ctx=64)
+    run_chain(p, syn.make_prompt(TINY, 8), 8, TOL_F32, "tiny")
+    p.close()
+
+
+def test_tiny_kv_cache_matches_oracle(tiny_w):
+    p = Pair(TINY, tiny_w, n_ctx=64)
+    toks = syn.make_prompt(TINY, 8)
+    p.prefill(0, toks, np.arange(8))
+    nkv, hd = TINY.n_head_kv, TINY.head_dim
+    for l in range(TINY.n_layer):
+        k = torch.empty((nkv, 8, hd), device=DEV)
+        v = torch.empty((nkv, 8, hd), device=DEV)
+        p.m.kv_read(l, 0, 0, 8, k, v)
+        torch.cuda.synchronize()
+        check(k.cpu().numpy(), p.o.k_cache[0][l][:, :8], TOL_F32, f"K layer {l}")
+        check(v.cpu().numpy(), p.o.v_cache[0][l][:, :8], TOL_F32, f"V layer {l}")
+    p.close()
+
+
+@pytest.mark.parametrize("n", [9, 40, 100])
+def test_tiny_mfma_prefill_path(tiny_w, n):
+    """Prompts longer than 8 rows take the MFMA GEMM + flash-attention path
+    (f16 operands): ragged 32-row tiles, hd = 16."""
+    p = Pair(TINY, tiny_w, n_ctx=128)
+    run_chain(p, syn.make_prompt(TINY, n, 3), 3, TOL, f"tiny-mfma-{n}")
+    p.close()
+
+
+def test_tiny_positions_with_gaps_and_continuation(tiny_w):
+    """Positions are data: a continuation prefill and gapped positions (unwritten
+    slots read as zero on both sides)."""
+    p = Pair(TINY, tiny_w, n_ctx=64)
+    lg, _, r = p.prefill(0, [5, 6, 7], [0, 2, 5])
+    check(lg, r.logits[0], TOL_F32, "gapped prefill")
+    lg, _, r = p.prefill(0, [8, 9], [6, 7])
+    check(lg, r.logits[0], TOL_F32, "continuation prefill")
+    lg, _, r = p.decode([0], [10], [20])
+    check(lg[0], r.logits[0], TOL_F32, "decode after a gap")
+    p.close()
+
+
+def test_hard_error_at_n_ctx_leaves_cache_unchanged(tiny_w):
+    import qwen2_decoder_forward_amd as q
+    p = Pair(TINY, tiny_w, n_ctx=16)
+    toks = syn.make_prompt(TINY, 6)
+    p.prefill(0, toks, np.arange(6))
+    nkv, hd = TINY.n_head_kv, TINY.head_dim
+
+    def snapshot():
+        out = []
+        for l in range(TINY.n_layer):
+            k = torch.empty((nkv, 16, hd), device=DEV)
+            v = torch.empty((nkv, 16, hd), device=DEV)
+            p.m.kv_read(l, 0, 0, 16, k, v)
+            out += [k, v]
+        torch.cuda.synchronize()
+        return [t.cpu().numpy() for t in out]
+
+    before = snapshot()
+    for call, code in [
+        (lambda: p.m.prefill(0, [1, 2], [6, 16]), "E_POS"),
+        (lambda: p.m.prefill(0, [1], [-1]), "E_POS"),
+        (lambda: p.m.prefill(0, [TINY.n_vocab], [6]), "E_TOKEN"),
+        (lambda: p.m.prefill(0, [1, 2], [7, 7]), "E_ORDER"),
+        (lambda: p.m.prefill(1, [1], [6]), "E_SEQ"),
+        (lambda: p.m.decode([0], torch.zeros(1, dtype=torch.int32, device=DEV), [16]), "E_POS"),
+    ]:
+        with pytest.raises(q.Qwen2Error) as e:
+            call()
+        assert e.value.name == code
+    after = snapshot()
+    for a, b in zip(before, after):
+        assert np.array_equal(a, b)
+    # a valid call after the errors behaves as if they never happened
+    lg, _, r = p.decode([0], [3], [6])
+    check(lg[0], r.logits[0], TOL_F32, "decode after rejected calls")
+    p.close()
+
+
+def test_device_token_out_of_range_is_latched(tiny_w):
+    import qwen2_decoder_forward_amd as q
+    p = Pair(TINY, tiny_w, n_ctx=16)
+    bad = torch.tensor([TINY.n_vocab + 3], dtype=torch.int32, device=DEV)
+    p.m.decode([0], bad, [0], p.logits[:1], p.ids[:1])
+    assert q.CODES[p.m.sync_status()] == "E_TOKEN"
+    assert p.m.sync_status() == 0
+    p.close()
+
+
+@pytest.mark.parametrize("B", [3, 12])
+def test_batched_decode(tiny_w, B):
+    """Several sequences in one decode call: B <= 8 on the GEMV path, B > 8 on
+    the MFMA path; prefixes of different lengths."""
+    p = Pair(TINY, tiny_w, n_ctx=64, n_seq=16)
+    # B <= 8: prefixes of at most 8 rows keep the whole chain on the f32 path
+    lens = [2 + (5 * s) % 7 for s in range(B)] if B <= 8 else [3 + (7 * s) % 11 for s in range(B)]
+    for s in range(B):
+        p.prefill(s, syn.make_prompt(TINY, lens[s], 10 + s), np.arange(lens[s]))
+    seqs = list(range(B))[::-1]
+    toks = [int(t) for t in syn.make_prompt(TINY, B, 99)]
+    pos = [lens[s] for s in seqs]
+    lg, ids, r = p.decode(seqs, toks, pos)
+    tol = TOL_F32 if B <= 8 else TOL
+    for b in range(B):
+        check(lg[b], r.logits[b], tol, f"batched B={B} row {b}")
+        check_id(ids[b], r.logits[b], r.argmax[b], f"batched row {b}")
+    h = p.hidden(0, B)
+    check(h, r.layer_output, tol, "batched layer_output")
+    p.close()
+
+
+def test_multi_pass_prefill(tiny_w):
+    """A prompt longer than the 4096-row pass is processed in passes."""
+    p = Pair(TINY, tiny_w, n_ctx=8192)
+    toks = syn.make_prompt(TINY, 4100, 5)
+    lg, gid, r = p.prefill(0, toks, np.arange(4100))
+    check(lg, r.logits[0], TOL, "multi-pass prefill logits")
+    check_id(gid, r.logits[0], r.argmax[0], "multi-pass prefill")
+    p.close()
+
+
+HD128 = dataclasses.replace(syn.MODELS["qwen2-hd128"], name="hd128-narrow", n_layer=2,
+                            n_embd=896, n_head=7, n_head_kv=1, n_ff=640, n_vocab=4096)
+
+
+@pytest.mark.parametrize("n", [5, 70])
+def test_hd128_untied_group7(n):
+    """head_dim 128, group 7, untied lm_head (the large shape's kernels) at a
+    narrow width."""
+    w = syn.make_weights(HD128)
+    p = Pair(HD128, w, n_ctx=256)
+    run_chain(p, syn.make_prompt(HD128, n), 4, TOL if n > 8 else TOL_F32 * 10, f"hd128-{n}")
+    p.close()
