@@ -171,6 +171,26 @@ int qwen2_kv_write(qwen2_ctx *ctx, int32_t layer, int32_t seq, int32_t pos0, int
 int qwen2_sync_status(qwen2_ctx *ctx, void *stream);
 
 int qwen2_info(const qwen2_ctx *ctx, qwen2_info_t *out);
+
+/* Per-op timing for benchmarks.  While enabled for a set of op kinds, every
+ * launch of such an op is bracketed by two HIP events recorded on the call's
+ * stream (at most 16384 launches between two reads).  qwen2_prof_read waits
+ * for the recorded events, returns the number of timed launches and their
+ * summed duration in milliseconds for one kind, and forgets them.  The GEMV
+ * (M <= 8) and MFMA (M > 8) variants of an op share its kind. */
+enum {
+  QWEN2_OP_EMBED = 0,
+  QWEN2_OP_QKV = 1,      /* RMSNorm + fused QKV + bias + RoPE + KV store */
+  QWEN2_OP_ATTN = 2,     /* causal GQA attention */
+  QWEN2_OP_WO = 3,       /* WO + residual */
+  QWEN2_OP_GATEUP = 4,   /* RMSNorm + fused gate/up + SwiGLU */
+  QWEN2_OP_DOWN = 5,     /* down + residual */
+  QWEN2_OP_LMHEAD = 6,   /* final RMSNorm + lm_head + argmax */
+  QWEN2_OP_NORM = 7,     /* standalone RMSNorm of the MFMA path */
+  QWEN2_OP_COUNT = 8
+};
+int qwen2_prof_enable(qwen2_ctx *ctx, uint32_t op_mask /* bit k = op kind k; 0 disables */);
+int qwen2_prof_read(qwen2_ctx *ctx, int32_t op, int32_t *launches, double *total_ms);
 const char *qwen2_last_error(const qwen2_ctx *ctx); /* ctx may be NULL: last load error */
 const char *qwen2_strerror(int code);
 

@@ -19,13 +19,16 @@ __all__ = [
     "qwen2_check_hparams", "qwen2_check_prefill", "qwen2_check_decode", "qwen2_load",
     "qwen2_prefill", "qwen2_decode", "qwen2_read_hidden", "qwen2_kv_read", "qwen2_kv_write",
     "qwen2_sync_status", "qwen2_info", "qwen2_last_error", "qwen2_strerror", "qwen2_free",
-    "make_hparams", "Model",
+    "qwen2_prof_enable", "qwen2_prof_read", "OPS", "make_hparams", "Model",
 ]
 
 LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), "libqwen2_mi355x.so")
 
 CODES = {0: "OK", -1: "E_ARG", -2: "E_HPARAMS", -3: "E_POS", -4: "E_TOKEN", -5: "E_SEQ",
          -6: "E_ORDER", -7: "E_HIP", -8: "E_OOM"}
+
+# op kinds of qwen2_prof_enable / qwen2_prof_read (QWEN2_OP_* in the header)
+OPS = {"embed": 0, "qkv": 1, "attn": 2, "wo": 3, "gateup": 4, "down": 5, "lmhead": 6, "norm": 7}
 
 i32, f32, u16 = C.c_int32, C.c_float, C.c_uint16
 PF, PU16, PI32 = C.POINTER(C.c_float), C.POINTER(C.c_uint16), C.POINTER(C.c_int32)
@@ -90,6 +93,8 @@ def lib() -> C.CDLL:
             "qwen2_last_error": (C.c_char_p, [vp]),
             "qwen2_strerror": (C.c_char_p, [i32]),
             "qwen2_free": (None, [vp]),
+            "qwen2_prof_enable": (i32, [vp, C.c_uint32]),
+            "qwen2_prof_read": (i32, [vp, i32, PI32, C.POINTER(C.c_double)]),
         }
         for name, (res, args) in sig.items():
             f = getattr(L, name)
@@ -222,6 +227,21 @@ def qwen2_last_error(ctx: Optional[int] = None) -> str:
 
 def qwen2_strerror(code: int) -> str:
     return lib().qwen2_strerror(code).decode()
+
+
+def qwen2_prof_enable(ctx: int, ops) -> None:
+    """Time every launch of the given op kinds (names of OPS) with HIP events."""
+    mask = 0
+    for o in ops:
+        mask |= 1 << OPS[o]
+    _check(lib().qwen2_prof_enable(ctx, mask), ctx)
+
+
+def qwen2_prof_read(ctx: int, op: str):
+    """(launches, total milliseconds) of one op kind since the last read."""
+    n, ms = C.c_int32(), C.c_double()
+    _check(lib().qwen2_prof_read(ctx, OPS[op], C.byref(n), C.byref(ms)), ctx)
+    return n.value, ms.value
 
 
 def qwen2_free(ctx: int) -> None:

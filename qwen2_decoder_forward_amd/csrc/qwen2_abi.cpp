@@ -21,6 +21,7 @@ namespace {
 constexpr int kRing = 4;          // pinned staging slots for per-call row data
 constexpr int kGemvRows = 8;      // rows up to this use the f32 GEMV path
 constexpr int kMaxPassRows = 4096;  // rows per prefill pass
+constexpr int kProfMax = 16384;     // timed launches between two reads
 
 thread_local std::string g_load_error;
 
@@ -64,6 +65,11 @@ struct qwen2_ctx {
   // last read-out rows
   const float *last_h = nullptr;
   int last_rows = 0;
+  // per-op timing (qwen2_prof_*)
+  uint32_t prof_mask = 0;
+  std::vector<hipEvent_t> prof_ev;  // 2 per timed launch
+  int prof_used = 0;
+  std::vector<std::pair<int, int>> prof_rec;  // (op, event pair)
   std::string err;
 };
 
@@ -85,15 +91,16 @@ int set_err(qwen2_ctx *c, int code, const std::string &m) {
 
 void release(qwen2_ctx *c) {
   if (!c) return;
-  hipDeviceSynchronize();
-  if (c->warena) hipFree(c->warena);
-  if (c->kc) hipFree(c->kc);
-  if (c->vc) hipFree(c->vc);
-  if (c->rope_cos) hipFree(c->rope_cos);
-  if (c->sarena) hipFree(c->sarena);
-  if (c->pinned) hipHostFree(c->pinned);
+  (void)hipDeviceSynchronize();
+  if (c->warena) (void)hipFree(c->warena);
+  if (c->kc) (void)hipFree(c->kc);
+  if (c->vc) (void)hipFree(c->vc);
+  if (c->rope_cos) (void)hipFree(c->rope_cos);
+  if (c->sarena) (void)hipFree(c->sarena);
+  if (c->pinned) (void)hipHostFree(c->pinned);
   for (auto &e : c->ev)
-    if (e) hipEventDestroy(e);
+    if (e) (void)hipEventDestroy(e);
+  for (auto &e : c->prof_ev) (void)hipEventDestroy(e);
   delete c;
 }
 
@@ -342,6 +349,30 @@ int stage_rows(qwen2_ctx *c, hipStream_t st, int n, const int32_t *f0, const int
   return QWEN2_OK;
 }
 
+// Brackets one op launch with two events when that op kind is being timed.
+struct OpTimer {
+  qwen2_ctx *c;
+  int op, idx = -1;
+  hipStream_t st;
+  OpTimer(qwen2_ctx *c_, int op_, hipStream_t st_) : c(c_), op(op_), st(st_) {
+    if ((c->prof_mask >> op) & 1u && c->prof_used < kProfMax) {
+      idx = c->prof_used++;
+      (void)hipEventRecord(c->prof_ev[2 * idx], st);
+    }
+  }
+  ~OpTimer() {
+    if (idx >= 0) {
+      (void)hipEventRecord(c->prof_ev[2 * idx + 1], st);
+      c->prof_rec.emplace_back(op, idx);
+    }
+  }
+};
+#define TIMED(op, call)             \
+  do {                              \
+    OpTimer t_(c, (op), st);        \
+    call;                           \
+  } while (0)
+
 q2::QkvEpi qkv_epi(qwen2_ctx *c, int l, const int *pos, const int *seq) {
   q2::QkvEpi e;
   e.bias = c->layers[l].bqkv;
@@ -363,13 +394,15 @@ void tail_row(qwen2_ctx *c, int r, const int *pos, const int *seq, float *logits
   const LayerW &w = c->layers[l];
   const int nhd = d.nh * d.hd;
   float *hr = c->h + (size_t)r * d.H;
-  q2::attn_decode(d, l, q2::KVCache{c->kc, c->vc}, c->q32 + (size_t)r * nhd, nhd,
-                  q2::RowInfo{pos + r, seq + r}, 1, c->part, c->o32, nullptr, nhd, st);
-  q2::gemv_resid(w.wo, d.H, nhd, c->o32, nhd, 1, hr, d.H, st);
-  q2::gemv_swiglu(d, w, hr, 1, c->a32, d.I_pad, c->hp.rms_eps, st);
-  q2::gemv_resid(w.wd, d.H, d.I_pad, c->a32, d.I_pad, 1, hr, d.H, st);
+  TIMED(QWEN2_OP_ATTN, q2::attn_decode(d, l, q2::KVCache{c->kc, c->vc}, c->q32 + (size_t)r * nhd,
+                                       nhd, q2::RowInfo{pos + r, seq + r}, 1, c->part, c->o32,
+                                       nullptr, nhd, st));
+  TIMED(QWEN2_OP_WO, q2::gemv_resid(w.wo, d.H, nhd, c->o32, nhd, 1, hr, d.H, st));
+  TIMED(QWEN2_OP_GATEUP, q2::gemv_swiglu(d, w, hr, 1, c->a32, d.I_pad, c->hp.rms_eps, st));
+  TIMED(QWEN2_OP_DOWN, q2::gemv_resid(w.wd, d.H, d.I_pad, c->a32, d.I_pad, 1, hr, d.H, st));
   q2::ArgmaxEpi am{logits, c->best, c->best_cnt, argmax};
-  q2::gemv_lmhead(d, c->lm_head, c->out_norm, hr, 1, c->normed, am, c->hp.rms_eps, st);
+  TIMED(QWEN2_OP_LMHEAD,
+        q2::gemv_lmhead(d, c->lm_head, c->out_norm, hr, 1, c->normed, am, c->hp.rms_eps, st));
   c->last_h = hr;
   c->last_rows = 1;
 }
@@ -382,29 +415,33 @@ void prefill_pass(qwen2_ctx *c, int M, const int *tok, const int *pos, const int
   const int nhd = d.nh * d.hd;
   const q2::KVCache kv{c->kc, c->vc};
   const q2::RowInfo rows{pos, seq};
-  q2::embed_rows(c->tok_embd, d.H, d.V, tok, M, c->h, c->bad_flag, st);
+  TIMED(QWEN2_OP_EMBED, q2::embed_rows(c->tok_embd, d.H, d.V, tok, M, c->h, c->bad_flag, st));
   const bool gemv = M <= kGemvRows;
   for (int l = 0; l < d.L; ++l) {
     const LayerW &w = c->layers[l];
     const q2::QkvEpi e = qkv_epi(c, l, pos, seq);
     if (gemv) {
-      q2::gemv_qkv(d, w, c->h, M, e, eps, st);
+      TIMED(QWEN2_OP_QKV, q2::gemv_qkv(d, w, c->h, M, e, eps, st));
     } else {
-      q2::rmsnorm_rows_f16(c->h, d.H, w.attn_norm, d.H, M, eps, c->x16, d.H, nullptr, st);
-      q2::gemm_qkv(d, w, c->x16, d.H, M, e, st);
+      TIMED(QWEN2_OP_NORM, q2::rmsnorm_rows_f16(c->h, d.H, w.attn_norm, d.H, M, eps, c->x16, d.H,
+                                                nullptr, st));
+      TIMED(QWEN2_OP_QKV, q2::gemm_qkv(d, w, c->x16, d.H, M, e, st));
     }
     if (l == d.L - 1) break;  // the last layer continues on the last row only
     if (gemv) {
-      q2::attn_decode(d, l, kv, c->q32, nhd, rows, M, c->part, c->o32, nullptr, nhd, st);
-      q2::gemv_resid(w.wo, d.H, nhd, c->o32, nhd, M, c->h, d.H, st);
-      q2::gemv_swiglu(d, w, c->h, M, c->a32, d.I_pad, eps, st);
-      q2::gemv_resid(w.wd, d.H, d.I_pad, c->a32, d.I_pad, M, c->h, d.H, st);
+      TIMED(QWEN2_OP_ATTN,
+            q2::attn_decode(d, l, kv, c->q32, nhd, rows, M, c->part, c->o32, nullptr, nhd, st));
+      TIMED(QWEN2_OP_WO, q2::gemv_resid(w.wo, d.H, nhd, c->o32, nhd, M, c->h, d.H, st));
+      TIMED(QWEN2_OP_GATEUP, q2::gemv_swiglu(d, w, c->h, M, c->a32, d.I_pad, eps, st));
+      TIMED(QWEN2_OP_DOWN, q2::gemv_resid(w.wd, d.H, d.I_pad, c->a32, d.I_pad, M, c->h, d.H, st));
     } else {
-      q2::attn_prefill(d, l, kv, c->q32, nhd, rows, M, c->x16, nhd, st);
-      q2::gemm_resid(w.wo, d.H, nhd, c->x16, nhd, M, c->h, d.H, st);
-      q2::rmsnorm_rows_f16(c->h, d.H, w.ffn_norm, d.H, M, eps, c->x16, d.H, nullptr, st);
-      q2::gemm_swiglu(d, w, c->x16, d.H, M, c->a16, d.I_pad, st);
-      q2::gemm_resid(w.wd, d.H, d.I_pad, c->a16, d.I_pad, M, c->h, d.H, st);
+      TIMED(QWEN2_OP_ATTN, q2::attn_prefill(d, l, kv, c->q32, nhd, rows, M, c->x16, nhd, st));
+      TIMED(QWEN2_OP_WO, q2::gemm_resid(w.wo, d.H, nhd, c->x16, nhd, M, c->h, d.H, st));
+      TIMED(QWEN2_OP_NORM, q2::rmsnorm_rows_f16(c->h, d.H, w.ffn_norm, d.H, M, eps, c->x16, d.H,
+                                                nullptr, st));
+      TIMED(QWEN2_OP_GATEUP, q2::gemm_swiglu(d, w, c->x16, d.H, M, c->a16, d.I_pad, st));
+      TIMED(QWEN2_OP_DOWN,
+            q2::gemm_resid(w.wd, d.H, d.I_pad, c->a16, d.I_pad, M, c->h, d.H, st));
     }
   }
   if (last) tail_row(c, M - 1, pos, seq, logits, argmax, st);
@@ -448,33 +485,41 @@ int qwen2_decode(qwen2_ctx *c, int32_t B, const int32_t *seq_ids, const int32_t 
   const int nhd = d.nh * d.hd;
   const q2::KVCache kv{c->kc, c->vc};
   const q2::RowInfo rows{dpos, dseq};
-  q2::embed_rows(c->tok_embd, d.H, d.V, tokens_dev, B, c->h, c->bad_flag, st);
+  TIMED(QWEN2_OP_EMBED,
+        q2::embed_rows(c->tok_embd, d.H, d.V, tokens_dev, B, c->h, c->bad_flag, st));
   const bool gemv = B <= kGemvRows;
   for (int l = 0; l < d.L; ++l) {
     const LayerW &w = c->layers[l];
     const q2::QkvEpi e = qkv_epi(c, l, dpos, dseq);
     if (gemv) {
-      q2::gemv_qkv(d, w, c->h, B, e, eps, st);
-      q2::attn_decode(d, l, kv, c->q32, nhd, rows, B, c->part, c->o32, nullptr, nhd, st);
-      q2::gemv_resid(w.wo, d.H, nhd, c->o32, nhd, B, c->h, d.H, st);
-      q2::gemv_swiglu(d, w, c->h, B, c->a32, d.I_pad, eps, st);
-      q2::gemv_resid(w.wd, d.H, d.I_pad, c->a32, d.I_pad, B, c->h, d.H, st);
+      TIMED(QWEN2_OP_QKV, q2::gemv_qkv(d, w, c->h, B, e, eps, st));
+      TIMED(QWEN2_OP_ATTN,
+            q2::attn_decode(d, l, kv, c->q32, nhd, rows, B, c->part, c->o32, nullptr, nhd, st));
+      TIMED(QWEN2_OP_WO, q2::gemv_resid(w.wo, d.H, nhd, c->o32, nhd, B, c->h, d.H, st));
+      TIMED(QWEN2_OP_GATEUP, q2::gemv_swiglu(d, w, c->h, B, c->a32, d.I_pad, eps, st));
+      TIMED(QWEN2_OP_DOWN, q2::gemv_resid(w.wd, d.H, d.I_pad, c->a32, d.I_pad, B, c->h, d.H, st));
     } else {
-      q2::rmsnorm_rows_f16(c->h, d.H, w.attn_norm, d.H, B, eps, c->x16, d.H, nullptr, st);
-      q2::gemm_qkv(d, w, c->x16, d.H, B, e, st);
-      q2::attn_decode(d, l, kv, c->q32, nhd, rows, B, c->part, nullptr, c->x16, nhd, st);
-      q2::gemm_resid(w.wo, d.H, nhd, c->x16, nhd, B, c->h, d.H, st);
-      q2::rmsnorm_rows_f16(c->h, d.H, w.ffn_norm, d.H, B, eps, c->x16, d.H, nullptr, st);
-      q2::gemm_swiglu(d, w, c->x16, d.H, B, c->a16, d.I_pad, st);
-      q2::gemm_resid(w.wd, d.H, d.I_pad, c->a16, d.I_pad, B, c->h, d.H, st);
+      TIMED(QWEN2_OP_NORM, q2::rmsnorm_rows_f16(c->h, d.H, w.attn_norm, d.H, B, eps, c->x16, d.H,
+                                                nullptr, st));
+      TIMED(QWEN2_OP_QKV, q2::gemm_qkv(d, w, c->x16, d.H, B, e, st));
+      TIMED(QWEN2_OP_ATTN,
+            q2::attn_decode(d, l, kv, c->q32, nhd, rows, B, c->part, nullptr, c->x16, nhd, st));
+      TIMED(QWEN2_OP_WO, q2::gemm_resid(w.wo, d.H, nhd, c->x16, nhd, B, c->h, d.H, st));
+      TIMED(QWEN2_OP_NORM, q2::rmsnorm_rows_f16(c->h, d.H, w.ffn_norm, d.H, B, eps, c->x16, d.H,
+                                                nullptr, st));
+      TIMED(QWEN2_OP_GATEUP, q2::gemm_swiglu(d, w, c->x16, d.H, B, c->a16, d.I_pad, st));
+      TIMED(QWEN2_OP_DOWN,
+            q2::gemm_resid(w.wd, d.H, d.I_pad, c->a16, d.I_pad, B, c->h, d.H, st));
     }
   }
   q2::ArgmaxEpi am{logits_dev, c->best, c->best_cnt, argmax_dev};
   if (gemv) {
-    q2::gemv_lmhead(d, c->lm_head, c->out_norm, c->h, B, c->normed, am, eps, st);
+    TIMED(QWEN2_OP_LMHEAD,
+          q2::gemv_lmhead(d, c->lm_head, c->out_norm, c->h, B, c->normed, am, eps, st));
   } else {
-    q2::rmsnorm_rows_f16(c->h, d.H, c->out_norm, d.H, B, eps, c->x16, d.H, c->normed, st);
-    q2::gemm_lmhead(d, c->lm_head, c->x16, d.H, B, am, st);
+    TIMED(QWEN2_OP_NORM, q2::rmsnorm_rows_f16(c->h, d.H, c->out_norm, d.H, B, eps, c->x16, d.H,
+                                              c->normed, st));
+    TIMED(QWEN2_OP_LMHEAD, q2::gemm_lmhead(d, c->lm_head, c->x16, d.H, B, am, st));
   }
   c->last_h = c->h;
   c->last_rows = B;
@@ -550,6 +595,40 @@ int qwen2_info(const qwen2_ctx *c, qwen2_info_t *o) {
   o->n_ctx = c->d.n_ctx;
   o->n_seq = c->d.n_seq;
   o->max_rows = c->max_rows;
+  return QWEN2_OK;
+}
+
+int qwen2_prof_enable(qwen2_ctx *c, uint32_t mask) {
+  if (!c) return QWEN2_E_ARG;
+  if (mask && c->prof_ev.empty()) {
+    c->prof_ev.resize(2 * kProfMax);
+    for (auto &e : c->prof_ev) HIP_TRY(c, hipEventCreate(&e));
+  }
+  c->prof_mask = mask;
+  return QWEN2_OK;
+}
+
+int qwen2_prof_read(qwen2_ctx *c, int32_t op, int32_t *launches, double *total_ms) {
+  if (!c || !launches || !total_ms || op < 0 || op >= QWEN2_OP_COUNT)
+    return set_err(c, QWEN2_E_ARG, "bad prof_read argument");
+  int n = 0;
+  double ms = 0.0;
+  std::vector<std::pair<int, int>> keep;
+  for (const auto &r : c->prof_rec) {
+    if (r.first != op) {
+      keep.push_back(r);
+      continue;
+    }
+    HIP_TRY(c, hipEventSynchronize(c->prof_ev[2 * r.second + 1]));
+    float t = 0.f;
+    HIP_TRY(c, hipEventElapsedTime(&t, c->prof_ev[2 * r.second], c->prof_ev[2 * r.second + 1]));
+    ms += t;
+    ++n;
+  }
+  c->prof_rec.swap(keep);
+  if (c->prof_rec.empty()) c->prof_used = 0;
+  *launches = n;
+  *total_ms = ms;
   return QWEN2_OK;
 }
 
