@@ -11,13 +11,13 @@
 namespace q2 {
 
 // ------------------------------------------------------------------ decode
-// Split-KV: one block per (64-key chunk, KV head, query row).  A block scores
-// its chunk for all `group` query heads, keeps the chunk's max, exp-sum and
-// un-normalised output, and the last block of a (row, KV head) merges the
-// chunks with the usual log-sum-exp rescaling.  Blocks past the row's
-// position exit at once (the grid covers n_ctx so it never depends on the
-// call's positions).
-constexpr int kChunk = 64;
+// One block per (split of up to 256 keys, KV head, query row).  A block walks
+// its split in 64-key tiles with an online softmax for all `group` query
+// heads of the KV head, so each K/V tile is read once per KV head.  With a
+// single split the block writes the normalised output itself; otherwise it
+// writes (max, exp-sum, un-normalised output) and k_attn_merge combines the
+// splits with log-sum-exp rescaling.  No block waits on another.
+constexpr int kTile = 64;
 
 struct AttnDecP {
   Dims d;
@@ -33,33 +33,43 @@ struct AttnDecP {
   float scale;
 };
 
-template <int HD>
+template <int HD, bool DIRECT>
 __global__ __launch_bounds__(256) void k_attn_decode(AttnDecP p) {
-  constexpr int C = kChunk;
-  constexpr int KS = HD + 1;  // padded row stride of K in LDS
-  __shared__ __attribute__((aligned(16))) float sK[C * KS];
+  constexpr int KS = HD + 1;  // padded K row in LDS (conflict-free column walk)
+  constexpr int PER = (8 * HD + 255) / 256;
+  __shared__ __attribute__((aligned(16))) float sK[kTile * KS];
   __shared__ __attribute__((aligned(16))) float sQ[8 * HD];
-  __shared__ __attribute__((aligned(16))) float sP[8 * C];
-  __shared__ int s_last;
+  __shared__ float sP[8 * kTile];
+  __shared__ float sM[8], sL[8], sA[8];
 
   const int tid = threadIdx.x;
   const int c = blockIdx.x, g = blockIdx.y, m = blockIdx.z;
   const int G = p.d.group;
-  const int nkv = p.d.nkv;
   const int pos = p.rows.pos[m];
   const int seq = p.rows.seq[m];
   const int P = pos + 1;
-  const int k0 = c * C;
-  const int nk = min(C, P - k0);
-  const int rec = G * (HD + 2);
-  float *part = p.part.buf + (((size_t)m * nkv + g) * p.part.n_chunks + c) * rec;
+  const int kb = c * kSplitKeys;
+  const int ke = min(P, kb + kSplitKeys);
+  if (kb >= ke) return;  // uniform across the block
 
-  if (nk > 0) {
-    const float *qrow = p.q + (size_t)m * p.ldq + (size_t)g * G * HD;
-    for (int i = tid; i < G * HD; i += 256) sQ[i] = qrow[i] * p.scale;
-    const float *kb = p.kv.k + p.kv.off(p.d, p.layer, seq, g, k0);
+  const float *qrow = p.q + (size_t)m * p.ldq + (size_t)g * G * HD;
+  for (int i = tid; i < G * HD; i += 256) sQ[i] = qrow[i] * p.scale;
+  if (tid < 8) {
+    sM[tid] = kNegInf;
+    sL[tid] = 0.f;
+  }
+  float o[PER];
+#pragma unroll
+  for (int i = 0; i < PER; ++i) o[i] = 0.f;
+  const float *kbase = p.kv.k + p.kv.off(p.d, p.layer, seq, g, 0);
+  const float *vbase = p.kv.v + p.kv.off(p.d, p.layer, seq, g, 0);
+  const int j = tid & 63, wv = tid >> 6;
+
+  for (int k0 = kb; k0 < ke; k0 += kTile) {
+    const int nk = min(kTile, ke - k0);
+    __syncthreads();
     for (int i = tid * 4; i < nk * HD; i += 1024) {
-      const f4 v = *(const f4 *)(kb + i);
+      const f4 v = *(const f4 *)(kbase + (size_t)k0 * HD + i);
       const int r = i / HD, cc = i - r * HD;
       sK[r * KS + cc + 0] = v.x;
       sK[r * KS + cc + 1] = v.y;
@@ -67,9 +77,7 @@ __global__ __launch_bounds__(256) void k_attn_decode(AttnDecP p) {
       sK[r * KS + cc + 3] = v.w;
     }
     __syncthreads();
-
-    const int j = tid & 63, wv = tid >> 6;
-    float s[2] = {kNegInf, kNegInf};
+    float s0 = kNegInf, s1 = kNegInf;
     if (j < nk) {
       float a0 = 0.f, a1 = 0.f;
       const bool h1 = wv + 4 < G;
@@ -79,48 +87,80 @@ __global__ __launch_bounds__(256) void k_attn_decode(AttnDecP p) {
         a0 = fmaf(sQ[wv * HD + dd], kd, a0);
         if (h1) a1 = fmaf(sQ[(wv + 4) * HD + dd], kd, a1);
       }
-      s[0] = a0;
-      s[1] = a1;
+      s0 = a0;
+      s1 = a1;
     }
 #pragma unroll
     for (int i = 0; i < 2; ++i) {
       const int h = wv + 4 * i;
-      if (h < G) {  // uniform across the wave
-        const float mx = wave_max(s[i]);
-        const float e = (j < nk) ? __expf(s[i] - mx) : 0.f;
+      if (h < G) {  // uniform across the wave: wave wv owns heads wv and wv + 4
+        const float s = i ? s1 : s0;
+        const float m_old = sM[h];
+        const float m_new = fmaxf(m_old, wave_max(s));
+        const float e = (j < nk) ? __expf(s - m_new) : 0.f;
         const float sum = wave_sum(e);
-        sP[h * C + j] = e;
+        sP[h * kTile + j] = e;
         if (j == 0) {
-          part[h] = mx;
-          part[G + h] = sum;
+          const float alpha = __expf(m_old - m_new);
+          sA[h] = alpha;
+          sL[h] = sL[h] * alpha + sum;
+          sM[h] = m_new;
         }
       }
     }
     __syncthreads();
-    const float *vb = p.kv.v + p.kv.off(p.d, p.layer, seq, g, k0);
-    for (int i = tid * 4; i < nk * HD; i += 1024) *(f4 *)(sK + i) = *(const f4 *)(vb + i);
+    for (int i = tid * 4; i < nk * HD; i += 1024)
+      *(f4 *)(sK + i) = *(const f4 *)(vbase + (size_t)k0 * HD + i);
     __syncthreads();
-    for (int idx = tid; idx < G * HD; idx += 256) {
-      const int h = idx / HD, dd = idx - h * HD;
-      float acc = 0.f;
-      for (int jj = 0; jj < nk; ++jj) acc = fmaf(sP[h * C + jj], sK[jj * HD + dd], acc);
-      part[2 * G + idx] = acc;
+#pragma unroll
+    for (int i = 0; i < PER; ++i) {
+      const int idx = tid + 256 * i;
+      if (idx < G * HD) {
+        const int h = idx / HD, dd = idx - h * HD;
+        float acc = o[i] * sA[h];
+        for (int jj = 0; jj < nk; ++jj) acc = fmaf(sP[h * kTile + jj], sK[jj * HD + dd], acc);
+        o[i] = acc;
+      }
     }
   }
 
-  // The last block of this (row, KV head) merges the chunks.
-  __threadfence();
-  __syncthreads();
-  if (tid == 0) {
-    const unsigned prev = atomicAdd(&p.part.counters[m * nkv + g], 1u);
-    s_last = (prev == gridDim.x - 1);
+  if (DIRECT) {
+#pragma unroll
+    for (int i = 0; i < PER; ++i) {
+      const int idx = tid + 256 * i;
+      if (idx < G * HD) {
+        const float v = o[i] / sL[idx / HD];
+        const size_t oi = (size_t)m * p.ldo + (size_t)g * G * HD + idx;
+        if (p.o32) p.o32[oi] = v;
+        if (p.o16) p.o16[oi] = (_Float16)v;
+      }
+    }
+  } else {
+    const int rec = G * (HD + 2);
+    float *part = p.part.buf + (((size_t)m * p.d.nkv + g) * p.part.n_chunks + c) * rec;
+    if (tid < G) {
+      part[tid] = sM[tid];
+      part[G + tid] = sL[tid];
+    }
+#pragma unroll
+    for (int i = 0; i < PER; ++i) {
+      const int idx = tid + 256 * i;
+      if (idx < G * HD) part[2 * G + idx] = o[i];
+    }
   }
-  __syncthreads();
-  if (!s_last) return;
-  __threadfence();
-  const int nch = (P + C - 1) / C;
-  const float *base = p.part.buf + ((size_t)m * nkv + g) * p.part.n_chunks * rec;
-  for (int idx = tid; idx < G * HD; idx += 256) {
+}
+
+// Combines the splits of each (row, KV head): O = sum_c e^(m_c - M) o_c /
+// sum_c e^(m_c - M) l_c with M the largest split maximum.
+template <int HD>
+__global__ __launch_bounds__(256) void k_attn_merge(AttnDecP p) {
+  const int g = blockIdx.x, m = blockIdx.y;
+  const int G = p.d.group;
+  const int P = p.rows.pos[m] + 1;
+  const int nch = (P + kSplitKeys - 1) / kSplitKeys;
+  const int rec = G * (HD + 2);
+  const float *base = p.part.buf + ((size_t)m * p.d.nkv + g) * p.part.n_chunks * rec;
+  for (int idx = threadIdx.x; idx < G * HD; idx += 256) {
     const int h = idx / HD;
     float mx = kNegInf;
     for (int cc = 0; cc < nch; ++cc) mx = fmaxf(mx, base[(size_t)cc * rec + h]);
@@ -131,23 +171,31 @@ __global__ __launch_bounds__(256) void k_attn_decode(AttnDecP p) {
       l = fmaf(r[G + h], wgt, l);
       acc = fmaf(r[2 * G + idx], wgt, acc);
     }
-    const float o = acc / l;
+    const float v = acc / l;
     const size_t oi = (size_t)m * p.ldo + (size_t)g * G * HD + idx;
-    if (p.o32) p.o32[oi] = o;
-    if (p.o16) p.o16[oi] = (_Float16)o;
+    if (p.o32) p.o32[oi] = v;
+    if (p.o16) p.o16[oi] = (_Float16)v;
   }
-  if (tid == 0) atomicExch(&p.part.counters[m * nkv + g], 0u);
+}
+
+template <int HD>
+static void attn_decode_hd(const AttnDecP &p, int M, int n_split, hipStream_t st) {
+  if (n_split <= 1) {
+    hipLaunchKernelGGL((k_attn_decode<HD, true>), dim3(1, p.d.nkv, M), dim3(256), 0, st, p);
+  } else {
+    hipLaunchKernelGGL((k_attn_decode<HD, false>), dim3(n_split, p.d.nkv, M), dim3(256), 0, st, p);
+    hipLaunchKernelGGL((k_attn_merge<HD>), dim3(p.d.nkv, M), dim3(256), 0, st, p);
+  }
 }
 
 void attn_decode(const Dims &d, int layer, const KVCache &kv, const float *q, int ldq,
-                 RowInfo rows, int M, const AttnPartials &part, float *o32, _Float16 *o16,
-                 int ldo, hipStream_t st) {
+                 RowInfo rows, int M, int n_split, const AttnPartials &part, float *o32,
+                 _Float16 *o16, int ldo, hipStream_t st) {
   AttnDecP p{d, layer, kv, q, ldq, rows, part, o32, o16, ldo, 1.0f / sqrtf((float)d.hd)};
-  dim3 grid(part.n_chunks, d.nkv, M);
   switch (d.hd) {
-    case 16: hipLaunchKernelGGL(k_attn_decode<16>, grid, dim3(256), 0, st, p); break;
-    case 64: hipLaunchKernelGGL(k_attn_decode<64>, grid, dim3(256), 0, st, p); break;
-    default: hipLaunchKernelGGL(k_attn_decode<128>, grid, dim3(256), 0, st, p); break;
+    case 16: attn_decode_hd<16>(p, M, n_split, st); break;
+    case 64: attn_decode_hd<64>(p, M, n_split, st); break;
+    default: attn_decode_hd<128>(p, M, n_split, st); break;
   }
 }
 

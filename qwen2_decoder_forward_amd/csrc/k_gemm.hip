@@ -98,7 +98,7 @@ __global__ __launch_bounds__(256) void k_gemm(GemmP p) {
   // ---------------------------------------------------------------- epilogue
   if (EPI == G_LMHEAD) {
     __shared__ unsigned long long sBest[2][BM];
-    __shared__ int s_last;
+    float *logits = *p.am.logits;
     unsigned long long kb[2][16];
 #pragma unroll
     for (int i = 0; i < 2; ++i)
@@ -111,7 +111,7 @@ __global__ __launch_bounds__(256) void k_gemm(GemmP p) {
           const int n = n0 + wn * 64 + j * 32 + l32;
           if (m < M && n < N) {
             const float v = acc[i][j][r];
-            if (p.am.logits) p.am.logits[(size_t)m * N + n] = v;
+            if (logits) logits[(size_t)m * N + n] = v;
             const unsigned long long key = argmax_key(v, n);
             b = key > b ? key : b;
           }
@@ -133,18 +133,6 @@ __global__ __launch_bounds__(256) void k_gemm(GemmP p) {
     if (tid < BM && m0 + tid < M) {
       const unsigned long long b = sBest[0][tid] > sBest[1][tid] ? sBest[0][tid] : sBest[1][tid];
       atomicMax(&p.am.best[m0 + tid], b);
-    }
-    __threadfence();
-    __syncthreads();
-    if (tid == 0) s_last = (atomicAdd(p.am.counter, 1u) == gridDim.x * gridDim.y - 1);
-    __syncthreads();
-    if (s_last) {
-      __threadfence();
-      for (int m = tid; m < M; m += 256) {
-        const unsigned long long b = atomicExch(&p.am.best[m], 0ull);
-        if (p.am.out) p.am.out[m] = argmax_index(b);
-      }
-      if (tid == 0) atomicExch(p.am.counter, 0u);
     }
     return;
   }
@@ -215,6 +203,7 @@ void gemm_lmhead(const Dims &d, const uint16_t *W, const _Float16 *x, int lda, i
   GemmP p = base(x, lda, M, W, d.V, d.H);
   p.am = e;
   hipLaunchKernelGGL(k_gemm<G_LMHEAD>, grid_for(M, d.V), dim3(256), 0, st, p);
+  argmax_finalize(e, M, st);
 }
 
 }  // namespace q2

@@ -1,16 +1,21 @@
 // GEMV kernels of the decode path (M <= 8 rows, f32 activations).
 //
-// Every weight byte is read exactly once per call: a wavefront owns R output
-// rows and its 64 lanes stream those rows with 16-byte loads (8 halves per
-// lane, 1 KiB per wave instruction), converting binary16 to f32 in registers
-// (weights are never expanded in memory).  The activation rows are read
-// through the cache by every wave.  Partial sums are reduced across the wave
-// with xor shuffles, then the epilogue of the fused op runs on one lane per
-// output.  Epilogues:
-//   QKV    RMSNorm prologue, bias, RoPE, q write and K/V cache store
-//   RESID  h += W x           (WO and down projections)
-//   SWIGLU RMSNorm prologue, a = silu(gate) * up on pair-packed rows
-//   LMHEAD RMSNorm prologue, logits and greedy argmax (packed 64-bit max)
+// Every weight byte is read exactly once per call.  A wavefront owns R
+// output rows; its 64 lanes cover a row with 16-byte loads (8 halves per
+// lane, 1 KiB per wave instruction).  All of a wave's weight loads for a
+// K batch (KB chunks of 512 halves) are issued before anything else, so the
+// HBM latency overlaps the activation loads and the RMSNorm prologue; the
+// binary16 values are converted to f32 in registers (weights are never
+// expanded in memory).  The activation chunks a lane loads are exactly the
+// ones it multiplies, and for the normed variants they also give the RMS:
+// the chunks of the 64 lanes partition the row, so one wave reduction of
+// their squares is the row's sum of squares.  Epilogues:
+//   QKV    bias, RoPE, q write and K/V cache store (pair-packed rows)
+//   RESID  h += W x                 (WO and down projections)
+//   SWIGLU a = silu(gate) * up      (pair-packed gate/up rows)
+//   LMHEAD logits and a per-block greedy key, folded into a per-row 64-bit
+//          maximum with a relaxed device-scope atomicMax (the argmax kernel
+//          that follows turns it into an index and clears it)
 #include "q2_device.h"
 
 namespace q2 {
@@ -22,44 +27,35 @@ struct GemvP {
   int N, K;  // W [N, K], K % 8 == 0
   const float *x;
   int ldx, M;
-  const float *norm_w;  // RMSNorm prologue when non-null (width K)
+  const float *norm_w;  // RMSNorm prologue when non-null (then K is the normed width)
   float eps;
   int n_groups;  // row groups of 4 waves * R rows
   Dims d;
   QkvEpi qkv;
   float *out;
   int ldo;
-  ArgmaxEpi am;
-  float *normed_out;  // LMHEAD: f32 copy of the normed rows [M, K]
+  unsigned long long *best;  // LMHEAD: per-row packed maxima
+  float *const *logits;      // LMHEAD: device-resident pointer to [M, V] logits (may hold null)
+  float *normed_out;         // LMHEAD: f32 copy of the normed rows [M, K]
 };
 
-template <int MT, int R, int EPI>
+template <int MT, int R, int KB, int EPI>
 __global__ __launch_bounds__(256) void k_gemv(GemvP p) {
   const int lane = threadIdx.x & 63;
   const int wave = threadIdx.x >> 6;
   const int K = p.K, M = p.M;
+  const bool norm = EPI != EPI_RESID && p.norm_w != nullptr;
+  float *logits = nullptr;
+  if (EPI == EPI_LMHEAD) logits = *p.logits;
 
   float inv[MT];
-#pragma unroll
-  for (int m = 0; m < MT; ++m) inv[m] = 1.0f;
-  if (EPI != EPI_RESID && p.norm_w) {
-#pragma unroll
-    for (int m = 0; m < MT; ++m) {
-      if (m < M) {
-        float ss = 0.f;
-        for (int k = lane * 4; k < K; k += 256) {
-          const f4 v = *(const f4 *)(p.x + (size_t)m * p.ldx + k);
-          ss += v.x * v.x + v.y * v.y + v.z * v.z + v.w * v.w;
-        }
-        ss = wave_sum(ss);
-        inv[m] = 1.0f / sqrtf(ss / (float)K + p.eps);
-      }
-    }
-  }
-
   unsigned long long best[MT];
 #pragma unroll
-  for (int m = 0; m < MT; ++m) best[m] = 0ull;
+  for (int m = 0; m < MT; ++m) {
+    inv[m] = 1.0f;
+    best[m] = 0ull;
+  }
+  bool have_inv = false;
 
   for (int rg = blockIdx.x; rg < p.n_groups; rg += gridDim.x) {
     const int row0 = (rg * 4 + wave) * R;
@@ -69,38 +65,79 @@ __global__ __launch_bounds__(256) void k_gemv(GemvP p) {
 #pragma unroll
       for (int m = 0; m < MT; ++m) acc[r][m] = 0.f;
 
-#pragma unroll 2
-    for (int k0 = lane * 8; k0 < K; k0 += 512) {
-      h8 wv[R];
+    for (int kb0 = 0; kb0 < K; kb0 += KB * 512) {
+      // 1. the weight stream: every load of this batch in flight at once
+      h8 wv[KB][R];
 #pragma unroll
-      for (int r = 0; r < R; ++r) {
-        const int n = row0 + r;
-        if (n < p.N)
-          wv[r] = __builtin_nontemporal_load((const h8 *)(p.W + (size_t)n * K + k0));
-        else
-          wv[r] = (h8){0, 0, 0, 0, 0, 0, 0, 0};
-      }
-      f4 nw0 = {1.f, 1.f, 1.f, 1.f}, nw1 = {1.f, 1.f, 1.f, 1.f};
-      if (EPI != EPI_RESID && p.norm_w) {
-        nw0 = *(const f4 *)(p.norm_w + k0);
-        nw1 = *(const f4 *)(p.norm_w + k0 + 4);
-      }
+      for (int c = 0; c < KB; ++c) {
+        const int k = kb0 + c * 512 + lane * 8;
 #pragma unroll
-      for (int m = 0; m < MT; ++m) {
-        if (m < M) {
-          f4 x0 = *(const f4 *)(p.x + (size_t)m * p.ldx + k0);
-          f4 x1 = *(const f4 *)(p.x + (size_t)m * p.ldx + k0 + 4);
-          if (EPI != EPI_RESID) {
-            x0 = x0 * inv[m] * nw0;
-            x1 = x1 * inv[m] * nw1;
+        for (int r = 0; r < R; ++r) {
+          const int n = row0 + r;
+          if (k < K && n < p.N)
+            wv[c][r] = __builtin_nontemporal_load((const h8 *)(p.W + (size_t)n * K + k));
+          else
+            wv[c][r] = (h8){0, 0, 0, 0, 0, 0, 0, 0};
+        }
+      }
+      // 2. activations (and the RMS of each row on the first pass)
+      f4 xv[KB][MT][2];
+#pragma unroll
+      for (int c = 0; c < KB; ++c) {
+        const int k = kb0 + c * 512 + lane * 8;
+#pragma unroll
+        for (int m = 0; m < MT; ++m) {
+          if (k < K && m < M) {
+            xv[c][m][0] = *(const f4 *)(p.x + (size_t)m * p.ldx + k);
+            xv[c][m][1] = *(const f4 *)(p.x + (size_t)m * p.ldx + k + 4);
+          } else {
+            xv[c][m][0] = (f4){0.f, 0.f, 0.f, 0.f};
+            xv[c][m][1] = (f4){0.f, 0.f, 0.f, 0.f};
           }
-          const float xs[8] = {x0.x, x0.y, x0.z, x0.w, x1.x, x1.y, x1.z, x1.w};
+        }
+      }
+      if (norm) {
+        if (!have_inv) {  // normed variants have K <= KB * 512: one batch holds the row
+#pragma unroll
+          for (int m = 0; m < MT; ++m) {
+            float ss = 0.f;
+#pragma unroll
+            for (int c = 0; c < KB; ++c)
+#pragma unroll
+              for (int hh = 0; hh < 2; ++hh) {
+                const f4 v = xv[c][m][hh];
+                ss += v.x * v.x + v.y * v.y + v.z * v.z + v.w * v.w;
+              }
+            ss = wave_sum(ss);
+            inv[m] = 1.0f / sqrtf(ss / (float)K + p.eps);
+          }
+          have_inv = true;
+        }
+#pragma unroll
+        for (int c = 0; c < KB; ++c) {
+          const int k = kb0 + c * 512 + lane * 8;
+          if (k < K) {
+            const f4 g0 = *(const f4 *)(p.norm_w + k), g1 = *(const f4 *)(p.norm_w + k + 4);
+#pragma unroll
+            for (int m = 0; m < MT; ++m) {
+              xv[c][m][0] = xv[c][m][0] * inv[m] * g0;
+              xv[c][m][1] = xv[c][m][1] * inv[m] * g1;
+            }
+          }
+        }
+      }
+      // 3. multiply-accumulate in f32
+#pragma unroll
+      for (int c = 0; c < KB; ++c)
+#pragma unroll
+        for (int m = 0; m < MT; ++m) {
+          const float xs[8] = {xv[c][m][0].x, xv[c][m][0].y, xv[c][m][0].z, xv[c][m][0].w,
+                               xv[c][m][1].x, xv[c][m][1].y, xv[c][m][1].z, xv[c][m][1].w};
 #pragma unroll
           for (int r = 0; r < R; ++r)
 #pragma unroll
-            for (int j = 0; j < 8; ++j) acc[r][m] = fmaf((float)wv[r][j], xs[j], acc[r][m]);
+            for (int j = 0; j < 8; ++j) acc[r][m] = fmaf((float)wv[c][r][j], xs[j], acc[r][m]);
         }
-      }
     }
 #pragma unroll
     for (int r = 0; r < R; ++r)
@@ -135,7 +172,7 @@ __global__ __launch_bounds__(256) void k_gemv(GemvP p) {
         for (int m = 0; m < MT; ++m) {
           const int n = row0 + r;
           if (m < M && n < p.N) {
-            if (p.am.logits && lane == r * MT + m) p.am.logits[(size_t)m * p.N + n] = acc[r][m];
+            if (logits && lane == r * MT + m) logits[(size_t)m * p.N + n] = acc[r][m];
             const unsigned long long key = argmax_key(acc[r][m], n);
             best[m] = key > best[m] ? key : best[m];
           }
@@ -145,7 +182,6 @@ __global__ __launch_bounds__(256) void k_gemv(GemvP p) {
 
   if (EPI == EPI_LMHEAD) {
     __shared__ unsigned long long s_best[4][MT];
-    __shared__ int s_last;
     if (lane == 0)
 #pragma unroll
       for (int m = 0; m < MT; ++m) s_best[wave][m] = best[m];
@@ -157,40 +193,48 @@ __global__ __launch_bounds__(256) void k_gemv(GemvP p) {
             p.normed_out[(size_t)m * K + k] = p.x[(size_t)m * p.ldx + k] * inv[m] * p.norm_w[k];
     }
     __syncthreads();
-    if (threadIdx.x < MT && (int)threadIdx.x < M) {
+    if ((int)threadIdx.x < M && threadIdx.x < MT) {
       const int m = threadIdx.x;
       unsigned long long b = s_best[0][m];
       for (int w = 1; w < 4; ++w) b = s_best[w][m] > b ? s_best[w][m] : b;
-      atomicMax(&p.am.best[m], b);
-    }
-    __threadfence();
-    __syncthreads();
-    if (threadIdx.x == 0) s_last = (atomicAdd(p.am.counter, 1u) == gridDim.x - 1);
-    __syncthreads();
-    if (s_last) {
-      __threadfence();
-      if ((int)threadIdx.x < M) {
-        const unsigned long long b = atomicExch(&p.am.best[threadIdx.x], 0ull);
-        if (p.am.out) p.am.out[threadIdx.x] = argmax_index(b);
-      }
-      if (threadIdx.x == 0) atomicExch(p.am.counter, 0u);
+      atomicMax(&p.best[m], b);
     }
   }
 }
 
+// The greedy result: index of each row's packed maximum, which is then
+// cleared for the next call.  Runs after the lm_head kernel (the kernel
+// boundary orders the atomics before these reads).
+__global__ void k_argmax_finalize(unsigned long long *best, int M, int *const *out) {
+  const int m = blockIdx.x * blockDim.x + threadIdx.x;
+  if (m < M) {
+    const unsigned long long b = best[m];
+    best[m] = 0ull;
+    int *o = *out;
+    if (o) o[m] = argmax_index(b);
+  }
+}
+
 // ------------------------------------------------------------------ launch
+template <int R, int EPI, int MT>
+static void launch_kb(GemvP &p, int grid, hipStream_t st) {
+  const int kc = (p.K + 511) / 512;
+  if (kc <= 2)
+    hipLaunchKernelGGL((k_gemv<MT, R, 2, EPI>), dim3(grid), dim3(256), 0, st, p);
+  else if (kc <= 8)
+    hipLaunchKernelGGL((k_gemv<MT, R, 8, EPI>), dim3(grid), dim3(256), 0, st, p);
+  else
+    hipLaunchKernelGGL((k_gemv<MT, R, 10, EPI>), dim3(grid), dim3(256), 0, st, p);
+}
+
 template <int R, int EPI>
 static void launch(GemvP &p, int max_grid, hipStream_t st) {
   p.n_groups = (p.N + 4 * R - 1) / (4 * R);
-  int grid = p.n_groups < max_grid ? p.n_groups : max_grid;
+  const int grid = p.n_groups < max_grid ? p.n_groups : max_grid;
   if (p.M <= 1)
-    hipLaunchKernelGGL((k_gemv<1, R, EPI>), dim3(grid), dim3(256), 0, st, p);
-  else if (p.M <= 2)
-    hipLaunchKernelGGL((k_gemv<2, R, EPI>), dim3(grid), dim3(256), 0, st, p);
-  else if (p.M <= 4)
-    hipLaunchKernelGGL((k_gemv<4, R, EPI>), dim3(grid), dim3(256), 0, st, p);
+    launch_kb<R, EPI, 1>(p, grid, st);
   else
-    hipLaunchKernelGGL((k_gemv<8, R, EPI>), dim3(grid), dim3(256), 0, st, p);
+    launch_kb<R, EPI, 8>(p, grid, st);
 }
 
 static GemvP base(const uint16_t *W, int N, int K, const float *x, int ldx, int M) {
@@ -211,7 +255,7 @@ void gemv_qkv(const Dims &d, const LayerW &w, const float *h, int M, const QkvEp
   p.eps = eps;
   p.d = d;
   p.qkv = e;
-  launch<4, EPI_QKV>(p, 1 << 30, st);
+  launch<2, EPI_QKV>(p, 1 << 30, st);
 }
 
 void gemv_resid(const uint16_t *W, int N, int K, const float *x, int ldx, int M, float *h,
@@ -240,9 +284,15 @@ void gemv_lmhead(const Dims &d, const uint16_t *W, const float *norm_w, const fl
   GemvP p = base(W, d.V, d.H, h, d.H, M);
   p.norm_w = norm_w;
   p.eps = eps;
-  p.am = e;
+  p.best = e.best;
+  p.logits = e.logits;
   p.normed_out = normed_out;
-  launch<4, EPI_LMHEAD>(p, 2048, st);
+  launch<4, EPI_LMHEAD>(p, 4096, st);
+  argmax_finalize(e, M, st);
+}
+
+void argmax_finalize(const ArgmaxEpi &e, int M, hipStream_t st) {
+  hipLaunchKernelGGL(k_argmax_finalize, dim3((M + 255) / 256), dim3(256), 0, st, e.best, M, e.out);
 }
 
 }  // namespace q2

@@ -6,10 +6,11 @@ namespace q2 {
 // h[m] = f32(E[tokens[m]]): the embedding output enters the first layer
 // unscaled.  An id outside [0, V) cannot be rejected on the host when the
 // tokens live on the device; it reads row 0 and latches *bad.
-__global__ __launch_bounds__(256) void k_embed(const uint16_t *E, int H, int V, const int *tokens,
-                                               float *h, unsigned int *bad) {
+__global__ __launch_bounds__(256) void k_embed(const uint16_t *E, int H, int V,
+                                               const int *const *tokens, int tok_off, float *h,
+                                               unsigned int *bad) {
   const int m = blockIdx.x;
-  int t = tokens[m];
+  int t = (*tokens)[tok_off + m];
   if (t < 0 || t >= V) {
     if (threadIdx.x == 0) *bad = 1u;
     t = 0;
@@ -24,9 +25,9 @@ __global__ __launch_bounds__(256) void k_embed(const uint16_t *E, int H, int V, 
   }
 }
 
-void embed_rows(const uint16_t *E, int H, int V, const int *tokens, int M, float *h,
-                unsigned int *bad_flag, hipStream_t st) {
-  hipLaunchKernelGGL(k_embed, dim3(M), dim3(256), 0, st, E, H, V, tokens, h, bad_flag);
+void embed_rows(const uint16_t *E, int H, int V, const int *const *tokens, int tok_off, int M,
+                float *h, unsigned int *bad_flag, hipStream_t st) {
+  hipLaunchKernelGGL(k_embed, dim3(M), dim3(256), 0, st, E, H, V, tokens, tok_off, h, bad_flag);
 }
 
 // One wavefront per row: y = w * x / sqrt(mean(x^2) + eps), stored as f16

@@ -54,14 +54,14 @@ struct QkvEpi {
   RopeTable rope;
 };
 
-// Greedy readout: packed (ordered-key, ~index) 64-bit maxima per row, a
-// block counter and the int32 result.  `best` and `counter` are zero between
-// calls (the last block resets them).
+// Greedy readout: packed (ordered-key, ~index) 64-bit maxima per row, zero
+// between calls (the finalize kernel clears them).  The output pointers are
+// read on the device from a slot the host staged with the call, so a
+// captured graph can write to a different buffer on every replay.
 struct ArgmaxEpi {
-  float *logits;            // [M, V] or null
+  float *const *logits;      // -> [M, V] f32 or null
   unsigned long long *best;  // [M]
-  unsigned int *counter;     // [1]
-  int *out;                  // [M] or null
+  int *const *out;           // -> [M] int32 or null
 };
 
 // ---------------------------------------------------------------- launchers
@@ -76,6 +76,10 @@ void gemv_swiglu(const Dims &d, const LayerW &w, const float *h, int M, float *a
                  float eps, hipStream_t st);
 void gemv_lmhead(const Dims &d, const uint16_t *W, const float *norm_w, const float *h, int M,
                  float *normed_out, const ArgmaxEpi &e, float eps, hipStream_t st);
+
+// Writes the index of each row's packed maximum and clears it; launched after
+// an lm_head kernel.
+void argmax_finalize(const ArgmaxEpi &e, int M, hipStream_t st);
 
 // MFMA GEMM family (rows M > 8): A f16 [M, lda], W f16 [N, K], K % 32 == 0.
 void gemm_qkv(const Dims &d, const LayerW &w, const _Float16 *x, int lda, int M,
@@ -93,19 +97,20 @@ void rmsnorm_rows_f16(const float *h, int ldh, const float *w, int H, int M, flo
                       _Float16 *x, int ldx, float *y32, hipStream_t st);
 // Embedding gather h[m] = f32(E[tokens[m]]) without scaling; an id outside
 // [0, V) reads row 0 and sets *bad_flag to 1.
-void embed_rows(const uint16_t *E, int H, int V, const int *tokens, int M, float *h,
-                unsigned int *bad_flag, hipStream_t st);
+void embed_rows(const uint16_t *E, int H, int V, const int *const *tokens, int tok_off, int M,
+                float *h, unsigned int *bad_flag, hipStream_t st);
 
 // Attention.
+constexpr int kSplitKeys = 256;  // keys per split of the decode attention
 struct AttnPartials {
-  float *buf;              // [rows][nkv][n_chunks][group][hd + 2]
-  unsigned int *counters;  // [rows][nkv], zero between calls
-  int n_chunks;
+  float *buf;    // [rows][nkv][n_chunks][group][hd + 2]
+  int n_chunks;  // splits per row: ceil(n_ctx / kSplitKeys)
 };
 // Split-KV attention, one row per query token (decode and short prefills).
+// n_split = ceil((max position of the rows + 1) / kSplitKeys).
 void attn_decode(const Dims &d, int layer, const KVCache &kv, const float *q, int ldq,
-                 RowInfo rows, int M, const AttnPartials &p, float *o32, _Float16 *o16,
-                 int ldo, hipStream_t st);
+                 RowInfo rows, int M, int n_split, const AttnPartials &p, float *o32,
+                 _Float16 *o16, int ldo, hipStream_t st);
 // Causal flash attention over MFMA for one prefill pass of M rows of one
 // sequence (positions strictly increasing).
 void attn_prefill(const Dims &d, int layer, const KVCache &kv, const float *q, int ldq,

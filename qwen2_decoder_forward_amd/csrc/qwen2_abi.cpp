@@ -6,7 +6,9 @@
 #include <string.h>
 
 #include <algorithm>
+#include <map>
 #include <string>
+#include <utility>
 #include <vector>
 
 #include "../../include/qwen2.h"
@@ -22,6 +24,7 @@ constexpr int kRing = 4;          // pinned staging slots for per-call row data
 constexpr int kGemvRows = 8;      // rows up to this use the f32 GEMV path
 constexpr int kMaxPassRows = 4096;  // rows per prefill pass
 constexpr int kProfMax = 16384;     // timed launches between two reads
+constexpr size_t kSlotBytes = 64;   // pointer slots at the head of a staged call
 
 thread_local std::string g_load_error;
 
@@ -52,14 +55,21 @@ struct qwen2_ctx {
   int dec_rows = 0;   // rows of the GEMV / decode-attention buffers: max(n_seq, 8)
   float *h = nullptr, *q32 = nullptr, *o32 = nullptr, *a32 = nullptr, *normed = nullptr;
   _Float16 *x16 = nullptr, *a16 = nullptr;
-  int *io = nullptr;  // device copy of the per-call rows: tokens | positions | seqs
-  size_t io_cap = 0;  // entries per field
+  // Device copy of the per-call block: pointer slots (tokens, logits, argmax)
+  // then the row data (prefill: tokens | positions | seqs; decode:
+  // positions | seqs).  Kernels read everything per call from here, so a
+  // captured decode graph serves every call of its batch size.
+  char *io = nullptr;
+  size_t io_cap = 0;  // int entries per field
   q2::AttnPartials part{};
   unsigned long long *best = nullptr;
-  unsigned int *best_cnt = nullptr;
   unsigned int *bad_flag = nullptr;
+  // captured decode steps, keyed by (batch size, attention splits)
+  std::map<std::pair<int, int>, hipGraphExec_t> graphs;
+  hipStream_t cap_stream = nullptr;  // captures only (never runs work)
+  bool use_graphs = true;
   // pinned staging ring
-  int32_t *pinned = nullptr;
+  char *pinned = nullptr;
   hipEvent_t ev[kRing] = {};
   int ring = 0;
   // last read-out rows
@@ -101,6 +111,8 @@ void release(qwen2_ctx *c) {
   for (auto &e : c->ev)
     if (e) (void)hipEventDestroy(e);
   for (auto &e : c->prof_ev) (void)hipEventDestroy(e);
+  for (auto &g : c->graphs) (void)hipGraphExecDestroy(g.second);
+  if (c->cap_stream) (void)hipStreamDestroy(c->cap_stream);
   delete c;
 }
 
@@ -280,17 +292,18 @@ int qwen2_load(const qwen2_hparams *hp, const qwen2_weights *w, void *stream, qw
   c->max_rows = std::min(d.n_ctx, kMaxPassRows);
   c->rows_cap = std::max(c->max_rows, d.n_seq);
   c->dec_rows = std::max(d.n_seq, kGemvRows);
-  c->part.n_chunks = (d.n_ctx + 63) / 64;
+  c->part.n_chunks = (d.n_ctx + q2::kSplitKeys - 1) / q2::kSplitKeys;
   c->io_cap = (size_t)std::max(d.n_ctx, d.n_seq);
+  const char *ng = getenv("QWEN2_NO_GRAPH");
+  c->use_graphs = !(ng && ng[0] == '1');
   {
     const size_t R = c->rows_cap, D = c->dec_rows;
     cur = 0;
     Slot s_h = take(R * H * 4), s_q = take(R * nhd * 4), s_x16 = take(R * H * 2),
          s_a16 = take(R * Ip * 2), s_o32 = take(D * nhd * 4), s_a32 = take(D * Ip * 4),
-         s_norm = take(D * H * 4), s_io = take(3 * c->io_cap * 4),
+         s_norm = take(D * H * 4), s_io = take(kSlotBytes + 3 * c->io_cap * 4),
          s_part = take((size_t)D * d.nkv * c->part.n_chunks * d.group * (d.hd + 2) * 4),
-         s_pcnt = take((size_t)D * d.nkv * 4), s_best = take(D * 8), s_bcnt = take(4),
-         s_bad = take(4);
+         s_best = take(D * 8), s_bad = take(4);
     c->sarena_bytes = cur;
     LTRY([&]() -> int {
       HIP_TRY(c, hipMalloc(&c->sarena, c->sarena_bytes));
@@ -305,16 +318,16 @@ int qwen2_load(const qwen2_hparams *hp, const qwen2_weights *w, void *stream, qw
     c->o32 = (float *)(S + s_o32.off);
     c->a32 = (float *)(S + s_a32.off);
     c->normed = (float *)(S + s_norm.off);
-    c->io = (int *)(S + s_io.off);
+    c->io = S + s_io.off;
     c->part.buf = (float *)(S + s_part.off);
-    c->part.counters = (unsigned *)(S + s_pcnt.off);
     c->best = (unsigned long long *)(S + s_best.off);
-    c->best_cnt = (unsigned *)(S + s_bcnt.off);
     c->bad_flag = (unsigned *)(S + s_bad.off);
   }
   LTRY([&]() -> int {
-    HIP_TRY(c, hipHostMalloc((void **)&c->pinned, kRing * 3 * c->io_cap * 4, hipHostMallocDefault));
+    HIP_TRY(c, hipHostMalloc((void **)&c->pinned, kRing * (kSlotBytes + 3 * c->io_cap * 4),
+                             hipHostMallocDefault));
     for (auto &e : c->ev) HIP_TRY(c, hipEventCreateWithFlags(&e, hipEventDisableTiming));
+    HIP_TRY(c, hipStreamCreateWithFlags(&c->cap_stream, hipStreamNonBlocking));
     HIP_TRY(c, hipStreamSynchronize(st));
     HIP_TRY(c, hipDeviceSynchronize());
     return 0;
@@ -328,26 +341,41 @@ int qwen2_load(const qwen2_hparams *hp, const qwen2_weights *w, void *stream, qw
 
 namespace {
 
-// Copies `nf` fields of n int32 each to the device row buffer through the
-// pinned ring; returns device pointers to the fields.
-int stage_rows(qwen2_ctx *c, hipStream_t st, int n, const int32_t *f0, const int32_t *f1,
-               const int32_t *f2_or_null, int32_t seq_fill, int **d0, int **d1, int **d2) {
+// Pointer slots at the head of the staged per-call block.
+struct CallSlots {
+  const int *tokens;
+  float *logits;
+  int *argmax;
+};
+
+// Writes the call block (pointer slots + `nf` int32 fields of n entries)
+// into the next pinned ring slot and copies it to the device block; returns
+// device addresses of the fields.
+int stage_call(qwen2_ctx *c, hipStream_t st, const CallSlots &slots, int n, int nf,
+               const int32_t *const *fields, int **dev_fields) {
   const int slot = c->ring;
   c->ring = (c->ring + 1) % kRing;
   HIP_TRY(c, hipEventSynchronize(c->ev[slot]));
-  int32_t *hbuf = c->pinned + (size_t)slot * 3 * c->io_cap;
-  memcpy(hbuf, f0, n * 4);
-  memcpy(hbuf + n, f1, n * 4);
-  if (f2_or_null) memcpy(hbuf + 2 * n, f2_or_null, n * 4);
-  else
-    for (int i = 0; i < n; ++i) hbuf[2 * n + i] = seq_fill;
-  HIP_TRY(c, hipMemcpyAsync(c->io, hbuf, (size_t)3 * n * 4, hipMemcpyHostToDevice, st));
+  char *hb = c->pinned + (size_t)slot * (kSlotBytes + 3 * c->io_cap * 4);
+  memcpy(hb, &slots, sizeof slots);
+  int32_t *hi = (int32_t *)(hb + kSlotBytes);
+  for (int f = 0; f < nf; ++f) {
+    memcpy(hi + (size_t)f * n, fields[f], (size_t)n * 4);
+    dev_fields[f] = (int *)(c->io + kSlotBytes) + (size_t)f * n;
+  }
+  HIP_TRY(c, hipMemcpyAsync(c->io, hb, kSlotBytes + (size_t)nf * n * 4, hipMemcpyHostToDevice, st));
   HIP_TRY(c, hipEventRecord(c->ev[slot], st));
-  *d0 = c->io;
-  *d1 = c->io + n;
-  *d2 = c->io + 2 * n;
   return QWEN2_OK;
 }
+
+const CallSlots *dev_slots(qwen2_ctx *c) { return (const CallSlots *)c->io; }
+
+q2::ArgmaxEpi argmax_epi(qwen2_ctx *c) {
+  const CallSlots *ds = dev_slots(c);
+  return q2::ArgmaxEpi{(float *const *)&ds->logits, c->best, (int *const *)&ds->argmax};
+}
+
+int splits_for(int max_pos) { return (max_pos + q2::kSplitKeys) / q2::kSplitKeys; }
 
 // Brackets one op launch with two events when that op kind is being timed.
 struct OpTimer {
@@ -387,35 +415,35 @@ q2::QkvEpi qkv_epi(qwen2_ctx *c, int l, const int *pos, const int *seq) {
 
 // The last layer of a prefill pass after its K/V are stored: only the last
 // row goes on (attention, WO, FFN, final norm, lm_head, argmax).
-void tail_row(qwen2_ctx *c, int r, const int *pos, const int *seq, float *logits, int *argmax,
-              hipStream_t st) {
+void tail_row(qwen2_ctx *c, int r, const int *pos, const int *seq, int last_pos, hipStream_t st) {
   const Dims &d = c->d;
   const int l = d.L - 1;
   const LayerW &w = c->layers[l];
   const int nhd = d.nh * d.hd;
   float *hr = c->h + (size_t)r * d.H;
   TIMED(QWEN2_OP_ATTN, q2::attn_decode(d, l, q2::KVCache{c->kc, c->vc}, c->q32 + (size_t)r * nhd,
-                                       nhd, q2::RowInfo{pos + r, seq + r}, 1, c->part, c->o32,
-                                       nullptr, nhd, st));
+                                       nhd, q2::RowInfo{pos + r, seq + r}, 1, splits_for(last_pos),
+                                       c->part, c->o32, nullptr, nhd, st));
   TIMED(QWEN2_OP_WO, q2::gemv_resid(w.wo, d.H, nhd, c->o32, nhd, 1, hr, d.H, st));
   TIMED(QWEN2_OP_GATEUP, q2::gemv_swiglu(d, w, hr, 1, c->a32, d.I_pad, c->hp.rms_eps, st));
   TIMED(QWEN2_OP_DOWN, q2::gemv_resid(w.wd, d.H, d.I_pad, c->a32, d.I_pad, 1, hr, d.H, st));
-  q2::ArgmaxEpi am{logits, c->best, c->best_cnt, argmax};
-  TIMED(QWEN2_OP_LMHEAD,
-        q2::gemv_lmhead(d, c->lm_head, c->out_norm, hr, 1, c->normed, am, c->hp.rms_eps, st));
+  TIMED(QWEN2_OP_LMHEAD, q2::gemv_lmhead(d, c->lm_head, c->out_norm, hr, 1, c->normed,
+                                         argmax_epi(c), c->hp.rms_eps, st));
   c->last_h = hr;
   c->last_rows = 1;
 }
 
 // One pass of at most max_rows rows; `last` marks the pass that reads out.
-void prefill_pass(qwen2_ctx *c, int M, const int *tok, const int *pos, const int *seq, bool last,
-                  float *logits, int *argmax, hipStream_t st) {
+void prefill_pass(qwen2_ctx *c, int M, int off, const int *pos, const int *seq, bool last,
+                  const int32_t *host_pos, hipStream_t st) {
   const Dims &d = c->d;
   const float eps = c->hp.rms_eps;
   const int nhd = d.nh * d.hd;
   const q2::KVCache kv{c->kc, c->vc};
   const q2::RowInfo rows{pos, seq};
-  TIMED(QWEN2_OP_EMBED, q2::embed_rows(c->tok_embd, d.H, d.V, tok, M, c->h, c->bad_flag, st));
+  TIMED(QWEN2_OP_EMBED, q2::embed_rows(c->tok_embd, d.H, d.V, &dev_slots(c)->tokens, off, M,
+                                       c->h, c->bad_flag, st));
+  const int n_split = splits_for(host_pos[M - 1]);
   const bool gemv = M <= kGemvRows;
   for (int l = 0; l < d.L; ++l) {
     const LayerW &w = c->layers[l];
@@ -429,8 +457,8 @@ void prefill_pass(qwen2_ctx *c, int M, const int *tok, const int *pos, const int
     }
     if (l == d.L - 1) break;  // the last layer continues on the last row only
     if (gemv) {
-      TIMED(QWEN2_OP_ATTN,
-            q2::attn_decode(d, l, kv, c->q32, nhd, rows, M, c->part, c->o32, nullptr, nhd, st));
+      TIMED(QWEN2_OP_ATTN, q2::attn_decode(d, l, kv, c->q32, nhd, rows, M, n_split, c->part,
+                                           c->o32, nullptr, nhd, st));
       TIMED(QWEN2_OP_WO, q2::gemv_resid(w.wo, d.H, nhd, c->o32, nhd, M, c->h, d.H, st));
       TIMED(QWEN2_OP_GATEUP, q2::gemv_swiglu(d, w, c->h, M, c->a32, d.I_pad, eps, st));
       TIMED(QWEN2_OP_DOWN, q2::gemv_resid(w.wd, d.H, d.I_pad, c->a32, d.I_pad, M, c->h, d.H, st));
@@ -444,7 +472,52 @@ void prefill_pass(qwen2_ctx *c, int M, const int *tok, const int *pos, const int
             q2::gemm_resid(w.wd, d.H, d.I_pad, c->a16, d.I_pad, M, c->h, d.H, st));
     }
   }
-  if (last) tail_row(c, M - 1, pos, seq, logits, argmax, st);
+  if (last) tail_row(c, M - 1, pos, seq, host_pos[M - 1], st);
+}
+
+// Every kernel of one decode step for B rows (replayed from a graph).
+void decode_launches(qwen2_ctx *c, int B, int n_split, const int *dpos, const int *dseq,
+                     hipStream_t st) {
+  const Dims &d = c->d;
+  const float eps = c->hp.rms_eps;
+  const int nhd = d.nh * d.hd;
+  const q2::KVCache kv{c->kc, c->vc};
+  const q2::RowInfo rows{dpos, dseq};
+  TIMED(QWEN2_OP_EMBED, q2::embed_rows(c->tok_embd, d.H, d.V, &dev_slots(c)->tokens, 0, B, c->h,
+                                       c->bad_flag, st));
+  const bool gemv = B <= kGemvRows;
+  for (int l = 0; l < d.L; ++l) {
+    const LayerW &w = c->layers[l];
+    const q2::QkvEpi e = qkv_epi(c, l, dpos, dseq);
+    if (gemv) {
+      TIMED(QWEN2_OP_QKV, q2::gemv_qkv(d, w, c->h, B, e, eps, st));
+      TIMED(QWEN2_OP_ATTN, q2::attn_decode(d, l, kv, c->q32, nhd, rows, B, n_split, c->part,
+                                           c->o32, nullptr, nhd, st));
+      TIMED(QWEN2_OP_WO, q2::gemv_resid(w.wo, d.H, nhd, c->o32, nhd, B, c->h, d.H, st));
+      TIMED(QWEN2_OP_GATEUP, q2::gemv_swiglu(d, w, c->h, B, c->a32, d.I_pad, eps, st));
+      TIMED(QWEN2_OP_DOWN, q2::gemv_resid(w.wd, d.H, d.I_pad, c->a32, d.I_pad, B, c->h, d.H, st));
+    } else {
+      TIMED(QWEN2_OP_NORM, q2::rmsnorm_rows_f16(c->h, d.H, w.attn_norm, d.H, B, eps, c->x16, d.H,
+                                                nullptr, st));
+      TIMED(QWEN2_OP_QKV, q2::gemm_qkv(d, w, c->x16, d.H, B, e, st));
+      TIMED(QWEN2_OP_ATTN, q2::attn_decode(d, l, kv, c->q32, nhd, rows, B, n_split, c->part,
+                                           nullptr, c->x16, nhd, st));
+      TIMED(QWEN2_OP_WO, q2::gemm_resid(w.wo, d.H, nhd, c->x16, nhd, B, c->h, d.H, st));
+      TIMED(QWEN2_OP_NORM, q2::rmsnorm_rows_f16(c->h, d.H, w.ffn_norm, d.H, B, eps, c->x16, d.H,
+                                                nullptr, st));
+      TIMED(QWEN2_OP_GATEUP, q2::gemm_swiglu(d, w, c->x16, d.H, B, c->a16, d.I_pad, st));
+      TIMED(QWEN2_OP_DOWN,
+            q2::gemm_resid(w.wd, d.H, d.I_pad, c->a16, d.I_pad, B, c->h, d.H, st));
+    }
+  }
+  if (gemv) {
+    TIMED(QWEN2_OP_LMHEAD, q2::gemv_lmhead(d, c->lm_head, c->out_norm, c->h, B, c->normed,
+                                           argmax_epi(c), eps, st));
+  } else {
+    TIMED(QWEN2_OP_NORM, q2::rmsnorm_rows_f16(c->h, d.H, c->out_norm, d.H, B, eps, c->x16, d.H,
+                                              c->normed, st));
+    TIMED(QWEN2_OP_LMHEAD, q2::gemm_lmhead(d, c->lm_head, c->x16, d.H, B, argmax_epi(c), st));
+  }
 }
 
 }  // namespace
@@ -458,12 +531,15 @@ int qwen2_prefill(qwen2_ctx *c, int32_t seq, const int32_t *tokens, const int32_
   int rc = q2::check_prefill(&c->hp, seq, tokens, positions, n, &msg);
   if (rc) return set_err(c, rc, msg);
   hipStream_t st = (hipStream_t)stream;
-  int *dtok, *dpos, *dseq;
-  rc = stage_rows(c, st, n, tokens, positions, nullptr, seq, &dtok, &dpos, &dseq);
+  std::vector<int32_t> seqs(n, seq);
+  const int32_t *fields[3] = {tokens, positions, seqs.data()};
+  int *df[3];
+  const CallSlots slots{(const int *)(c->io + kSlotBytes), logits_dev, argmax_dev};
+  rc = stage_call(c, st, slots, n, 3, fields, df);
   if (rc) return rc;
   for (int off = 0; off < n; off += c->max_rows) {
     const int M = std::min(c->max_rows, n - off);
-    prefill_pass(c, M, dtok + off, dpos + off, dseq + off, off + M == n, logits_dev, argmax_dev, st);
+    prefill_pass(c, M, off, df[1] + off, df[2] + off, off + M == n, positions + off, st);
   }
   HIP_TRY(c, hipGetLastError());
   return QWEN2_OK;
@@ -477,53 +553,37 @@ int qwen2_decode(qwen2_ctx *c, int32_t B, const int32_t *seq_ids, const int32_t 
   if (rc) return set_err(c, rc, msg);
   if (!tokens_dev) return set_err(c, QWEN2_E_ARG, "null tokens_dev");
   hipStream_t st = (hipStream_t)stream;
-  int *dpos, *dseq, *dunused;
-  rc = stage_rows(c, st, B, positions, seq_ids, positions, 0, &dpos, &dseq, &dunused);
+  const int32_t *fields[2] = {positions, seq_ids};
+  int *df[2];
+  const CallSlots slots{tokens_dev, logits_dev, argmax_dev};
+  rc = stage_call(c, st, slots, B, 2, fields, df);
   if (rc) return rc;
-  const Dims &d = c->d;
-  const float eps = c->hp.rms_eps;
-  const int nhd = d.nh * d.hd;
-  const q2::KVCache kv{c->kc, c->vc};
-  const q2::RowInfo rows{dpos, dseq};
-  TIMED(QWEN2_OP_EMBED,
-        q2::embed_rows(c->tok_embd, d.H, d.V, tokens_dev, B, c->h, c->bad_flag, st));
-  const bool gemv = B <= kGemvRows;
-  for (int l = 0; l < d.L; ++l) {
-    const LayerW &w = c->layers[l];
-    const q2::QkvEpi e = qkv_epi(c, l, dpos, dseq);
-    if (gemv) {
-      TIMED(QWEN2_OP_QKV, q2::gemv_qkv(d, w, c->h, B, e, eps, st));
-      TIMED(QWEN2_OP_ATTN,
-            q2::attn_decode(d, l, kv, c->q32, nhd, rows, B, c->part, c->o32, nullptr, nhd, st));
-      TIMED(QWEN2_OP_WO, q2::gemv_resid(w.wo, d.H, nhd, c->o32, nhd, B, c->h, d.H, st));
-      TIMED(QWEN2_OP_GATEUP, q2::gemv_swiglu(d, w, c->h, B, c->a32, d.I_pad, eps, st));
-      TIMED(QWEN2_OP_DOWN, q2::gemv_resid(w.wd, d.H, d.I_pad, c->a32, d.I_pad, B, c->h, d.H, st));
-    } else {
-      TIMED(QWEN2_OP_NORM, q2::rmsnorm_rows_f16(c->h, d.H, w.attn_norm, d.H, B, eps, c->x16, d.H,
-                                                nullptr, st));
-      TIMED(QWEN2_OP_QKV, q2::gemm_qkv(d, w, c->x16, d.H, B, e, st));
-      TIMED(QWEN2_OP_ATTN,
-            q2::attn_decode(d, l, kv, c->q32, nhd, rows, B, c->part, nullptr, c->x16, nhd, st));
-      TIMED(QWEN2_OP_WO, q2::gemm_resid(w.wo, d.H, nhd, c->x16, nhd, B, c->h, d.H, st));
-      TIMED(QWEN2_OP_NORM, q2::rmsnorm_rows_f16(c->h, d.H, w.ffn_norm, d.H, B, eps, c->x16, d.H,
-                                                nullptr, st));
-      TIMED(QWEN2_OP_GATEUP, q2::gemm_swiglu(d, w, c->x16, d.H, B, c->a16, d.I_pad, st));
-      TIMED(QWEN2_OP_DOWN,
-            q2::gemm_resid(w.wd, d.H, d.I_pad, c->a16, d.I_pad, B, c->h, d.H, st));
-    }
-  }
-  q2::ArgmaxEpi am{logits_dev, c->best, c->best_cnt, argmax_dev};
-  if (gemv) {
-    TIMED(QWEN2_OP_LMHEAD,
-          q2::gemv_lmhead(d, c->lm_head, c->out_norm, c->h, B, c->normed, am, eps, st));
-  } else {
-    TIMED(QWEN2_OP_NORM, q2::rmsnorm_rows_f16(c->h, d.H, c->out_norm, d.H, B, eps, c->x16, d.H,
-                                              c->normed, st));
-    TIMED(QWEN2_OP_LMHEAD, q2::gemm_lmhead(d, c->lm_head, c->x16, d.H, B, am, st));
-  }
+  const int n_split = splits_for(*std::max_element(positions, positions + B));
   c->last_h = c->h;
   c->last_rows = B;
-  HIP_TRY(c, hipGetLastError());
+  if (!c->use_graphs || c->prof_mask) {
+    decode_launches(c, B, n_split, df[0], df[1], st);
+    HIP_TRY(c, hipGetLastError());
+    return QWEN2_OK;
+  }
+  auto key = std::make_pair((int)B, n_split);
+  auto it = c->graphs.find(key);
+  if (it == c->graphs.end()) {
+    hipGraph_t g = nullptr;
+    hipGraphExec_t ge = nullptr;
+    // capture on the library's own stream (the caller's may be the null
+    // stream, which cannot be captured); the graph then runs on the caller's
+    hipStream_t cs = c->cap_stream;
+    HIP_TRY(c, hipStreamBeginCapture(cs, hipStreamCaptureModeThreadLocal));
+    decode_launches(c, B, n_split, df[0], df[1], cs);
+    hipError_t e1 = hipStreamEndCapture(cs, &g);
+    if (e1 != hipSuccess) return set_err(c, QWEN2_E_HIP, std::string("graph capture: ") + hipGetErrorString(e1));
+    hipError_t e2 = hipGraphInstantiate(&ge, g, nullptr, nullptr, 0);
+    (void)hipGraphDestroy(g);
+    if (e2 != hipSuccess) return set_err(c, QWEN2_E_HIP, std::string("graph instantiate: ") + hipGetErrorString(e2));
+    it = c->graphs.emplace(key, ge).first;
+  }
+  HIP_TRY(c, hipGraphLaunch(it->second, st));
   return QWEN2_OK;
 }
 
