@@ -11,14 +11,15 @@
 namespace q2 {
 
 // ------------------------------------------------------------------ decode
-// One block per (split of up to 256 keys, KV head, query row).  A block walks
-// its split in 64-key tiles with an online softmax for all `group` query
-// heads of the KV head, so each K/V tile is read once per KV head.  With a
-// single split the block writes the normalised output itself; otherwise it
-// writes (max, exp-sum, un-normalised output) and k_attn_merge combines the
-// splits with log-sum-exp rescaling.  No block waits on another.
-constexpr int kTile = 64;
-
+// One block per (64-key chunk, KV head, query row), 256 threads.  The chunk's
+// K and V rows are staged in LDS with coalesced loads and shared by the
+// `group` query heads of the KV head.  Scores: thread t takes key t % 64 for
+// heads t / 64 and t / 64 + 4, so each head's 64 scores sit in one wavefront
+// and its max and exp-sum are wave reductions.  P.V: thread (head, d) sums
+// over the chunk's keys.  A single-chunk call writes the normalised output;
+// otherwise every block writes its chunk's (max, exp-sum, un-normalised
+// output) record and the records are merged (k_attn_merge, or the prologue
+// of the WO GEMV).  No block waits on another.
 struct AttnDecP {
   Dims d;
   int layer;
@@ -33,120 +34,83 @@ struct AttnDecP {
   float scale;
 };
 
-template <int HD, bool DIRECT>
+template <int HD, int G, bool DIRECT>
 __global__ __launch_bounds__(256) void k_attn_decode(AttnDecP p) {
-  constexpr int KS = HD + 1;  // padded K row in LDS (conflict-free column walk)
-  constexpr int PER = (8 * HD + 255) / 256;
-  __shared__ __attribute__((aligned(16))) float sK[kTile * KS];
-  __shared__ __attribute__((aligned(16))) float sQ[8 * HD];
-  __shared__ float sP[8 * kTile];
-  __shared__ float sM[8], sL[8], sA[8];
+  constexpr int C = kChunkKeys;
+  static_assert(C == 64, "one wavefront per head's chunk scores");
+  constexpr int KS = HD + 1;  // padded K row: conflict-free row walk
+  __shared__ float sK[C * KS];
+  __shared__ __attribute__((aligned(16))) float sV[C * HD];
+  __shared__ __attribute__((aligned(16))) float sQ[G * HD];
+  __shared__ float sP[G * C];
+  __shared__ float sM[G], sL[G];
 
-  const int tid = threadIdx.x;
+  const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
   const int c = blockIdx.x, g = blockIdx.y, m = blockIdx.z;
-  const int G = p.d.group;
   const int pos = p.rows.pos[m];
   const int seq = p.rows.seq[m];
-  const int P = pos + 1;
-  const int kb = c * kSplitKeys;
-  const int ke = min(P, kb + kSplitKeys);
-  if (kb >= ke) return;  // uniform across the block
-
+  const int kb = c * C;
+  const int nk = min(C, pos + 1 - kb);
+  if (nk <= 0) return;  // uniform across the block
+  const float *kbase = p.kv.k + p.kv.off(p.d, p.layer, seq, g, kb);
+  const float *vbase = p.kv.v + p.kv.off(p.d, p.layer, seq, g, kb);
   const float *qrow = p.q + (size_t)m * p.ldq + (size_t)g * G * HD;
+
+  for (int i = tid * 4; i < nk * HD; i += 1024) {
+    const f4 kv4 = *(const f4 *)(kbase + i);
+    const f4 vv4 = *(const f4 *)(vbase + i);
+    const int r = i / HD, cc = i - r * HD;
+    sK[r * KS + cc + 0] = kv4.x;
+    sK[r * KS + cc + 1] = kv4.y;
+    sK[r * KS + cc + 2] = kv4.z;
+    sK[r * KS + cc + 3] = kv4.w;
+    *(f4 *)(sV + i) = vv4;
+  }
   for (int i = tid; i < G * HD; i += 256) sQ[i] = qrow[i] * p.scale;
-  if (tid < 8) {
-    sM[tid] = kNegInf;
-    sL[tid] = 0.f;
-  }
-  float o[PER];
-#pragma unroll
-  for (int i = 0; i < PER; ++i) o[i] = 0.f;
-  const float *kbase = p.kv.k + p.kv.off(p.d, p.layer, seq, g, 0);
-  const float *vbase = p.kv.v + p.kv.off(p.d, p.layer, seq, g, 0);
-  const int j = tid & 63, wv = tid >> 6;
+  __syncthreads();
 
-  for (int k0 = kb; k0 < ke; k0 += kTile) {
-    const int nk = min(kTile, ke - k0);
-    __syncthreads();
-    for (int i = tid * 4; i < nk * HD; i += 1024) {
-      const f4 v = *(const f4 *)(kbase + (size_t)k0 * HD + i);
-      const int r = i / HD, cc = i - r * HD;
-      sK[r * KS + cc + 0] = v.x;
-      sK[r * KS + cc + 1] = v.y;
-      sK[r * KS + cc + 2] = v.z;
-      sK[r * KS + cc + 3] = v.w;
+  const int j = lane;
+#pragma unroll
+  for (int hi = 0; hi < (G + 3) / 4; ++hi) {
+    const int h = w + 4 * hi;
+    if (h < G) {  // uniform across the wave
+      float a = 0.f;
+      if (j < nk) {
+#pragma unroll 16
+        for (int dd = 0; dd < HD; ++dd) a = fmaf(sQ[h * HD + dd], sK[j * KS + dd], a);
+      }
+      const float s = j < nk ? a : kNegInf;
+      const float mx = wave_max(s);
+      const float e = j < nk ? __expf(s - mx) : 0.f;
+      const float sum = wave_sum(e);
+      sP[h * C + j] = e;
+      if (lane == 0) {
+        sM[h] = mx;
+        sL[h] = sum;
+      }
     }
-    __syncthreads();
-    float s0 = kNegInf, s1 = kNegInf;
-    if (j < nk) {
-      float a0 = 0.f, a1 = 0.f;
-      const bool h1 = wv + 4 < G;
+  }
+  __syncthreads();
+
+  const int rec = G * (HD + 2);
+  float *part = p.part.buf + (((size_t)m * p.d.nkv + g) * p.part.n_chunks + c) * rec;
+  for (int idx = tid; idx < G * HD; idx += 256) {
+    const int h = idx / HD, dd = idx - h * HD;
+    float acc = 0.f;
 #pragma unroll 8
-      for (int dd = 0; dd < HD; ++dd) {
-        const float kd = sK[j * KS + dd];
-        a0 = fmaf(sQ[wv * HD + dd], kd, a0);
-        if (h1) a1 = fmaf(sQ[(wv + 4) * HD + dd], kd, a1);
-      }
-      s0 = a0;
-      s1 = a1;
-    }
-#pragma unroll
-    for (int i = 0; i < 2; ++i) {
-      const int h = wv + 4 * i;
-      if (h < G) {  // uniform across the wave: wave wv owns heads wv and wv + 4
-        const float s = i ? s1 : s0;
-        const float m_old = sM[h];
-        const float m_new = fmaxf(m_old, wave_max(s));
-        const float e = (j < nk) ? __expf(s - m_new) : 0.f;
-        const float sum = wave_sum(e);
-        sP[h * kTile + j] = e;
-        if (j == 0) {
-          const float alpha = __expf(m_old - m_new);
-          sA[h] = alpha;
-          sL[h] = sL[h] * alpha + sum;
-          sM[h] = m_new;
-        }
-      }
-    }
-    __syncthreads();
-    for (int i = tid * 4; i < nk * HD; i += 1024)
-      *(f4 *)(sK + i) = *(const f4 *)(vbase + (size_t)k0 * HD + i);
-    __syncthreads();
-#pragma unroll
-    for (int i = 0; i < PER; ++i) {
-      const int idx = tid + 256 * i;
-      if (idx < G * HD) {
-        const int h = idx / HD, dd = idx - h * HD;
-        float acc = o[i] * sA[h];
-        for (int jj = 0; jj < nk; ++jj) acc = fmaf(sP[h * kTile + jj], sK[jj * HD + dd], acc);
-        o[i] = acc;
-      }
+    for (int jj = 0; jj < nk; ++jj) acc = fmaf(sP[h * C + jj], sV[jj * HD + dd], acc);
+    if (DIRECT) {
+      const float v = acc / sL[h];
+      const size_t oi = (size_t)m * p.ldo + (size_t)g * G * HD + idx;
+      if (p.o32) p.o32[oi] = v;
+      if (p.o16) p.o16[oi] = (_Float16)v;
+    } else {
+      part[2 * G + idx] = acc;
     }
   }
-
-  if (DIRECT) {
-#pragma unroll
-    for (int i = 0; i < PER; ++i) {
-      const int idx = tid + 256 * i;
-      if (idx < G * HD) {
-        const float v = o[i] / sL[idx / HD];
-        const size_t oi = (size_t)m * p.ldo + (size_t)g * G * HD + idx;
-        if (p.o32) p.o32[oi] = v;
-        if (p.o16) p.o16[oi] = (_Float16)v;
-      }
-    }
-  } else {
-    const int rec = G * (HD + 2);
-    float *part = p.part.buf + (((size_t)m * p.d.nkv + g) * p.part.n_chunks + c) * rec;
-    if (tid < G) {
-      part[tid] = sM[tid];
-      part[G + tid] = sL[tid];
-    }
-#pragma unroll
-    for (int i = 0; i < PER; ++i) {
-      const int idx = tid + 256 * i;
-      if (idx < G * HD) part[2 * G + idx] = o[i];
-    }
+  if (!DIRECT && tid < G) {
+    part[tid] = sM[tid];
+    part[G + tid] = sL[tid];
   }
 }
 
@@ -157,7 +121,7 @@ __global__ __launch_bounds__(256) void k_attn_merge(AttnDecP p) {
   const int g = blockIdx.x, m = blockIdx.y;
   const int G = p.d.group;
   const int P = p.rows.pos[m] + 1;
-  const int nch = (P + kSplitKeys - 1) / kSplitKeys;
+  const int nch = (P + kChunkKeys - 1) / kChunkKeys;
   const int rec = G * (HD + 2);
   const float *base = p.part.buf + ((size_t)m * p.d.nkv + g) * p.part.n_chunks * rec;
   for (int idx = threadIdx.x; idx < G * HD; idx += 256) {
@@ -178,24 +142,227 @@ __global__ __launch_bounds__(256) void k_attn_merge(AttnDecP p) {
   }
 }
 
+// ------------------------------------------------- attention fused with WO
+// For short contexts (all rows at positions < kFusedKeys) on the decode
+// path: one block per (WO row chunk, query head).  The block computes its
+// head's attention output for every row (online softmax over 256-key tiles:
+// thread t scores key t, wavefront w and lane d accumulate P.V for keys
+// 64w..64w+63 of the tile), then multiplies it by its slice of WO,
+// WO[chunk rows, head columns], and adds the partial sums into the residual
+// rows with float atomics.  Nothing reads the residual while this kernel
+// runs, so the adds only race with each other (summation order varies by an
+// ulp from run to run).  The WO slice is loaded at kernel start, so its
+// latency overlaps the attention.
+struct AttnWoP {
+  Dims d;
+  int layer;
+  KVCache kv;
+  const float *q;
+  int ldq;
+  RowInfo rows;
+  int M;
+  const _Float16 *wo;
+  float *h;
+  int ldh;
+  int rows_per_block;
+  float scale;
+};
+
+template <int N>
+__device__ __forceinline__ float group_sum(float v) {  // sum within aligned groups of N lanes
+  if (N >= 2) v += dpp<0xB1>(v);
+  if (N >= 4) v += dpp<0x4E>(v);
+  if (N >= 8) v += dpp<0x141>(v);
+  if (N >= 16) v += dpp<0x140>(v);
+  return v;
+}
+
+template <int HD, int MT>
+__global__ __launch_bounds__(256) void k_attn_wo(AttnWoP p) {
+  constexpr int LD = HD >= 64 ? 64 : HD;  // lanes along the head dimension in P.V
+  constexpr int PH = 64 / LD;
+  constexpr int DPL = HD / LD;
+  constexpr int KPL = 64 / PH;
+  constexpr int LPR = HD / 8;              // lanes per WO row segment (8 halves each)
+  constexpr int RPI = 64 / LPR;            // WO rows per wavefront load
+  constexpr int WI = kWoLoadsPerWave;      // WO loads per wavefront
+  __shared__ __attribute__((aligned(16))) float sQ[HD];
+  __shared__ float sP[256];
+  __shared__ float sRed[2][4];
+  __shared__ float sOp[4 * PH * HD];
+  __shared__ __attribute__((aligned(16))) float sO[MT * HD];
+
+  const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
+  const int rc = blockIdx.x, head = blockIdx.y;
+  const int G = p.d.group, H = p.d.H, nhd = p.d.nh * HD;
+  const int g = head / G;
+  const int M = p.M;
+
+  // WO slice loads first
+  const int r0 = rc * p.rows_per_block;
+  const int rend = min(H, r0 + p.rows_per_block);
+  const int kc = lane % LPR;
+  h8 wreg[WI];
+#pragma unroll
+  for (int i = 0; i < WI; ++i) {
+    const int row = r0 + (w * WI + i) * RPI + lane / LPR;
+    if (row < rend)
+      wreg[i] = __builtin_nontemporal_load(
+          (const h8 *)(p.wo + (size_t)row * nhd + (size_t)head * HD + kc * 8));
+    else
+      wreg[i] = (h8){0, 0, 0, 0, 0, 0, 0, 0};
+  }
+
+  const int d_lane = lane % LD, ph = lane / LD;
+  for (int m = 0; m < M; ++m) {
+    const int pos = p.rows.pos[m], seq = p.rows.seq[m];
+    const int P = pos + 1;
+    const float *kbase = p.kv.k + p.kv.off(p.d, p.layer, seq, g, 0);
+    const float *vbase = p.kv.v + p.kv.off(p.d, p.layer, seq, g, 0);
+    __syncthreads();  // sQ / sOp of the previous row are consumed
+    if (tid < HD) sQ[tid] = p.q[(size_t)m * p.ldq + (size_t)head * HD + tid] * p.scale;
+    __syncthreads();
+    float m_run = kNegInf, l_run = 0.f;
+    float o[DPL];
+#pragma unroll
+    for (int dd = 0; dd < DPL; ++dd) o[dd] = 0.f;
+    for (int t0 = 0; t0 < P; t0 += 256) {
+      const int j = t0 + tid;
+      // V values this lane needs for the tile, loaded before the softmax
+      float v[KPL][DPL];
+#pragma unroll
+      for (int i = 0; i < KPL; ++i) {
+        const int jj = t0 + 64 * w + ph + PH * i;
+#pragma unroll
+        for (int dd = 0; dd < DPL; ++dd)
+          v[i][dd] = jj < P ? vbase[(size_t)jj * HD + d_lane + LD * dd] : 0.f;
+      }
+      float s = kNegInf;
+      if (j < P) {
+        float a = 0.f;
+#pragma unroll
+        for (int i = 0; i < HD / 4; ++i) {
+          const f4 kv4 = *(const f4 *)(kbase + (size_t)j * HD + 4 * i);
+          const f4 qv = *(const f4 *)(sQ + 4 * i);
+          a = fmaf(qv.x, kv4.x, fmaf(qv.y, kv4.y, fmaf(qv.z, kv4.z, fmaf(qv.w, kv4.w, a))));
+        }
+        s = a;
+      }
+      const float wm = wave_max(s);
+      if (lane == 0) sRed[0][w] = wm;
+      __syncthreads();
+      const float mx = fmaxf(fmaxf(sRed[0][0], sRed[0][1]), fmaxf(sRed[0][2], sRed[0][3]));
+      const float m_new = fmaxf(m_run, mx);
+      const float alpha = __expf(m_run - m_new);
+      const float e = j < P ? __expf(s - m_new) : 0.f;
+      sP[tid] = e;
+      const float ws = wave_sum(e);
+      if (lane == 0) sRed[1][w] = ws;
+      __syncthreads();
+      const float sum = (sRed[1][0] + sRed[1][1]) + (sRed[1][2] + sRed[1][3]);
+      l_run = l_run * alpha + sum;
+      m_run = m_new;
+#pragma unroll
+      for (int dd = 0; dd < DPL; ++dd) o[dd] *= alpha;
+#pragma unroll
+      for (int i = 0; i < KPL; ++i) {
+        const float pj = sP[64 * w + ph + PH * i];
+#pragma unroll
+        for (int dd = 0; dd < DPL; ++dd) o[dd] = fmaf(pj, v[i][dd], o[dd]);
+      }
+      __syncthreads();  // sP and sRed are reused by the next tile
+    }
+#pragma unroll
+    for (int dd = 0; dd < DPL; ++dd) sOp[(w * PH + ph) * HD + d_lane + LD * dd] = o[dd];
+    __syncthreads();
+    if (tid < HD) {
+      float acc = 0.f;
+#pragma unroll
+      for (int k = 0; k < 4 * PH; ++k) acc += sOp[k * HD + tid];
+      sO[m * HD + tid] = acc / l_run;
+    }
+  }
+  __syncthreads();
+
+  // WO slice times the head outputs; partial row sums added into the residual
+#pragma unroll
+  for (int i = 0; i < WI; ++i) {
+    const int row = r0 + (w * WI + i) * RPI + lane / LPR;
+#pragma unroll
+    for (int m = 0; m < MT; ++m) {
+      if (m < M) {
+        const f4 o0 = *(const f4 *)(sO + m * HD + kc * 8);
+        const f4 o1 = *(const f4 *)(sO + m * HD + kc * 8 + 4);
+        float a = (float)wreg[i][0] * o0.x;
+        a = fmaf((float)wreg[i][1], o0.y, a);
+        a = fmaf((float)wreg[i][2], o0.z, a);
+        a = fmaf((float)wreg[i][3], o0.w, a);
+        a = fmaf((float)wreg[i][4], o1.x, a);
+        a = fmaf((float)wreg[i][5], o1.y, a);
+        a = fmaf((float)wreg[i][6], o1.z, a);
+        a = fmaf((float)wreg[i][7], o1.w, a);
+        a = group_sum<LPR>(a);
+        if (kc == 0 && row < rend) atomicAdd(p.h + (size_t)m * p.ldh + row, a);
+      }
+    }
+  }
+}
+
 template <int HD>
-static void attn_decode_hd(const AttnDecP &p, int M, int n_split, hipStream_t st) {
-  if (n_split <= 1) {
-    hipLaunchKernelGGL((k_attn_decode<HD, true>), dim3(1, p.d.nkv, M), dim3(256), 0, st, p);
+static void attn_wo_hd(const AttnWoP &p, int grid_x, hipStream_t st) {
+  dim3 grid(grid_x, p.d.nh);
+  if (p.M <= 1)
+    hipLaunchKernelGGL((k_attn_wo<HD, 1>), grid, dim3(256), 0, st, p);
+  else
+    hipLaunchKernelGGL((k_attn_wo<HD, 8>), grid, dim3(256), 0, st, p);
+}
+
+void attn_wo_fused(const Dims &d, int layer, const KVCache &kv, const float *q, int ldq,
+                   RowInfo rows, int M, const uint16_t *wo, float *h, int ldh, hipStream_t st) {
+  const int rpb = 4 * kWoLoadsPerWave * (64 / (d.hd / 8));  // WO rows per block
+  AttnWoP p{d, layer, kv, q, ldq, rows, M, (const _Float16 *)wo, h, ldh, rpb,
+            1.0f / sqrtf((float)d.hd)};
+  const int gx = (d.H + rpb - 1) / rpb;
+  switch (d.hd) {
+    case 16: attn_wo_hd<16>(p, gx, st); break;
+    case 64: attn_wo_hd<64>(p, gx, st); break;
+    default: attn_wo_hd<128>(p, gx, st); break;
+  }
+}
+
+template <int HD, int G>
+static void attn_decode_g(const AttnDecP &p, int M, int n_chunks, bool merge, hipStream_t st) {
+  if (n_chunks <= 1) {
+    hipLaunchKernelGGL((k_attn_decode<HD, G, true>), dim3(1, p.d.nkv, M), dim3(256), 0, st, p);
   } else {
-    hipLaunchKernelGGL((k_attn_decode<HD, false>), dim3(n_split, p.d.nkv, M), dim3(256), 0, st, p);
-    hipLaunchKernelGGL((k_attn_merge<HD>), dim3(p.d.nkv, M), dim3(256), 0, st, p);
+    hipLaunchKernelGGL((k_attn_decode<HD, G, false>), dim3(n_chunks, p.d.nkv, M), dim3(256), 0,
+                       st, p);
+    if (merge) hipLaunchKernelGGL((k_attn_merge<HD>), dim3(p.d.nkv, M), dim3(256), 0, st, p);
+  }
+}
+
+template <int HD>
+static void attn_decode_hd(const AttnDecP &p, int M, int n_chunks, bool merge, hipStream_t st) {
+  switch (p.d.group) {  // the group size is a compile-time constant of the kernel
+    case 1: attn_decode_g<HD, 1>(p, M, n_chunks, merge, st); break;
+    case 2: attn_decode_g<HD, 2>(p, M, n_chunks, merge, st); break;
+    case 3: attn_decode_g<HD, 3>(p, M, n_chunks, merge, st); break;
+    case 4: attn_decode_g<HD, 4>(p, M, n_chunks, merge, st); break;
+    case 5: attn_decode_g<HD, 5>(p, M, n_chunks, merge, st); break;
+    case 6: attn_decode_g<HD, 6>(p, M, n_chunks, merge, st); break;
+    case 7: attn_decode_g<HD, 7>(p, M, n_chunks, merge, st); break;
+    default: attn_decode_g<HD, 8>(p, M, n_chunks, merge, st); break;
   }
 }
 
 void attn_decode(const Dims &d, int layer, const KVCache &kv, const float *q, int ldq,
-                 RowInfo rows, int M, int n_split, const AttnPartials &part, float *o32,
-                 _Float16 *o16, int ldo, hipStream_t st) {
+                 RowInfo rows, int M, int n_chunks, bool merge, const AttnPartials &part,
+                 float *o32, _Float16 *o16, int ldo, hipStream_t st) {
   AttnDecP p{d, layer, kv, q, ldq, rows, part, o32, o16, ldo, 1.0f / sqrtf((float)d.hd)};
   switch (d.hd) {
-    case 16: attn_decode_hd<16>(p, M, n_split, st); break;
-    case 64: attn_decode_hd<64>(p, M, n_split, st); break;
-    default: attn_decode_hd<128>(p, M, n_split, st); break;
+    case 16: attn_decode_hd<16>(p, M, n_chunks, merge, st); break;
+    case 64: attn_decode_hd<64>(p, M, n_chunks, merge, st); break;
+    default: attn_decode_hd<128>(p, M, n_chunks, merge, st); break;
   }
 }
 

@@ -44,7 +44,10 @@ __global__ __launch_bounds__(256) void k_gemv(GemvP p) {
   const int lane = threadIdx.x & 63;
   const int wave = threadIdx.x >> 6;
   const int K = p.K, M = p.M;
-  const bool norm = EPI != EPI_RESID && p.norm_w != nullptr;
+  constexpr bool kResid = EPI == EPI_RESID;
+  const bool norm = !kResid && p.norm_w != nullptr;
+  const float *xsrc = p.x;
+  const int ldx = p.ldx;
   float *logits = nullptr;
   if (EPI == EPI_LMHEAD) logits = *p.logits;
 
@@ -88,8 +91,8 @@ __global__ __launch_bounds__(256) void k_gemv(GemvP p) {
 #pragma unroll
         for (int m = 0; m < MT; ++m) {
           if (k < K && m < M) {
-            xv[c][m][0] = *(const f4 *)(p.x + (size_t)m * p.ldx + k);
-            xv[c][m][1] = *(const f4 *)(p.x + (size_t)m * p.ldx + k + 4);
+            xv[c][m][0] = *(const f4 *)(xsrc + (size_t)m * ldx + k);
+            xv[c][m][1] = *(const f4 *)(xsrc + (size_t)m * ldx + k + 4);
           } else {
             xv[c][m][0] = (f4){0.f, 0.f, 0.f, 0.f};
             xv[c][m][1] = (f4){0.f, 0.f, 0.f, 0.f};
@@ -144,7 +147,7 @@ __global__ __launch_bounds__(256) void k_gemv(GemvP p) {
 #pragma unroll
       for (int m = 0; m < MT; ++m) acc[r][m] = wave_sum(acc[r][m]);
 
-    if (EPI == EPI_RESID) {
+    if (kResid) {
 #pragma unroll
       for (int r = 0; r < R; ++r)
 #pragma unroll

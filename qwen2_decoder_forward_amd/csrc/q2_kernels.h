@@ -101,16 +101,24 @@ void embed_rows(const uint16_t *E, int H, int V, const int *const *tokens, int t
                 float *h, unsigned int *bad_flag, hipStream_t st);
 
 // Attention.
-constexpr int kSplitKeys = 256;  // keys per split of the decode attention
+constexpr int kChunkKeys = 64;  // keys per block of the decode attention
 struct AttnPartials {
-  float *buf;    // [rows][nkv][n_chunks][group][hd + 2]
-  int n_chunks;  // splits per row: ceil(n_ctx / kSplitKeys)
+  float *buf;    // [rows][nkv][n_chunks][group][hd + 2]: (max, exp-sum, o) per head
+  int n_chunks;  // chunk slots per row: ceil(n_ctx / kChunkKeys)
 };
 // Split-KV attention, one row per query token (decode and short prefills).
-// n_split = ceil((max position of the rows + 1) / kSplitKeys).
+// n_chunks = ceil((max position of the rows + 1) / kChunkKeys).  With one
+// chunk the output is written directly; otherwise the chunk records are
+// merged by the merge kernel when `merge` (else left in the records).
 void attn_decode(const Dims &d, int layer, const KVCache &kv, const float *q, int ldq,
-                 RowInfo rows, int M, int n_split, const AttnPartials &p, float *o32,
-                 _Float16 *o16, int ldo, hipStream_t st);
+                 RowInfo rows, int M, int n_chunks, bool merge, const AttnPartials &p,
+                 float *o32, _Float16 *o16, int ldo, hipStream_t st);
+// Attention fused with WO + residual for M <= 8 rows at positions below
+// kFusedKeys: per (WO row chunk, query head) block, partial row sums added
+// into h with float atomics.
+constexpr int kFusedKeys = 1024, kWoLoadsPerWave = 8;
+void attn_wo_fused(const Dims &d, int layer, const KVCache &kv, const float *q, int ldq,
+                   RowInfo rows, int M, const uint16_t *wo, float *h, int ldh, hipStream_t st);
 // Causal flash attention over MFMA for one prefill pass of M rows of one
 // sequence (positions strictly increasing).
 void attn_prefill(const Dims &d, int layer, const KVCache &kv, const float *q, int ldq,

@@ -292,7 +292,7 @@ int qwen2_load(const qwen2_hparams *hp, const qwen2_weights *w, void *stream, qw
   c->max_rows = std::min(d.n_ctx, kMaxPassRows);
   c->rows_cap = std::max(c->max_rows, d.n_seq);
   c->dec_rows = std::max(d.n_seq, kGemvRows);
-  c->part.n_chunks = (d.n_ctx + q2::kSplitKeys - 1) / q2::kSplitKeys;
+  c->part.n_chunks = (d.n_ctx + q2::kChunkKeys - 1) / q2::kChunkKeys;
   c->io_cap = (size_t)std::max(d.n_ctx, d.n_seq);
   const char *ng = getenv("QWEN2_NO_GRAPH");
   c->use_graphs = !(ng && ng[0] == '1');
@@ -375,7 +375,7 @@ q2::ArgmaxEpi argmax_epi(qwen2_ctx *c) {
   return q2::ArgmaxEpi{(float *const *)&ds->logits, c->best, (int *const *)&ds->argmax};
 }
 
-int splits_for(int max_pos) { return (max_pos + q2::kSplitKeys) / q2::kSplitKeys; }
+int chunks_for(int max_pos) { return (max_pos + q2::kChunkKeys) / q2::kChunkKeys; }
 
 // Brackets one op launch with two events when that op kind is being timed.
 struct OpTimer {
@@ -401,6 +401,25 @@ struct OpTimer {
     call;                           \
   } while (0)
 
+// Attention then WO + residual on the GEMV path (M <= 8 rows, q in q32,
+// output added to rows h).  Short contexts run one fused kernel (head
+// attention times a WO slice, atomically added to h); longer ones run the
+// chunked attention with its merge kernel, then the WO GEMV.
+void attn_wo_gemv(qwen2_ctx *c, int l, const float *q, q2::RowInfo rows, int M, int n_chunks,
+                  float *h, hipStream_t st) {
+  const Dims &d = c->d;
+  const LayerW &w = c->layers[l];
+  const int nhd = d.nh * d.hd;
+  const q2::KVCache kv{c->kc, c->vc};
+  if (n_chunks * q2::kChunkKeys <= q2::kFusedKeys) {
+    TIMED(QWEN2_OP_ATTN, q2::attn_wo_fused(d, l, kv, q, nhd, rows, M, w.wo, h, d.H, st));
+    return;
+  }
+  TIMED(QWEN2_OP_ATTN, q2::attn_decode(d, l, kv, q, nhd, rows, M, n_chunks, true, c->part,
+                                       c->o32, nullptr, nhd, st));
+  TIMED(QWEN2_OP_WO, q2::gemv_resid(w.wo, d.H, nhd, c->o32, nhd, M, h, d.H, st));
+}
+
 q2::QkvEpi qkv_epi(qwen2_ctx *c, int l, const int *pos, const int *seq) {
   q2::QkvEpi e;
   e.bias = c->layers[l].bqkv;
@@ -421,10 +440,8 @@ void tail_row(qwen2_ctx *c, int r, const int *pos, const int *seq, int last_pos,
   const LayerW &w = c->layers[l];
   const int nhd = d.nh * d.hd;
   float *hr = c->h + (size_t)r * d.H;
-  TIMED(QWEN2_OP_ATTN, q2::attn_decode(d, l, q2::KVCache{c->kc, c->vc}, c->q32 + (size_t)r * nhd,
-                                       nhd, q2::RowInfo{pos + r, seq + r}, 1, splits_for(last_pos),
-                                       c->part, c->o32, nullptr, nhd, st));
-  TIMED(QWEN2_OP_WO, q2::gemv_resid(w.wo, d.H, nhd, c->o32, nhd, 1, hr, d.H, st));
+  attn_wo_gemv(c, l, c->q32 + (size_t)r * nhd, q2::RowInfo{pos + r, seq + r}, 1,
+               chunks_for(last_pos), hr, st);
   TIMED(QWEN2_OP_GATEUP, q2::gemv_swiglu(d, w, hr, 1, c->a32, d.I_pad, c->hp.rms_eps, st));
   TIMED(QWEN2_OP_DOWN, q2::gemv_resid(w.wd, d.H, d.I_pad, c->a32, d.I_pad, 1, hr, d.H, st));
   TIMED(QWEN2_OP_LMHEAD, q2::gemv_lmhead(d, c->lm_head, c->out_norm, hr, 1, c->normed,
@@ -443,7 +460,7 @@ void prefill_pass(qwen2_ctx *c, int M, int off, const int *pos, const int *seq, 
   const q2::RowInfo rows{pos, seq};
   TIMED(QWEN2_OP_EMBED, q2::embed_rows(c->tok_embd, d.H, d.V, &dev_slots(c)->tokens, off, M,
                                        c->h, c->bad_flag, st));
-  const int n_split = splits_for(host_pos[M - 1]);
+  const int n_chunks = chunks_for(host_pos[M - 1]);
   const bool gemv = M <= kGemvRows;
   for (int l = 0; l < d.L; ++l) {
     const LayerW &w = c->layers[l];
@@ -457,9 +474,7 @@ void prefill_pass(qwen2_ctx *c, int M, int off, const int *pos, const int *seq, 
     }
     if (l == d.L - 1) break;  // the last layer continues on the last row only
     if (gemv) {
-      TIMED(QWEN2_OP_ATTN, q2::attn_decode(d, l, kv, c->q32, nhd, rows, M, n_split, c->part,
-                                           c->o32, nullptr, nhd, st));
-      TIMED(QWEN2_OP_WO, q2::gemv_resid(w.wo, d.H, nhd, c->o32, nhd, M, c->h, d.H, st));
+      attn_wo_gemv(c, l, c->q32, rows, M, n_chunks, c->h, st);
       TIMED(QWEN2_OP_GATEUP, q2::gemv_swiglu(d, w, c->h, M, c->a32, d.I_pad, eps, st));
       TIMED(QWEN2_OP_DOWN, q2::gemv_resid(w.wd, d.H, d.I_pad, c->a32, d.I_pad, M, c->h, d.H, st));
     } else {
@@ -476,7 +491,7 @@ void prefill_pass(qwen2_ctx *c, int M, int off, const int *pos, const int *seq, 
 }
 
 // Every kernel of one decode step for B rows (replayed from a graph).
-void decode_launches(qwen2_ctx *c, int B, int n_split, const int *dpos, const int *dseq,
+void decode_launches(qwen2_ctx *c, int B, int n_chunks, const int *dpos, const int *dseq,
                      hipStream_t st) {
   const Dims &d = c->d;
   const float eps = c->hp.rms_eps;
@@ -491,17 +506,15 @@ void decode_launches(qwen2_ctx *c, int B, int n_split, const int *dpos, const in
     const q2::QkvEpi e = qkv_epi(c, l, dpos, dseq);
     if (gemv) {
       TIMED(QWEN2_OP_QKV, q2::gemv_qkv(d, w, c->h, B, e, eps, st));
-      TIMED(QWEN2_OP_ATTN, q2::attn_decode(d, l, kv, c->q32, nhd, rows, B, n_split, c->part,
-                                           c->o32, nullptr, nhd, st));
-      TIMED(QWEN2_OP_WO, q2::gemv_resid(w.wo, d.H, nhd, c->o32, nhd, B, c->h, d.H, st));
+      attn_wo_gemv(c, l, c->q32, rows, B, n_chunks, c->h, st);
       TIMED(QWEN2_OP_GATEUP, q2::gemv_swiglu(d, w, c->h, B, c->a32, d.I_pad, eps, st));
       TIMED(QWEN2_OP_DOWN, q2::gemv_resid(w.wd, d.H, d.I_pad, c->a32, d.I_pad, B, c->h, d.H, st));
     } else {
       TIMED(QWEN2_OP_NORM, q2::rmsnorm_rows_f16(c->h, d.H, w.attn_norm, d.H, B, eps, c->x16, d.H,
                                                 nullptr, st));
       TIMED(QWEN2_OP_QKV, q2::gemm_qkv(d, w, c->x16, d.H, B, e, st));
-      TIMED(QWEN2_OP_ATTN, q2::attn_decode(d, l, kv, c->q32, nhd, rows, B, n_split, c->part,
-                                           nullptr, c->x16, nhd, st));
+      TIMED(QWEN2_OP_ATTN, q2::attn_decode(d, l, kv, c->q32, nhd, rows, B, n_chunks, true,
+                                           c->part, nullptr, c->x16, nhd, st));
       TIMED(QWEN2_OP_WO, q2::gemm_resid(w.wo, d.H, nhd, c->x16, nhd, B, c->h, d.H, st));
       TIMED(QWEN2_OP_NORM, q2::rmsnorm_rows_f16(c->h, d.H, w.ffn_norm, d.H, B, eps, c->x16, d.H,
                                                 nullptr, st));
@@ -558,15 +571,15 @@ int qwen2_decode(qwen2_ctx *c, int32_t B, const int32_t *seq_ids, const int32_t 
   const CallSlots slots{tokens_dev, logits_dev, argmax_dev};
   rc = stage_call(c, st, slots, B, 2, fields, df);
   if (rc) return rc;
-  const int n_split = splits_for(*std::max_element(positions, positions + B));
+  const int n_chunks = chunks_for(*std::max_element(positions, positions + B));
   c->last_h = c->h;
   c->last_rows = B;
   if (!c->use_graphs || c->prof_mask) {
-    decode_launches(c, B, n_split, df[0], df[1], st);
+    decode_launches(c, B, n_chunks, df[0], df[1], st);
     HIP_TRY(c, hipGetLastError());
     return QWEN2_OK;
   }
-  auto key = std::make_pair((int)B, n_split);
+  auto key = std::make_pair((int)B, n_chunks);
   auto it = c->graphs.find(key);
   if (it == c->graphs.end()) {
     hipGraph_t g = nullptr;
@@ -575,7 +588,7 @@ int qwen2_decode(qwen2_ctx *c, int32_t B, const int32_t *seq_ids, const int32_t 
     // stream, which cannot be captured); the graph then runs on the caller's
     hipStream_t cs = c->cap_stream;
     HIP_TRY(c, hipStreamBeginCapture(cs, hipStreamCaptureModeThreadLocal));
-    decode_launches(c, B, n_split, df[0], df[1], cs);
+    decode_launches(c, B, n_chunks, df[0], df[1], cs);
     hipError_t e1 = hipStreamEndCapture(cs, &g);
     if (e1 != hipSuccess) return set_err(c, QWEN2_E_HIP, std::string("graph capture: ") + hipGetErrorString(e1));
     hipError_t e2 = hipGraphInstantiate(&ge, g, nullptr, nullptr, 0);

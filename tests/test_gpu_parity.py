@@ -170,7 +170,8 @@ def test_hd128_untied_group7(n):
 def test_graph_replay_matches_direct_launches(tiny_w, monkeypatch):
     """Decode steps replayed from captured graphs (different pointers and
     positions on every replay, eager prefills and host syncs in between) give
-    bit-identical logits to the same kernels launched directly."""
+    the same ids and logits as the same kernels launched directly (up to the
+    float-atomic summation order of the fused attention + WO: 1e-6)."""
     import qwen2_decoder_forward_amd as q
     toks = syn.make_prompt(TINY, 8)
 
@@ -190,4 +191,4 @@ def test_graph_replay_matches_direct_launches(tiny_w, monkeypatch):
     monkeypatch.setenv("QWEN2_NO_GRAPH", "1")
     lg_direct, ids_direct = chain()
     assert np.array_equal(ids_graph, ids_direct)
-    assert np.array_equal(lg_graph, lg_direct)
+    check(lg_graph, lg_direct, 1e-6, "graph vs direct logits")
