@@ -191,6 +191,16 @@ enum {
 };
 int qwen2_prof_enable(qwen2_ctx *ctx, uint32_t op_mask /* bit k = op kind k; 0 disables */);
 int qwen2_prof_read(qwen2_ctx *ctx, int32_t op, int32_t *launches, double *total_ms);
+
+/* Kernel timing for benchmarks: enqueues `iters` back-to-back launches of
+ * one decode-path op (rows <= 8 rows of the context's current activations),
+ * layer i % n_layer for launch i, so that a caller's event pair around the
+ * call measures the op's average duration with the launch-to-launch
+ * overhead amortised.  Cycling through the layers keeps the weight stream
+ * coming from HBM rather than a cache.  Only QWEN2_OP_GATEUP is supported
+ * (it writes only a scratch buffer, so the model state is unchanged);
+ * anything else is QWEN2_E_ARG. */
+int qwen2_prof_repeat(qwen2_ctx *ctx, int32_t op, int32_t rows, int32_t iters, void *stream);
 const char *qwen2_last_error(const qwen2_ctx *ctx); /* ctx may be NULL: last load error */
 const char *qwen2_strerror(int code);
 

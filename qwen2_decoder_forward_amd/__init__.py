@@ -19,7 +19,7 @@ __all__ = [
     "qwen2_check_hparams", "qwen2_check_prefill", "qwen2_check_decode", "qwen2_load",
     "qwen2_prefill", "qwen2_decode", "qwen2_read_hidden", "qwen2_kv_read", "qwen2_kv_write",
     "qwen2_sync_status", "qwen2_info", "qwen2_last_error", "qwen2_strerror", "qwen2_free",
-    "qwen2_prof_enable", "qwen2_prof_read", "OPS", "make_hparams", "Model",
+    "qwen2_prof_enable", "qwen2_prof_read", "qwen2_prof_repeat", "OPS", "make_hparams", "Model",
 ]
 
 LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), "libqwen2_mi355x.so")
@@ -95,6 +95,7 @@ def lib() -> C.CDLL:
             "qwen2_free": (None, [vp]),
             "qwen2_prof_enable": (i32, [vp, C.c_uint32]),
             "qwen2_prof_read": (i32, [vp, i32, PI32, C.POINTER(C.c_double)]),
+            "qwen2_prof_repeat": (i32, [vp, i32, i32, i32, vp]),
         }
         for name, (res, args) in sig.items():
             f = getattr(L, name)
@@ -242,6 +243,11 @@ def qwen2_prof_read(ctx: int, op: str):
     n, ms = C.c_int32(), C.c_double()
     _check(lib().qwen2_prof_read(ctx, OPS[op], C.byref(n), C.byref(ms)), ctx)
     return n.value, ms.value
+
+
+def qwen2_prof_repeat(ctx: int, op: str, rows: int, iters: int, stream=None) -> None:
+    """Enqueue `iters` back-to-back launches of one op (layer i % n_layer)."""
+    _check(lib().qwen2_prof_repeat(ctx, OPS[op], rows, iters, _stream(stream)), ctx)
 
 
 def qwen2_free(ctx: int) -> None:

@@ -705,6 +705,18 @@ int qwen2_prof_read(qwen2_ctx *c, int32_t op, int32_t *launches, double *total_m
   return QWEN2_OK;
 }
 
+int qwen2_prof_repeat(qwen2_ctx *c, int32_t op, int32_t rows, int32_t iters, void *stream) {
+  if (!c || op != QWEN2_OP_GATEUP || rows < 1 || rows > kGemvRows || iters < 1)
+    return set_err(c, QWEN2_E_ARG, "prof_repeat supports QWEN2_OP_GATEUP with 1..8 rows");
+  hipStream_t st = (hipStream_t)stream;
+  for (int i = 0; i < iters; ++i) {
+    const LayerW &w = c->layers[i % c->d.L];
+    q2::gemv_swiglu(c->d, w, c->h, rows, c->a32, c->d.I_pad, c->hp.rms_eps, st);
+  }
+  HIP_TRY(c, hipGetLastError());
+  return QWEN2_OK;
+}
+
 const char *qwen2_last_error(const qwen2_ctx *c) {
   return c ? c->err.c_str() : g_load_error.c_str();
 }
