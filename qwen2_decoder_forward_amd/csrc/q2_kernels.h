@@ -82,12 +82,18 @@ void gemv_lmhead(const Dims &d, const uint16_t *W, const float *norm_w, const fl
 void argmax_finalize(const ArgmaxEpi &e, int M, hipStream_t st);
 
 // MFMA GEMM family (rows M > 8): A f16 [M, lda], W f16 [N, K], K % 32 == 0.
+// GEMMs with few output tiles (small M) split K over blocks; the f32 partial
+// sums go to a context-owned workspace and a small kernel applies the op.
+struct Workspace {
+  float *buf;
+  size_t bytes;
+};
 void gemm_qkv(const Dims &d, const LayerW &w, const _Float16 *x, int lda, int M,
-              const QkvEpi &e, hipStream_t st);
+              const QkvEpi &e, const Workspace &ws, hipStream_t st);
 void gemm_resid(const uint16_t *W, int N, int K, const _Float16 *x, int lda, int M, float *h,
-                int ldh, hipStream_t st);
+                int ldh, const Workspace &ws, hipStream_t st);
 void gemm_swiglu(const Dims &d, const LayerW &w, const _Float16 *x, int lda, int M,
-                 _Float16 *a, int ld_a, hipStream_t st);
+                 _Float16 *a, int ld_a, const Workspace &ws, hipStream_t st);
 void gemm_lmhead(const Dims &d, const uint16_t *W, const _Float16 *x, int lda, int M,
                  const ArgmaxEpi &e, hipStream_t st);
 

@@ -25,6 +25,7 @@ constexpr int kGemvRows = 8;      // rows up to this use the f32 GEMV path
 constexpr int kMaxPassRows = 4096;  // rows per prefill pass
 constexpr int kProfMax = 16384;     // timed launches between two reads
 constexpr size_t kSlotBytes = 64;   // pointer slots at the head of a staged call
+constexpr size_t kSplitKBytes = 48ull << 20;  // split-K partial sums
 
 thread_local std::string g_load_error;
 
@@ -62,6 +63,7 @@ struct qwen2_ctx {
   char *io = nullptr;
   size_t io_cap = 0;  // int entries per field
   q2::AttnPartials part{};
+  q2::Workspace splitk{};  // split-K partial sums of the small-M GEMMs
   unsigned long long *best = nullptr;
   unsigned int *bad_flag = nullptr;
   // captured decode steps, keyed by (batch size, attention splits)
@@ -303,7 +305,7 @@ int qwen2_load(const qwen2_hparams *hp, const qwen2_weights *w, void *stream, qw
          s_a16 = take(R * Ip * 2), s_o32 = take(D * nhd * 4), s_a32 = take(D * Ip * 4),
          s_norm = take(D * H * 4), s_io = take(kSlotBytes + 3 * c->io_cap * 4),
          s_part = take((size_t)D * d.nkv * c->part.n_chunks * d.group * (d.hd + 2) * 4),
-         s_best = take(D * 8), s_bad = take(4);
+         s_best = take(D * 8), s_bad = take(4), s_splitk = take(kSplitKBytes);
     c->sarena_bytes = cur;
     LTRY([&]() -> int {
       HIP_TRY(c, hipMalloc(&c->sarena, c->sarena_bytes));
@@ -321,6 +323,7 @@ int qwen2_load(const qwen2_hparams *hp, const qwen2_weights *w, void *stream, qw
     c->io = S + s_io.off;
     c->part.buf = (float *)(S + s_part.off);
     c->best = (unsigned long long *)(S + s_best.off);
+    c->splitk = q2::Workspace{(float *)(S + s_splitk.off), kSplitKBytes};
     c->bad_flag = (unsigned *)(S + s_bad.off);
   }
   LTRY([&]() -> int {
@@ -470,7 +473,7 @@ void prefill_pass(qwen2_ctx *c, int M, int off, const int *pos, const int *seq, 
     } else {
       TIMED(QWEN2_OP_NORM, q2::rmsnorm_rows_f16(c->h, d.H, w.attn_norm, d.H, M, eps, c->x16, d.H,
                                                 nullptr, st));
-      TIMED(QWEN2_OP_QKV, q2::gemm_qkv(d, w, c->x16, d.H, M, e, st));
+      TIMED(QWEN2_OP_QKV, q2::gemm_qkv(d, w, c->x16, d.H, M, e, c->splitk, st));
     }
     if (l == d.L - 1) break;  // the last layer continues on the last row only
     if (gemv) {
@@ -479,12 +482,12 @@ void prefill_pass(qwen2_ctx *c, int M, int off, const int *pos, const int *seq, 
       TIMED(QWEN2_OP_DOWN, q2::gemv_resid(w.wd, d.H, d.I_pad, c->a32, d.I_pad, M, c->h, d.H, st));
     } else {
       TIMED(QWEN2_OP_ATTN, q2::attn_prefill(d, l, kv, c->q32, nhd, rows, M, c->x16, nhd, st));
-      TIMED(QWEN2_OP_WO, q2::gemm_resid(w.wo, d.H, nhd, c->x16, nhd, M, c->h, d.H, st));
+      TIMED(QWEN2_OP_WO, q2::gemm_resid(w.wo, d.H, nhd, c->x16, nhd, M, c->h, d.H, c->splitk, st));
       TIMED(QWEN2_OP_NORM, q2::rmsnorm_rows_f16(c->h, d.H, w.ffn_norm, d.H, M, eps, c->x16, d.H,
                                                 nullptr, st));
-      TIMED(QWEN2_OP_GATEUP, q2::gemm_swiglu(d, w, c->x16, d.H, M, c->a16, d.I_pad, st));
+      TIMED(QWEN2_OP_GATEUP, q2::gemm_swiglu(d, w, c->x16, d.H, M, c->a16, d.I_pad, c->splitk, st));
       TIMED(QWEN2_OP_DOWN,
-            q2::gemm_resid(w.wd, d.H, d.I_pad, c->a16, d.I_pad, M, c->h, d.H, st));
+            q2::gemm_resid(w.wd, d.H, d.I_pad, c->a16, d.I_pad, M, c->h, d.H, c->splitk, st));
     }
   }
   if (last) tail_row(c, M - 1, pos, seq, host_pos[M - 1], st);
@@ -512,15 +515,15 @@ void decode_launches(qwen2_ctx *c, int B, int n_chunks, const int *dpos, const i
     } else {
       TIMED(QWEN2_OP_NORM, q2::rmsnorm_rows_f16(c->h, d.H, w.attn_norm, d.H, B, eps, c->x16, d.H,
                                                 nullptr, st));
-      TIMED(QWEN2_OP_QKV, q2::gemm_qkv(d, w, c->x16, d.H, B, e, st));
+      TIMED(QWEN2_OP_QKV, q2::gemm_qkv(d, w, c->x16, d.H, B, e, c->splitk, st));
       TIMED(QWEN2_OP_ATTN, q2::attn_decode(d, l, kv, c->q32, nhd, rows, B, n_chunks, true,
                                            c->part, nullptr, c->x16, nhd, st));
-      TIMED(QWEN2_OP_WO, q2::gemm_resid(w.wo, d.H, nhd, c->x16, nhd, B, c->h, d.H, st));
+      TIMED(QWEN2_OP_WO, q2::gemm_resid(w.wo, d.H, nhd, c->x16, nhd, B, c->h, d.H, c->splitk, st));
       TIMED(QWEN2_OP_NORM, q2::rmsnorm_rows_f16(c->h, d.H, w.ffn_norm, d.H, B, eps, c->x16, d.H,
                                                 nullptr, st));
-      TIMED(QWEN2_OP_GATEUP, q2::gemm_swiglu(d, w, c->x16, d.H, B, c->a16, d.I_pad, st));
+      TIMED(QWEN2_OP_GATEUP, q2::gemm_swiglu(d, w, c->x16, d.H, B, c->a16, d.I_pad, c->splitk, st));
       TIMED(QWEN2_OP_DOWN,
-            q2::gemm_resid(w.wd, d.H, d.I_pad, c->a16, d.I_pad, B, c->h, d.H, st));
+            q2::gemm_resid(w.wd, d.H, d.I_pad, c->a16, d.I_pad, B, c->h, d.H, c->splitk, st));
     }
   }
   if (gemv) {

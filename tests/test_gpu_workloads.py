@@ -1,0 +1,120 @@
+"""GPU parity on the full-size workloads (besides the benchmark's own):
+
+* 0.5B shape, 4096-token prompt (n_ctx 8192), then decode steps past 4096
+  (chunked attention with the merge kernel);
+* 0.5B shape, 64 sequences with 1024-token prefixes, one batched decode step
+  at position 1024 (MFMA path): the oracle prefills sequences 0 and 63 itself
+  and, for the others, decodes from the GPU's KV cache read back;
+* the hd-128 / group-7 / untied shape at full width (2 layers) with a
+  2048-token prompt against the oracle, and the full 28-layer model checked
+  for properties that hold at any size (prefill of n+1 tokens = prefill of n
+  then one decode step; argmax = lowest index of the largest logit).
+"""
+import numpy as np
+import pytest
+
+torch = pytest.importorskip("torch")
+if not torch.cuda.is_available():
+    pytest.skip("no GPU", allow_module_level=True)
+
+import qwen2_synth as syn  # noqa: E402
+from gpu_common import DEV, Pair, check, check_id, run_chain, say  # noqa: E402
+
+pytestmark = pytest.mark.gpu
+
+S = syn.MODELS["qwen2.5-0.5b"]
+TOL = 1e-2
+
+
+@pytest.fixture(scope="module")
+def w05():
+    say("[workloads] drawing 0.5B weights")
+    return syn.make_weights(S)
+
+
+def test_long_context_prompt_4096_then_decode(w05):
+    p = Pair(S, w05, n_ctx=8192, cache_decoded=True)
+    run_chain(p, syn.make_prompt(S, 4096, 7), 4, TOL, "0.5b-long")
+    p.close()
+
+
+def test_batched_decode_64_sequences_at_1024(w05):
+    B, n = 64, 1024
+    p = Pair(S, w05, n_ctx=2048, n_seq=B, cache_decoded=True)
+    prompts = [syn.make_prompt(S, n, 100 + j) for j in range(B)]
+    say("[batched] GPU prefill of 64 x 1024")
+    for j in range(B):
+        p.m.prefill(j, prompts[j], np.arange(n), None, None)
+    torch.cuda.synchronize()
+    L, nkv, hd = S.n_layer, S.n_head_kv, S.head_dim
+    k = torch.empty((nkv, n, hd), device=DEV)
+    v = torch.empty((nkv, n, hd), device=DEV)
+    for j in (0, B - 1):
+        say(f"[batched] oracle prefill of sequence {j}")
+        p.o.prefill(j, prompts[j], np.arange(n))
+        for l in range(L):
+            p.m.kv_read(l, j, 0, n, k, v)
+            torch.cuda.synchronize()
+            check(k.cpu().numpy(), p.o.k_cache[j][l][:, :n], TOL, f"seq {j} layer {l} K")
+            check(v.cpu().numpy(), p.o.v_cache[j][l][:, :n], TOL, f"seq {j} layer {l} V")
+    say("[batched] handing the GPU cache of sequences 1..62 to the oracle")
+    for j in range(1, B - 1):
+        Kc, Vc = p.o._cache(j)
+        for l in range(L):
+            p.m.kv_read(l, j, 0, n, k, v)
+            torch.cuda.synchronize()
+            Kc[l][:, :n] = k.cpu().numpy()
+            Vc[l][:, :n] = v.cpu().numpy()
+    seqs = list(range(B))
+    toks = [int(t) for t in syn.make_prompt(S, B, 999)]
+    say("[batched] decode step of 64 rows")
+    lg, ids, r = p.decode(seqs, toks, [n] * B)
+    n_ids = 0
+    for b in range(B):
+        check(lg[b], r.logits[b], TOL, f"batched row {b} logits")
+        n_ids += int(check_id(ids[b], r.logits[b], r.argmax[b], f"batched row {b}"))
+    check(p.hidden(0, B), r.layer_output, TOL, "batched layer_output")
+    check(p.hidden(1, B), r.final_norm_output, TOL, "batched final_norm_output")
+    say(f"[batched] ids checked {n_ids}/{B}")
+    p.close()
+
+
+def test_hd128_full_width_two_layers_prompt_2048():
+    G2 = syn.model_shape("qwen2-hd128", n_layer=2)
+    say("[hd128-L2] drawing weights")
+    w = syn.make_weights(G2)
+    p = Pair(G2, w, n_ctx=4096)
+    run_chain(p, syn.make_prompt(G2, 2048), 2, TOL, "hd128-L2")
+    p.close()
+
+
+def test_hd128_full_model_properties():
+    """28 layers, hidden 3584: no oracle at this size; properties that hold at
+    any size, checked on the GPU path itself."""
+    import qwen2_decoder_forward_amd as q
+    G = syn.MODELS["qwen2-hd128"]
+    say("[hd128] drawing 28-layer weights")
+    w = syn.make_weights(G)
+    m = q.Model(G, w, n_ctx=4096)
+    info = m.info()
+    assert info.weight_bytes_f16 == syn.weight_bytes(G)["f16"]
+    prompt = syn.make_prompt(G, 2048)
+    V = G.n_vocab
+    lg_a = torch.empty(V, device=DEV)
+    id_a = torch.zeros(1, dtype=torch.int32, device=DEV)
+    say("[hd128] prefill 2048")
+    m.prefill(0, prompt, np.arange(2048), lg_a, id_a)
+    lg_b = torch.empty(V, device=DEV)
+    id_b = torch.zeros(1, dtype=torch.int32, device=DEV)
+    m2 = q.Model(G, w, n_ctx=4096)
+    say("[hd128] prefill 2047 + decode 1")
+    m2.prefill(0, prompt[:2047], np.arange(2047), None, None)
+    m2.decode([0], torch.tensor(prompt[2047:], dtype=torch.int32, device=DEV), [2047], lg_b, id_b)
+    torch.cuda.synchronize()
+    a, b = lg_a.cpu().numpy(), lg_b.cpu().numpy()
+    assert np.all(np.isfinite(a)) and np.all(np.isfinite(b))
+    check(b, a, TOL, "hd128: prefill(n) vs prefill(n-1) + decode")
+    assert int(id_a.item()) == int(np.argmax(a))
+    assert int(id_b.item()) == int(np.argmax(b))
+    m.close()
+    m2.close()
