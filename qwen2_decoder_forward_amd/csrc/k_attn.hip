@@ -179,17 +179,28 @@ __device__ __forceinline__ float group_sum(float v) {  // sum within aligned gro
 
 template <int HD, int MT>
 __global__ __launch_bounds__(256) void k_attn_wo(AttnWoP p) {
-  constexpr int LD = HD >= 64 ? 64 : HD;  // lanes along the head dimension in P.V
+  constexpr int TK = HD >= 128 ? 128 : 256;  // keys per tile (one per thread up to TK)
+  constexpr int C4 = HD / 4;                 // 16-byte chunks per K row
+  constexpr int KPT = TK * C4 / 256;         // K chunks loaded per thread
+  constexpr int KW = TK / 4;                 // keys per wavefront in P.V
+  // P.V: a lane holds 4 consecutive dims (one 16-byte load per key), LD lanes
+  // cover a V row and the PH lane groups of a wavefront take interleaved keys,
+  // so a lane issues KPL 16-byte V loads (K: KPT, WO: 8; all within the 63
+  // loads a wavefront can have outstanding).
+  constexpr int LD = HD / 4;
   constexpr int PH = 64 / LD;
-  constexpr int DPL = HD / LD;
-  constexpr int KPL = 64 / PH;
+  constexpr int KPL = KW / PH;
   constexpr int LPR = HD / 8;              // lanes per WO row segment (8 halves each)
   constexpr int RPI = 64 / LPR;            // WO rows per wavefront load
   constexpr int WI = kWoLoadsPerWave;      // WO loads per wavefront
+  // K tile in LDS, 16-byte chunk c of key row j stored at chunk c ^ (j % C4):
+  // a lane walking its own row meets a different bank group than its
+  // neighbours, so the row reads are conflict-free without padding.
+  __shared__ f4 sK[TK * C4];
   __shared__ __attribute__((aligned(16))) float sQ[HD];
-  __shared__ float sP[256];
+  __shared__ float sP[TK];
   __shared__ float sRed[2][4];
-  __shared__ float sOp[4 * PH * HD];
+  __shared__ __attribute__((aligned(16))) float sOp[4 * PH * HD];
   __shared__ __attribute__((aligned(16))) float sO[MT * HD];
 
   const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
@@ -217,34 +228,42 @@ __global__ __launch_bounds__(256) void k_attn_wo(AttnWoP p) {
   for (int m = 0; m < M; ++m) {
     const int pos = p.rows.pos[m], seq = p.rows.seq[m];
     const int P = pos + 1;
-    const float *kbase = p.kv.k + p.kv.off(p.d, p.layer, seq, g, 0);
+    const f4 *kbase = (const f4 *)(p.kv.k + p.kv.off(p.d, p.layer, seq, g, 0));
     const float *vbase = p.kv.v + p.kv.off(p.d, p.layer, seq, g, 0);
-    __syncthreads();  // sQ / sOp of the previous row are consumed
-    if (tid < HD) sQ[tid] = p.q[(size_t)m * p.ldq + (size_t)head * HD + tid] * p.scale;
-    __syncthreads();
+    const float qv = tid < HD ? p.q[(size_t)m * p.ldq + (size_t)head * HD + tid] * p.scale : 0.f;
     float m_run = kNegInf, l_run = 0.f;
-    float o[DPL];
+    f4 o = {0.f, 0.f, 0.f, 0.f};
+    for (int t0 = 0; t0 < P; t0 += TK) {
+      // this tile's K chunks (coalesced) and the V values of this lane's keys
+      f4 kr[KPT];
 #pragma unroll
-    for (int dd = 0; dd < DPL; ++dd) o[dd] = 0.f;
-    for (int t0 = 0; t0 < P; t0 += 256) {
-      const int j = t0 + tid;
-      // V values this lane needs for the tile, loaded before the softmax
-      float v[KPL][DPL];
+      for (int i = 0; i < KPT; ++i) {
+        const int ci = tid + 256 * i, j = ci / C4;
+        kr[i] = t0 + j < P ? kbase[(size_t)t0 * C4 + ci] : (f4){0.f, 0.f, 0.f, 0.f};
+      }
+      f4 v[KPL];
 #pragma unroll
       for (int i = 0; i < KPL; ++i) {
-        const int jj = t0 + 64 * w + ph + PH * i;
-#pragma unroll
-        for (int dd = 0; dd < DPL; ++dd)
-          v[i][dd] = jj < P ? vbase[(size_t)jj * HD + d_lane + LD * dd] : 0.f;
+        const int jj = t0 + KW * w + ph + PH * i;
+        v[i] = jj < P ? *(const f4 *)(vbase + (size_t)jj * HD + 4 * d_lane) : (f4){0.f, 0.f, 0.f, 0.f};
       }
+      __syncthreads();  // the previous tile's (or row's) LDS reads are done
+#pragma unroll
+      for (int i = 0; i < KPT; ++i) {
+        const int ci = tid + 256 * i, j = ci / C4, c = ci - j * C4;
+        sK[j * C4 + (c ^ (j % C4))] = kr[i];
+      }
+      if (tid < HD) sQ[tid] = qv;
+      __syncthreads();
+      const int j = t0 + tid;
       float s = kNegInf;
-      if (j < P) {
+      if (tid < TK && j < P) {
         float a = 0.f;
 #pragma unroll
-        for (int i = 0; i < HD / 4; ++i) {
-          const f4 kv4 = *(const f4 *)(kbase + (size_t)j * HD + 4 * i);
-          const f4 qv = *(const f4 *)(sQ + 4 * i);
-          a = fmaf(qv.x, kv4.x, fmaf(qv.y, kv4.y, fmaf(qv.z, kv4.z, fmaf(qv.w, kv4.w, a))));
+        for (int c = 0; c < C4; ++c) {
+          const f4 kv4 = sK[tid * C4 + (c ^ (tid % C4))];
+          const f4 q4 = *(const f4 *)(sQ + 4 * c);
+          a = fmaf(q4.x, kv4.x, fmaf(q4.y, kv4.y, fmaf(q4.z, kv4.z, fmaf(q4.w, kv4.w, a))));
         }
         s = a;
       }
@@ -254,26 +273,20 @@ __global__ __launch_bounds__(256) void k_attn_wo(AttnWoP p) {
       const float mx = fmaxf(fmaxf(sRed[0][0], sRed[0][1]), fmaxf(sRed[0][2], sRed[0][3]));
       const float m_new = fmaxf(m_run, mx);
       const float alpha = __expf(m_run - m_new);
-      const float e = j < P ? __expf(s - m_new) : 0.f;
-      sP[tid] = e;
+      const float e = (tid < TK && j < P) ? __expf(s - m_new) : 0.f;
+      if (tid < TK) sP[tid] = e;
       const float ws = wave_sum(e);
       if (lane == 0) sRed[1][w] = ws;
       __syncthreads();
       const float sum = (sRed[1][0] + sRed[1][1]) + (sRed[1][2] + sRed[1][3]);
       l_run = l_run * alpha + sum;
       m_run = m_new;
+      o *= alpha;
 #pragma unroll
-      for (int dd = 0; dd < DPL; ++dd) o[dd] *= alpha;
-#pragma unroll
-      for (int i = 0; i < KPL; ++i) {
-        const float pj = sP[64 * w + ph + PH * i];
-#pragma unroll
-        for (int dd = 0; dd < DPL; ++dd) o[dd] = fmaf(pj, v[i][dd], o[dd]);
-      }
-      __syncthreads();  // sP and sRed are reused by the next tile
+      for (int i = 0; i < KPL; ++i) o += sP[KW * w + ph + PH * i] * v[i];
     }
-#pragma unroll
-    for (int dd = 0; dd < DPL; ++dd) sOp[(w * PH + ph) * HD + d_lane + LD * dd] = o[dd];
+    __syncthreads();  // sOp of the previous row is consumed
+    *(f4 *)(sOp + (w * PH + ph) * HD + 4 * d_lane) = o;
     __syncthreads();
     if (tid < HD) {
       float acc = 0.f;
