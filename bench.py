@@ -13,6 +13,10 @@ tokens/s, the HBM fractions and the roofline of the dominant kernel (the
 fused RMSNorm + gate/up + SwiGLU GEMV, timed per launch with HIP events on
 the stream it runs on) sit beside it, with the CPU oracle timed on a bounded
 sample of the same workload.
+
+`--workload` selects one of the other workloads of the same model family
+(4096-token prompt, 64 sequences decoded together, the hd-128 shape); for
+those the line also carries per-projection MFMA fractions of the prefill.
 """
 from __future__ import annotations
 
@@ -74,6 +78,50 @@ def cpu_baseline(shape, weights, prompt, n_ctx, budget_s):
     }
 
 
+def prefill_gemm_flops(shape, n: int) -> dict:
+    """Dense flops of each projection of a prefill of n rows (the last layer's
+    FFN runs on the last row only) and of the lm_head on that row."""
+    H, I, hd = shape.n_embd, shape.n_ff, shape.head_dim
+    nq, nkv, L = shape.n_head * hd, shape.n_head_kv * hd, shape.n_layer
+    return {
+        "qkv": 2 * n * L * H * (nq + 2 * nkv),
+        "wo": 2 * n * L * nq * H,
+        "gateup": 2 * (n * (L - 1) + 1) * 2 * I * H,
+        "down": 2 * (n * (L - 1) + 1) * I * H,
+        "lmhead": 2 * shape.n_vocab * H,
+    }
+
+
+def attn_prefill_flops(shape, n: int) -> int:
+    """QK^T and PV flops of causal attention over positions 0..n-1."""
+    return 4 * shape.n_layer * shape.n_head * shape.head_dim * n * (n + 1) // 2
+
+
+def prefill_op_fractions(q, model, shape, prompt, n_ctx):
+    """Per-op MFMA fractions of one prefill, timed per launch with HIP events
+    (qwen2_prof_*) in a separate untimed pass."""
+    ops = ["qkv", "attn", "wo", "gateup", "down", "lmhead"]
+    n = len(prompt)
+    q.qwen2_prof_enable(model.ctx, ops)
+    model.prefill(0, prompt, np.arange(n, dtype=np.int32), None, None)
+    out = {}
+    fl = prefill_gemm_flops(shape, n)
+    fl["attn"] = attn_prefill_flops(shape, n)
+    for op in ops:
+        cnt, ms = q.qwen2_prof_read(model.ctx, op)
+        if cnt:
+            out[op] = {"launches": cnt, "ms": ms,
+                       "tflops": fl[op] / (ms / 1e3) / 1e12,
+                       "mfma_frac": fl[op] / (ms / 1e3) / 1e12 / MFMA_F16_PEAK_TFS}
+    q.qwen2_prof_enable(model.ctx, [])
+    gem = [o for o in ("qkv", "wo", "gateup", "down") if o in out]
+    tot_fl = sum(fl[o] for o in gem)
+    tot_ms = sum(out[o]["ms"] for o in gem)
+    out["linear_aggregate"] = {"ms": tot_ms, "tflops": tot_fl / (tot_ms / 1e3) / 1e12,
+                               "mfma_frac": tot_fl / (tot_ms / 1e3) / 1e12 / MFMA_F16_PEAK_TFS}
+    return out
+
+
 def main():
     ap = argparse.ArgumentParser(description=__doc__)
     ap.add_argument("--gpus", type=int, default=1)
@@ -81,9 +129,12 @@ def main():
     ap.add_argument("--warmup", type=int, default=1)
     ap.add_argument("--cpu-seconds", type=float, default=15.0)
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--workload", default="0.5b",
+                    help="0.5b (the benchmark line, default), 0.5b-long, 0.5b-batched, hd128, tiny")
     args = ap.parse_args()
     if args.gpus != 1:
-        print(json.dumps({"error": "this build runs on one GPU only; --gpus must be 1"}))
+        print(json.dumps({"error": "this implementation runs on one GPU; --gpus must be 1 "
+                                   "(figures for several GPUs are not produced)"}))
         sys.exit(2)
 
     import torch
@@ -91,34 +142,57 @@ def main():
     import qwen2_decoder_forward_amd as q
     import qwen2_synth as syn
 
-    wl = syn.WORKLOADS["0.5b"]
+    wl = syn.WORKLOADS[args.workload]
     shape = syn.MODELS[wl.model]
-    n, steps_dec, n_ctx = wl.prompt_len, wl.decode_steps, wl.n_ctx
+    n, steps_dec, n_ctx, n_seq = wl.prompt_len, wl.decode_steps, wl.n_ctx, wl.n_seq
+    batched = n_seq > 1
     t = time.perf_counter()
     weights = syn.make_weights(shape)
     prompt = syn.make_prompt(shape, n)
-    log(f"weights drawn in {time.perf_counter() - t:.1f} s")
+    log(f"[{wl.name}] weights drawn in {time.perf_counter() - t:.1f} s")
     dev = torch.device("cuda:0")
     torch.cuda.set_device(dev)
-    model = q.Model(shape, weights, n_ctx=n_ctx)
+    model = q.Model(shape, weights, n_ctx=n_ctx, n_seq=n_seq)
     info = model.info()
     wb = syn.weight_bytes(shape)
     assert info.weight_bytes_f16 == wb["f16"] and info.weight_bytes_f32 == wb["f32"]
     stream = torch.cuda.current_stream()
-    logits = torch.empty(shape.n_vocab, dtype=torch.float32, device=dev)
-    ids = torch.zeros(steps_dec + 1, dtype=torch.int32, device=dev)
+    V = shape.n_vocab
     pos_prompt = np.arange(n, dtype=np.int32)
 
-    def one_step(ev=None):
-        if ev:
-            ev[0].record(stream)
-        model.prefill(0, prompt, pos_prompt, logits, ids[0:1])
-        if ev:
-            ev[1].record(stream)
-        for s in range(steps_dec):
-            model.decode([0], ids[s:s + 1], [n + s], logits, ids[s + 1:s + 2])
-        if ev:
-            ev[2].record(stream)
+    if batched:
+        # setup (untimed): every sequence slot holds a prefix of n tokens
+        prompts = [syn.make_prompt(shape, n, 100 + j) for j in range(n_seq)]
+        for j in range(n_seq):
+            model.prefill(j, prompts[j], pos_prompt, None, None)
+        torch.cuda.synchronize()
+        log(f"[{wl.name}] {n_seq} prefixes of {n} tokens prefilled")
+        seqs = list(range(n_seq))
+        toks = torch.tensor(syn.make_prompt(shape, n_seq, 999), dtype=torch.int32, device=dev)
+        logits = torch.empty((n_seq, V), dtype=torch.float32, device=dev)
+        ids = torch.zeros(n_seq, dtype=torch.int32, device=dev)
+
+        def one_step(ev=None):
+            if ev:
+                ev[0].record(stream)
+                ev[1].record(stream)
+            model.decode(seqs, toks, [n] * n_seq, logits, ids)
+            if ev:
+                ev[2].record(stream)
+    else:
+        logits = torch.empty(V, dtype=torch.float32, device=dev)
+        ids = torch.zeros(steps_dec + 1, dtype=torch.int32, device=dev)
+
+        def one_step(ev=None):
+            if ev:
+                ev[0].record(stream)
+            model.prefill(0, prompt, pos_prompt, logits, ids[0:1])
+            if ev:
+                ev[1].record(stream)
+            for s in range(steps_dec):
+                model.decode([0], ids[s:s + 1], [n + s], logits, ids[s + 1:s + 2])
+            if ev:
+                ev[2].record(stream)
 
     for _ in range(args.warmup):
         one_step()
@@ -136,11 +210,22 @@ def main():
     if model.sync_status() != 0:
         raise RuntimeError("device-side error flag set during the benchmark")
 
-    # dominant kernel: fused RMSNorm + gate/up + SwiGLU GEMV (24 launches per
-    # decode token).  Its average duration is measured with HIP events on the
-    # stream it runs on, around 480 back-to-back launches that cycle through
-    # the 24 layers (418 MB of weights, more than the 256 MB Infinity Cache,
-    # so every launch streams its weights from HBM as in the decode loop).
+    kv_pos = shape.n_layer * 2 * shape.n_head_kv * shape.head_dim * 4
+    if batched:
+        dec_tokens = n_seq
+        dec_bytes = wb["f16"] + wb["f32"] + n_seq * kv_pos * (n + 2)
+    else:
+        dec_tokens = steps_dec
+        dec_bytes = sum(decode_bytes(shape, n + s, wb) for s in range(steps_dec))
+    dec_gbs = dec_bytes / (decode_ms / 1e3) / 1e9
+    dec_tok_s = dec_tokens / (decode_ms / 1e3)
+
+    # dominant decode kernel: fused RMSNorm + gate/up + SwiGLU GEMV (one launch
+    # per layer and token).  Its average duration is measured with HIP events
+    # on the stream it runs on, around 20 launches per layer that cycle
+    # through the layers (on the 0.5B shape 418 MB of weights, more than the
+    # 256 MB Infinity Cache, so every launch streams its weights from HBM as
+    # in the decode loop).
     reps = 20 * shape.n_layer
     q.qwen2_prof_repeat(model.ctx, "gateup", 1, shape.n_layer)  # warm the launch path
     ev_k = [torch.cuda.Event(enable_timing=True) for _ in range(2)]
@@ -149,23 +234,20 @@ def main():
     q.qwen2_prof_repeat(model.ctx, "gateup", 1, reps)
     ev_k[1].record(stream)
     torch.cuda.synchronize()
-    dl = reps
     gu_avg_s = ev_k[0].elapsed_time(ev_k[1]) / reps / 1e3
     gu_bytes = gateup_bytes(shape)
     achieved = gu_bytes / gu_avg_s / 1e9
 
-    dec_bytes = sum(decode_bytes(shape, n + s, wb) for s in range(steps_dec))
-    dec_gbs = dec_bytes / (decode_ms / 1e3) / 1e9
-    prefill_flops = 2 * n * (shape.n_layer * (shape.n_embd * (shape.n_head + 2 * shape.n_head_kv) *
-                                             shape.head_dim + shape.n_head * shape.head_dim *
-                                             shape.n_embd + 3 * shape.n_embd * shape.n_ff))
-    prefill_flops += 4 * shape.n_layer * shape.n_head * shape.head_dim * n * (n + 1) // 2
-    prefill_flops += 2 * shape.n_vocab * shape.n_embd
-    prefill_bytes = wb["f16"] + wb["f32"] + n * shape.n_layer * 2 * shape.n_head_kv * shape.head_dim * 4
+    fl = prefill_gemm_flops(shape, n)
+    prefill_flops = sum(fl.values()) + attn_prefill_flops(shape, n)
+    prefill_bytes = wb["f16"] + wb["f32"] + n * kv_pos
 
+    desc = (f"{wl.description}; model {shape.name}: {shape.n_layer} layers, hidden "
+            f"{shape.n_embd}, {shape.n_head}/{shape.n_head_kv} heads, hd {shape.head_dim}, "
+            f"FFN {shape.n_ff}, vocab {shape.n_vocab}, {'tied' if shape.tied else 'untied'}")
     out = {
         "metric": "decode tok/s (batch 1) + prefill tok/s, 0.5B shape; % HBM/MFMA peak",
-        "value": steps_dec / (decode_ms / 1e3),
+        "value": dec_tok_s,
         "unit": "tok/s",
         "n_gpus": 1,
         "steps": args.steps,
@@ -176,33 +258,41 @@ def main():
         "vs_baseline": None,
         "dtype": "f16 weights, f32 activations and accumulation",
         "data": "synthetic",
-        "config": {"workload": "Qwen2.5-0.5B shape (24 layers, hidden 896, 14/2 heads, hd 64, "
-                               "FFN 4864, vocab 151936, tied), batch 1: 128-token random prompt "
-                               "prefilled, then 128 greedy decode steps, n_ctx 4096",
-                   "prompt": n, "decode_steps": steps_dec, "n_ctx": n_ctx, "batch": 1},
-        "decode_tok_s": steps_dec / (decode_ms / 1e3),
-        "decode_ms_per_token": decode_ms / steps_dec,
+        "config": {"workload": desc, "prompt": n, "decode_steps": steps_dec, "n_ctx": n_ctx,
+                   "batch": n_seq},
+        "decode_tok_s": dec_tok_s,
+        "decode_ms_per_step": decode_ms / (1 if batched else steps_dec),
         "decode_hbm_gbs": dec_gbs,
         "decode_hbm_frac": dec_gbs / HBM_PEAK_GBS,
-        "prefill_tok_s": n / (prefill_ms / 1e3),
-        "prefill_ms": prefill_ms,
-        "prefill_hbm_frac": prefill_bytes / (prefill_ms / 1e3) / 1e9 / HBM_PEAK_GBS,
-        "prefill_mfma_frac": prefill_flops / (prefill_ms / 1e3) / 1e12 / MFMA_F16_PEAK_TFS,
         "wall_s_timed": wall,
         "roofline": {
             "kernel": "k_gemv<1,4,EPI_SWIGLU> (RMSNorm + gate/up + SwiGLU, decode M=1)",
             "bound": "hbm", "achieved": achieved, "peak": HBM_PEAK_GBS, "unit": "GB/s",
             "frac": achieved / HBM_PEAK_GBS, "traffic": None,
-            "bytes_per_launch": gu_bytes, "avg_launch_us": gu_avg_s * 1e6, "launches_timed": dl,
-            "timing": "HIP events around back-to-back launches cycling through the 24 layers",
+            "bytes_per_launch": gu_bytes, "avg_launch_us": gu_avg_s * 1e6, "launches_timed": reps,
+            "timing": "HIP events around back-to-back launches cycling through the layers",
         },
         "cpu_baseline": None,
     }
-    log(f"prefill {out['prefill_tok_s']:.0f} tok/s ({prefill_ms:.3f} ms), decode "
-        f"{out['decode_tok_s']:.1f} tok/s ({decode_ms / steps_dec * 1e3:.1f} us/token, "
-        f"{dec_gbs:.0f} GB/s), gate/up GEMV {gu_avg_s * 1e6:.2f} us = {achieved:.0f} GB/s")
+    if not batched:
+        out["prefill_tok_s"] = n / (prefill_ms / 1e3)
+        out["prefill_ms"] = prefill_ms
+        out["prefill_hbm_frac"] = prefill_bytes / (prefill_ms / 1e3) / 1e9 / HBM_PEAK_GBS
+        out["prefill_mfma_frac"] = prefill_flops / (prefill_ms / 1e3) / 1e12 / MFMA_F16_PEAK_TFS
+        if n > 8:
+            # a fresh context, so the prefill runs on an empty cache as above
+            model.close()
+            model = q.Model(shape, weights, n_ctx=n_ctx, n_seq=n_seq)
+            out["prefill_ops"] = prefill_op_fractions(q, model, shape, prompt, n_ctx)
+        log(f"[{wl.name}] prefill {out['prefill_tok_s']:.0f} tok/s ({prefill_ms:.3f} ms, "
+            f"{out['prefill_mfma_frac'] * 100:.1f}% MFMA)")
+    log(f"[{wl.name}] decode {dec_tok_s:.1f} tok/s ({decode_ms:.3f} ms, {dec_gbs:.0f} GB/s), "
+        f"gate/up GEMV {gu_avg_s * 1e6:.2f} us = {achieved:.0f} GB/s")
+    if "prefill_ops" in out:
+        log(f"[{wl.name}] prefill ops: " + ", ".join(
+            f"{k} {v['mfma_frac'] * 100:.1f}%" for k, v in out["prefill_ops"].items()))
     model.close()
-    if not args.no_cpu_baseline:
+    if not args.no_cpu_baseline and wl.name == "0.5b":
         out["cpu_baseline"] = cpu_baseline(shape, weights, prompt, n_ctx, args.cpu_seconds)
         log(f"cpu oracle: {out['cpu_baseline']}")
     print(json.dumps(out), flush=True)
