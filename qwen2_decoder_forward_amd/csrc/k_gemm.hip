@@ -1,13 +1,14 @@
-// MFMA GEMM of the prefill and batched-decode projections:
+// MFMA GEMMs of the prefill and batched-decode projections (rows M > 8):
 //   C[M, N] = A[M, K] * W[N, K]^T,  A and W binary16, f32 accumulation,
-// on v_mfma_f32_32x32x16_f16.  Block tile 128 x 128 x 32, four wavefronts in
-// a 2 x 2 arrangement, each owning 64 x 64 (2 x 2 MFMA tiles).  The next K
-// slice is fetched into registers while the current one is multiplied out of
-// LDS.  Epilogues are fused:
+// on v_mfma_f32_32x32x16_f16, with the projection's op fused into the
+// epilogue:
 //   QKV    bias + RoPE + q write / K,V cache store (pair partner via lane^1)
 //   RESID  h += C                (WO, down)
 //   SWIGLU a = silu(gate) * up   (pair-packed gate/up rows, f16 out)
-//   LMHEAD logits + per-row greedy argmax
+//   LMHEAD logits + per-row greedy argmax key
+// k_gemm_big (QKV, RESID, SWIGLU) uses 64-wide K slices double-buffered in
+// LDS; k_gemm_lmhead (the lm_head over the vocabulary, M <= a few hundred
+// rows) uses 128 x 128 x 32 tiles staged through registers.
 // MFMA 32x32 layout: lane l supplies A[l%32][8*(l/32)..+8] and
 // B[8*(l/32)..+8][l%32]; it receives D[8*(r/4) + 4*(l/32) + r%4][l%32].
 #include "q2_device.h"
@@ -16,6 +17,10 @@ namespace q2 {
 
 enum { G_QKV = 0, G_RESID = 1, G_SWIGLU = 2, G_LMHEAD = 3 };
 
+// k_gemm_lmhead: block tile 128 x 128 x 32, four wavefronts in a 2 x 2
+// arrangement, each owning 64 x 64 (2 x 2 MFMA tiles); a ring of kStages
+// register sets keeps the global loads of the next slices in flight while
+// one slice is multiplied out of LDS.
 constexpr int BM = 128, BN = 128, BK = 32, LDT = BK + 8;
 constexpr int kStages = 4;  // K slices in flight per block
 
@@ -31,12 +36,11 @@ struct GemmP {
   _Float16 *a16;
   int ld_a;
   ArgmaxEpi am;
-  float *ws;      // split-K: raw partial sums [splits][M][N] (epilogue runs later)
-  int k_steps;    // K slices of BK per split
+  float *ws;      // split-K: raw partial sums [splits][M][N] (RESID only)
+  int k_steps;    // K slices per block (per split)
 };
 
-template <int EPI>
-__global__ __launch_bounds__(256) void k_gemm(GemmP p) {
+__global__ __launch_bounds__(256) void k_gemm_lmhead(GemmP p) {
   __shared__ __attribute__((aligned(16))) _Float16 sA[BM * LDT];
   __shared__ __attribute__((aligned(16))) _Float16 sW[BN * LDT];
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
@@ -116,73 +120,184 @@ __global__ __launch_bounds__(256) void k_gemm(GemmP p) {
     }
   }
 
-  // ---------------------------------------------------------------- epilogue
-  if (p.ws) {  // split-K: store the raw partial sums
-    float *ws = p.ws + (size_t)blockIdx.z * M * N;
-#pragma unroll
-    for (int i = 0; i < 2; ++i)
-#pragma unroll
-      for (int j = 0; j < 2; ++j) {
-        const int n = n0 + wn * 64 + j * 32 + l32;
-#pragma unroll
-        for (int r = 0; r < 16; ++r) {
-          const int m = m0 + wm * 64 + i * 32 + 8 * (r >> 2) + 4 * hi + (r & 3);
-          if (m < M && n < N) ws[(size_t)m * N + n] = acc[i][j][r];
-        }
-      }
-    return;
-  }
-  if (EPI == G_LMHEAD) {
-    __shared__ unsigned long long sBest[2][BM];
-    float *logits = *p.am.logits;
-    unsigned long long kb[2][16];
-#pragma unroll
-    for (int i = 0; i < 2; ++i)
-#pragma unroll
-      for (int r = 0; r < 16; ++r) {
-        const int m = m0 + wm * 64 + i * 32 + 8 * (r >> 2) + 4 * hi + (r & 3);
-        unsigned long long b = 0ull;
-#pragma unroll
-        for (int j = 0; j < 2; ++j) {
-          const int n = n0 + wn * 64 + j * 32 + l32;
-          if (m < M && n < N) {
-            const float v = acc[i][j][r];
-            if (logits) logits[(size_t)m * N + n] = v;
-            const unsigned long long key = argmax_key(v, n);
-            b = key > b ? key : b;
-          }
-        }
-#pragma unroll
-        for (int o = 1; o < 32; o <<= 1) {
-          const unsigned long long x = shfl_xor_u64(b, o);
-          b = x > b ? x : b;
-        }
-        kb[i][r] = b;
-      }
-    if (l32 == 0) {
-#pragma unroll
-      for (int i = 0; i < 2; ++i)
-#pragma unroll
-        for (int r = 0; r < 16; ++r) sBest[wn][wm * 64 + i * 32 + 8 * (r >> 2) + 4 * hi + (r & 3)] = kb[i][r];
-    }
-    __syncthreads();
-    if (tid < BM && m0 + tid < M) {
-      const unsigned long long b = sBest[0][tid] > sBest[1][tid] ? sBest[0][tid] : sBest[1][tid];
-      atomicMax(&p.am.best[m0 + tid], b);
-    }
-    return;
-  }
-
+  // ------------------------------------------ epilogue: logits + argmax key
+  __shared__ unsigned long long sBest[2][BM];
+  float *logits = *p.am.logits;
+  unsigned long long kb[2][16];
 #pragma unroll
   for (int i = 0; i < 2; ++i)
 #pragma unroll
-    for (int j = 0; j < 2; ++j) {
-      const int n = n0 + wn * 64 + j * 32 + l32;
+    for (int r = 0; r < 16; ++r) {
+      const int m = m0 + wm * 64 + i * 32 + 8 * (r >> 2) + 4 * hi + (r & 3);
+      unsigned long long b = 0ull;
+#pragma unroll
+      for (int j = 0; j < 2; ++j) {
+        const int n = n0 + wn * 64 + j * 32 + l32;
+        if (m < M && n < N) {
+          const float v = acc[i][j][r];
+          if (logits) logits[(size_t)m * N + n] = v;
+          const unsigned long long key = argmax_key(v, n);
+          b = key > b ? key : b;
+        }
+      }
+#pragma unroll
+      for (int o = 1; o < 32; o <<= 1) {
+        const unsigned long long x = shfl_xor_u64(b, o);
+        b = x > b ? x : b;
+      }
+      kb[i][r] = b;
+    }
+  if (l32 == 0) {
+#pragma unroll
+    for (int i = 0; i < 2; ++i)
+#pragma unroll
+      for (int r = 0; r < 16; ++r) sBest[wn][wm * 64 + i * 32 + 8 * (r >> 2) + 4 * hi + (r & 3)] = kb[i][r];
+  }
+  __syncthreads();
+  if (tid < BM && m0 + tid < M) {
+    const unsigned long long b = sBest[0][tid] > sBest[1][tid] ? sBest[0][tid] : sBest[1][tid];
+    atomicMax(&p.am.best[m0 + tid], b);
+  }
+}
+
+// ------------------------------------------------------- large-M projections
+// Prefill GEMMs with many rows (M >= kBigM) are MFMA-bound.  Block tile
+// BM x BN x 64 with four wavefronts in a 2 x 2 arrangement, each owning
+// (BM/2) x (BN/2) of the output, i.e. (BM/64) x (BN/64) MFMA 32x32 tiles
+// (at 256 x 256: 256 f32 accumulators per lane, held in AGPRs at one wave
+// per SIMD).  Both 64-wide K slices live in LDS twice (double buffer, 64 KiB
+// per buffer at 256 x 256), so one barrier per K slice suffices:
+//   write slice t+1 (already in registers) to the free buffer, issue the
+//   global loads of slice t+2, multiply slice t, barrier.
+// LDS rows are 64 halves (128 B) without padding; 16-byte chunk c of row r
+// is stored at chunk c ^ ((r >> 1) & 7).  A 16-byte-per-lane LDS access is
+// served 16 lanes (256 B, the 64 banks) at a time, and the 16 consecutive
+// rows of an MFMA operand read (or the 2 rows x 8 chunks of a tile write)
+// then cover 16 distinct 16-byte bank groups.  Rows past M or N are clamped
+// to a valid row and their results are never stored.
+constexpr int kBK2 = 64;
+constexpr int kBigM = 512;
+
+template <int EPI, int BMT, int BNT, int WGM>
+__global__ __launch_bounds__(256) void k_gemm_big(GemmP p) {
+  constexpr int WGN = 4 / WGM;                   // wavefronts along M x along N
+  constexpr int WTM = BMT / WGM, WTN = BNT / WGN;  // wave tile
+  constexpr int TM = WTM / 32, TN = WTN / 32;      // MFMA tiles per wave
+  constexpr int CA = BMT / 32, CB = BNT / 32;      // 16-byte chunks per thread per slice
+  static_assert(TM >= 1 && TN >= 1 && CB >= 1, "tile shape");
+  __shared__ __attribute__((aligned(16))) _Float16 sA[2 * BMT * kBK2];
+  __shared__ __attribute__((aligned(16))) _Float16 sB[2 * BNT * kBK2];
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int wm = wave / WGN, wn = wave % WGN;
+  const int hi = lane >> 5, l32 = lane & 31;
+  const int M = p.M, N = p.N, K = p.K;
+
+  // tile order: consecutive blocks of one XCD (blocks are dealt round-robin
+  // over the 8 XCDs) walk the N tiles of one row band, so a band's A rows
+  // stay in that XCD's L2
+  const int gx = gridDim.x, gy = gridDim.y;
+  const int nb = gx * gy;
+  const int bid = blockIdx.y * gx + blockIdx.x;
+  int tile = bid;
+  if ((nb & 7) == 0) tile = (bid & 7) * (nb >> 3) + (bid >> 3);
+  const int m0 = (tile / gx) * BMT, n0 = (tile % gx) * BNT;
+
+  // global -> register staging: thread t moves chunk (t & 7) of rows (t >> 3) + 32 i
+  const int cc = tid & 7, r0 = tid >> 3;
+  const _Float16 *Ag[CA];
+  const _Float16 *Bg[CB];
+#pragma unroll
+  for (int i = 0; i < CA; ++i) {
+    const int m = min(m0 + r0 + 32 * i, M - 1);
+    Ag[i] = p.A + (size_t)m * p.lda + cc * 8;
+  }
+#pragma unroll
+  for (int i = 0; i < CB; ++i) {
+    const int n = min(n0 + r0 + 32 * i, N - 1);
+    Bg[i] = p.W + (size_t)n * K + cc * 8;
+  }
+  h8 ra[CA], rb[CB];
+  // this block's K slices (split-K: blockIdx.z takes p.k_steps of them)
+  const int kz0 = blockIdx.z * p.k_steps;
+  const int nk = min(K / kBK2 - kz0, p.k_steps);
+  auto gload = [&](int kt) {
+    const int ko = (kz0 + kt) * kBK2;
+#pragma unroll
+    for (int i = 0; i < CA; ++i) ra[i] = *(const h8 *)(Ag[i] + ko);
+#pragma unroll
+    for (int i = 0; i < CB; ++i) rb[i] = *(const h8 *)(Bg[i] + ko);
+  };
+  auto swrite = [&](int buf) {
+    _Float16 *a = sA + buf * BMT * kBK2;
+    _Float16 *b = sB + buf * BNT * kBK2;
+#pragma unroll
+    for (int i = 0; i < CA; ++i) {
+      const int r = r0 + 32 * i;
+      *(h8 *)(a + r * kBK2 + ((cc ^ ((r >> 1) & 7)) << 3)) = ra[i];
+    }
+#pragma unroll
+    for (int i = 0; i < CB; ++i) {
+      const int r = r0 + 32 * i;
+      *(h8 *)(b + r * kBK2 + ((cc ^ ((r >> 1) & 7)) << 3)) = rb[i];
+    }
+  };
+
+  f16x acc[TM][TN];
+#pragma unroll
+  for (int i = 0; i < TM; ++i)
+#pragma unroll
+    for (int j = 0; j < TN; ++j)
+#pragma unroll
+      for (int r = 0; r < 16; ++r) acc[i][j][r] = 0.f;
+
+  gload(0);
+  swrite(0);
+  if (nk > 1) gload(1);
+  __syncthreads();
+  for (int kt = 0; kt < nk; ++kt) {
+    const int buf = kt & 1;
+    if (kt + 1 < nk) swrite(buf ^ 1);  // slice kt+1: its buffer was last read in kt-1
+    if (kt + 2 < nk) gload(kt + 2);
+    const _Float16 *a = sA + buf * BMT * kBK2;
+    const _Float16 *b = sB + buf * BNT * kBK2;
+#pragma unroll
+    for (int ks = 0; ks < kBK2 / 16; ++ks) {
+      const int ch = ks * 2 + hi;  // logical 16-byte chunk of this lane's operand
+      h8 af[TM], bf[TN];
+#pragma unroll
+      for (int i = 0; i < TM; ++i) {
+        const int r = wm * WTM + i * 32 + l32;
+        af[i] = *(const h8 *)(a + r * kBK2 + ((ch ^ ((r >> 1) & 7)) << 3));
+      }
+#pragma unroll
+      for (int j = 0; j < TN; ++j) {
+        const int r = wn * WTN + j * 32 + l32;
+        bf[j] = *(const h8 *)(b + r * kBK2 + ((ch ^ ((r >> 1) & 7)) << 3));
+      }
+#pragma unroll
+      for (int i = 0; i < TM; ++i)
+#pragma unroll
+        for (int j = 0; j < TN; ++j)
+          acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_f16(af[i], bf[j], acc[i][j], 0, 0, 0);
+    }
+    __syncthreads();
+  }
+
+  // epilogue (same ops as k_gemm's, over TM x TN tiles); split-K blocks
+  // store raw partial sums [split][M][N] instead (residual GEMMs only; the
+  // RMSNorm kernel that follows folds them into the residual rows)
+#pragma unroll
+  for (int i = 0; i < TM; ++i)
+#pragma unroll
+    for (int j = 0; j < TN; ++j) {
+      const int n = n0 + wn * WTN + j * 32 + l32;
 #pragma unroll
       for (int r = 0; r < 16; ++r) {
-        const int m = m0 + wm * 64 + i * 32 + 8 * (r >> 2) + 4 * hi + (r & 3);
+        const int m = m0 + wm * WTM + i * 32 + 8 * (r >> 2) + 4 * hi + (r & 3);
         const float v = acc[i][j][r];
-        if (EPI == G_RESID) {
+        if (EPI == G_RESID && p.ws) {
+          if (m < M && n < N) p.ws[((size_t)blockIdx.z * M + m) * N + n] = v;
+        } else if (EPI == G_RESID) {
           if (m < M && n < N) p.h[(size_t)m * p.ldh + n] += v;
         } else {
           const float partner = __shfl_xor(v, 1, 64);
@@ -197,64 +312,180 @@ __global__ __launch_bounds__(256) void k_gemm(GemmP p) {
     }
 }
 
-// Split-K epilogue: sums the partials of a column pair and applies the op.
-template <int EPI>
-__global__ __launch_bounds__(256) void k_splitk_epi(GemmP p, int splits) {
-  const int M = p.M, N = p.N;
-  const int half = N >> 1;
-  for (int t = blockIdx.x * 256 + threadIdx.x; t < M * half; t += gridDim.x * 256) {
-    const int m = t / half, n = 2 * (t - m * half);
-    float a = 0.f, b = 0.f;
-    for (int z = 0; z < splits; ++z) {
-      const float *w = p.ws + ((size_t)z * M + m) * N + n;
-      a += w[0];
-      b += w[1];
+template <int EPI, int BMT, int BNT, int WGM>
+static void launch_big(GemmP p, int splits, hipStream_t st) {
+  const int nk = p.K / kBK2;
+  p.k_steps = (nk + splits - 1) / splits;
+  splits = (nk + p.k_steps - 1) / p.k_steps;
+  if (splits <= 1) p.ws = nullptr;
+  dim3 grid((p.N + BNT - 1) / BNT, (p.M + BMT - 1) / BMT, splits);
+  hipLaunchKernelGGL((k_gemm_big<EPI, BMT, BNT, WGM>), grid, dim3(256), 0, st, p);
+}
+
+// ------------------------------------------------------ skinny projections
+// Fewer rows (8 < M < kBigM): weight streaming and latency dominate.  Block
+// tile (32 TM) x 32 with the four wavefronts splitting the block's K range
+// (wave w takes a contiguous quarter of the 16-wide MFMA steps).  Operands
+// are read straight from global memory into MFMA registers (every weight
+// and activation element is used by exactly one wavefront of the block, so
+// LDS staging would not save a load); U steps of loads are kept in flight.
+// One load instruction covers 32 B of each of 32 rows, so the loads are
+// cached: the following steps of the same wavefront read the rest of each
+// 128-byte line from the cache instead of HBM.
+// The four partial tiles are summed through LDS, wavefront t finishing
+// tile t.  A block may also take only a share of K (split-K, residual
+// GEMMs only: raw partial sums, folded in by the next RMSNorm).
+template <int EPI, int TM>
+__global__ __launch_bounds__(256) void k_gemm_skinny(GemmP p) {
+  constexpr int U = TM >= 4 ? 4 : 8;  // MFMA steps of loads in flight per wavefront
+  __shared__ f16x sRed[4][TM][64];
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int hi = lane >> 5, l32 = lane & 31;
+  const int M = p.M, N = p.N, K = p.K;
+  const int m0 = blockIdx.y * 32 * TM, n0 = blockIdx.x * 32;
+
+  // K steps of this block, then of this wavefront
+  const int steps = K / 16;
+  const int bs0 = blockIdx.z * p.k_steps, bs1 = min(steps, bs0 + p.k_steps);
+  const int per = (bs1 - bs0 + 3) / 4;
+  const int s0 = bs0 + wave * per, s1 = min(bs1, s0 + per);
+
+  const _Float16 *Ap[TM];
+#pragma unroll
+  for (int i = 0; i < TM; ++i)
+    Ap[i] = p.A + (size_t)min(m0 + i * 32 + l32, M - 1) * p.lda + hi * 8;
+  const _Float16 *Bp = p.W + (size_t)min(n0 + l32, N - 1) * K + hi * 8;
+
+  f16x acc[TM];
+#pragma unroll
+  for (int i = 0; i < TM; ++i)
+#pragma unroll
+    for (int r = 0; r < 16; ++r) acc[i][r] = 0.f;
+
+  for (int s = s0; s < s1; s += U) {
+    h8 af[U][TM], bf[U];
+#pragma unroll
+    for (int u = 0; u < U; ++u) {
+      const int k = min(s + u, s1 - 1) * 16;  // (a step past s1 repeats the last, unused)
+      bf[u] = *(const h8 *)(Bp + k);  // (cached: the next steps read the rest of each line)
+#pragma unroll
+      for (int i = 0; i < TM; ++i) af[u][i] = *(const h8 *)(Ap[i] + k);
     }
-    if (EPI == G_QKV) {
-      qkv_store_pair(p.d, p.qkv, m, n, a, b);
-    } else if (EPI == G_SWIGLU) {
-      p.a16[(size_t)m * p.ld_a + (n >> 1)] = (_Float16)(silu(a) * b);
+#pragma unroll
+    for (int u = 0; u < U; ++u)
+      if (s + u < s1)
+#pragma unroll
+        for (int i = 0; i < TM; ++i)
+          acc[i] = __builtin_amdgcn_mfma_f32_32x32x16_f16(af[u][i], bf[u], acc[i], 0, 0, 0);
+  }
+#pragma unroll
+  for (int i = 0; i < TM; ++i) sRed[wave][i][lane] = acc[i];
+  __syncthreads();
+  if (wave >= TM) return;
+  f16x v = sRed[0][wave][lane];
+#pragma unroll
+  for (int w = 1; w < 4; ++w) v += sRed[w][wave][lane];
+
+  const int n = n0 + l32;
+#pragma unroll
+  for (int r = 0; r < 16; ++r) {
+    const int m = m0 + wave * 32 + 8 * (r >> 2) + 4 * hi + (r & 3);
+    const float x = v[r];
+    if (EPI == G_RESID && p.ws) {
+      if (m < M && n < N) p.ws[((size_t)blockIdx.z * M + m) * N + n] = x;
+    } else if (EPI == G_RESID) {
+      if (m < M && n < N) p.h[(size_t)m * p.ldh + n] += x;
     } else {
-      p.h[(size_t)m * p.ldh + n] += a;
-      p.h[(size_t)m * p.ldh + n + 1] += b;
+      const float partner = __shfl_xor(x, 1, 64);
+      if ((n & 1) == 0 && m < M && n < N) {
+        if (EPI == G_QKV)
+          qkv_store_pair(p.d, p.qkv, m, n, x, partner);
+        else
+          p.a16[(size_t)m * p.ld_a + (n >> 1)] = (_Float16)(silu(x) * partner);
+      }
     }
   }
+}
+
+// Launch shape of a skinny GEMM: rows per block 32 TM (TM = 4, 2, 1) and,
+// for residual GEMMs, K splits; the choice minimises the bytes the busiest
+// CU loads (A and W of its blocks), with blocks dealt evenly over 256 CUs.
+template <int EPI>
+static int launch_skinny(GemmP p, const Workspace &wsp, hipStream_t st) {
+  const int steps = p.K / 16;
+  const int nt = (p.N + 31) / 32;
+  int best_tm = 1, best_sp = 1;
+  double best_cost = 1e30;
+  for (int tm = 4; tm >= 1; tm >>= 1) {
+    const int mt = (p.M + 32 * tm - 1) / (32 * tm);
+    const int max_sp = (EPI == G_RESID && wsp.buf) ? 16 : 1;
+    for (int sp = 1; sp <= max_sp; ++sp) {
+      if ((size_t)sp * p.M * p.N * 4 > wsp.bytes && sp > 1) break;
+      const int ks = (steps + sp - 1) / sp;
+      const int blocks = nt * mt * ((steps + ks - 1) / ks);
+      const double vol = (32.0 * tm + 32.0) * ks * 16 * 2;
+      const double cost = vol * ((blocks + 255) / 256) + (sp > 1 ? sp * 4.0 * p.M * 32 : 0.0);
+      if (cost < best_cost * 0.98) {
+        best_cost = cost;
+        best_tm = tm;
+        best_sp = sp;
+      }
+    }
+  }
+  p.k_steps = (steps + best_sp - 1) / best_sp;
+  const int splits = (steps + p.k_steps - 1) / p.k_steps;
+  p.ws = splits > 1 ? wsp.buf : nullptr;
+  dim3 grid(nt, (p.M + 32 * best_tm - 1) / (32 * best_tm), splits);
+  switch (best_tm) {
+    case 4: hipLaunchKernelGGL((k_gemm_skinny<EPI, 4>), grid, dim3(256), 0, st, p); break;
+    case 2: hipLaunchKernelGGL((k_gemm_skinny<EPI, 2>), grid, dim3(256), 0, st, p); break;
+    default: hipLaunchKernelGGL((k_gemm_skinny<EPI, 1>), grid, dim3(256), 0, st, p); break;
+  }
+  return splits > 1 ? splits : 0;
+}
+
+// K % 64 == 0.  Many rows: 128 x 128 tiles (2 x 2 wavefronts; measured on
+// the prefill shapes against 256 x 256 and 256 x 128, it is the fastest or
+// within 3 %).  Fewer rows: narrow, short-K projections (QKV, WO) run on the
+// skinny kernel; the others on 128 x 32 LDS-staged tiles (4 x 1 wavefronts,
+// coalesced loads), so a 128-row GEMM has a block per 32 weight rows, and a
+// residual GEMM with a long K (down) also splits K.  (Measured at M = 128 on
+// the 0.5B shape: skinny QKV 17 vs 21 us, WO 8.5 vs 17; tiles gate/up 16 vs
+// 30, down 12 vs 21.)  Returns the number of split-K partial-sum sets left
+// pending (0 when the result was applied directly).
+template <int EPI>
+static int launch_tiles(GemmP p, const Workspace &wsp, hipStream_t st) {
+  if (p.M >= kBigM) {
+    launch_big<EPI, 128, 128, 2>(p, 1, st);
+    return 0;
+  }
+  if (p.K <= 1024 && p.N <= 2048) return launch_skinny<EPI>(p, wsp, st);
+  const int nk = p.K / kBK2;
+  int splits = 1;
+  if (EPI == G_RESID && p.K >= 2048 && wsp.buf) {
+    const int blocks = ((p.N + 31) / 32) * ((p.M + 127) / 128);
+    splits = (256 + blocks - 1) / blocks;
+    splits = min(splits, min(16, nk));
+    const size_t per = (size_t)p.M * p.N * 4;
+    splits = min(splits, (int)(wsp.bytes / per));
+    if (splits < 1) splits = 1;
+  }
+  p.ws = splits > 1 ? wsp.buf : nullptr;
+  const int ks = (nk + splits - 1) / splits;
+  const int used = (nk + ks - 1) / ks;  // launch_big's effective split count
+  launch_big<EPI, 128, 32, 4>(p, splits, st);
+  return used > 1 ? used : 0;
+}
+
+// Every projection but the lm_head runs on the tile kernels (K is a
+// multiple of 64 for every supported shape: n_embd % 64 == 0 and the FFN
+// width is padded to 64).
+template <int EPI>
+static int launch(GemmP p, const Workspace &wsp, hipStream_t st) {
+  return launch_tiles<EPI>(p, wsp, st);
 }
 
 static dim3 grid_for(int M, int N) { return dim3((N + BN - 1) / BN, (M + BM - 1) / BM); }
-
-// Few output tiles (small M): split K across blocks so the weight stream is
-// spread over the whole chip; the partials are reduced by k_splitk_epi.
-template <int EPI>
-static void launch(GemmP p, const Workspace &wsp, hipStream_t st) {
-  dim3 grid = grid_for(p.M, p.N);
-  const int tiles = grid.x * grid.y;
-  const int ksteps = p.K / BK;
-  int splits = 1;
-  if (EPI != G_LMHEAD && tiles < 192 && wsp.buf) {
-    splits = (256 + tiles - 1) / tiles;
-    splits = splits < ksteps / kStages ? splits : ksteps / kStages;
-    splits = splits < 16 ? splits : 16;
-    const size_t per = (size_t)p.M * p.N * 4;
-    const int cap = (int)(wsp.bytes / per);
-    splits = splits < cap ? splits : cap;
-  }
-  if (splits <= 1) {
-    p.ws = nullptr;
-    p.k_steps = ksteps;
-    hipLaunchKernelGGL(k_gemm<EPI>, grid, dim3(256), 0, st, p);
-    return;
-  }
-  p.k_steps = (ksteps + splits - 1) / splits;
-  splits = (ksteps + p.k_steps - 1) / p.k_steps;
-  p.ws = wsp.buf;
-  grid.z = splits;
-  hipLaunchKernelGGL(k_gemm<EPI>, grid, dim3(256), 0, st, p);
-  const int pairs = p.M * (p.N / 2);
-  int blocks = (pairs + 255) / 256;
-  blocks = blocks < 2048 ? blocks : 2048;
-  hipLaunchKernelGGL(k_splitk_epi<EPI>, dim3(blocks), dim3(256), 0, st, p, splits);
-}
 
 static GemmP base(const _Float16 *A, int lda, int M, const uint16_t *W, int N, int K) {
   GemmP p{};
@@ -275,12 +506,12 @@ void gemm_qkv(const Dims &d, const LayerW &w, const _Float16 *x, int lda, int M,
   launch<G_QKV>(p, ws, st);
 }
 
-void gemm_resid(const uint16_t *W, int N, int K, const _Float16 *x, int lda, int M, float *h,
-                int ldh, const Workspace &ws, hipStream_t st) {
+int gemm_resid(const uint16_t *W, int N, int K, const _Float16 *x, int lda, int M, float *h,
+               int ldh, const Workspace &ws, hipStream_t st) {
   GemmP p = base(x, lda, M, W, N, K);
   p.h = h;
   p.ldh = ldh;
-  launch<G_RESID>(p, ws, st);
+  return launch<G_RESID>(p, ws, st);
 }
 
 void gemm_swiglu(const Dims &d, const LayerW &w, const _Float16 *x, int lda, int M,
@@ -296,7 +527,7 @@ void gemm_lmhead(const Dims &d, const uint16_t *W, const _Float16 *x, int lda, i
   GemmP p = base(x, lda, M, W, d.V, d.H);
   p.am = e;
   p.k_steps = d.H / BK;
-  hipLaunchKernelGGL(k_gemm<G_LMHEAD>, grid_for(M, d.V), dim3(256), 0, st, p);
+  hipLaunchKernelGGL(k_gemm_lmhead, grid_for(M, d.V), dim3(256), 0, st, p);
   argmax_finalize(e, M, st);
 }
 

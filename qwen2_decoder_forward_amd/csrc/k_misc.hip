@@ -31,35 +31,50 @@ void embed_rows(const uint16_t *E, int H, int V, const int *const *tokens, int t
 }
 
 // One wavefront per row: y = w * x / sqrt(mean(x^2) + eps), stored as f16
-// (MFMA operand) and optionally f32.
-__global__ __launch_bounds__(256) void k_rmsnorm_rows(const float *h, int ldh, const float *w,
-                                                      int H, int M, float eps, _Float16 *x,
-                                                      int ldx, float *y32) {
+// (MFMA operand) and optionally f32.  When a split-K residual GEMM left
+// `splits` partial sums part[z][m][k] (z < splits), they are first added to
+// the row, which is written back: h[m] += sum_z part[z][m].
+__global__ __launch_bounds__(256) void k_rmsnorm_rows(float *h, int ldh, const float *w, int H,
+                                                      int M, float eps, _Float16 *x, int ldx,
+                                                      float *y32, const float *part, int splits) {
   const int lane = threadIdx.x & 63;
   const int m = blockIdx.x * 4 + (threadIdx.x >> 6);
   if (m >= M) return;
-  const float *row = h + (size_t)m * ldh;
+  float *row = h + (size_t)m * ldh;
+  constexpr int kMaxChunks = 20;  // H <= 64 lanes * 4 * 20 = 5120 (the supported maximum)
+  f4 v[kMaxChunks];
   float ss = 0.f;
-  for (int k = lane * 4; k < H; k += 256) {
-    const f4 v = *(const f4 *)(row + k);
-    ss += v.x * v.x + v.y * v.y + v.z * v.z + v.w * v.w;
+#pragma unroll
+  for (int c = 0; c < kMaxChunks; ++c) {
+    const int k = lane * 4 + c * 256;
+    if (k < H) {
+      v[c] = *(const f4 *)(row + k);
+      if (splits > 0) {
+        for (int z = 0; z < splits; ++z) v[c] += *(const f4 *)(part + ((size_t)z * M + m) * H + k);
+        *(f4 *)(row + k) = v[c];
+      }
+      ss += v[c].x * v[c].x + v[c].y * v[c].y + v[c].z * v[c].z + v[c].w * v[c].w;
+    }
   }
   ss = wave_sum(ss);
   const float inv = 1.0f / sqrtf(ss / (float)H + eps);
-  for (int k = lane * 4; k < H; k += 256) {
-    const f4 v = *(const f4 *)(row + k);
-    const f4 g = *(const f4 *)(w + k);
-    const f4 y = v * inv * g;
-    h4 yh = {(_Float16)y.x, (_Float16)y.y, (_Float16)y.z, (_Float16)y.w};
-    *(h4 *)(x + (size_t)m * ldx + k) = yh;
-    if (y32) *(f4 *)(y32 + (size_t)m * H + k) = y;
+#pragma unroll
+  for (int c = 0; c < kMaxChunks; ++c) {
+    const int k = lane * 4 + c * 256;
+    if (k < H) {
+      const f4 g = *(const f4 *)(w + k);
+      const f4 y = v[c] * inv * g;
+      h4 yh = {(_Float16)y.x, (_Float16)y.y, (_Float16)y.z, (_Float16)y.w};
+      *(h4 *)(x + (size_t)m * ldx + k) = yh;
+      if (y32) *(f4 *)(y32 + (size_t)m * H + k) = y;
+    }
   }
 }
 
-void rmsnorm_rows_f16(const float *h, int ldh, const float *w, int H, int M, float eps,
-                      _Float16 *x, int ldx, float *y32, hipStream_t st) {
+void rmsnorm_rows_f16(float *h, int ldh, const float *w, int H, int M, float eps, _Float16 *x,
+                      int ldx, float *y32, const float *part, int splits, hipStream_t st) {
   hipLaunchKernelGGL(k_rmsnorm_rows, dim3((M + 3) / 4), dim3(256), 0, st, h, ldh, w, H, M, eps,
-                     x, ldx, y32);
+                     x, ldx, y32, part, splits);
 }
 
 }  // namespace q2

@@ -74,33 +74,83 @@ __device__ __forceinline__ float silu(float z) { return z / (1.0f + __expf(-z));
 // Fused-QKV epilogue for one packed row pair (n even): adds the bias, rotates
 // q and k pairs (NonInterleaved RoPE: packed rows n, n+1 are the natural
 // dimensions j and j + hd/2 of one head), then writes q or stores k / v into
-// the KV cache slot of row m's sequence at row m's position.
-__device__ __forceinline__ void qkv_store_pair(const Dims &d, const QkvEpi &e, int m, int n,
-                                               float a, float b) {
-  a += e.bias[n];
-  b += e.bias[n + 1];
+// the KV cache slot of row m's sequence at row m's position.  Split in two so
+// a kernel can issue the loads the epilogue needs (position, sequence slot,
+// bias, then cos/sin of the position) long before its sums are ready.
+struct QkvPair {
+  float *dst;      // element j of the q row or KV cache slot (j + hd/2 is the partner)
+  float ba, bb;    // bias of the two rows
+  float c, s;      // rotation (1, 0 for v)
+  int half;
+};
+
+// Vector-memory load of a value that would otherwise become a scalar load:
+// vector loads complete in issue order, so one issued before a kernel's
+// weight stream can be waited for without waiting for the stream, while a
+// scalar load's result would be waited for before the stream is issued.
+// Loaded as unsigned: widening it to 64 bits (done next to the load by the
+// compiler) is then a zero-extension that does not wait for the value.
+// The index is passed through an empty asm in a vector register, so the
+// value counts as per-lane and is not moved to a scalar register (which
+// would also wait for it right away); the base keeps its global address
+// space, so the load stays a global (not flat) load.
+__device__ __forceinline__ unsigned vload(const int *base, int i) {
+  asm volatile("" : "+v"(i));
+  return __hip_atomic_load((const unsigned *)base + i, __ATOMIC_RELAXED,
+                           __HIP_MEMORY_SCOPE_WORKGROUP);
+}
+
+// First half: the position / sequence loads (no dependent loads yet).
+__device__ __forceinline__ void qkv_pair_begin(const QkvEpi &e, int m, int n, unsigned &pos,
+                                               unsigned &seq, float &ba, float &bb) {
+  pos = vload(e.rows.pos, m);
+  seq = vload(e.rows.seq, m);
+  ba = e.bias[n];
+  bb = e.bias[n + 1];
+}
+
+// Second half: destination address and the cos/sin loads, given the position.
+__device__ __forceinline__ QkvPair qkv_pair_end(const Dims &d, const QkvEpi &e, int m, int n,
+                                                unsigned pos, unsigned seq, float ba, float bb) {
   const int hd = d.hd, half = hd >> 1;
   const int head = n / hd;
   const int j = (n - head * hd) >> 1;
-  const int p = e.rows.pos[m];
+  QkvPair q;
+  q.ba = ba;
+  q.bb = bb;
+  q.half = half;
+  q.c = 1.0f;
+  q.s = 0.0f;
   if (head < d.nh + d.nkv) {
-    const float c = e.rope.cos[(size_t)p * half + j];
-    const float s = e.rope.sin[(size_t)p * half + j];
-    const float a2 = a * c - b * s;
-    const float b2 = b * c + a * s;
-    a = a2;
-    b = b2;
+    q.c = e.rope.cos[(size_t)pos * half + j];
+    q.s = e.rope.sin[(size_t)pos * half + j];
   }
-  float *dst;
-  if (head < d.nh) {
-    dst = e.q + (size_t)m * e.ldq + (size_t)head * hd;
-  } else if (head < d.nh + d.nkv) {
-    dst = e.kv.k + e.kv.off(d, e.layer, e.rows.seq[m], head - d.nh, p);
-  } else {
-    dst = e.kv.v + e.kv.off(d, e.layer, e.rows.seq[m], head - d.nh - d.nkv, p);
-  }
-  dst[j] = a;
-  dst[j + half] = b;
+  // KV slot offset as in KVCache::off, with the (non-negative) sequence and
+  // position widened as unsigned values
+  const bool is_k = head < d.nh + d.nkv;
+  const size_t g = (size_t)(is_k ? head - d.nh : head - d.nh - d.nkv);
+  const size_t slot = ((((size_t)e.layer * d.n_seq + (size_t)seq) * d.nkv + g) * d.n_ctx +
+                       (size_t)pos) * (size_t)hd + (size_t)j;
+  if (head < d.nh)
+    q.dst = e.q + (size_t)m * e.ldq + (size_t)head * hd + j;
+  else
+    q.dst = (is_k ? e.kv.k : e.kv.v) + slot;
+  return q;
+}
+
+__device__ __forceinline__ void qkv_pair_store(const QkvPair &q, float a, float b) {
+  a += q.ba;
+  b += q.bb;
+  q.dst[0] = a * q.c - b * q.s;
+  q.dst[q.half] = b * q.c + a * q.s;
+}
+
+__device__ __forceinline__ void qkv_store_pair(const Dims &d, const QkvEpi &e, int m, int n,
+                                               float a, float b) {
+  unsigned pos, seq;
+  float ba, bb;
+  qkv_pair_begin(e, m, n, pos, seq, ba, bb);
+  qkv_pair_store(qkv_pair_end(d, e, m, n, pos, seq, ba, bb), a, b);
 }
 
 }  // namespace q2

@@ -90,17 +90,20 @@ struct Workspace {
 };
 void gemm_qkv(const Dims &d, const LayerW &w, const _Float16 *x, int lda, int M,
               const QkvEpi &e, const Workspace &ws, hipStream_t st);
-void gemm_resid(const uint16_t *W, int N, int K, const _Float16 *x, int lda, int M, float *h,
-                int ldh, const Workspace &ws, hipStream_t st);
+// Returns the number of split-K partial-sum sets left in ws.buf ([z][M][N]);
+// when nonzero the next rmsnorm_rows_f16 of h must fold them in.
+int gemm_resid(const uint16_t *W, int N, int K, const _Float16 *x, int lda, int M, float *h,
+               int ldh, const Workspace &ws, hipStream_t st);
 void gemm_swiglu(const Dims &d, const LayerW &w, const _Float16 *x, int lda, int M,
                  _Float16 *a, int ld_a, const Workspace &ws, hipStream_t st);
 void gemm_lmhead(const Dims &d, const uint16_t *W, const _Float16 *x, int lda, int M,
                  const ArgmaxEpi &e, hipStream_t st);
 
 // RMSNorm of rows into an f16 copy (the MFMA A operand) and, when y32 is
-// given, also into f32 [M, H].
-void rmsnorm_rows_f16(const float *h, int ldh, const float *w, int H, int M, float eps,
-                      _Float16 *x, int ldx, float *y32, hipStream_t st);
+// given, also into f32 [M, H].  `splits` pending partial-sum sets part[z][M][H]
+// of a residual GEMM are added into h first (H <= 5120).
+void rmsnorm_rows_f16(float *h, int ldh, const float *w, int H, int M, float eps, _Float16 *x,
+                      int ldx, float *y32, const float *part, int splits, hipStream_t st);
 // Embedding gather h[m] = f32(E[tokens[m]]) without scaling; an id outside
 // [0, V) reads row 0 and sets *bad_flag to 1.
 void embed_rows(const uint16_t *E, int H, int V, const int *const *tokens, int tok_off, int M,

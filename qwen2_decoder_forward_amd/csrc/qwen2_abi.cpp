@@ -465,6 +465,7 @@ void prefill_pass(qwen2_ctx *c, int M, int off, const int *pos, const int *seq, 
                                        c->h, c->bad_flag, st));
   const int n_chunks = chunks_for(host_pos[M - 1]);
   const bool gemv = M <= kGemvRows;
+  int pending = 0;  // split-K partial sums of the last residual GEMM not yet in h
   for (int l = 0; l < d.L; ++l) {
     const LayerW &w = c->layers[l];
     const q2::QkvEpi e = qkv_epi(c, l, pos, seq);
@@ -472,7 +473,8 @@ void prefill_pass(qwen2_ctx *c, int M, int off, const int *pos, const int *seq, 
       TIMED(QWEN2_OP_QKV, q2::gemv_qkv(d, w, c->h, M, e, eps, st));
     } else {
       TIMED(QWEN2_OP_NORM, q2::rmsnorm_rows_f16(c->h, d.H, w.attn_norm, d.H, M, eps, c->x16, d.H,
-                                                nullptr, st));
+                                                nullptr, c->splitk.buf, pending, st));
+      pending = 0;
       TIMED(QWEN2_OP_QKV, q2::gemm_qkv(d, w, c->x16, d.H, M, e, c->splitk, st));
     }
     if (l == d.L - 1) break;  // the last layer continues on the last row only
@@ -482,14 +484,16 @@ void prefill_pass(qwen2_ctx *c, int M, int off, const int *pos, const int *seq, 
       TIMED(QWEN2_OP_DOWN, q2::gemv_resid(w.wd, d.H, d.I_pad, c->a32, d.I_pad, M, c->h, d.H, st));
     } else {
       TIMED(QWEN2_OP_ATTN, q2::attn_prefill(d, l, kv, c->q32, nhd, rows, M, c->x16, nhd, st));
-      TIMED(QWEN2_OP_WO, q2::gemm_resid(w.wo, d.H, nhd, c->x16, nhd, M, c->h, d.H, c->splitk, st));
+      TIMED(QWEN2_OP_WO, pending = q2::gemm_resid(w.wo, d.H, nhd, c->x16, nhd, M, c->h, d.H,
+                                                  c->splitk, st));
       TIMED(QWEN2_OP_NORM, q2::rmsnorm_rows_f16(c->h, d.H, w.ffn_norm, d.H, M, eps, c->x16, d.H,
-                                                nullptr, st));
+                                                nullptr, c->splitk.buf, pending, st));
       TIMED(QWEN2_OP_GATEUP, q2::gemm_swiglu(d, w, c->x16, d.H, M, c->a16, d.I_pad, c->splitk, st));
-      TIMED(QWEN2_OP_DOWN,
-            q2::gemm_resid(w.wd, d.H, d.I_pad, c->a16, d.I_pad, M, c->h, d.H, c->splitk, st));
+      TIMED(QWEN2_OP_DOWN, pending = q2::gemm_resid(w.wd, d.H, d.I_pad, c->a16, d.I_pad, M, c->h,
+                                                    d.H, c->splitk, st));
     }
   }
+  // (the last layer's QKV norm above folded every pending partial sum)
   if (last) tail_row(c, M - 1, pos, seq, host_pos[M - 1], st);
 }
 
@@ -504,6 +508,7 @@ void decode_launches(qwen2_ctx *c, int B, int n_chunks, const int *dpos, const i
   TIMED(QWEN2_OP_EMBED, q2::embed_rows(c->tok_embd, d.H, d.V, &dev_slots(c)->tokens, 0, B, c->h,
                                        c->bad_flag, st));
   const bool gemv = B <= kGemvRows;
+  int pending = 0;  // split-K partial sums of the last residual GEMM not yet in h
   for (int l = 0; l < d.L; ++l) {
     const LayerW &w = c->layers[l];
     const q2::QkvEpi e = qkv_epi(c, l, dpos, dseq);
@@ -514,16 +519,18 @@ void decode_launches(qwen2_ctx *c, int B, int n_chunks, const int *dpos, const i
       TIMED(QWEN2_OP_DOWN, q2::gemv_resid(w.wd, d.H, d.I_pad, c->a32, d.I_pad, B, c->h, d.H, st));
     } else {
       TIMED(QWEN2_OP_NORM, q2::rmsnorm_rows_f16(c->h, d.H, w.attn_norm, d.H, B, eps, c->x16, d.H,
-                                                nullptr, st));
+                                                nullptr, c->splitk.buf, pending, st));
+      pending = 0;
       TIMED(QWEN2_OP_QKV, q2::gemm_qkv(d, w, c->x16, d.H, B, e, c->splitk, st));
       TIMED(QWEN2_OP_ATTN, q2::attn_decode(d, l, kv, c->q32, nhd, rows, B, n_chunks, true,
                                            c->part, nullptr, c->x16, nhd, st));
-      TIMED(QWEN2_OP_WO, q2::gemm_resid(w.wo, d.H, nhd, c->x16, nhd, B, c->h, d.H, c->splitk, st));
+      TIMED(QWEN2_OP_WO, pending = q2::gemm_resid(w.wo, d.H, nhd, c->x16, nhd, B, c->h, d.H,
+                                                  c->splitk, st));
       TIMED(QWEN2_OP_NORM, q2::rmsnorm_rows_f16(c->h, d.H, w.ffn_norm, d.H, B, eps, c->x16, d.H,
-                                                nullptr, st));
+                                                nullptr, c->splitk.buf, pending, st));
       TIMED(QWEN2_OP_GATEUP, q2::gemm_swiglu(d, w, c->x16, d.H, B, c->a16, d.I_pad, c->splitk, st));
-      TIMED(QWEN2_OP_DOWN,
-            q2::gemm_resid(w.wd, d.H, d.I_pad, c->a16, d.I_pad, B, c->h, d.H, c->splitk, st));
+      TIMED(QWEN2_OP_DOWN, pending = q2::gemm_resid(w.wd, d.H, d.I_pad, c->a16, d.I_pad, B, c->h,
+                                                    d.H, c->splitk, st));
     }
   }
   if (gemv) {
@@ -531,7 +538,7 @@ void decode_launches(qwen2_ctx *c, int B, int n_chunks, const int *dpos, const i
                                            argmax_epi(c), eps, st));
   } else {
     TIMED(QWEN2_OP_NORM, q2::rmsnorm_rows_f16(c->h, d.H, c->out_norm, d.H, B, eps, c->x16, d.H,
-                                              c->normed, st));
+                                              c->normed, c->splitk.buf, pending, st));
     TIMED(QWEN2_OP_LMHEAD, q2::gemm_lmhead(d, c->lm_head, c->x16, d.H, B, argmax_epi(c), st));
   }
 }

@@ -51,11 +51,12 @@ def test_tiny_kv_cache_matches_oracle(tiny_w):
     p.close()
 
 
-@pytest.mark.parametrize("n", [9, 40, 100])
+@pytest.mark.parametrize("n", [9, 40, 100, 600, 1100])
 def test_tiny_mfma_prefill_path(tiny_w, n):
     """Prompts longer than 8 rows take the MFMA GEMM + flash-attention path
-    (f16 operands): ragged 32-row tiles, hd = 16."""
-    p = Pair(TINY, tiny_w, n_ctx=128)
+    (f16 operands): ragged 32-row tiles, hd = 16; from 512 rows on the
+    large-tile GEMM (128-row tiles, a ragged last band at 1100)."""
+    p = Pair(TINY, tiny_w, n_ctx=max(128, n + 8))
     run_chain(p, syn.make_prompt(TINY, n, 3), 3, TOL, f"tiny-mfma-{n}")
     p.close()
 
