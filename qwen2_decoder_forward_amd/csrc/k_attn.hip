@@ -380,43 +380,97 @@ void attn_decode(const Dims &d, int layer, const KVCache &kv, const float *q, in
 }
 
 // ------------------------------------------------------------------ prefill
-// Flash attention on v_mfma_f32_32x32x16_f16, one block per (32-query tile,
-// KV head) with one wavefront per query head of the group.  Per 32-key tile:
-//   S^T[key, query] = K_tile (A: 32 keys x 16 d) * Q^T (B: 16 d x 32 queries)
-// so each lane owns one query column and 16 of the tile's keys (the other 16
+// Causal flash attention on v_mfma_f32_32x32x16_f16 for one prefill pass of
+// one sequence, on the binary16 mirror of the cache (K as [pos][d], V
+// transposed as [d][pos]: the MFMA operand layouts; written by every K/V
+// store, and by k_kv_f16 after a direct write of the f32 cache).  One block
+// per (32-query tile, KV head) with one wavefront per query head of the
+// group, so each K / V tile in LDS serves the whole group.  Per 64-key tile
+// and 32-key half:
+//   S^T[key, query] = K (A: 32 keys x 16 d) * Q^T (B: 16 d x 32 queries)
+// so each lane owns one query column and 16 of the half's keys (the other 16
 // sit in lane ^ 32): the online-softmax max and sum need one cross-lane step,
 // and the probabilities are already in the B-operand layout of
 //   O^T[d, query] += V^T (A: 32 d x 16 keys) * P^T (B: 16 keys x 32 queries)
-// once V^T's key order is matched to the lanes' key order.  K and V are read
-// from the f32 cache, rounded to f16 in LDS; accumulation stays in f32.
+// once V^T's key order is matched to the lanes' key order.  Key tiles are
+// double-buffered in LDS (loads of tile t+2 in flight while tile t is
+// multiplied; one barrier per tile).  Accumulation stays in f32.
 // MFMA 32x32 operand layout: lane l supplies A[l%32][8*(l/32)..+8] and
 // B[8*(l/32)..+8][l%32]; it receives D[8*(r/4) + 4*(l/32) + r%4][l%32], r<16.
+constexpr int kPreKeys = 64;  // keys per tile of the prefill attention
+
+struct KvF16P {
+  Dims d;
+  int layer, seq, pos0, n;
+  KVCache kv;
+};
+
+// One block per (64 positions, KV head) of the range: K rows are converted
+// in place order, V through an LDS transpose.
+template <int HD>
+__global__ __launch_bounds__(256) void k_kv_f16(KvF16P p) {
+  __shared__ float sT[HD][kPreKeys + 1];
+  const int g = blockIdx.y, p0 = p.pos0 + blockIdx.x * kPreKeys;
+  const int np = min(kPreKeys, p.pos0 + p.n - p0);
+  const int tid = threadIdx.x;
+  const float *kb = p.kv.k + p.kv.off(p.d, p.layer, p.seq, g, 0);
+  const float *vb = p.kv.v + p.kv.off(p.d, p.layer, p.seq, g, 0);
+  const size_t b16 = p.kv.off16(p.d, p.layer, p.seq, g);
+  _Float16 *ko = p.kv.k16 + b16 + (size_t)p0 * HD;
+  for (int i = tid; i < np * HD; i += 256) {
+    const int pp = i / HD, dd = i - pp * HD;
+    ko[i] = (_Float16)kb[(size_t)(p0 + pp) * HD + dd];
+    sT[dd][pp] = vb[(size_t)(p0 + pp) * HD + dd];
+  }
+  __syncthreads();
+  _Float16 *vo = p.kv.v16t + b16 + p0;
+  for (int i = tid; i < kPreKeys * HD; i += 256) {
+    const int dd = i / kPreKeys, pp = i - dd * kPreKeys;
+    if (pp < np) vo[(size_t)dd * p.kv.ldp + pp] = (_Float16)sT[dd][pp];
+  }
+}
+
+void kv_mirror(const Dims &d, const KVCache &kv, int layer, int seq, int pos0, int n,
+               hipStream_t st) {
+  const KvF16P cp{d, layer, seq, pos0, n, kv};
+  const dim3 grid((n + kPreKeys - 1) / kPreKeys, d.nkv);
+  switch (d.hd) {
+    case 16: hipLaunchKernelGGL(k_kv_f16<16>, grid, dim3(256), 0, st, cp); break;
+    case 64: hipLaunchKernelGGL(k_kv_f16<64>, grid, dim3(256), 0, st, cp); break;
+    default: hipLaunchKernelGGL(k_kv_f16<128>, grid, dim3(256), 0, st, cp); break;
+  }
+}
+
 struct AttnPreP {
   Dims d;
-  int layer;
-  KVCache kv;
   const float *q;
   int ldq;
   RowInfo rows;
   int M;
+  const _Float16 *k16, *v16t;  // (layer, seq, KV head 0) blocks of the mirror
+  size_t gstride;              // elements between KV heads in either mirror
+  int ldp;
   _Float16 *o16;
   int ldo;
   float qscale;  // head_dim^-0.5 * log2(e): scores in base 2
 };
 
-template <int HD>
+template <int HD, int G>
 __global__ __launch_bounds__(512) void k_attn_prefill(AttnPreP p) {
   constexpr int KSTEPS = (HD + 15) / 16;
   constexpr int DT = HD >= 32 ? HD / 32 : 1;  // 32-row d tiles of O^T
   constexpr int DV = DT * 32;
-  constexpr int KP = HD + 8;   // padded LDS row of K (halves)
-  constexpr int VP = 32 + 8;   // padded LDS row of V^T (halves)
-  __shared__ __attribute__((aligned(16))) _Float16 sK[32 * KP];
-  __shared__ __attribute__((aligned(16))) _Float16 sV[DV * VP];
+  constexpr int KT = kPreKeys;
+  constexpr int KP = HD + 8;    // padded LDS row of K (halves)
+  constexpr int VP = KT + 8;    // padded LDS row of V^T (halves)
+  constexpr int NTHR = 64 * G;       // one wavefront per query head of the group
+  constexpr int KCH = KT * HD / 8;   // 16-byte chunks of a K tile (and of a V^T tile)
+  constexpr int CPT = (KCH + NTHR - 1) / NTHR;  // chunks per thread
+  __shared__ __attribute__((aligned(16))) _Float16 sK[2][KT * KP];
+  __shared__ __attribute__((aligned(16))) _Float16 sV[2][DV * VP];
 
-  const int tid = threadIdx.x, nthr = blockDim.x;
+  const int tid = threadIdx.x, nthr = NTHR;
   const int lane = tid & 63, w = tid >> 6;
-  const int G = p.d.group;
   const int tile = gridDim.x - 1 - blockIdx.x;  // longest tiles first
   const int g = blockIdx.y;
   const int h = g * G + w;
@@ -424,14 +478,17 @@ __global__ __launch_bounds__(512) void k_attn_prefill(AttnPreP p) {
   const int M = p.M;
   const int last_row = min(r0 + 31, M - 1);
   const int kmax = p.rows.pos[last_row];
-  const int seq = p.rows.seq[r0];
   const int qrow = r0 + (lane & 31);
   const bool qvalid = qrow < M;
   const int qpos = qvalid ? p.rows.pos[qrow] : kmax;
+  const int qpos_min = p.rows.pos[r0];  // keys <= this are visible to every row
   const int hi = lane >> 5;
 
-  if (HD < 32) {
-    for (int i = tid; i < DV * VP; i += nthr) sV[i] = (_Float16)0.f;
+  if (HD < 32) {  // d rows HD .. 31 of V^T (never loaded) stay zero
+    for (int i = tid; i < 2 * (DV - HD) * VP; i += nthr) {
+      const int b = i / ((DV - HD) * VP), j = i - b * (DV - HD) * VP;
+      sV[b][HD * VP + j] = (_Float16)0.f;
+    }
   }
 
   h8 qf[KSTEPS];
@@ -450,81 +507,115 @@ __global__ __launch_bounds__(512) void k_attn_prefill(AttnPreP p) {
     for (int r = 0; r < 16; ++r) o[t][r] = 0.f;
   float m_run = kNegInf, l_run = 0.f;
 
-  const float *kbase = p.kv.k + p.kv.off(p.d, p.layer, seq, g, 0);
-  const float *vbase = p.kv.v + p.kv.off(p.d, p.layer, seq, g, 0);
-  const int ntiles = kmax / 32 + 1;
-  const int n_ctx = p.d.n_ctx;
+  const _Float16 *kg = p.k16 + (size_t)g * p.gstride;
+  const _Float16 *vg = p.v16t + (size_t)g * p.gstride;
+  const int ntiles = kmax / KT + 1;
 
-  for (int kt = 0; kt < ntiles; ++kt) {
-    const int key0 = kt * 32;
-    __syncthreads();
-    for (int i = tid; i < 32 * HD / 4; i += nthr) {
-      const int key = (i * 4) / HD, dd = (i * 4) - key * HD;
-      f4 kv4 = {0.f, 0.f, 0.f, 0.f}, vv4 = {0.f, 0.f, 0.f, 0.f};
-      if (key0 + key < n_ctx) {
-        kv4 = *(const f4 *)(kbase + (size_t)(key0 + key) * HD + dd);
-        vv4 = *(const f4 *)(vbase + (size_t)(key0 + key) * HD + dd);
+  // tile loads: chunk c of the K tile is key c / (HD/8), d-chunk c % (HD/8);
+  // chunk c of the V^T tile is d c / (KT/8), key-chunk c % (KT/8)
+  h8 rk[CPT], rv[CPT];
+  auto gload = [&](int kt) {
+#pragma unroll
+    for (int i = 0; i < CPT; ++i) {
+      const int c = tid + i * nthr;
+      if (c < KCH) {
+        const int kk = c / (HD / 8), kc = c - kk * (HD / 8);
+        rk[i] = *(const h8 *)(kg + (size_t)(kt * KT + kk) * HD + kc * 8);
+        const int dd = c / (KT / 8), vc = c - dd * (KT / 8);
+        rv[i] = *(const h8 *)(vg + (size_t)dd * p.ldp + kt * KT + vc * 8);
       }
-      h4 kh = {(_Float16)kv4.x, (_Float16)kv4.y, (_Float16)kv4.z, (_Float16)kv4.w};
-      *(h4 *)(sK + key * KP + dd) = kh;
-      sV[(dd + 0) * VP + key] = (_Float16)vv4.x;
-      sV[(dd + 1) * VP + key] = (_Float16)vv4.y;
-      sV[(dd + 2) * VP + key] = (_Float16)vv4.z;
-      sV[(dd + 3) * VP + key] = (_Float16)vv4.w;
+    }
+  };
+  auto swrite = [&](int buf) {
+#pragma unroll
+    for (int i = 0; i < CPT; ++i) {
+      const int c = tid + i * nthr;
+      if (c < KCH) {
+        const int kk = c / (HD / 8), kc = c - kk * (HD / 8);
+        *(h8 *)(&sK[buf][kk * KP + kc * 8]) = rk[i];
+        const int dd = c / (KT / 8), vc = c - dd * (KT / 8);
+        *(h8 *)(&sV[buf][dd * VP + vc * 8]) = rv[i];
+      }
+    }
+  };
+
+  gload(0);
+  swrite(0);
+  if (ntiles > 1) gload(1);
+  __syncthreads();
+  for (int kt = 0; kt < ntiles; ++kt) {
+    const int buf = kt & 1;
+    if (kt + 1 < ntiles) swrite(buf ^ 1);  // its buffer was last read in kt - 1
+    if (kt + 2 < ntiles) gload(kt + 2);
+    {
+      const _Float16 *sk = sK[buf];
+      const _Float16 *sv = sV[buf];
+      const int key0 = kt * KT;
+      f16x s[2];
+#pragma unroll
+      for (int hf = 0; hf < 2; ++hf) {
+#pragma unroll
+        for (int r = 0; r < 16; ++r) s[hf][r] = 0.f;
+#pragma unroll
+        for (int st = 0; st < KSTEPS; ++st) {
+          const h8 a = *(const h8 *)(sk + (hf * 32 + (lane & 31)) * KP + st * 16 + hi * 8);
+          s[hf] = __builtin_amdgcn_mfma_f32_32x32x16_f16(a, qf[st], s[hf], 0, 0, 0);
+        }
+      }
+      // causal mask (only tiles that reach past the first row's position)
+      if (key0 + KT - 1 > qpos_min) {
+#pragma unroll
+        for (int hf = 0; hf < 2; ++hf)
+#pragma unroll
+          for (int r = 0; r < 16; ++r) {
+            const int key = key0 + hf * 32 + 8 * (r >> 2) + 4 * hi + (r & 3);
+            if (key > qpos) s[hf][r] = kNegInf;
+          }
+      }
+      float mt = kNegInf;
+#pragma unroll
+      for (int hf = 0; hf < 2; ++hf)
+#pragma unroll
+        for (int r = 0; r < 16; ++r) mt = fmaxf(mt, s[hf][r]);
+      mt = fmaxf(mt, __shfl_xor(mt, 32, 64));
+      const float m_new = fmaxf(m_run, mt);
+      const float alpha = exp2f(m_run - m_new);
+      float ls = 0.f;
+      h8 pb[2][2];
+#pragma unroll
+      for (int hf = 0; hf < 2; ++hf)
+#pragma unroll
+        for (int r = 0; r < 16; ++r) {
+          const float e = exp2f(s[hf][r] - m_new);
+          ls += e;
+          pb[hf][r >> 3][r & 7] = (_Float16)e;
+        }
+      ls += __shfl_xor(ls, 32, 64);
+      l_run = l_run * alpha + ls;
+      m_run = m_new;
+#pragma unroll
+      for (int t = 0; t < DT; ++t) {
+#pragma unroll
+        for (int r = 0; r < 16; ++r) o[t][r] *= alpha;
+        const _Float16 *vr = sv + (t * 32 + (lane & 31)) * VP;
+#pragma unroll
+        for (int hf = 0; hf < 2; ++hf) {
+          const _Float16 *vk = vr + hf * 32;
+          const h4 x0 = *(const h4 *)(vk + 4 * hi);
+          const h4 x1 = *(const h4 *)(vk + 8 + 4 * hi);
+          const h4 x2 = *(const h4 *)(vk + 16 + 4 * hi);
+          const h4 x3 = *(const h4 *)(vk + 24 + 4 * hi);
+          const h8 a0 = (h8){x0[0], x0[1], x0[2], x0[3], x1[0], x1[1], x1[2], x1[3]};
+          const h8 a1 = (h8){x2[0], x2[1], x2[2], x2[3], x3[0], x3[1], x3[2], x3[3]};
+          o[t] = __builtin_amdgcn_mfma_f32_32x32x16_f16(a0, pb[hf][0], o[t], 0, 0, 0);
+          o[t] = __builtin_amdgcn_mfma_f32_32x32x16_f16(a1, pb[hf][1], o[t], 0, 0, 0);
+        }
+      }
     }
     __syncthreads();
-    if (w >= G) continue;
-
-    f16x s;
-#pragma unroll
-    for (int r = 0; r < 16; ++r) s[r] = 0.f;
-#pragma unroll
-    for (int st = 0; st < KSTEPS; ++st) {
-      h8 a;
-      if (HD >= 16) a = *(const h8 *)(sK + (lane & 31) * KP + st * 16 + hi * 8);
-      s = __builtin_amdgcn_mfma_f32_32x32x16_f16(a, qf[st], s, 0, 0, 0);
-    }
-    // causal mask and online softmax (base 2)
-    float mt = kNegInf;
-#pragma unroll
-    for (int r = 0; r < 16; ++r) {
-      const int key = key0 + 8 * (r >> 2) + 4 * hi + (r & 3);
-      if (key > qpos) s[r] = kNegInf;
-      mt = fmaxf(mt, s[r]);
-    }
-    mt = fmaxf(mt, __shfl_xor(mt, 32, 64));
-    const float m_new = fmaxf(m_run, mt);
-    const float alpha = exp2f(m_run - m_new);
-    float ls = 0.f;
-    h8 pb0, pb1;
-#pragma unroll
-    for (int r = 0; r < 16; ++r) {
-      const float e = exp2f(s[r] - m_new);
-      ls += e;
-      if (r < 8) pb0[r] = (_Float16)e;
-      else pb1[r - 8] = (_Float16)e;
-    }
-    ls += __shfl_xor(ls, 32, 64);
-    l_run = l_run * alpha + ls;
-    m_run = m_new;
-#pragma unroll
-    for (int t = 0; t < DT; ++t) {
-#pragma unroll
-      for (int r = 0; r < 16; ++r) o[t][r] *= alpha;
-      const _Float16 *vr = sV + (t * 32 + (lane & 31)) * VP;
-      h8 a0, a1;
-      const h4 x0 = *(const h4 *)(vr + 4 * hi);
-      const h4 x1 = *(const h4 *)(vr + 8 + 4 * hi);
-      const h4 x2 = *(const h4 *)(vr + 16 + 4 * hi);
-      const h4 x3 = *(const h4 *)(vr + 24 + 4 * hi);
-      a0 = (h8){x0[0], x0[1], x0[2], x0[3], x1[0], x1[1], x1[2], x1[3]};
-      a1 = (h8){x2[0], x2[1], x2[2], x2[3], x3[0], x3[1], x3[2], x3[3]};
-      o[t] = __builtin_amdgcn_mfma_f32_32x32x16_f16(a0, pb0, o[t], 0, 0, 0);
-      o[t] = __builtin_amdgcn_mfma_f32_32x32x16_f16(a1, pb1, o[t], 0, 0, 0);
-    }
   }
 
-  if (w >= G || !qvalid) return;
+  if (!qvalid) return;
   const float inv_l = 1.0f / l_run;
   _Float16 *orow = p.o16 + (size_t)qrow * p.ldo + (size_t)h * HD;
 #pragma unroll
@@ -540,16 +631,37 @@ __global__ __launch_bounds__(512) void k_attn_prefill(AttnPreP p) {
     }
 }
 
+template <int HD, int G>
+static void attn_prefill_g(const AttnPreP &p, dim3 grid, hipStream_t st) {
+  hipLaunchKernelGGL((k_attn_prefill<HD, G>), grid, dim3(64 * G), 0, st, p);
+}
+
+template <int HD>
+static void attn_prefill_hd(const AttnPreP &p, hipStream_t st) {
+  const dim3 grid((p.M + 31) / 32, p.d.nkv);
+  switch (p.d.group) {  // the group size is a compile-time constant of the kernel
+    case 1: attn_prefill_g<HD, 1>(p, grid, st); break;
+    case 2: attn_prefill_g<HD, 2>(p, grid, st); break;
+    case 3: attn_prefill_g<HD, 3>(p, grid, st); break;
+    case 4: attn_prefill_g<HD, 4>(p, grid, st); break;
+    case 5: attn_prefill_g<HD, 5>(p, grid, st); break;
+    case 6: attn_prefill_g<HD, 6>(p, grid, st); break;
+    case 7: attn_prefill_g<HD, 7>(p, grid, st); break;
+    default: attn_prefill_g<HD, 8>(p, grid, st); break;
+  }
+}
+
 void attn_prefill(const Dims &d, int layer, const KVCache &kv, const float *q, int ldq,
-                  RowInfo rows, int M, _Float16 *o16, int ldo, hipStream_t st) {
-  AttnPreP p{d, layer, kv, q, ldq, rows, M, o16, ldo,
-             (1.0f / sqrtf((float)d.hd)) * 1.4426950408889634f};
-  dim3 grid((M + 31) / 32, d.nkv);
-  dim3 block(64 * d.group);
+                  RowInfo rows, int M, int seq, int kmax, _Float16 *o16, int ldo, hipStream_t st) {
+  (void)kmax;  // (read on the device from the rows' positions)
+  const size_t b16 = kv.off16(d, layer, seq, 0);
+  const AttnPreP p{d, q, ldq, rows, M, kv.k16 + b16, kv.v16t + b16,
+                   (size_t)kv.ldp * d.hd, kv.ldp, o16, ldo,
+                   (1.0f / sqrtf((float)d.hd)) * 1.4426950408889634f};
   switch (d.hd) {
-    case 16: hipLaunchKernelGGL(k_attn_prefill<16>, grid, block, 0, st, p); break;
-    case 64: hipLaunchKernelGGL(k_attn_prefill<64>, grid, block, 0, st, p); break;
-    default: hipLaunchKernelGGL(k_attn_prefill<128>, grid, block, 0, st, p); break;
+    case 16: attn_prefill_hd<16>(p, st); break;
+    case 64: attn_prefill_hd<64>(p, st); break;
+    default: attn_prefill_hd<128>(p, st); break;
   }
 }
 

@@ -68,29 +68,8 @@ __global__ __launch_bounds__(256) void k_gemv(GemvP p) {
 #pragma unroll
       for (int m = 0; m < MT; ++m) acc[r][m] = 0.f;
 
-    // Epilogue inputs are loaded before the weight stream, so their latency
-    // (and for QKV the dependent cos/sin loads) overlaps it: lane r*MT + m
-    // owns output (row0 + r, m).
-    // (loads from clamped, always valid indices: no branch around them)
-    const int my_r = lane / MT, my_m = lane % MT;
-    const bool mine = my_r < R && my_m < M && row0 + my_r < p.N &&
-                      (EPI == EPI_RESID || (my_r & 1) == 0);
-    const int cm = my_m < M ? my_m : 0;
-    const int cn = mine ? row0 + my_r : 0;
-    float old = 0.f;  // RESID: the residual value the sum is added to
-    unsigned q_pos = 0, q_seq = 0;
-    float q_ba = 0.f, q_bb = 0.f;
-    if (kResid) old = p.out[(size_t)cm * p.ldo + cn];
-    if (EPI == EPI_QKV) qkv_pair_begin(p.qkv, cm, cn, q_pos, q_seq, q_ba, q_bb);
-    QkvPair qp{};
-    bool qp_ready = false;
-
     for (int kb0 = 0; kb0 < K; kb0 += KB * 512) {
       // 1. the weight stream: every load of this batch in flight at once
-      // (branch-free: an out-of-range chunk re-reads element 0, which then
-      // meets a zeroed activation, and a row past N is summed but never
-      // stored; so every wave issues a static number of loads and the
-      // epilogue loads issued before the stream can be waited for alone)
       h8 wv[KB][R];
 #pragma unroll
       for (int c = 0; c < KB; ++c) {
@@ -98,13 +77,12 @@ __global__ __launch_bounds__(256) void k_gemv(GemvP p) {
 #pragma unroll
         for (int r = 0; r < R; ++r) {
           const int n = row0 + r;
-          const bool ok = k < K && n < p.N;
-          wv[c][r] = __builtin_nontemporal_load((const h8 *)(p.W + (ok ? (size_t)n * K + k : 0)));
+          if (k < K && n < p.N)
+            wv[c][r] = __builtin_nontemporal_load((const h8 *)(p.W + (size_t)n * K + k));
+          else
+            wv[c][r] = (h8){0, 0, 0, 0, 0, 0, 0, 0};
         }
       }
-      // keep every weight load of the batch ahead of what follows (the
-      // scheduler would otherwise interleave them with the arithmetic)
-      __builtin_amdgcn_sched_barrier(0);
       // 2. activations (and the RMS of each row on the first pass)
       f4 xv[KB][MT][2];
 #pragma unroll
@@ -112,29 +90,15 @@ __global__ __launch_bounds__(256) void k_gemv(GemvP p) {
         const int k = kb0 + c * 512 + lane * 8;
 #pragma unroll
         for (int m = 0; m < MT; ++m) {
-          const bool ok = k < K && m < M;
-          const float *xp = xsrc + (ok ? (size_t)m * ldx + k : 0);
-          const float keep = ok ? 1.0f : 0.0f;  // values are finite: x * 0 == 0
-          xv[c][m][0] = *(const f4 *)xp * keep;
-          xv[c][m][1] = *(const f4 *)(xp + 4) * keep;
+          if (k < K && m < M) {
+            xv[c][m][0] = *(const f4 *)(xsrc + (size_t)m * ldx + k);
+            xv[c][m][1] = *(const f4 *)(xsrc + (size_t)m * ldx + k + 4);
+          } else {
+            xv[c][m][0] = (f4){0.f, 0.f, 0.f, 0.f};
+            xv[c][m][1] = (f4){0.f, 0.f, 0.f, 0.f};
+          }
         }
       }
-      f4 gv[KB][2];  // RMSNorm weights of the lane's chunks (normed variants)
-#pragma unroll
-      for (int c = 0; c < KB; ++c) {
-        const int k = kb0 + c * 512 + lane * 8;
-        const float *gp = p.norm_w + (norm && k < K ? k : 0);
-        if (norm) {
-          gv[c][0] = *(const f4 *)gp;
-          gv[c][1] = *(const f4 *)(gp + 4);
-        }
-      }
-      __builtin_amdgcn_sched_barrier(0);
-      // the rotation of the QKV epilogue, once the position has arrived (the
-      // activation loads above are already in flight)
-      if (EPI == EPI_QKV && !qp_ready)
-        qp = qkv_pair_end(p.d, p.qkv, cm, cn, q_pos, q_seq, q_ba, q_bb);
-      qp_ready = true;
       if (norm) {
         if (!have_inv) {  // normed variants have K <= KB * 512: one batch holds the row
 #pragma unroll
@@ -153,12 +117,17 @@ __global__ __launch_bounds__(256) void k_gemv(GemvP p) {
           have_inv = true;
         }
 #pragma unroll
-        for (int c = 0; c < KB; ++c)
+        for (int c = 0; c < KB; ++c) {
+          const int k = kb0 + c * 512 + lane * 8;
+          if (k < K) {
+            const f4 g0 = *(const f4 *)(p.norm_w + k), g1 = *(const f4 *)(p.norm_w + k + 4);
 #pragma unroll
-          for (int m = 0; m < MT; ++m) {  // (chunks past K hold zero activations)
-            xv[c][m][0] = xv[c][m][0] * inv[m] * gv[c][0];
-            xv[c][m][1] = xv[c][m][1] * inv[m] * gv[c][1];
+            for (int m = 0; m < MT; ++m) {
+              xv[c][m][0] = xv[c][m][0] * inv[m] * g0;
+              xv[c][m][1] = xv[c][m][1] * inv[m] * g1;
+            }
           }
+        }
       }
       // 3. multiply-accumulate in f32
 #pragma unroll
@@ -179,13 +148,12 @@ __global__ __launch_bounds__(256) void k_gemv(GemvP p) {
       for (int m = 0; m < MT; ++m) acc[r][m] = wave_sum(acc[r][m]);
 
     if (kResid) {
-      float mysum = 0.f;
 #pragma unroll
       for (int r = 0; r < R; ++r)
 #pragma unroll
         for (int m = 0; m < MT; ++m)
-          if (lane == r * MT + m) mysum = acc[r][m];
-      if (mine) p.out[(size_t)my_m * p.ldo + row0 + my_r] = old + mysum;
+          if (lane == r * MT + m && m < M && row0 + r < p.N)
+            p.out[(size_t)m * p.ldo + row0 + r] += acc[r][m];
     } else if (EPI == EPI_SWIGLU) {
 #pragma unroll
       for (int r = 0; r < R; r += 2)
@@ -194,16 +162,12 @@ __global__ __launch_bounds__(256) void k_gemv(GemvP p) {
           if (lane == r * MT + m && m < M && row0 + r < p.N)
             p.out[(size_t)m * p.ldo + ((row0 + r) >> 1)] = silu(acc[r][m]) * acc[r + 1][m];
     } else if (EPI == EPI_QKV) {
-      float a = 0.f, b = 0.f;
 #pragma unroll
       for (int r = 0; r < R; r += 2)
 #pragma unroll
         for (int m = 0; m < MT; ++m)
-          if (lane == r * MT + m) {
-            a = acc[r][m];
-            b = acc[r + 1][m];
-          }
-      if (mine) qkv_pair_store(qp, a, b);
+          if (lane == r * MT + m && m < M && row0 + r < p.N)
+            qkv_store_pair(p.d, p.qkv, m, row0 + r, acc[r][m], acc[r + 1][m]);
     } else {  // EPI_LMHEAD
 #pragma unroll
       for (int r = 0; r < R; ++r)

@@ -79,6 +79,8 @@ __device__ __forceinline__ float silu(float z) { return z / (1.0f + __expf(-z));
 // bias, then cos/sin of the position) long before its sums are ready.
 struct QkvPair {
   float *dst;      // element j of the q row or KV cache slot (j + hd/2 is the partner)
+  _Float16 *d16;   // the same element in the binary16 mirror (k, v only)
+  int stride16;    // mirror distance from element j to j + hd/2
   float ba, bb;    // bias of the two rows
   float c, s;      // rotation (1, 0 for v)
   int half;
@@ -129,20 +131,35 @@ __device__ __forceinline__ QkvPair qkv_pair_end(const Dims &d, const QkvEpi &e, 
   // position widened as unsigned values
   const bool is_k = head < d.nh + d.nkv;
   const size_t g = (size_t)(is_k ? head - d.nh : head - d.nh - d.nkv);
-  const size_t slot = ((((size_t)e.layer * d.n_seq + (size_t)seq) * d.nkv + g) * d.n_ctx +
-                       (size_t)pos) * (size_t)hd + (size_t)j;
-  if (head < d.nh)
+  const size_t blk = ((size_t)e.layer * d.n_seq + (size_t)seq) * d.nkv + g;
+  const size_t slot = (blk * d.n_ctx + (size_t)pos) * (size_t)hd + (size_t)j;
+  const size_t b16 = blk * (size_t)e.kv.ldp * hd;
+  q.d16 = nullptr;
+  q.stride16 = 0;
+  if (head < d.nh) {
     q.dst = e.q + (size_t)m * e.ldq + (size_t)head * hd + j;
-  else
-    q.dst = (is_k ? e.kv.k : e.kv.v) + slot;
+  } else if (is_k) {
+    q.dst = e.kv.k + slot;
+    q.d16 = e.kv.k16 + b16 + (size_t)pos * hd + j;
+    q.stride16 = half;
+  } else {
+    q.dst = e.kv.v + slot;
+    q.d16 = e.kv.v16t + b16 + (size_t)j * e.kv.ldp + pos;
+    q.stride16 = half * e.kv.ldp;
+  }
   return q;
 }
 
 __device__ __forceinline__ void qkv_pair_store(const QkvPair &q, float a, float b) {
   a += q.ba;
   b += q.bb;
-  q.dst[0] = a * q.c - b * q.s;
-  q.dst[q.half] = b * q.c + a * q.s;
+  const float x = a * q.c - b * q.s, y = b * q.c + a * q.s;
+  q.dst[0] = x;
+  q.dst[q.half] = y;
+  if (q.d16) {
+    q.d16[0] = (_Float16)x;
+    q.d16[q.stride16] = (_Float16)y;
+  }
 }
 
 __device__ __forceinline__ void qkv_store_pair(const Dims &d, const QkvEpi &e, int m, int n,

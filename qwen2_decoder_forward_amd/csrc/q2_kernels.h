@@ -32,10 +32,20 @@ struct RowInfo {
   const int *seq;  // [M] sequence slot of each row
 };
 
+// The f32 cache is the one decode attention reads; every K/V store also
+// writes a binary16 mirror laid out for the MFMA prefill attention: K as
+// [L][n_seq][nkv][ldp][hd] and V transposed as [L][n_seq][nkv][hd][ldp],
+// ldp = n_ctx rounded up to 64 positions (zero where nothing was written).
 struct KVCache {
   float *k, *v;  // [L][n_seq][nkv][n_ctx][hd] each
+  _Float16 *k16, *v16t;
+  int ldp;
   __host__ __device__ size_t off(const Dims &d, int l, int s, int g, int p) const {
     return ((((size_t)l * d.n_seq + s) * d.nkv + g) * d.n_ctx + p) * (size_t)d.hd;
+  }
+  // start of the (l, s, g) block of either mirror
+  __host__ __device__ size_t off16(const Dims &d, int l, int s, int g) const {
+    return (((size_t)l * d.n_seq + s) * d.nkv + g) * (size_t)ldp * d.hd;
   }
 };
 
@@ -128,9 +138,14 @@ void attn_decode(const Dims &d, int layer, const KVCache &kv, const float *q, in
 constexpr int kFusedKeys = 1024, kWoLoadsPerWave = 8;
 void attn_wo_fused(const Dims &d, int layer, const KVCache &kv, const float *q, int ldq,
                    RowInfo rows, int M, const uint16_t *wo, float *h, int ldh, hipStream_t st);
-// Causal flash attention over MFMA for one prefill pass of M rows of one
-// sequence (positions strictly increasing).
+// Causal flash attention over MFMA for one prefill pass of M rows of
+// sequence `seq` (positions strictly increasing, the last one kmax), on the
+// binary16 mirror of the cache.
 void attn_prefill(const Dims &d, int layer, const KVCache &kv, const float *q, int ldq,
-                  RowInfo rows, int M, _Float16 *o16, int ldo, hipStream_t st);
+                  RowInfo rows, int M, int seq, int kmax, _Float16 *o16, int ldo, hipStream_t st);
+// Rewrites the binary16 mirror of positions pos0 .. pos0+n-1 of (layer, seq)
+// from the f32 cache (after a direct write of the f32 cache).
+void kv_mirror(const Dims &d, const KVCache &kv, int layer, int seq, int pos0, int n,
+               hipStream_t st);
 
 }  // namespace q2

@@ -46,6 +46,8 @@ struct qwen2_ctx {
   uint64_t w_f16 = 0, w_f32 = 0;
   // KV cache and RoPE table
   float *kc = nullptr, *vc = nullptr;
+  _Float16 *kc16 = nullptr, *vc16t = nullptr;  // binary16 mirror (prefill attention)
+  int ldp = 0;                                 // mirror positions: n_ctx rounded up to 64
   size_t kv_elems = 0;
   float *rope_cos = nullptr, *rope_sin = nullptr;
   // scratch
@@ -107,6 +109,8 @@ void release(qwen2_ctx *c) {
   if (c->warena) (void)hipFree(c->warena);
   if (c->kc) (void)hipFree(c->kc);
   if (c->vc) (void)hipFree(c->vc);
+  if (c->kc16) (void)hipFree(c->kc16);
+  if (c->vc16t) (void)hipFree(c->vc16t);
   if (c->rope_cos) (void)hipFree(c->rope_cos);
   if (c->sarena) (void)hipFree(c->sarena);
   if (c->pinned) (void)hipHostFree(c->pinned);
@@ -266,6 +270,12 @@ int qwen2_load(const qwen2_hparams *hp, const qwen2_weights *w, void *stream, qw
     HIP_TRY(c, hipMalloc(&c->vc, c->kv_elems * 4));
     HIP_TRY(c, hipMemset(c->kc, 0, c->kv_elems * 4));
     HIP_TRY(c, hipMemset(c->vc, 0, c->kv_elems * 4));
+    c->ldp = (d.n_ctx + 63) / 64 * 64;
+    const size_t e16 = (size_t)d.L * d.n_seq * d.nkv * c->ldp * d.hd;
+    HIP_TRY(c, hipMalloc(&c->kc16, e16 * 2));
+    HIP_TRY(c, hipMalloc(&c->vc16t, e16 * 2));
+    HIP_TRY(c, hipMemset(c->kc16, 0, e16 * 2));
+    HIP_TRY(c, hipMemset(c->vc16t, 0, e16 * 2));
     return 0;
   }());
 
@@ -373,6 +383,8 @@ int stage_call(qwen2_ctx *c, hipStream_t st, const CallSlots &slots, int n, int 
 
 const CallSlots *dev_slots(qwen2_ctx *c) { return (const CallSlots *)c->io; }
 
+q2::KVCache kv_of(const qwen2_ctx *c) { return q2::KVCache{c->kc, c->vc, c->kc16, c->vc16t, c->ldp}; }
+
 q2::ArgmaxEpi argmax_epi(qwen2_ctx *c) {
   const CallSlots *ds = dev_slots(c);
   return q2::ArgmaxEpi{(float *const *)&ds->logits, c->best, (int *const *)&ds->argmax};
@@ -413,7 +425,7 @@ void attn_wo_gemv(qwen2_ctx *c, int l, const float *q, q2::RowInfo rows, int M, 
   const Dims &d = c->d;
   const LayerW &w = c->layers[l];
   const int nhd = d.nh * d.hd;
-  const q2::KVCache kv{c->kc, c->vc};
+  const q2::KVCache kv = kv_of(c);
   if (n_chunks * q2::kChunkKeys <= q2::kFusedKeys) {
     TIMED(QWEN2_OP_ATTN, q2::attn_wo_fused(d, l, kv, q, nhd, rows, M, w.wo, h, d.H, st));
     return;
@@ -428,7 +440,7 @@ q2::QkvEpi qkv_epi(qwen2_ctx *c, int l, const int *pos, const int *seq) {
   e.bias = c->layers[l].bqkv;
   e.q = c->q32;
   e.ldq = c->d.nh * c->d.hd;
-  e.kv = q2::KVCache{c->kc, c->vc};
+  e.kv = kv_of(c);
   e.layer = l;
   e.rows = q2::RowInfo{pos, seq};
   e.rope = q2::RopeTable{c->rope_cos, c->rope_sin};
@@ -454,12 +466,12 @@ void tail_row(qwen2_ctx *c, int r, const int *pos, const int *seq, int last_pos,
 }
 
 // One pass of at most max_rows rows; `last` marks the pass that reads out.
-void prefill_pass(qwen2_ctx *c, int M, int off, const int *pos, const int *seq, bool last,
-                  const int32_t *host_pos, hipStream_t st) {
+void prefill_pass(qwen2_ctx *c, int M, int off, const int *pos, const int *seq, int seq_id,
+                  bool last, const int32_t *host_pos, hipStream_t st) {
   const Dims &d = c->d;
   const float eps = c->hp.rms_eps;
   const int nhd = d.nh * d.hd;
-  const q2::KVCache kv{c->kc, c->vc};
+  const q2::KVCache kv = kv_of(c);
   const q2::RowInfo rows{pos, seq};
   TIMED(QWEN2_OP_EMBED, q2::embed_rows(c->tok_embd, d.H, d.V, &dev_slots(c)->tokens, off, M,
                                        c->h, c->bad_flag, st));
@@ -483,7 +495,8 @@ void prefill_pass(qwen2_ctx *c, int M, int off, const int *pos, const int *seq, 
       TIMED(QWEN2_OP_GATEUP, q2::gemv_swiglu(d, w, c->h, M, c->a32, d.I_pad, eps, st));
       TIMED(QWEN2_OP_DOWN, q2::gemv_resid(w.wd, d.H, d.I_pad, c->a32, d.I_pad, M, c->h, d.H, st));
     } else {
-      TIMED(QWEN2_OP_ATTN, q2::attn_prefill(d, l, kv, c->q32, nhd, rows, M, c->x16, nhd, st));
+      TIMED(QWEN2_OP_ATTN, q2::attn_prefill(d, l, kv, c->q32, nhd, rows, M, seq_id,
+                                            host_pos[M - 1], c->x16, nhd, st));
       TIMED(QWEN2_OP_WO, pending = q2::gemm_resid(w.wo, d.H, nhd, c->x16, nhd, M, c->h, d.H,
                                                   c->splitk, st));
       TIMED(QWEN2_OP_NORM, q2::rmsnorm_rows_f16(c->h, d.H, w.ffn_norm, d.H, M, eps, c->x16, d.H,
@@ -503,7 +516,7 @@ void decode_launches(qwen2_ctx *c, int B, int n_chunks, const int *dpos, const i
   const Dims &d = c->d;
   const float eps = c->hp.rms_eps;
   const int nhd = d.nh * d.hd;
-  const q2::KVCache kv{c->kc, c->vc};
+  const q2::KVCache kv = kv_of(c);
   const q2::RowInfo rows{dpos, dseq};
   TIMED(QWEN2_OP_EMBED, q2::embed_rows(c->tok_embd, d.H, d.V, &dev_slots(c)->tokens, 0, B, c->h,
                                        c->bad_flag, st));
@@ -562,7 +575,7 @@ int qwen2_prefill(qwen2_ctx *c, int32_t seq, const int32_t *tokens, const int32_
   if (rc) return rc;
   for (int off = 0; off < n; off += c->max_rows) {
     const int M = std::min(c->max_rows, n - off);
-    prefill_pass(c, M, off, df[1] + off, df[2] + off, off + M == n, positions + off, st);
+    prefill_pass(c, M, off, df[1] + off, df[2] + off, seq, off + M == n, positions + off, st);
   }
   HIP_TRY(c, hipGetLastError());
   return QWEN2_OK;
@@ -626,7 +639,7 @@ static int kv_copy(qwen2_ctx *c, int32_t layer, int32_t seq, int32_t pos0, int32
   if (seq < 0 || seq >= c->d.n_seq) return set_err(c, QWEN2_E_SEQ, "bad sequence slot");
   if (pos0 < 0 || (long long)pos0 + n > c->d.n_ctx)
     return set_err(c, QWEN2_E_POS, "kv range outside [0, n_ctx)");
-  const q2::KVCache kv{c->kc, c->vc};
+  const q2::KVCache kv = kv_of(c);
   const size_t bytes = (size_t)n * c->d.hd * 4;
   for (int g = 0; g < c->d.nkv; ++g) {
     float *ck = c->kc + kv.off(c->d, layer, seq, g, pos0);
@@ -640,6 +653,10 @@ static int kv_copy(qwen2_ctx *c, int32_t layer, int32_t seq, int32_t pos0, int32
       HIP_TRY(c, hipMemcpyAsync(bk, ck, bytes, hipMemcpyDeviceToDevice, st));
       HIP_TRY(c, hipMemcpyAsync(bv, cv, bytes, hipMemcpyDeviceToDevice, st));
     }
+  }
+  if (to_cache) {
+    q2::kv_mirror(c->d, kv, layer, seq, pos0, n, (hipStream_t)stream);
+    HIP_TRY(c, hipGetLastError());
   }
   return QWEN2_OK;
 }
