@@ -184,6 +184,7 @@ def test_graph_replay_matches_direct_launches(tiny_w, monkeypatch):
         for s in range(5):
             m.decode([0], ids[s:s + 1], [8 + s], lg[s + 1], ids[s + 1:s + 2])
             torch.cuda.synchronize()
+        assert m.sync_status() == 0
         out = lg.cpu().numpy(), ids.cpu().numpy()
         m.close()
         return out
