@@ -205,6 +205,146 @@ __global__ __launch_bounds__(256) void k_gemv(GemvP p) {
   }
 }
 
+// lm_head of the GEMV path: logits = W_lm RMSNorm(h) w_out, and each row's
+// greedy key.  A persistent grid (a few blocks per CU) walks the vocabulary
+// in row groups of 4 R rows per block; the normed activations are built once
+// per block and kept in registers, and the weights of a block's next row
+// group are requested before the current group is multiplied (two register
+// sets), so the 272 MB weight stream of the 0.5B shape never drains between
+// rounds.  K <= KB * 512.
+template <int MT, int R, int KB>
+__global__ __launch_bounds__(256) void k_lmhead(GemvP p) {
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  const int K = p.K, M = p.M, N = p.N;
+  float *logits = *p.logits;
+
+  auto wload = [&](int rg, h8 (&w)[KB][R]) {
+    const int row0 = (rg * 4 + wave) * R;
+#pragma unroll
+    for (int c = 0; c < KB; ++c) {
+      const int k = c * 512 + lane * 8;
+#pragma unroll
+      for (int r = 0; r < R; ++r) {
+        const int n = min(row0 + r, N - 1);  // (rows past N: loaded, never stored)
+        if (k < K)
+          w[c][r] = __builtin_nontemporal_load((const h8 *)(p.W + (size_t)n * K + k));
+        else
+          w[c][r] = (h8){0, 0, 0, 0, 0, 0, 0, 0};
+      }
+    }
+  };
+
+  int rg = blockIdx.x;
+  h8 wa[KB][R];
+  wload(rg, wa);
+
+  // normed activations of the lane's chunks: x * inv_rms * w_out
+  f4 xn[KB][MT][2];
+  float inv[MT];
+#pragma unroll
+  for (int c = 0; c < KB; ++c) {
+    const int k = c * 512 + lane * 8;
+#pragma unroll
+    for (int m = 0; m < MT; ++m) {
+      if (k < K && m < M) {
+        xn[c][m][0] = *(const f4 *)(p.x + (size_t)m * p.ldx + k);
+        xn[c][m][1] = *(const f4 *)(p.x + (size_t)m * p.ldx + k + 4);
+      } else {
+        xn[c][m][0] = (f4){0.f, 0.f, 0.f, 0.f};
+        xn[c][m][1] = (f4){0.f, 0.f, 0.f, 0.f};
+      }
+    }
+  }
+#pragma unroll
+  for (int m = 0; m < MT; ++m) {
+    float ss = 0.f;
+#pragma unroll
+    for (int c = 0; c < KB; ++c)
+#pragma unroll
+      for (int hh = 0; hh < 2; ++hh) {
+        const f4 v = xn[c][m][hh];
+        ss += v.x * v.x + v.y * v.y + v.z * v.z + v.w * v.w;
+      }
+    inv[m] = 1.0f / sqrtf(wave_sum(ss) / (float)K + p.eps);
+  }
+#pragma unroll
+  for (int c = 0; c < KB; ++c) {
+    const int k = c * 512 + lane * 8;
+    if (k < K) {
+      const f4 g0 = *(const f4 *)(p.norm_w + k), g1 = *(const f4 *)(p.norm_w + k + 4);
+#pragma unroll
+      for (int m = 0; m < MT; ++m) {
+        xn[c][m][0] = xn[c][m][0] * inv[m] * g0;
+        xn[c][m][1] = xn[c][m][1] * inv[m] * g1;
+      }
+    }
+  }
+
+  unsigned long long best[MT];
+#pragma unroll
+  for (int m = 0; m < MT; ++m) best[m] = 0ull;
+
+  for (; rg < p.n_groups; rg += gridDim.x) {
+    h8 wb[KB][R];
+    const bool more = rg + (int)gridDim.x < p.n_groups;  // (uniform across the block)
+    if (more) wload(rg + gridDim.x, wb);
+    const int row0 = (rg * 4 + wave) * R;
+    float acc[R][MT];
+#pragma unroll
+    for (int r = 0; r < R; ++r)
+#pragma unroll
+      for (int m = 0; m < MT; ++m) acc[r][m] = 0.f;
+#pragma unroll
+    for (int c = 0; c < KB; ++c)
+#pragma unroll
+      for (int m = 0; m < MT; ++m) {
+        const float xs[8] = {xn[c][m][0].x, xn[c][m][0].y, xn[c][m][0].z, xn[c][m][0].w,
+                             xn[c][m][1].x, xn[c][m][1].y, xn[c][m][1].z, xn[c][m][1].w};
+#pragma unroll
+        for (int r = 0; r < R; ++r)
+#pragma unroll
+          for (int j = 0; j < 8; ++j) acc[r][m] = fmaf((float)wa[c][r][j], xs[j], acc[r][m]);
+      }
+#pragma unroll
+    for (int r = 0; r < R; ++r)
+#pragma unroll
+      for (int m = 0; m < MT; ++m) {
+        const float v = wave_sum(acc[r][m]);
+        const int n = row0 + r;
+        if (m < M && n < N) {
+          if (logits && lane == r * MT + m) logits[(size_t)m * N + n] = v;
+          const unsigned long long key = argmax_key(v, n);
+          best[m] = key > best[m] ? key : best[m];
+        }
+      }
+    if (more) {
+#pragma unroll
+      for (int c = 0; c < KB; ++c)
+#pragma unroll
+        for (int r = 0; r < R; ++r) wa[c][r] = wb[c][r];
+    }
+  }
+
+  __shared__ unsigned long long s_best[4][MT];
+  if (lane == 0)
+#pragma unroll
+    for (int m = 0; m < MT; ++m) s_best[wave][m] = best[m];
+  if (blockIdx.x == 0 && wave == 0 && p.normed_out) {
+#pragma unroll
+    for (int m = 0; m < MT; ++m)
+      if (m < M)
+        for (int k = lane; k < K; k += 64)
+          p.normed_out[(size_t)m * K + k] = p.x[(size_t)m * p.ldx + k] * inv[m] * p.norm_w[k];
+  }
+  __syncthreads();
+  if ((int)threadIdx.x < M && threadIdx.x < MT) {
+    const int m = threadIdx.x;
+    unsigned long long b = s_best[0][m];
+    for (int w = 1; w < 4; ++w) b = s_best[w][m] > b ? s_best[w][m] : b;
+    atomicMax(&p.best[m], b);
+  }
+}
+
 // The greedy result: index of each row's packed maximum, which is then
 // cleared for the next call.  Runs after the lm_head kernel (the kernel
 // boundary orders the atomics before these reads).
@@ -282,6 +422,13 @@ void gemv_swiglu(const Dims &d, const LayerW &w, const float *h, int M, float *a
   launch<4, EPI_SWIGLU>(p, 1 << 30, st);
 }
 
+template <int MT, int R, int KB>
+static void launch_lmhead(GemvP &p, hipStream_t st) {
+  p.n_groups = (p.N + 4 * R - 1) / (4 * R);
+  const int grid = p.n_groups < 1024 ? p.n_groups : 1024;  // 4 blocks per CU
+  hipLaunchKernelGGL((k_lmhead<MT, R, KB>), dim3(grid), dim3(256), 0, st, p);
+}
+
 void gemv_lmhead(const Dims &d, const uint16_t *W, const float *norm_w, const float *h, int M,
                  float *normed_out, const ArgmaxEpi &e, float eps, hipStream_t st) {
   GemvP p = base(W, d.V, d.H, h, d.H, M);
@@ -290,7 +437,15 @@ void gemv_lmhead(const Dims &d, const uint16_t *W, const float *norm_w, const fl
   p.best = e.best;
   p.logits = e.logits;
   p.normed_out = normed_out;
-  launch<4, EPI_LMHEAD>(p, 4096, st);
+  const int kc = (d.H + 511) / 512;  // 512-half chunks per row (H <= 5120)
+  if (M <= 1) {  // one row: the persistent kernel (its normed row stays in registers)
+    if (kc <= 2) launch_lmhead<1, 4, 2>(p, st);
+    else if (kc <= 4) launch_lmhead<1, 2, 4>(p, st);
+    else if (kc <= 8) launch_lmhead<1, 1, 8>(p, st);
+    else launch_lmhead<1, 1, 10>(p, st);
+  } else {  // up to 8 rows: the GEMV kernel (8 normed rows would not fit in registers)
+    launch<4, EPI_LMHEAD>(p, 4096, st);
+  }
   argmax_finalize(e, M, st);
 }
 
