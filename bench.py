@@ -31,6 +31,24 @@ import numpy as np
 HBM_PEAK_GBS = 8000.0      # MI355X HBM3E
 MFMA_F16_PEAK_TFS = 2500.0  # MI355X dense f16 MFMA
 
+# HBM bytes per launch of the 0.5B gate/up GEMV from rocprofv3 FETCH_SIZE and
+# WRITE_SIZE passes, scaled by what the counters read for a 256 MiB copy
+# (profiles/qwen2.5-0.5b_gateup_gemv_hbm_traffic.md); valid only while the
+# kernel source is the one the counters were taken on.
+GATEUP_TRAFFIC_BYTES = 17573508
+GATEUP_TRAFFIC_SRC_SHA = "2ffa8faf8854b10d"
+
+
+def gateup_traffic(shape):
+    import hashlib
+    src = os.path.join(os.path.dirname(os.path.abspath(__file__)), "qwen2_decoder_forward_amd",
+                       "csrc", "k_gemv.hip")
+    with open(src, "rb") as f:
+        sha = hashlib.sha256(f.read()).hexdigest()[:16]
+    if sha != GATEUP_TRAFFIC_SRC_SHA or shape.name != "qwen2.5-0.5b":
+        return None
+    return GATEUP_TRAFFIC_BYTES
+
 
 def log(*a):
     print(*a, file=sys.stderr, flush=True)
@@ -122,6 +140,26 @@ def prefill_op_fractions(q, model, shape, prompt, n_ctx):
     return out
 
 
+def pmc_pass(torch, q, syn):
+    """Launches for the HBM traffic counters: torch's copy of a 256 MiB tensor
+    (every byte read once and written once: the calibration of FETCH_SIZE and
+    WRITE_SIZE), then 48 launches of the decode gate/up GEMV on the 0.5B shape
+    (two per layer, so 418 MB of weights > the 256 MB Infinity Cache)."""
+    shape = syn.MODELS["qwen2.5-0.5b"]
+    torch.cuda.set_device(0)
+    src = torch.ones(64 << 20, dtype=torch.float32, device="cuda")
+    dst = torch.empty_like(src)
+    dst.copy_(src)
+    torch.cuda.synchronize()
+    weights = syn.make_weights(shape)
+    model = q.Model(shape, weights, n_ctx=256)
+    q.qwen2_prof_repeat(model.ctx, "gateup", 1, 2 * shape.n_layer)
+    torch.cuda.synchronize()
+    model.close()
+    log(f"pmc pass: copy of {src.numel() * 4} bytes, {2 * shape.n_layer} gate/up launches "
+        f"of {gateup_bytes(shape)} algorithmic bytes")
+
+
 def main():
     ap = argparse.ArgumentParser(description=__doc__)
     ap.add_argument("--gpus", type=int, default=1)
@@ -131,6 +169,9 @@ def main():
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--workload", default="0.5b",
                     help="0.5b (the benchmark line, default), 0.5b-long, 0.5b-batched, hd128, tiny")
+    ap.add_argument("--pmc-pass", action="store_true",
+                    help="only the launches a rocprofv3 --pmc counter pass reads: a plain 256 MiB "
+                         "device copy (calibration), then 48 launches of the gate/up GEMV")
     args = ap.parse_args()
     if args.gpus != 1:
         print(json.dumps({"error": "this implementation runs on one GPU; --gpus must be 1 "
@@ -141,6 +182,10 @@ def main():
 
     import qwen2_decoder_forward_amd as q
     import qwen2_synth as syn
+
+    if args.pmc_pass:
+        pmc_pass(torch, q, syn)
+        return
 
     wl = syn.WORKLOADS[args.workload]
     shape = syn.MODELS[wl.model]
@@ -268,7 +313,7 @@ def main():
         "roofline": {
             "kernel": "k_gemv<1,4,EPI_SWIGLU> (RMSNorm + gate/up + SwiGLU, decode M=1)",
             "bound": "hbm", "achieved": achieved, "peak": HBM_PEAK_GBS, "unit": "GB/s",
-            "frac": achieved / HBM_PEAK_GBS, "traffic": None,
+            "frac": achieved / HBM_PEAK_GBS, "traffic": gateup_traffic(shape),
             "bytes_per_launch": gu_bytes, "avg_launch_us": gu_avg_s * 1e6, "launches_timed": reps,
             "timing": "HIP events around back-to-back launches cycling through the layers",
         },
