@@ -54,7 +54,7 @@ enum {
 /* Model and cache hyperparameters (HParams of the minfer page, section 2;
  * QwenConfig of xinfer Module 7, section 7.1).
  * Supported: n_embd == n_head * head_dim, n_embd % 64 == 0, n_embd <= 5120,
- * n_head % n_head_kv == 0 with n_head / n_head_kv <= 8,
+ * n_ctx <= 131072, n_head % n_head_kv == 0 with n_head / n_head_kv <= 8,
  * head_dim in {16, 64, 128}, rope_style == 0 (NonInterleaved, the Qwen2
  * convention of the minfer page, section 3), rope_theta > 0,
  * rope_freq_scale > 0, rms_eps >= 0, every size > 0. */

@@ -121,6 +121,7 @@ void embed_rows(const uint16_t *E, int H, int V, const int *const *tokens, int t
 
 // Attention.
 constexpr int kChunkKeys = 64;  // keys per block of the decode attention
+constexpr int kMaxMergeChunks = 2048;  // chunks the merge kernel holds: n_ctx <= 131072
 struct AttnPartials {
   float *buf;    // [rows][nkv][n_chunks][group][hd + 2]: (max, exp-sum, o) per head
   int n_chunks;  // chunk slots per row: ceil(n_ctx / kChunkKeys)

@@ -41,6 +41,8 @@ int check_hparams(const qwen2_hparams *hp, std::string *msg) {
     return fail(msg, QWEN2_E_HPARAMS, "n_embd %lld is not a multiple of 64", hp->n_embd);
   if (hp->n_embd > 5120)  // the decode GEMV keeps a whole normed row in registers
     return fail(msg, QWEN2_E_HPARAMS, "n_embd %lld > 5120 is not supported", hp->n_embd);
+  if (hp->n_ctx > 131072)  // the decode attention merges at most 2048 64-key chunks
+    return fail(msg, QWEN2_E_HPARAMS, "n_ctx %lld > 131072 is not supported", hp->n_ctx);
   if (hp->rope_style != 0)
     return fail(msg, QWEN2_E_HPARAMS, "rope_style %lld: only 0 (NonInterleaved) is supported",
                 hp->rope_style);
