@@ -162,11 +162,10 @@ __global__ __launch_bounds__(256) void k_gemm_lmhead(GemmP p) {
 
 // ------------------------------------------------------- large-M projections
 // Prefill GEMMs with many rows (M >= kBigM) are MFMA-bound.  Block tile
-// BM x BN x 64 with four wavefronts in a 2 x 2 arrangement, each owning
-// (BM/2) x (BN/2) of the output, i.e. (BM/64) x (BN/64) MFMA 32x32 tiles
-// (at 256 x 256: 256 f32 accumulators per lane, held in AGPRs at one wave
-// per SIMD).  Both 64-wide K slices live in LDS twice (double buffer, 64 KiB
-// per buffer at 256 x 256), so one barrier per K slice suffices:
+// BM x BN x 64 with NW wavefronts, WGM along M by NW/WGM along N, each owning
+// one (BM/WGM) x (BN*WGM/NW) piece of the output as 32 x 32 MFMA tiles.  Both
+// operands' 64-wide K slices live in LDS twice (double buffer), so one
+// barrier per K slice suffices:
 //   write slice t+1 (already in registers) to the free buffer, issue the
 //   global loads of slice t+2, multiply slice t, barrier.
 // LDS rows are 64 halves (128 B) without padding; 16-byte chunk c of row r
@@ -178,12 +177,14 @@ __global__ __launch_bounds__(256) void k_gemm_lmhead(GemmP p) {
 constexpr int kBK2 = 64;
 constexpr int kBigM = 512;
 
-template <int EPI, int BMT, int BNT, int WGM>
-__global__ __launch_bounds__(256) void k_gemm_big(GemmP p) {
-  constexpr int WGN = 4 / WGM;                   // wavefronts along M x along N
+template <int EPI, int BMT, int BNT, int WGM, int FB = 1, int NW = 4>
+__global__ __launch_bounds__(64 * NW) void k_gemm_big(GemmP p) {
+  constexpr int NT = 64 * NW;                      // threads
+  constexpr int WGN = NW / WGM;                    // wavefronts along M x along N
   constexpr int WTM = BMT / WGM, WTN = BNT / WGN;  // wave tile
   constexpr int TM = WTM / 32, TN = WTN / 32;      // MFMA tiles per wave
-  constexpr int CA = BMT / 32, CB = BNT / 32;      // 16-byte chunks per thread per slice
+  constexpr int RS = NT / 8;                       // rows a loader pass covers
+  constexpr int CA = BMT / RS, CB = BNT / RS;      // 16-byte chunks per thread per slice
   static_assert(TM >= 1 && TN >= 1 && CB >= 1, "tile shape");
   __shared__ __attribute__((aligned(16))) _Float16 sA[2 * BMT * kBK2];
   __shared__ __attribute__((aligned(16))) _Float16 sB[2 * BNT * kBK2];
@@ -202,42 +203,41 @@ __global__ __launch_bounds__(256) void k_gemm_big(GemmP p) {
   if ((nb & 7) == 0) tile = (bid & 7) * (nb >> 3) + (bid >> 3);
   const int m0 = (tile / gx) * BMT, n0 = (tile % gx) * BNT;
 
-  // global -> register staging: thread t moves chunk (t & 7) of rows (t >> 3) + 32 i
+  // global -> register staging: thread t moves chunk (t & 7) of rows (t >> 3) + RS i
   const int cc = tid & 7, r0 = tid >> 3;
   const _Float16 *Ag[CA];
   const _Float16 *Bg[CB];
 #pragma unroll
   for (int i = 0; i < CA; ++i) {
-    const int m = min(m0 + r0 + 32 * i, M - 1);
+    const int m = min(m0 + r0 + RS * i, M - 1);
     Ag[i] = p.A + (size_t)m * p.lda + cc * 8;
   }
 #pragma unroll
   for (int i = 0; i < CB; ++i) {
-    const int n = min(n0 + r0 + 32 * i, N - 1);
+    const int n = min(n0 + r0 + RS * i, N - 1);
     Bg[i] = p.W + (size_t)n * K + cc * 8;
   }
-  h8 ra[CA], rb[CB];
   // this block's K slices (split-K: blockIdx.z takes p.k_steps of them)
   const int kz0 = blockIdx.z * p.k_steps;
   const int nk = min(K / kBK2 - kz0, p.k_steps);
-  auto gload = [&](int kt) {
+  auto gload = [&](h8 (&ra)[CA], h8 (&rb)[CB], int kt) {
     const int ko = (kz0 + kt) * kBK2;
 #pragma unroll
     for (int i = 0; i < CA; ++i) ra[i] = *(const h8 *)(Ag[i] + ko);
 #pragma unroll
     for (int i = 0; i < CB; ++i) rb[i] = *(const h8 *)(Bg[i] + ko);
   };
-  auto swrite = [&](int buf) {
+  auto swrite = [&](int buf, const h8 (&ra)[CA], const h8 (&rb)[CB]) {
     _Float16 *a = sA + buf * BMT * kBK2;
     _Float16 *b = sB + buf * BNT * kBK2;
 #pragma unroll
     for (int i = 0; i < CA; ++i) {
-      const int r = r0 + 32 * i;
+      const int r = r0 + RS * i;
       *(h8 *)(a + r * kBK2 + ((cc ^ ((r >> 1) & 7)) << 3)) = ra[i];
     }
 #pragma unroll
     for (int i = 0; i < CB; ++i) {
-      const int r = r0 + 32 * i;
+      const int r = r0 + RS * i;
       *(h8 *)(b + r * kBK2 + ((cc ^ ((r >> 1) & 7)) << 3)) = rb[i];
     }
   };
@@ -250,36 +250,65 @@ __global__ __launch_bounds__(256) void k_gemm_big(GemmP p) {
 #pragma unroll
       for (int r = 0; r < 16; ++r) acc[i][j][r] = 0.f;
 
-  gload(0);
-  swrite(0);
-  if (nk > 1) gload(1);
+  // multiplies one 64-wide K slice out of LDS buffer buf: four 16-wide MFMA
+  // steps; with FB the operand fragments of step ks+1 are read from LDS
+  // before the MFMAs of step ks are issued
+  auto frag = [&](const _Float16 *a, const _Float16 *b, int ks, h8 (&af)[TM], h8 (&bf)[TN]) {
+    const int ch = ks * 2 + hi;  // logical 16-byte chunk of this lane's operand
+#pragma unroll
+    for (int i = 0; i < TM; ++i) {
+      const int r = wm * WTM + i * 32 + l32;
+      af[i] = *(const h8 *)(a + r * kBK2 + ((ch ^ ((r >> 1) & 7)) << 3));
+    }
+#pragma unroll
+    for (int j = 0; j < TN; ++j) {
+      const int r = wn * WTN + j * 32 + l32;
+      bf[j] = *(const h8 *)(b + r * kBK2 + ((ch ^ ((r >> 1) & 7)) << 3));
+    }
+  };
+  auto mfma = [&](const h8 (&af)[TM], const h8 (&bf)[TN]) {
+#pragma unroll
+    for (int i = 0; i < TM; ++i)
+#pragma unroll
+      for (int j = 0; j < TN; ++j)
+        acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_f16(af[i], bf[j], acc[i][j], 0, 0, 0);
+  };
+  auto compute = [&](int buf) {
+    const _Float16 *a = sA + buf * BMT * kBK2;
+    const _Float16 *b = sB + buf * BNT * kBK2;
+    if (FB) {
+      h8 af0[TM], bf0[TN], af1[TM], bf1[TN];
+      frag(a, b, 0, af0, bf0);
+      frag(a, b, 1, af1, bf1);
+      mfma(af0, bf0);
+      frag(a, b, 2, af0, bf0);
+      mfma(af1, bf1);
+      frag(a, b, 3, af1, bf1);
+      mfma(af0, bf0);
+      mfma(af1, bf1);
+    } else {
+#pragma unroll
+      for (int ks = 0; ks < kBK2 / 16; ++ks) {
+        h8 af[TM], bf[TN];
+        frag(a, b, ks, af, bf);
+        mfma(af, bf);
+      }
+    }
+  };
+
+  // Slice kt+1 sits in registers until it is written to LDS buffer
+  // (kt+1) & 1; one iteration writes it, requests slice kt+2, multiplies
+  // slice kt and ends on the barrier.
+  h8 ra[CA], rb[CB];
+  gload(ra, rb, 0);
+  swrite(0, ra, rb);
+  if (nk > 1) gload(ra, rb, 1);
   __syncthreads();
   for (int kt = 0; kt < nk; ++kt) {
     const int buf = kt & 1;
-    if (kt + 1 < nk) swrite(buf ^ 1);  // slice kt+1: its buffer was last read in kt-1
-    if (kt + 2 < nk) gload(kt + 2);
-    const _Float16 *a = sA + buf * BMT * kBK2;
-    const _Float16 *b = sB + buf * BNT * kBK2;
-#pragma unroll
-    for (int ks = 0; ks < kBK2 / 16; ++ks) {
-      const int ch = ks * 2 + hi;  // logical 16-byte chunk of this lane's operand
-      h8 af[TM], bf[TN];
-#pragma unroll
-      for (int i = 0; i < TM; ++i) {
-        const int r = wm * WTM + i * 32 + l32;
-        af[i] = *(const h8 *)(a + r * kBK2 + ((ch ^ ((r >> 1) & 7)) << 3));
-      }
-#pragma unroll
-      for (int j = 0; j < TN; ++j) {
-        const int r = wn * WTN + j * 32 + l32;
-        bf[j] = *(const h8 *)(b + r * kBK2 + ((ch ^ ((r >> 1) & 7)) << 3));
-      }
-#pragma unroll
-      for (int i = 0; i < TM; ++i)
-#pragma unroll
-        for (int j = 0; j < TN; ++j)
-          acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_f16(af[i], bf[j], acc[i][j], 0, 0, 0);
-    }
+    if (kt + 1 < nk) swrite(buf ^ 1, ra, rb);  // its buffer was last read in kt - 1
+    if (kt + 2 < nk) gload(ra, rb, kt + 2);
+    compute(buf);
     __syncthreads();
   }
 
@@ -312,14 +341,45 @@ __global__ __launch_bounds__(256) void k_gemm_big(GemmP p) {
     }
 }
 
-template <int EPI, int BMT, int BNT, int WGM>
+template <int EPI, int BMT, int BNT, int WGM, int FB = 0, int NW = 4>
 static void launch_big(GemmP p, int splits, hipStream_t st) {
   const int nk = p.K / kBK2;
   p.k_steps = (nk + splits - 1) / splits;
   splits = (nk + p.k_steps - 1) / p.k_steps;
   if (splits <= 1) p.ws = nullptr;
   dim3 grid((p.N + BNT - 1) / BNT, (p.M + BMT - 1) / BMT, splits);
-  hipLaunchKernelGGL((k_gemm_big<EPI, BMT, BNT, WGM>), grid, dim3(256), 0, st, p);
+  hipLaunchKernelGGL((k_gemm_big<EPI, BMT, BNT, WGM, FB, NW>), grid, dim3(64 * NW), 0, st, p);
+}
+
+// Tile of a large-M GEMM.  Short K (< 2048, the 0.5B shape's 896): 128 x 128
+// with 4 wavefronts.  Long K: the tile whose measured per-CU rate times the
+// number of rounds of blocks over the 256 CUs is cheapest, among 256 x 256
+// with 8 wavefronts (2 x 4, each 128 x 64; 910 TFLOP/s on a 2048 x 37888 x
+// 3584 GEMM), 128 x 256 with 8 wavefronts (850) and 128 x 128 with 4 (720).
+template <int EPI>
+static void launch_large_m(const GemmP &p, hipStream_t st) {
+  if (p.K < 2048) {
+    launch_big<EPI, 128, 128, 2>(p, 1, st);
+    return;
+  }
+  struct Cand { int bm, bn; double rate; };
+  const Cand cand[3] = {{256, 256, 910.0}, {128, 256, 850.0}, {128, 128, 720.0}};
+  int best = 2;
+  double best_cost = 1e300;
+  for (int i = 0; i < 3; ++i) {
+    const long tiles = (long)((p.M + cand[i].bm - 1) / cand[i].bm) * ((p.N + cand[i].bn - 1) / cand[i].bn);
+    const double cost = (double)((tiles + 255) / 256) * cand[i].bm * cand[i].bn / cand[i].rate;
+    if (cost < best_cost) {
+      best_cost = cost;
+      best = i;
+    }
+  }
+  if (best == 0)
+    launch_big<EPI, 256, 256, 2, 1, 8>(p, 1, st);
+  else if (best == 1)
+    launch_big<EPI, 128, 256, 2, 1, 8>(p, 1, st);
+  else
+    launch_big<EPI, 128, 128, 2>(p, 1, st);
 }
 
 // ------------------------------------------------------ skinny projections
@@ -444,9 +504,8 @@ static int launch_skinny(GemmP p, const Workspace &wsp, hipStream_t st) {
   return splits > 1 ? splits : 0;
 }
 
-// K % 64 == 0.  Many rows: 128 x 128 tiles (2 x 2 wavefronts; measured on
-// the prefill shapes against 256 x 256 and 256 x 128, it is the fastest or
-// within 3 %).  Fewer rows: narrow, short-K projections (QKV, WO) run on the
+// K % 64 == 0.  Many rows: launch_large_m.  Fewer rows: narrow, short-K
+// projections (QKV, WO) run on the
 // skinny kernel; the others on 128 x 32 LDS-staged tiles (4 x 1 wavefronts,
 // coalesced loads), so a 128-row GEMM has a block per 32 weight rows, and a
 // residual GEMM with a long K (down) also splits K.  (Measured at M = 128 on
@@ -456,7 +515,7 @@ static int launch_skinny(GemmP p, const Workspace &wsp, hipStream_t st) {
 template <int EPI>
 static int launch_tiles(GemmP p, const Workspace &wsp, hipStream_t st) {
   if (p.M >= kBigM) {
-    launch_big<EPI, 128, 128, 2>(p, 1, st);
+    launch_large_m<EPI>(p, st);
     return 0;
   }
   if (p.K <= 1024 && p.N <= 2048) return launch_skinny<EPI>(p, wsp, st);
