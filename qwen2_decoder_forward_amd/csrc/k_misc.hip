@@ -30,23 +30,24 @@ void embed_rows(const uint16_t *E, int H, int V, const int *const *tokens, int t
   hipLaunchKernelGGL(k_embed, dim3(M), dim3(256), 0, st, E, H, V, tokens, tok_off, h, bad_flag);
 }
 
-// One wavefront per row: y = w * x / sqrt(mean(x^2) + eps), stored as f16
-// (MFMA operand) and optionally f32.  When a split-K residual GEMM left
-// `splits` partial sums part[z][m][k] (z < splits), they are first added to
-// the row, which is written back: h[m] += sum_z part[z][m].
+// One block per row: y = w * x / sqrt(mean(x^2) + eps), stored as f16 (MFMA
+// operand) and optionally f32.  When a split-K residual GEMM left `splits`
+// partial sums part[z][m][k] (z < splits), they are first added to the row,
+// which is written back: h[m] += sum_z part[z][m].  Thread t owns 4-float
+// chunks t, t + 256, ... of the row (H <= 5120: at most 5), and issues the
+// loads of its chunk of every partial at once.
 __global__ __launch_bounds__(256) void k_rmsnorm_rows(float *h, int ldh, const float *w, int H,
                                                       int M, float eps, _Float16 *x, int ldx,
                                                       float *y32, const float *part, int splits) {
-  const int lane = threadIdx.x & 63;
-  const int m = blockIdx.x * 4 + (threadIdx.x >> 6);
-  if (m >= M) return;
+  constexpr int kMaxChunks = 5;  // 256 threads * 4 floats * 5 = 5120 (the supported maximum)
+  __shared__ float sRed[4];
+  const int m = blockIdx.x, tid = threadIdx.x;
   float *row = h + (size_t)m * ldh;
-  constexpr int kMaxChunks = 20;  // H <= 64 lanes * 4 * 20 = 5120 (the supported maximum)
   f4 v[kMaxChunks];
   float ss = 0.f;
 #pragma unroll
   for (int c = 0; c < kMaxChunks; ++c) {
-    const int k = lane * 4 + c * 256;
+    const int k = (tid + c * 256) * 4;
     if (k < H) {
       v[c] = *(const f4 *)(row + k);
       if (splits > 0) {
@@ -57,10 +58,13 @@ __global__ __launch_bounds__(256) void k_rmsnorm_rows(float *h, int ldh, const f
     }
   }
   ss = wave_sum(ss);
+  if ((tid & 63) == 0) sRed[tid >> 6] = ss;
+  __syncthreads();
+  ss = (sRed[0] + sRed[1]) + (sRed[2] + sRed[3]);
   const float inv = 1.0f / sqrtf(ss / (float)H + eps);
 #pragma unroll
   for (int c = 0; c < kMaxChunks; ++c) {
-    const int k = lane * 4 + c * 256;
+    const int k = (tid + c * 256) * 4;
     if (k < H) {
       const f4 g = *(const f4 *)(w + k);
       const f4 y = v[c] * inv * g;
@@ -73,8 +77,8 @@ __global__ __launch_bounds__(256) void k_rmsnorm_rows(float *h, int ldh, const f
 
 void rmsnorm_rows_f16(float *h, int ldh, const float *w, int H, int M, float eps, _Float16 *x,
                       int ldx, float *y32, const float *part, int splits, hipStream_t st) {
-  hipLaunchKernelGGL(k_rmsnorm_rows, dim3((M + 3) / 4), dim3(256), 0, st, h, ldh, w, H, M, eps,
-                     x, ldx, y32, part, splits);
+  hipLaunchKernelGGL(k_rmsnorm_rows, dim3(M), dim3(256), 0, st, h, ldh, w, H, M, eps, x, ldx,
+                     y32, part, splits);
 }
 
 }  // namespace q2
