@@ -351,19 +351,20 @@ static void launch_big(GemmP p, int splits, hipStream_t st) {
   hipLaunchKernelGGL((k_gemm_big<EPI, BMT, BNT, WGM, FB, NW>), grid, dim3(64 * NW), 0, st, p);
 }
 
-// Tile of a large-M GEMM.  Short K (< 2048, the 0.5B shape's 896): 128 x 128
-// with 4 wavefronts.  Long K: the tile whose measured per-CU rate times the
-// number of rounds of blocks over the 256 CUs is cheapest, among 256 x 256
-// with 8 wavefronts (2 x 4, each 128 x 64; 910 TFLOP/s on a 2048 x 37888 x
-// 3584 GEMM), 128 x 256 with 8 wavefronts (850) and 128 x 128 with 4 (720).
+// Tile of a large-M GEMM (all with 8 wavefronts, 2 along M x 4 along N).
+// Short K (< 2048, the 0.5B shape's 896): 128 x 128 (measured 381-643
+// TFLOP/s on the 4096-row 0.5B projections, against 304-590 with 4
+// wavefronts).  Long K: the tile whose measured per-CU rate times the number
+// of rounds of blocks over the 256 CUs is cheapest, among 256 x 256 (910
+// TFLOP/s on a 2048 x 37888 x 3584 GEMM), 128 x 256 (850) and 128 x 128 (740).
 template <int EPI>
 static void launch_large_m(const GemmP &p, hipStream_t st) {
   if (p.K < 2048) {
-    launch_big<EPI, 128, 128, 2>(p, 1, st);
+    launch_big<EPI, 128, 128, 2, 0, 8>(p, 1, st);
     return;
   }
   struct Cand { int bm, bn; double rate; };
-  const Cand cand[3] = {{256, 256, 910.0}, {128, 256, 850.0}, {128, 128, 720.0}};
+  const Cand cand[3] = {{256, 256, 910.0}, {128, 256, 850.0}, {128, 128, 740.0}};
   int best = 2;
   double best_cost = 1e300;
   for (int i = 0; i < 3; ++i) {
@@ -379,7 +380,7 @@ static void launch_large_m(const GemmP &p, hipStream_t st) {
   else if (best == 1)
     launch_big<EPI, 128, 256, 2, 1, 8>(p, 1, st);
   else
-    launch_big<EPI, 128, 128, 2>(p, 1, st);
+    launch_big<EPI, 128, 128, 2, 0, 8>(p, 1, st);
 }
 
 // ------------------------------------------------------ skinny projections
