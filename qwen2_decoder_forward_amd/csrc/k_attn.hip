@@ -491,25 +491,39 @@ struct AttnPreP {
   float qscale;  // head_dim^-0.5 * log2(e): scores in base 2
 };
 
-template <int HD, int G>
-__global__ __launch_bounds__(512) void k_attn_prefill(AttnPreP p) {
+// S = 2 (head_dim <= 64): two wavefronts per query head; the block's two
+// halves take the first and the second half of the key tiles, each with its
+// own LDS buffers, and their online-softmax states (max, sum, output) are
+// merged through LDS at the end.  This doubles the wavefronts a CU runs
+// (the grid has about one block per CU) and halves the longest block.
+template <int HD, int G, int S>
+__global__ __launch_bounds__(64 * G * S) void k_attn_prefill(AttnPreP p) {
   constexpr int KSTEPS = (HD + 15) / 16;
   constexpr int DT = HD >= 32 ? HD / 32 : 1;  // 32-row d tiles of O^T
   constexpr int DV = DT * 32;
   constexpr int KT = kPreKeys;
   constexpr int KP = HD + 8;    // padded LDS row of K (halves)
   constexpr int VP = KT + 8;    // padded LDS row of V^T (halves)
-  constexpr int NTHR = 64 * G;       // one wavefront per query head of the group
+  constexpr int NTHR = 64 * G;       // threads of one half: one wavefront per query head
   constexpr int KCH = KT * HD / 8;   // 16-byte chunks of a K tile (and of a V^T tile)
   constexpr int CPT = (KCH + NTHR - 1) / NTHR;  // chunks per thread
-  __shared__ __attribute__((aligned(16))) _Float16 sK[2][KT * KP];
-  __shared__ __attribute__((aligned(16))) _Float16 sV[2][DV * VP];
+  static_assert(S == 1 || S == 2, "one or two halves");
+  constexpr int NF = 2 + 16 * DT;  // merge state per lane: max, sum, output accumulators
+  constexpr size_t kTiles = (size_t)S * 2 * (KT * KP + DV * VP) * sizeof(_Float16);
+  constexpr size_t kMerge = S == 2 ? (size_t)G * NF * 64 * sizeof(float) : 0;
+  // the K / V^T tile buffers, and after the key loop the merge state
+  __shared__ __attribute__((aligned(16))) char smem[kTiles > kMerge ? kTiles : kMerge];
+  typedef _Float16 KTile[2][KT * KP];
+  typedef _Float16 VTile[2][DV * VP];
+  KTile *sK = (KTile *)smem;                                      // [S]
+  VTile *sV = (VTile *)(smem + (size_t)S * 2 * KT * KP * sizeof(_Float16));  // [S]
 
-  const int tid = threadIdx.x, nthr = NTHR;
-  const int lane = tid & 63, w = tid >> 6;
+  const int lane = threadIdx.x & 63, w = threadIdx.x >> 6;
+  const int half = w / G, hw = w - half * G;
+  const int tid = threadIdx.x - half * NTHR, nthr = NTHR;  // index within the half
   const int tile = gridDim.x - 1 - blockIdx.x;  // longest tiles first
   const int g = blockIdx.y;
-  const int h = g * G + w;
+  const int h = g * G + hw;
   const int r0 = tile * 32;
   const int M = p.M;
   const int last_row = min(r0 + 31, M - 1);
@@ -519,11 +533,13 @@ __global__ __launch_bounds__(512) void k_attn_prefill(AttnPreP p) {
   const int qpos = qvalid ? p.rows.pos[qrow] : kmax;
   const int qpos_min = p.rows.pos[r0];  // keys <= this are visible to every row
   const int hi = lane >> 5;
+  _Float16(&hK)[2][KT * KP] = sK[half];
+  _Float16(&hV)[2][DV * VP] = sV[half];
 
   if (HD < 32) {  // d rows HD .. 31 of V^T (never loaded) stay zero
     for (int i = tid; i < 2 * (DV - HD) * VP; i += nthr) {
       const int b = i / ((DV - HD) * VP), j = i - b * (DV - HD) * VP;
-      sV[b][HD * VP + j] = (_Float16)0.f;
+      hV[b][HD * VP + j] = (_Float16)0.f;
     }
   }
 
@@ -546,6 +562,9 @@ __global__ __launch_bounds__(512) void k_attn_prefill(AttnPreP p) {
   const _Float16 *kg = p.k16 + (size_t)g * p.gstride;
   const _Float16 *vg = p.v16t + (size_t)g * p.gstride;
   const int ntiles = kmax / KT + 1;
+  const int n0 = (ntiles + S - 1) / S;              // tiles of the first half (>= 1)
+  const int kt0 = half * n0;                         // this half's first tile
+  const int cnt = min(ntiles, kt0 + n0) - kt0;       // and its tile count (may be 0)
 
   // tile loads: chunk c of the K tile is key c / (HD/8), d-chunk c % (HD/8);
   // chunk c of the V^T tile is d c / (KT/8), key-chunk c % (KT/8)
@@ -568,25 +587,28 @@ __global__ __launch_bounds__(512) void k_attn_prefill(AttnPreP p) {
       const int c = tid + i * nthr;
       if (c < KCH) {
         const int kk = c / (HD / 8), kc = c - kk * (HD / 8);
-        *(h8 *)(&sK[buf][kk * KP + kc * 8]) = rk[i];
+        *(h8 *)(&hK[buf][kk * KP + kc * 8]) = rk[i];
         const int dd = c / (KT / 8), vc = c - dd * (KT / 8);
-        *(h8 *)(&sV[buf][dd * VP + vc * 8]) = rv[i];
+        *(h8 *)(&hV[buf][dd * VP + vc * 8]) = rv[i];
       }
     }
   };
 
-  gload(0);
-  swrite(0);
-  if (ntiles > 1) gload(1);
+  if (cnt > 0) {
+    gload(kt0);
+    swrite(0);
+    if (cnt > 1) gload(kt0 + 1);
+  }
   __syncthreads();
-  for (int kt = 0; kt < ntiles; ++kt) {
-    const int buf = kt & 1;
-    if (kt + 1 < ntiles) swrite(buf ^ 1);  // its buffer was last read in kt - 1
-    if (kt + 2 < ntiles) gload(kt + 2);
-    {
-      const _Float16 *sk = sK[buf];
-      const _Float16 *sv = sV[buf];
-      const int key0 = kt * KT;
+  for (int it = 0; it < n0; ++it) {  // (every half runs n0 iterations: the barriers match)
+    const int buf = it & 1;
+    const bool live = it < cnt;
+    if (it + 1 < cnt) swrite(buf ^ 1);  // its buffer was last read in it - 1
+    if (it + 2 < cnt) gload(kt0 + it + 2);
+    if (live) {
+      const _Float16 *sk = hK[buf];
+      const _Float16 *sv = hV[buf];
+      const int key0 = (kt0 + it) * KT;
       f16x s[2];
 #pragma unroll
       for (int hf = 0; hf < 2; ++hf) {
@@ -651,6 +673,30 @@ __global__ __launch_bounds__(512) void k_attn_prefill(AttnPreP p) {
     __syncthreads();
   }
 
+  if constexpr (S == 2) {  // the second half hands its state to the first through LDS
+    float *xb = (float *)smem;  // ([hw][field][lane]; the tiles are no longer read)
+    if (half == 1) {
+      float *x = xb + (size_t)hw * NF * 64 + lane;
+      x[0] = m_run;
+      x[64] = l_run;
+#pragma unroll
+      for (int t = 0; t < DT; ++t)
+#pragma unroll
+        for (int r = 0; r < 16; ++r) x[(2 + t * 16 + r) * 64] = o[t][r];
+    }
+    __syncthreads();
+    if (half == 1) return;
+    const float *x = xb + (size_t)hw * NF * 64 + lane;
+    const float m1 = x[0], l1 = x[64];
+    const float mm = fmaxf(m_run, m1);  // (the first half always saw key 0: finite)
+    const float a0 = exp2f(m_run - mm), a1 = exp2f(m1 - mm);
+    l_run = l_run * a0 + l1 * a1;
+#pragma unroll
+    for (int t = 0; t < DT; ++t)
+#pragma unroll
+      for (int r = 0; r < 16; ++r) o[t][r] = o[t][r] * a0 + x[(2 + t * 16 + r) * 64] * a1;
+  }
+
   if (!qvalid) return;
   const float inv_l = 1.0f / l_run;
   _Float16 *orow = p.o16 + (size_t)qrow * p.ldo + (size_t)h * HD;
@@ -669,7 +715,8 @@ __global__ __launch_bounds__(512) void k_attn_prefill(AttnPreP p) {
 
 template <int HD, int G>
 static void attn_prefill_g(const AttnPreP &p, dim3 grid, hipStream_t st) {
-  hipLaunchKernelGGL((k_attn_prefill<HD, G>), grid, dim3(64 * G), 0, st, p);
+  constexpr int S = HD <= 64 ? 2 : 1;  // (hd 128 needs more registers than 2 halves allow)
+  hipLaunchKernelGGL((k_attn_prefill<HD, G, S>), grid, dim3(64 * G * S), 0, st, p);
 }
 
 template <int HD>
