@@ -43,8 +43,10 @@ template <int MT, int R, int KB, int EPI>
 __global__ __launch_bounds__(256) void k_gemv(GemvP p) {
   const int lane = threadIdx.x & 63;
   const int wave = threadIdx.x >> 6;
-  const int K = p.K, M = p.M;
+  const int K = p.K, M = p.M, N = p.N;
   constexpr bool kResid = EPI == EPI_RESID;
+  // norm gains loaded with the activations (short rows) or at their use
+  constexpr bool kEarlyGain = KB <= 2;
   const bool norm = !kResid && p.norm_w != nullptr;
   const float *xsrc = p.x;
   const int ldx = p.ldx;
@@ -58,78 +60,101 @@ __global__ __launch_bounds__(256) void k_gemv(GemvP p) {
     inv[m] = 1.0f;
     best[m] = 0ull;
   }
-  bool have_inv = false;
+  // The (row, column) a lane stores in the epilogue, clamped into range so
+  // that every lane's epilogue loads are issued without a branch.
+  const int er = lane / MT, em = lane - er * MT;
+  const int emc = em < M ? em : M - 1;
 
   for (int rg = blockIdx.x; rg < p.n_groups; rg += gridDim.x) {
     const int row0 = (rg * 4 + wave) * R;
+    // 0. The loads the epilogue needs go first: vector loads return in issue
+    //    order, so waiting for them later does not wait for the weights.
+    const int en = min(row0 + (er < R ? er : R - 1), N - 1);
+    unsigned e_pos = 0, e_seq = 0;
+    float e_ba = 0.f, e_bb = 0.f, e_old = 0.f;
+    if (EPI == EPI_QKV) qkv_pair_begin(p.qkv, emc, en & ~1, e_pos, e_seq, e_ba, e_bb);
+    if (kResid) e_old = p.out[(size_t)emc * p.ldo + en];
+
     float acc[R][MT];
 #pragma unroll
     for (int r = 0; r < R; ++r)
 #pragma unroll
       for (int m = 0; m < MT; ++m) acc[r][m] = 0.f;
 
+    QkvPair e_pair;
     for (int kb0 = 0; kb0 < K; kb0 += KB * 512) {
-      // 1. the weight stream: every load of this batch in flight at once
+      const bool first = kb0 == 0;
+      // 1. activations (and the norm gains, once) ahead of the weights, so the
+      //    RMS reduction overlaps the weight stream; out-of-range chunks load
+      //    a valid address and are zeroed
+      f4 xv[KB][MT][2], gv[KB][2];
+#pragma unroll
+      for (int c = 0; c < KB; ++c) {
+        const int k = kb0 + c * 512 + lane * 8;
+        const bool kin = k < K;
+        const int kc = kin ? k : K - 8;
+#pragma unroll
+        for (int m = 0; m < MT; ++m) {
+          const int mc = m < M ? m : M - 1;
+          const f4 a0 = *(const f4 *)(xsrc + (size_t)mc * ldx + kc);
+          const f4 a1 = *(const f4 *)(xsrc + (size_t)mc * ldx + kc + 4);
+          const bool ok = kin && m < M;
+          xv[c][m][0] = ok ? a0 : (f4){0.f, 0.f, 0.f, 0.f};
+          xv[c][m][1] = ok ? a1 : (f4){0.f, 0.f, 0.f, 0.f};
+        }
+        if (kEarlyGain && norm && first) {
+          const f4 g0 = *(const f4 *)(p.norm_w + kc), g1 = *(const f4 *)(p.norm_w + kc + 4);
+          gv[c][0] = kin ? g0 : (f4){0.f, 0.f, 0.f, 0.f};
+          gv[c][1] = kin ? g1 : (f4){0.f, 0.f, 0.f, 0.f};
+        }
+      }
+      // 2. the weight stream: every load of this batch in flight at once
       h8 wv[KB][R];
 #pragma unroll
       for (int c = 0; c < KB; ++c) {
         const int k = kb0 + c * 512 + lane * 8;
+        const bool kin = k < K;
+        const int kc = kin ? k : K - 8;
 #pragma unroll
         for (int r = 0; r < R; ++r) {
           const int n = row0 + r;
-          if (k < K && n < p.N)
-            wv[c][r] = __builtin_nontemporal_load((const h8 *)(p.W + (size_t)n * K + k));
-          else
-            wv[c][r] = (h8){0, 0, 0, 0, 0, 0, 0, 0};
+          const int nc = n < N ? n : N - 1;
+          const h8 w = __builtin_nontemporal_load((const h8 *)(p.W + (size_t)nc * K + kc));
+          wv[c][r] = kin && n < N ? w : (h8){0, 0, 0, 0, 0, 0, 0, 0};
         }
       }
-      // 2. activations (and the RMS of each row on the first pass)
-      f4 xv[KB][MT][2];
-#pragma unroll
-      for (int c = 0; c < KB; ++c) {
-        const int k = kb0 + c * 512 + lane * 8;
+      // 3. the epilogue's dependent loads (cos/sin at the row's position)
+      if (EPI == EPI_QKV && first) e_pair = qkv_pair_end(p.d, p.qkv, emc, en & ~1, e_pos, e_seq, e_ba, e_bb);
+      // 4. RMSNorm of the activations (normed variants: K <= KB * 512, one batch)
+      if (norm && first) {
 #pragma unroll
         for (int m = 0; m < MT; ++m) {
-          if (k < K && m < M) {
-            xv[c][m][0] = *(const f4 *)(xsrc + (size_t)m * ldx + k);
-            xv[c][m][1] = *(const f4 *)(xsrc + (size_t)m * ldx + k + 4);
-          } else {
-            xv[c][m][0] = (f4){0.f, 0.f, 0.f, 0.f};
-            xv[c][m][1] = (f4){0.f, 0.f, 0.f, 0.f};
-          }
-        }
-      }
-      if (norm) {
-        if (!have_inv) {  // normed variants have K <= KB * 512: one batch holds the row
+          float ss = 0.f;
 #pragma unroll
-          for (int m = 0; m < MT; ++m) {
-            float ss = 0.f;
+          for (int c = 0; c < KB; ++c)
 #pragma unroll
-            for (int c = 0; c < KB; ++c)
-#pragma unroll
-              for (int hh = 0; hh < 2; ++hh) {
-                const f4 v = xv[c][m][hh];
-                ss += v.x * v.x + v.y * v.y + v.z * v.z + v.w * v.w;
-              }
-            ss = wave_sum(ss);
-            inv[m] = 1.0f / sqrtf(ss / (float)K + p.eps);
-          }
-          have_inv = true;
+            for (int hh = 0; hh < 2; ++hh) {
+              const f4 v = xv[c][m][hh];
+              ss += v.x * v.x + v.y * v.y + v.z * v.z + v.w * v.w;
+            }
+          ss = wave_sum(ss);
+          inv[m] = 1.0f / sqrtf(ss / (float)K + p.eps);
         }
 #pragma unroll
         for (int c = 0; c < KB; ++c) {
-          const int k = kb0 + c * 512 + lane * 8;
-          if (k < K) {
-            const f4 g0 = *(const f4 *)(p.norm_w + k), g1 = *(const f4 *)(p.norm_w + k + 4);
+          if (!kEarlyGain) {  // (long rows: loaded here, keeping registers for occupancy)
+            const int kc = min(c * 512 + lane * 8, K - 8);
+            gv[c][0] = *(const f4 *)(p.norm_w + kc);
+            gv[c][1] = *(const f4 *)(p.norm_w + kc + 4);
+          }
 #pragma unroll
-            for (int m = 0; m < MT; ++m) {
-              xv[c][m][0] = xv[c][m][0] * inv[m] * g0;
-              xv[c][m][1] = xv[c][m][1] * inv[m] * g1;
-            }
+          for (int m = 0; m < MT; ++m) {
+            xv[c][m][0] = xv[c][m][0] * inv[m] * gv[c][0];
+            xv[c][m][1] = xv[c][m][1] * inv[m] * gv[c][1];
           }
         }
       }
-      // 3. multiply-accumulate in f32
+      // 5. multiply-accumulate in f32
 #pragma unroll
       for (int c = 0; c < KB; ++c)
 #pragma unroll
@@ -152,30 +177,30 @@ __global__ __launch_bounds__(256) void k_gemv(GemvP p) {
       for (int r = 0; r < R; ++r)
 #pragma unroll
         for (int m = 0; m < MT; ++m)
-          if (lane == r * MT + m && m < M && row0 + r < p.N)
-            p.out[(size_t)m * p.ldo + row0 + r] += acc[r][m];
+          if (lane == r * MT + m && m < M && row0 + r < N)
+            p.out[(size_t)m * p.ldo + row0 + r] = e_old + acc[r][m];
     } else if (EPI == EPI_SWIGLU) {
 #pragma unroll
       for (int r = 0; r < R; r += 2)
 #pragma unroll
         for (int m = 0; m < MT; ++m)
-          if (lane == r * MT + m && m < M && row0 + r < p.N)
+          if (lane == r * MT + m && m < M && row0 + r < N)
             p.out[(size_t)m * p.ldo + ((row0 + r) >> 1)] = silu(acc[r][m]) * acc[r + 1][m];
     } else if (EPI == EPI_QKV) {
 #pragma unroll
       for (int r = 0; r < R; r += 2)
 #pragma unroll
         for (int m = 0; m < MT; ++m)
-          if (lane == r * MT + m && m < M && row0 + r < p.N)
-            qkv_store_pair(p.d, p.qkv, m, row0 + r, acc[r][m], acc[r + 1][m]);
+          if (lane == r * MT + m && m < M && row0 + r < N)
+            qkv_pair_store(e_pair, acc[r][m], acc[r + 1][m]);
     } else {  // EPI_LMHEAD
 #pragma unroll
       for (int r = 0; r < R; ++r)
 #pragma unroll
         for (int m = 0; m < MT; ++m) {
           const int n = row0 + r;
-          if (m < M && n < p.N) {
-            if (logits && lane == r * MT + m) logits[(size_t)m * p.N + n] = acc[r][m];
+          if (m < M && n < N) {
+            if (logits && lane == r * MT + m) logits[(size_t)m * N + n] = acc[r][m];
             const unsigned long long key = argmax_key(acc[r][m], n);
             best[m] = key > best[m] ? key : best[m];
           }
