@@ -228,7 +228,7 @@ __global__ __launch_bounds__(256) void k_attn_wo(AttnWoP p) {
   constexpr int KPL = KW / PH;
   constexpr int LPR = HD / 8;              // lanes per WO row segment (8 halves each)
   constexpr int RPI = 64 / LPR;            // WO rows per wavefront load
-  constexpr int WI = kWoLoadsPerWave;      // WO loads per wavefront
+  constexpr int WI = wo_loads_per_wave(HD);  // WO loads per wavefront
   // K tile in LDS, 16-byte chunk c of key row j stored at chunk c ^ (j % C4):
   // a lane walking its own row meets a different bank group than its
   // neighbours, so the row reads are conflict-free without padding.
@@ -368,7 +368,7 @@ static void attn_wo_hd(const AttnWoP &p, int grid_x, hipStream_t st) {
 
 void attn_wo_fused(const Dims &d, int layer, const KVCache &kv, const float *q, int ldq,
                    RowInfo rows, int M, const uint16_t *wo, float *h, int ldh, hipStream_t st) {
-  const int rpb = 4 * kWoLoadsPerWave * (64 / (d.hd / 8));  // WO rows per block
+  const int rpb = 4 * wo_loads_per_wave(d.hd) * (64 / (d.hd / 8));  // WO rows per block
   AttnWoP p{d, layer, kv, q, ldq, rows, M, (const _Float16 *)wo, h, ldh, rpb,
             1.0f / sqrtf((float)d.hd)};
   const int gx = (d.H + rpb - 1) / rpb;

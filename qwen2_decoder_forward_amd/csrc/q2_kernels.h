@@ -135,8 +135,12 @@ void attn_decode(const Dims &d, int layer, const KVCache &kv, const float *q, in
                  float *o32, _Float16 *o16, int ldo, hipStream_t st);
 // Attention fused with WO + residual for M <= 8 rows at positions below
 // kFusedKeys: per (WO row chunk, query head) block, partial row sums added
-// into h with float atomics.
-constexpr int kFusedKeys = 1024, kWoLoadsPerWave = 8;
+// into h with float atomics.  A block's WO chunk is 4 wavefronts x
+// wo_loads_per_wave(hd) loads x 512 / hd rows: hd 64 takes 64-row chunks, so
+// 14 heads x 14 chunks of the 0.5B shape spread the (repeated) K/V reads of
+// a head over 196 blocks (measured faster than 32, 128 or 256 rows).
+constexpr int kFusedKeys = 1024;
+constexpr int wo_loads_per_wave(int hd) { return hd == 64 ? 2 : 8; }
 void attn_wo_fused(const Dims &d, int layer, const KVCache &kv, const float *q, int ldq,
                    RowInfo rows, int M, const uint16_t *wo, float *h, int ldh, hipStream_t st);
 // Causal flash attention over MFMA for one prefill pass of M rows of
