@@ -230,6 +230,126 @@ __global__ __launch_bounds__(256) void k_gemv(GemvP p) {
   }
 }
 
+// One-row variant (batch-1 decode).  The block stages the activation row in
+// LDS once instead of every wavefront loading all of it: thread t loads
+// KB / 2 16-byte pieces of the row (and of the norm gains), issued before
+// the wavefront's weight loads so their wait does not wait for the weight
+// stream; the block reduces the row's sum of squares, and each thread
+// writes its normed pieces.  The LDS row is laid out so that the two
+// 16-byte halves of the 8-value chunk a lane multiplies sit in two
+// contiguous 256-byte runs (conflict-free reads).  Weight loads, their
+// f32 conversion and the epilogues are those of k_gemv.
+__device__ __forceinline__ int xs_slot(int k) {  // LDS slot of element k of a batch
+  const int c = k >> 9, r = k & 511;
+  return (c << 9) + (((r >> 2) & 1) << 8) + ((r >> 3) << 2) + (r & 3);
+}
+
+template <int R, int KB, int EPI>
+__global__ __launch_bounds__(256) void k_gemv1(GemvP p) {
+  static_assert(KB % 2 == 0, "KB / 2 pieces per thread");
+  constexpr int XP = KB / 2;  // 16-byte activation pieces per thread and batch
+  __shared__ __attribute__((aligned(16))) float sx[KB * 512];
+  __shared__ float sRed[4];
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int K = p.K, N = p.N;
+  constexpr bool kResid = EPI == EPI_RESID;
+  const bool norm = !kResid && p.norm_w != nullptr;
+  const int er = lane < R ? lane : R - 1;  // the row this lane stores (lanes < R)
+
+  for (int rg = blockIdx.x; rg < p.n_groups; rg += gridDim.x) {
+    const int row0 = (rg * 4 + wave) * R;
+    const int en = min(row0 + er, N - 1);
+    unsigned e_pos = 0, e_seq = 0;
+    float e_ba = 0.f, e_bb = 0.f, e_old = 0.f;
+    if (EPI == EPI_QKV) qkv_pair_begin(p.qkv, 0, en & ~1, e_pos, e_seq, e_ba, e_bb);
+    if (kResid) e_old = p.out[en];
+
+    float acc[R];
+#pragma unroll
+    for (int r = 0; r < R; ++r) acc[r] = 0.f;
+    QkvPair e_pair;
+    float inv = 1.0f;
+    for (int kb0 = 0; kb0 < K; kb0 += KB * 512) {
+      const bool first = kb0 == 0;
+      // 1. this thread's pieces of the activation row (and gains)
+      f4 xp[XP], gp[XP];
+#pragma unroll
+      for (int i = 0; i < XP; ++i) {
+        const int k = kb0 + 4 * (tid + 256 * i);
+        const int kc = k < K ? k : K - 4;
+        const f4 a = *(const f4 *)(p.x + kc);
+        xp[i] = k < K ? a : (f4){0.f, 0.f, 0.f, 0.f};
+        if (norm && first) {
+          const f4 g = *(const f4 *)(p.norm_w + kc);
+          gp[i] = k < K ? g : (f4){0.f, 0.f, 0.f, 0.f};
+        }
+      }
+      // 2. the weight stream
+      h8 wv[KB][R];
+#pragma unroll
+      for (int c = 0; c < KB; ++c) {
+        const int k = kb0 + c * 512 + lane * 8;
+        const bool kin = k < K;
+        const int kc = kin ? k : K - 8;
+#pragma unroll
+        for (int r = 0; r < R; ++r) {
+          const int n = row0 + r;
+          const int nc = n < N ? n : N - 1;
+          const h8 w = __builtin_nontemporal_load((const h8 *)(p.W + (size_t)nc * K + kc));
+          wv[c][r] = kin && n < N ? w : (h8){0, 0, 0, 0, 0, 0, 0, 0};
+        }
+      }
+      if (EPI == EPI_QKV && first)
+        e_pair = qkv_pair_end(p.d, p.qkv, 0, en & ~1, e_pos, e_seq, e_ba, e_bb);
+      // 3. RMS of the row over the block (normed variants: one batch)
+      if (norm && first) {
+        float ss = 0.f;
+#pragma unroll
+        for (int i = 0; i < XP; ++i) ss += xp[i].x * xp[i].x + xp[i].y * xp[i].y + xp[i].z * xp[i].z + xp[i].w * xp[i].w;
+        ss = wave_sum(ss);
+        if (lane == 0) sRed[wave] = ss;
+        __syncthreads();
+        inv = 1.0f / sqrtf(((sRed[0] + sRed[1]) + (sRed[2] + sRed[3])) / (float)K + p.eps);
+#pragma unroll
+        for (int i = 0; i < XP; ++i) xp[i] = xp[i] * inv * gp[i];
+      } else {
+        __syncthreads();  // the previous batch's LDS reads are done
+      }
+#pragma unroll
+      for (int i = 0; i < XP; ++i) *(f4 *)(sx + xs_slot(4 * (tid + 256 * i))) = xp[i];
+      __syncthreads();
+      // 4. multiply-accumulate in f32
+#pragma unroll
+      for (int c = 0; c < KB; ++c) {
+        const f4 x0 = *(const f4 *)(sx + c * 512 + lane * 4);
+        const f4 x1 = *(const f4 *)(sx + c * 512 + 256 + lane * 4);
+        const float xs[8] = {x0.x, x0.y, x0.z, x0.w, x1.x, x1.y, x1.z, x1.w};
+#pragma unroll
+        for (int r = 0; r < R; ++r)
+#pragma unroll
+          for (int j = 0; j < 8; ++j) acc[r] = fmaf((float)wv[c][r][j], xs[j], acc[r]);
+      }
+    }
+#pragma unroll
+    for (int r = 0; r < R; ++r) acc[r] = wave_sum(acc[r]);
+
+    if (kResid) {
+#pragma unroll
+      for (int r = 0; r < R; ++r)
+        if (lane == r && row0 + r < N) p.out[row0 + r] = e_old + acc[r];
+    } else if (EPI == EPI_SWIGLU) {
+#pragma unroll
+      for (int r = 0; r < R; r += 2)
+        if (lane == r && row0 + r < N) p.out[(row0 + r) >> 1] = silu(acc[r]) * acc[r + 1];
+    } else if (EPI == EPI_QKV) {
+#pragma unroll
+      for (int r = 0; r < R; r += 2)
+        if (lane == r && row0 + r < N) qkv_pair_store(e_pair, acc[r], acc[r + 1]);
+    }
+    __syncthreads();  // (the next row group rewrites sx)
+  }
+}
+
 // lm_head of the GEMV path: logits = W_lm RMSNorm(h) w_out, and each row's
 // greedy key.  A persistent grid (a few blocks per CU) walks the vocabulary
 // in row groups of 4 R rows per block; the normed activations are built once
@@ -399,10 +519,18 @@ template <int R, int EPI>
 static void launch(GemvP &p, int max_grid, hipStream_t st) {
   p.n_groups = (p.N + 4 * R - 1) / (4 * R);
   const int grid = p.n_groups < max_grid ? p.n_groups : max_grid;
-  if (p.M <= 1)
-    launch_kb<R, EPI, 1>(p, grid, st);
-  else
+  if (EPI != EPI_LMHEAD && p.M <= 1) {  // (one-row lm_head: k_lmhead)
+    const int kc = (p.K + 511) / 512;
+    constexpr int E1 = EPI == EPI_LMHEAD ? EPI_RESID : EPI;  // (never launched for lm_head)
+    if (kc <= 2)
+      hipLaunchKernelGGL((k_gemv1<R, 2, E1>), dim3(grid), dim3(256), 0, st, p);
+    else if (kc <= 8)
+      hipLaunchKernelGGL((k_gemv1<R, 8, E1>), dim3(grid), dim3(256), 0, st, p);
+    else
+      hipLaunchKernelGGL((k_gemv1<R, 10, E1>), dim3(grid), dim3(256), 0, st, p);
+  } else {
     launch_kb<R, EPI, 8>(p, grid, st);
+  }
 }
 
 static GemvP base(const uint16_t *W, int N, int K, const float *x, int ldx, int M) {
