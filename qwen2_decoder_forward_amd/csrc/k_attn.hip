@@ -249,40 +249,54 @@ __global__ __launch_bounds__(256) void k_attn_wo(AttnWoP p) {
   const int r0 = rc * p.rows_per_block;
   const int rend = min(H, r0 + p.rows_per_block);
   const int kc = lane % LPR;
+  // Loads are unconditional, at clamped indices, with no select on their
+  // values (a load the compiler can tie to a condition is moved into a
+  // branch, and its value is then copied at the branch join, which waits for
+  // it on the spot): WO rows past the chunk are never stored, keys past the
+  // position get a -inf score and a zero weight.  The first row's position,
+  // sequence slot and q go out before the WO slice, so the K / V loads that
+  // depend on them do not wait for the slice (vector loads complete in order).
+  const int d_lane = lane % LD, ph = lane / LD;
+  const int last = p.d.n_ctx - 1;
+  int pos = (int)vload(p.rows.pos, 0), seq = (int)vload(p.rows.seq, 0);
+  float qraw = p.q[(size_t)head * HD + (tid < HD ? tid : 0)];
+  __builtin_amdgcn_sched_barrier(0);  // (keeps this issue order)
   h8 wreg[WI];
 #pragma unroll
   for (int i = 0; i < WI; ++i) {
     const int row = r0 + (w * WI + i) * RPI + lane / LPR;
-    if (row < rend)
-      wreg[i] = __builtin_nontemporal_load(
-          (const h8 *)(p.wo + (size_t)row * nhd + (size_t)head * HD + kc * 8));
-    else
-      wreg[i] = (h8){0, 0, 0, 0, 0, 0, 0, 0};
+    wreg[i] = __builtin_nontemporal_load(
+        (const h8 *)(p.wo + (size_t)min(row, H - 1) * nhd + (size_t)head * HD + kc * 8));
   }
 
-  const int d_lane = lane % LD, ph = lane / LD;
-  for (int m = 0; m < M; ++m) {
-    const int pos = p.rows.pos[m], seq = p.rows.seq[m];
+  const int M_rows = MT == 1 ? 1 : M;  // (one row: no reload path in the loop)
+  for (int m = 0; m < M_rows; ++m) {
+    if (m > 0) {
+      pos = (int)vload(p.rows.pos, m);
+      seq = (int)vload(p.rows.seq, m);
+      qraw = p.q[(size_t)m * p.ldq + (size_t)head * HD + (tid < HD ? tid : 0)];
+    }
     const int P = pos + 1;
     const f4 *kbase = (const f4 *)(p.kv.k + p.kv.off(p.d, p.layer, seq, g, 0));
     const float *vbase = p.kv.v + p.kv.off(p.d, p.layer, seq, g, 0);
-    const float qv = tid < HD ? p.q[(size_t)m * p.ldq + (size_t)head * HD + tid] * p.scale : 0.f;
     float m_run = kNegInf, l_run = 0.f;
     f4 o = {0.f, 0.f, 0.f, 0.f};
-    for (int t0 = 0; t0 < P; t0 += TK) {
+    int t0 = 0;
+    do {
       // this tile's K chunks (coalesced) and the V values of this lane's keys
       f4 kr[KPT];
 #pragma unroll
       for (int i = 0; i < KPT; ++i) {
         const int ci = tid + 256 * i, j = ci / C4;
-        kr[i] = t0 + j < P ? kbase[(size_t)t0 * C4 + ci] : (f4){0.f, 0.f, 0.f, 0.f};
+        kr[i] = kbase[(size_t)min(t0 + j, last) * C4 + (ci - j * C4)];
       }
       f4 v[KPL];
 #pragma unroll
       for (int i = 0; i < KPL; ++i) {
         const int jj = t0 + KW * w + ph + PH * i;
-        v[i] = jj < P ? *(const f4 *)(vbase + (size_t)jj * HD + 4 * d_lane) : (f4){0.f, 0.f, 0.f, 0.f};
+        v[i] = *(const f4 *)(vbase + (size_t)min(jj, last) * HD + 4 * d_lane);
       }
+      const float qv = tid < HD ? qraw * p.scale : 0.f;
       __syncthreads();  // the previous tile's (or row's) LDS reads are done
 #pragma unroll
       for (int i = 0; i < KPT; ++i) {
@@ -320,7 +334,8 @@ __global__ __launch_bounds__(256) void k_attn_wo(AttnWoP p) {
       o *= alpha;
 #pragma unroll
       for (int i = 0; i < KPL; ++i) o += sP[KW * w + ph + PH * i] * v[i];
-    }
+      t0 += TK;
+    } while (t0 < P);
     __syncthreads();  // sOp of the previous row is consumed
     *(f4 *)(sOp + (w * PH + ph) * HD + 4 * d_lane) = o;
     __syncthreads();

@@ -160,6 +160,56 @@ __global__ __launch_bounds__(256) void k_gemm_lmhead(GemmP p) {
   }
 }
 
+// Epilogue of one 32 x 32 MFMA tile held by a wavefront (lane l holds
+// D[8 (r/4) + 4 (l/32) + r%4][l%32], r = 0..15) whose first row is mt0 and
+// whose column is n.  Every load (the residual rows, the QKV epilogue's
+// tables) is issued before the first store, so the tile costs one or two
+// memory round trips: a load after a store to a possibly aliasing address
+// would wait for it.  Split-K residual blocks (p.ws) store raw partial sums
+// [split][M][N], folded in by the next RMSNorm.
+template <int EPI>
+__device__ __forceinline__ void tile_epilogue(const GemmP &p, const f16x &v, int mt0, int n) {
+  const int lane = threadIdx.x & 63, hi = lane >> 5;
+  const int M = p.M, N = p.N;
+  int m[16];
+  bool ok[16];
+#pragma unroll
+  for (int r = 0; r < 16; ++r) {
+    m[r] = mt0 + 8 * (r >> 2) + 4 * hi + (r & 3);
+    ok[r] = m[r] < M && n < N;
+    m[r] = min(m[r], M - 1);
+  }
+  if (EPI == G_RESID && p.ws) {
+#pragma unroll
+    for (int r = 0; r < 16; ++r)
+      if (ok[r]) p.ws[((size_t)blockIdx.z * M + m[r]) * N + n] = v[r];
+  } else if (EPI == G_RESID) {
+    const int nc = min(n, N - 1);
+    float old[16];
+#pragma unroll
+    for (int r = 0; r < 16; ++r) old[r] = p.h[(size_t)m[r] * p.ldh + nc];
+    pin_regs(old);
+#pragma unroll
+    for (int r = 0; r < 16; ++r)
+      if (ok[r]) p.h[(size_t)m[r] * p.ldh + n] = old[r] + v[r];
+  } else {
+    float a[16], b[16];
+#pragma unroll
+    for (int r = 0; r < 16; ++r) {
+      a[r] = v[r];
+      b[r] = __shfl_xor(v[r], 1, 64);  // the pair partner (column n + 1)
+      ok[r] = ok[r] && (n & 1) == 0;
+    }
+    if (EPI == G_QKV) {
+      qkv_store_rows<16>(p.d, p.qkv, m, min(n & ~1, N - 2), a, b, ok);
+    } else {
+#pragma unroll
+      for (int r = 0; r < 16; ++r)
+        if (ok[r]) p.a16[(size_t)m[r] * p.ld_a + (n >> 1)] = (_Float16)(silu(a[r]) * b[r]);
+    }
+  }
+}
+
 // ------------------------------------------------------- large-M projections
 // Prefill GEMMs with many rows (M >= kBigM) are MFMA-bound.  Block tile
 // BM x BN x 64 with NW wavefronts, WGM along M by NW/WGM along N, each owning
@@ -177,7 +227,7 @@ __global__ __launch_bounds__(256) void k_gemm_lmhead(GemmP p) {
 constexpr int kBK2 = 64;
 constexpr int kBigM = 512;
 
-template <int EPI, int BMT, int BNT, int WGM, int FB = 1, int NW = 4>
+template <int EPI, int BMT, int BNT, int WGM, int FB = 1, int NW = 4, int S = 1>
 __global__ __launch_bounds__(64 * NW) void k_gemm_big(GemmP p) {
   constexpr int NT = 64 * NW;                      // threads
   constexpr int WGN = NW / WGM;                    // wavefronts along M x along N
@@ -296,59 +346,70 @@ __global__ __launch_bounds__(64 * NW) void k_gemm_big(GemmP p) {
     }
   };
 
-  // Slice kt+1 sits in registers until it is written to LDS buffer
-  // (kt+1) & 1; one iteration writes it, requests slice kt+2, multiplies
-  // slice kt and ends on the barrier.
-  h8 ra[CA], rb[CB];
-  gload(ra, rb, 0);
-  swrite(0, ra, rb);
-  if (nk > 1) gload(ra, rb, 1);
-  __syncthreads();
-  for (int kt = 0; kt < nk; ++kt) {
-    const int buf = kt & 1;
-    if (kt + 1 < nk) swrite(buf ^ 1, ra, rb);  // its buffer was last read in kt - 1
-    if (kt + 2 < nk) gload(ra, rb, kt + 2);
-    compute(buf);
+  if constexpr (S == 1) {
+    // Slice kt+1 sits in registers until it is written to LDS buffer
+    // (kt+1) & 1; one iteration writes it, requests slice kt+2, multiplies
+    // slice kt and ends on the barrier.
+    h8 ra[CA], rb[CB];
+    gload(ra, rb, 0);
+    swrite(0, ra, rb);
+    if (nk > 1) gload(ra, rb, 1);
     __syncthreads();
+    for (int kt = 0; kt < nk; ++kt) {
+      const int buf = kt & 1;
+      if (kt + 1 < nk) swrite(buf ^ 1, ra, rb);  // its buffer was last read in kt - 1
+      if (kt + 2 < nk) gload(ra, rb, kt + 2);
+      compute(buf);
+      __syncthreads();
+    }
+  } else {
+    // Ring of S register sets: slices kt+1 .. kt+S-1 are in flight while
+    // slice kt is multiplied.  An iteration writes slice kt (its loads were
+    // issued S iterations earlier) to LDS buffer kt & 1, whose last reader
+    // was iteration kt - 2 (behind the barrier of kt - 1), requests slice
+    // kt + S into the freed register set, and multiplies slice kt.  Every
+    // iteration issues the same loads (past the last slice they re-read it,
+    // and the padding iterations multiply nothing), so the compiler's count
+    // of outstanding loads stays exact and each LDS write waits only for
+    // its own slice rather than draining the ring.
+    // (The scheduling barriers keep the sets' loads in issue order: sets
+    // issued out of order in the prologue would make the count at the loop
+    // head a full drain.)
+    h8 ra[S][CA], rb[S][CB];
+#pragma unroll
+    for (int s = 0; s < S; ++s) {
+      gload(ra[s], rb[s], min(s, nk - 1));
+      __builtin_amdgcn_sched_barrier(0);
+    }
+    for (int kb = 0; kb < nk; kb += S) {
+#pragma unroll
+      for (int s = 0; s < S; ++s) {
+        const int kt = kb + s;
+        swrite(kt & 1, ra[s], rb[s]);
+        __syncthreads();
+        gload(ra[s], rb[s], min(kt + S, nk - 1));
+        __builtin_amdgcn_sched_barrier(0);
+        if (kt < nk) compute(kt & 1);  // (uniform across the block)
+      }
+    }
   }
 
-  // epilogue (same ops as k_gemm's, over TM x TN tiles); split-K blocks
-  // store raw partial sums [split][M][N] instead (residual GEMMs only; the
-  // RMSNorm kernel that follows folds them into the residual rows)
+  // epilogue, one 32 x 32 tile at a time
 #pragma unroll
   for (int i = 0; i < TM; ++i)
 #pragma unroll
-    for (int j = 0; j < TN; ++j) {
-      const int n = n0 + wn * WTN + j * 32 + l32;
-#pragma unroll
-      for (int r = 0; r < 16; ++r) {
-        const int m = m0 + wm * WTM + i * 32 + 8 * (r >> 2) + 4 * hi + (r & 3);
-        const float v = acc[i][j][r];
-        if (EPI == G_RESID && p.ws) {
-          if (m < M && n < N) p.ws[((size_t)blockIdx.z * M + m) * N + n] = v;
-        } else if (EPI == G_RESID) {
-          if (m < M && n < N) p.h[(size_t)m * p.ldh + n] += v;
-        } else {
-          const float partner = __shfl_xor(v, 1, 64);
-          if ((n & 1) == 0 && m < M && n < N) {
-            if (EPI == G_QKV)
-              qkv_store_pair(p.d, p.qkv, m, n, v, partner);
-            else
-              p.a16[(size_t)m * p.ld_a + (n >> 1)] = (_Float16)(silu(v) * partner);
-          }
-        }
-      }
-    }
+    for (int j = 0; j < TN; ++j)
+      tile_epilogue<EPI>(p, acc[i][j], m0 + wm * WTM + i * 32, n0 + wn * WTN + j * 32 + l32);
 }
 
-template <int EPI, int BMT, int BNT, int WGM, int FB = 0, int NW = 4>
+template <int EPI, int BMT, int BNT, int WGM, int FB = 0, int NW = 4, int S = 1>
 static void launch_big(GemmP p, int splits, hipStream_t st) {
   const int nk = p.K / kBK2;
   p.k_steps = (nk + splits - 1) / splits;
   splits = (nk + p.k_steps - 1) / p.k_steps;
   if (splits <= 1) p.ws = nullptr;
   dim3 grid((p.N + BNT - 1) / BNT, (p.M + BMT - 1) / BMT, splits);
-  hipLaunchKernelGGL((k_gemm_big<EPI, BMT, BNT, WGM, FB, NW>), grid, dim3(64 * NW), 0, st, p);
+  hipLaunchKernelGGL((k_gemm_big<EPI, BMT, BNT, WGM, FB, NW, S>), grid, dim3(64 * NW), 0, st, p);
 }
 
 // Tile of a large-M GEMM (all with 8 wavefronts, 2 along M x 4 along N).
@@ -447,25 +508,7 @@ __global__ __launch_bounds__(256) void k_gemm_skinny(GemmP p) {
 #pragma unroll
   for (int w = 1; w < 4; ++w) v += sRed[w][wave][lane];
 
-  const int n = n0 + l32;
-#pragma unroll
-  for (int r = 0; r < 16; ++r) {
-    const int m = m0 + wave * 32 + 8 * (r >> 2) + 4 * hi + (r & 3);
-    const float x = v[r];
-    if (EPI == G_RESID && p.ws) {
-      if (m < M && n < N) p.ws[((size_t)blockIdx.z * M + m) * N + n] = x;
-    } else if (EPI == G_RESID) {
-      if (m < M && n < N) p.h[(size_t)m * p.ldh + n] += x;
-    } else {
-      const float partner = __shfl_xor(x, 1, 64);
-      if ((n & 1) == 0 && m < M && n < N) {
-        if (EPI == G_QKV)
-          qkv_store_pair(p.d, p.qkv, m, n, x, partner);
-        else
-          p.a16[(size_t)m * p.ld_a + (n >> 1)] = (_Float16)(silu(x) * partner);
-      }
-    }
-  }
+  tile_epilogue<EPI>(p, v, m0 + wave * 32, n0 + l32);
 }
 
 // Launch shape of a skinny GEMM: rows per block 32 TM (TM = 4, 2, 1) and,
@@ -505,13 +548,27 @@ static int launch_skinny(GemmP p, const Workspace &wsp, hipStream_t st) {
   return splits > 1 ? splits : 0;
 }
 
-// K % 64 == 0.  Many rows: launch_large_m.  Fewer rows: narrow, short-K
-// projections (QKV, WO) run on the
-// skinny kernel; the others on 128 x 32 LDS-staged tiles (4 x 1 wavefronts,
-// coalesced loads), so a 128-row GEMM has a block per 32 weight rows, and a
-// residual GEMM with a long K (down) also splits K.  (Measured at M = 128 on
-// the 0.5B shape: skinny QKV 17 vs 21 us, WO 8.5 vs 17; tiles gate/up 16 vs
-// 30, down 12 vs 21.)  Returns the number of split-K partial-sum sets left
+// Mid-M launch (8 < M < kBigM): tile BMT x BNT with NW wavefronts, S K
+// slices in flight (k_gemm_big's register ring), FB fragment read-ahead,
+// and for residual GEMMs a K split; returns the pending split count (0:
+// applied directly).
+template <int EPI, int BMT, int BNT, int WGM, int S, int FB = 0, int NW = 4>
+static int launch_ring(GemmP p, int splits, const Workspace &wsp, hipStream_t st) {
+  const int nk = p.K / kBK2;
+  if (EPI != G_RESID || !wsp.buf) splits = 1;
+  splits = max(1, min(splits, min(16, nk)));
+  while (splits > 1 && (size_t)splits * p.M * p.N * 4 > wsp.bytes) --splits;
+  p.ws = splits > 1 ? wsp.buf : nullptr;
+  const int ks = (nk + splits - 1) / splits;
+  const int used = (nk + ks - 1) / ks;  // launch_big's effective split count
+  launch_big<EPI, BMT, BNT, WGM, FB, NW, S>(p, splits, st);
+  return used > 1 ? used : 0;
+}
+
+
+// K % 64 == 0.  Many rows: launch_large_m.  Fewer rows: the weights
+// dominate and the K loop is latency-bound, so the tiles keep a ring of K
+// slices in flight.  Returns the number of split-K partial-sum sets left
 // pending (0 when the result was applied directly).
 template <int EPI>
 static int launch_tiles(GemmP p, const Workspace &wsp, hipStream_t st) {
@@ -520,6 +577,13 @@ static int launch_tiles(GemmP p, const Workspace &wsp, hipStream_t st) {
     return 0;
   }
   if (p.K <= 1024 && p.N <= 2048) return launch_skinny<EPI>(p, wsp, st);
+  // gate/up of up to 128 rows: a ring of two K slices in flight and the
+  // next step's LDS fragments read ahead (measured on the 0.5B gate/up
+  // GEMM: 64 rows 12.6 -> 9.2 us, 128 rows 13.0 -> 10.9 us)
+  if constexpr (EPI == G_SWIGLU) {
+    if (p.M <= 64) return launch_ring<EPI, 64, 64, 2, 2, 1, 4>(p, 1, wsp, st);
+    if (p.M <= 128) return launch_ring<EPI, 128, 64, 4, 2, 1, 8>(p, 1, wsp, st);
+  }
   const int nk = p.K / kBK2;
   int splits = 1;
   if (EPI == G_RESID && p.K >= 2048 && wsp.buf) {

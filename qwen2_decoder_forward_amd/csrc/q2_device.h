@@ -170,4 +170,94 @@ __device__ __forceinline__ void qkv_store_pair(const Dims &d, const QkvEpi &e, i
   qkv_pair_store(qkv_pair_end(d, e, m, n, pos, seq, ba, bb), a, b);
 }
 
+// Marks loaded values as used here, so the compiler cannot sink their loads
+// into the (predicated) blocks that consume them: loads sunk between stores
+// are each waited for, together with every store before them.
+template <typename T, int N>
+__device__ __forceinline__ void pin_regs(T (&a)[N]) {
+#pragma unroll
+  for (int i = 0; i < N; ++i) asm volatile("" : "+v"(a[i]));
+}
+
+// The same epilogue for NE rows m[] (valid row indices) of one packed column
+// pair (n even, n + 1 < nqkv).  Every load of the NE rows (position and
+// sequence slot, then cos / sin at those positions) is issued before any
+// store, so the loads cost two memory round trips in all.  The stores go
+// out in groups of four rows whose values and addresses are all computed
+// first: a register written after a store that reads it makes the compiler
+// wait for that store to complete (s_waitcnt vmcnt), so this bounds those
+// waits to one per group.  Rows with ok[] false store nothing.
+template <int NE>
+__device__ __forceinline__ void qkv_store_rows(const Dims &d, const QkvEpi &e, const int (&m)[NE],
+                                               int n, const float (&a)[NE], const float (&b)[NE],
+                                               const bool (&ok)[NE]) {
+  static_assert(NE % 4 == 0, "groups of four rows");
+  unsigned pos[NE], seq[NE];
+#pragma unroll
+  for (int k = 0; k < NE; ++k) {
+    pos[k] = (unsigned)e.rows.pos[m[k]];
+    seq[k] = (unsigned)e.rows.seq[m[k]];
+  }
+  float bias[2] = {e.bias[n], e.bias[n + 1]};
+  const int hd = d.hd, half = hd >> 1;
+  const int head = n / hd;
+  const int j = (n - head * hd) >> 1;
+  const bool rot = head < d.nh + d.nkv;
+  float cs[NE], sn[NE];
+#pragma unroll
+  for (int k = 0; k < NE; ++k) {
+    const float c = e.rope.cos[(size_t)pos[k] * half + j];
+    const float s = e.rope.sin[(size_t)pos[k] * half + j];
+    cs[k] = rot ? c : 1.0f;
+    sn[k] = rot ? s : 0.0f;
+  }
+  pin_regs(seq);
+  pin_regs(cs);
+  pin_regs(sn);
+  pin_regs(bias);
+  const bool is_q = head < d.nh, is_k = !is_q && rot;
+  const size_t g = (size_t)(is_k ? head - d.nh : head - d.nh - d.nkv);
+  const size_t s16 = is_k ? (size_t)half : (size_t)half * e.kv.ldp;  // mirror partner distance
+#pragma unroll
+  for (int k0 = 0; k0 < NE; k0 += 4) {
+    float xs[4], ys[4];
+    float *p0[4], *p1[4];
+    _Float16 *q0[4], *q1[4];
+#pragma unroll
+    for (int u = 0; u < 4; ++u) {
+      const int k = k0 + u;
+      const float x0 = a[k] + bias[0], y0 = b[k] + bias[1];
+      xs[u] = x0 * cs[k] - y0 * sn[k];
+      ys[u] = y0 * cs[k] + x0 * sn[k];
+      const size_t blk = ((size_t)e.layer * d.n_seq + (size_t)seq[k]) * d.nkv + g;
+      const size_t slot = (blk * d.n_ctx + (size_t)pos[k]) * (size_t)hd + (size_t)j;
+      const size_t b16 = blk * (size_t)e.kv.ldp * hd;
+      float *dst = is_q ? e.q + (size_t)m[k] * e.ldq + (size_t)head * hd + j
+                        : (is_k ? e.kv.k : e.kv.v) + slot;
+      _Float16 *d16 = is_k ? e.kv.k16 + b16 + (size_t)pos[k] * hd + j
+                           : e.kv.v16t + b16 + (size_t)j * e.kv.ldp + pos[k];
+      p0[u] = dst;
+      p1[u] = dst + half;
+      q0[u] = d16;
+      q1[u] = d16 + s16;
+    }
+    pin_regs(xs);
+    pin_regs(ys);
+    pin_regs(p0);
+    pin_regs(p1);
+    pin_regs(q0);
+    pin_regs(q1);
+#pragma unroll
+    for (int u = 0; u < 4; ++u) {
+      if (!ok[k0 + u]) continue;
+      *p0[u] = xs[u];
+      *p1[u] = ys[u];
+      if (!is_q) {
+        *q0[u] = (_Float16)xs[u];
+        *q1[u] = (_Float16)ys[u];
+      }
+    }
+  }
+}
+
 }  // namespace q2
