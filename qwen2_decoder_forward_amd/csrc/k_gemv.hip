@@ -65,7 +65,10 @@ __global__ __launch_bounds__(256) void k_gemv(GemvP p) {
   const int er = lane / MT, em = lane - er * MT;
   const int emc = em < M ? em : M - 1;
 
-  for (int rg = blockIdx.x; rg < p.n_groups; rg += gridDim.x) {
+  // (do-while: the grid never exceeds the row groups, and a loop-entry test
+  // would wait for its kernel-argument load before the pointers are loaded)
+  int rg = blockIdx.x;
+  do {
     const int row0 = (rg * 4 + wave) * R;
     // 0. The loads the epilogue needs go first: vector loads return in issue
     //    order, so waiting for them later does not wait for the weights.
@@ -206,7 +209,8 @@ __global__ __launch_bounds__(256) void k_gemv(GemvP p) {
           }
         }
     }
-  }
+    rg += gridDim.x;
+  } while (rg < p.n_groups);
 
   if (EPI == EPI_LMHEAD) {
     __shared__ unsigned long long s_best[4][MT];
@@ -256,7 +260,10 @@ __global__ __launch_bounds__(256) void k_gemv1(GemvP p) {
   const bool norm = !kResid && p.norm_w != nullptr;
   const int er = lane < R ? lane : R - 1;  // the row this lane stores (lanes < R)
 
-  for (int rg = blockIdx.x; rg < p.n_groups; rg += gridDim.x) {
+  // One row group per block (the launch gives every group its own block),
+  // so nothing waits for a loop bound before the pointers are loaded.
+  {
+    const int rg = blockIdx.x;
     const int row0 = (rg * 4 + wave) * R;
     const int en = min(row0 + er, N - 1);
     unsigned e_pos = 0, e_seq = 0;
@@ -346,7 +353,6 @@ __global__ __launch_bounds__(256) void k_gemv1(GemvP p) {
       for (int r = 0; r < R; r += 2)
         if (lane == r && row0 + r < N) qkv_pair_store(e_pair, acc[r], acc[r + 1]);
     }
-    __syncthreads();  // (the next row group rewrites sx)
   }
 }
 
@@ -520,6 +526,8 @@ static void launch(GemvP &p, int max_grid, hipStream_t st) {
   p.n_groups = (p.N + 4 * R - 1) / (4 * R);
   const int grid = p.n_groups < max_grid ? p.n_groups : max_grid;
   if (EPI != EPI_LMHEAD && p.M <= 1) {  // (one-row lm_head: k_lmhead)
+    // k_gemv1 takes exactly one row group per block: grid = n_groups
+    // (max_grid is never below n_groups on this path)
     const int kc = (p.K + 511) / 512;
     constexpr int E1 = EPI == EPI_LMHEAD ? EPI_RESID : EPI;  // (never launched for lm_head)
     if (kc <= 2)
