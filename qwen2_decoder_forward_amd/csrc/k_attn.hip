@@ -244,6 +244,17 @@ __global__ __launch_bounds__(256) void k_attn_wo(AttnWoP p) {
   const int G = p.d.group, H = p.d.H, nhd = p.d.nh * HD;
   const int g = head / G;
   const int M = p.M;
+  // Every kernel argument the loads below need, requested in the first
+  // scalar-load batch (the empty asm uses them here, so none of them is left
+  // to a later batch, whose round trip would come before the loads).
+  {
+    const int *rp = p.rows.pos, *rs = p.rows.seq;
+    const float *qp = p.q, *kp = p.kv.k, *vp = p.kv.v;
+    const _Float16 *wp = p.wo;
+    asm volatile("" ::"s"(rp), "s"(rs), "s"(qp), "s"(kp), "s"(vp), "s"(wp));
+    asm volatile("" ::"s"(G), "s"(H), "s"(p.d.nh), "s"(p.d.nkv), "s"(p.d.n_seq), "s"(p.d.n_ctx),
+                 "s"(p.layer), "s"(p.rows_per_block), "s"(p.scale));
+  }
 
   // WO slice loads first
   const int r0 = rc * p.rows_per_block;

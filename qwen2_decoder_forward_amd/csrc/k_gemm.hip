@@ -210,6 +210,132 @@ __device__ __forceinline__ void tile_epilogue(const GemmP &p, const f16x &v, int
   }
 }
 
+// f32 block tile in LDS for the QKV epilogue: element (r, c) of a BNT-wide
+// row, with 16-byte chunk c/4 stored at chunk (c/4) ^ (r % (BNT/4)) so the
+// column-wise writes from the MFMA layout spread over the banks.
+template <int BNT>
+__device__ __forceinline__ int qkv_tile_idx(int r, int c) {
+  return r * BNT + ((((c >> 2) ^ r) & (BNT / 4 - 1)) << 2) + (c & 3);
+}
+
+// QKV epilogue from the block tile T (rows m0.., packed columns n0..; the
+// tile is head-aligned: BNT is a multiple of head_dim).
+// Pass 1: item = (row, 4 consecutive pairs) -> bias, RoPE on q / k, then
+//   the natural dims d..d+3 and d+half..d+half+3 of the q row or the K / V
+//   cache slot go out as two 16-byte stores (K also two 8-byte binary16
+//   stores into its mirror).
+// Pass 2: the transposed binary16 V mirror [d][position], with consecutive
+//   lanes on consecutive rows (positions), so its 2-byte stores coalesce.
+// Each pass issues all of a thread's position / table loads before its
+// stores (a load behind a store to a possibly aliasing address waits for
+// it).
+template <int BMT, int BNT, int NT>
+__device__ __forceinline__ void qkv_epilogue_lds(const GemmP &p, const float *T, int m0, int n0) {
+  const Dims &d = p.d;
+  const QkvEpi &e = p.qkv;
+  const int tid = threadIdx.x;
+  const int M = p.M, N = p.N, hd = d.hd, half = hd >> 1;
+  constexpr int IPR = BNT / 8;  // items per row
+  constexpr int PER = BMT * IPR / NT;
+  static_assert(BMT * IPR % NT == 0, "items per thread");
+  // pass 1
+  int mi[PER];
+  unsigned ps[PER], sq[PER];
+#pragma unroll
+  for (int k = 0; k < PER; ++k) {
+    const int item = tid + NT * k;
+    mi[k] = min(m0 + item / IPR, M - 1);
+    ps[k] = (unsigned)e.rows.pos[mi[k]];
+    sq[k] = (unsigned)e.rows.seq[mi[k]];
+  }
+  f4 cs[PER], sn[PER];
+#pragma unroll
+  for (int k = 0; k < PER; ++k) {
+    const int item = tid + NT * k;
+    const int n = min(n0 + 8 * (item % IPR), N - 8);
+    const int head = n / hd;
+    const int jd = (n - head * hd) >> 1;
+    const size_t t = (size_t)ps[k] * half + jd;
+    cs[k] = *(const f4 *)(e.rope.cos + t);
+    sn[k] = *(const f4 *)(e.rope.sin + t);
+  }
+  pin_regs(sq);
+  pin_regs(cs);
+  pin_regs(sn);
+#pragma unroll
+  for (int k = 0; k < PER; ++k) {
+    const int item = tid + NT * k;
+    const int r = item / IPR, c0 = 8 * (item % IPR);
+    const int n = n0 + c0;
+    if (m0 + r >= M || n >= N) continue;
+    const int head = n / hd;
+    const int jd = (n - head * hd) >> 1;
+    const bool is_q = head < d.nh, is_k = !is_q && head < d.nh + d.nkv;
+    const f4 t0 = *(const f4 *)(T + qkv_tile_idx<BNT>(r, c0));
+    const f4 t1 = *(const f4 *)(T + qkv_tile_idx<BNT>(r, c0 + 4));
+    const f4 b0 = *(const f4 *)(e.bias + n), b1 = *(const f4 *)(e.bias + n + 4);
+    const f4 a = {t0.x + b0.x, t0.z + b0.z, t1.x + b1.x, t1.z + b1.z};  // dims jd..jd+3
+    const f4 b = {t0.y + b0.y, t0.w + b0.w, t1.y + b1.y, t1.w + b1.w};  // dims jd+half..
+    f4 x = a, y = b;
+    if (!(head >= d.nh + d.nkv)) {
+      x = a * cs[k] - b * sn[k];
+      y = b * cs[k] + a * sn[k];
+    }
+    if (is_q) {
+      float *dst = e.q + (size_t)mi[k] * e.ldq + (size_t)head * hd + jd;
+      *(f4 *)dst = x;
+      *(f4 *)(dst + half) = y;
+    } else {
+      const size_t g = (size_t)(is_k ? head - d.nh : head - d.nh - d.nkv);
+      const size_t blk = ((size_t)e.layer * d.n_seq + sq[k]) * d.nkv + g;
+      float *dst = (is_k ? e.kv.k : e.kv.v) + (blk * d.n_ctx + ps[k]) * (size_t)hd + jd;
+      *(f4 *)dst = x;
+      *(f4 *)(dst + half) = y;
+      if (is_k) {
+        _Float16 *d16 = e.kv.k16 + blk * (size_t)e.kv.ldp * hd + (size_t)ps[k] * hd + jd;
+        *(h4 *)d16 = (h4){(_Float16)x.x, (_Float16)x.y, (_Float16)x.z, (_Float16)x.w};
+        *(h4 *)(d16 + half) = (h4){(_Float16)y.x, (_Float16)y.y, (_Float16)y.z, (_Float16)y.w};
+      }
+    }
+  }
+  // pass 2: the V columns of the tile (a suffix: V heads come last)
+  const int v0 = (d.nh + d.nkv) * hd;
+  const int cv0 = max(0, min(BNT, v0 - n0));
+  const int nv = (min(BNT, N - n0) - cv0) * BMT;  // (column, row) items, rows fastest
+  for (int base = 0; base < nv; base += 8 * NT) {
+    int mv[8];
+    bool okv[8];
+    unsigned pv[8], sv[8];
+#pragma unroll
+    for (int u = 0; u < 8; ++u) {
+      const int item = base + tid + NT * u;
+      const int r = item % BMT;
+      okv[u] = item < nv && m0 + r < M;
+      mv[u] = min(m0 + r, M - 1);
+      pv[u] = (unsigned)e.rows.pos[mv[u]];
+      sv[u] = (unsigned)e.rows.seq[mv[u]];
+    }
+    pin_regs(pv);
+    pin_regs(sv);
+    _Float16 hv[8];
+    _Float16 *dv[8];
+#pragma unroll
+    for (int u = 0; u < 8; ++u) {
+      const int item = base + tid + NT * u;
+      const int r = item % BMT, c = cv0 + min(item / BMT, BNT - 1 - cv0);
+      const int n = n0 + c;
+      const int head = n / hd, cl = n - head * hd;
+      const int dim = (cl >> 1) + (cl & 1) * half;  // natural dim of packed column cl
+      const size_t blk = ((size_t)e.layer * d.n_seq + sv[u]) * d.nkv + (size_t)(head - d.nh - d.nkv);
+      hv[u] = (_Float16)(T[qkv_tile_idx<BNT>(r, c)] + e.bias[n]);
+      dv[u] = e.kv.v16t + blk * (size_t)e.kv.ldp * hd + (size_t)dim * e.kv.ldp + pv[u];
+    }
+#pragma unroll
+    for (int u = 0; u < 8; ++u)
+      if (okv[u]) *dv[u] = hv[u];
+  }
+}
+
 // ------------------------------------------------------- large-M projections
 // Prefill GEMMs with many rows (M >= kBigM) are MFMA-bound.  Block tile
 // BM x BN x 64 with NW wavefronts, WGM along M by NW/WGM along N, each owning
@@ -236,8 +362,9 @@ __global__ __launch_bounds__(64 * NW) void k_gemm_big(GemmP p) {
   constexpr int RS = NT / 8;                       // rows a loader pass covers
   constexpr int CA = BMT / RS, CB = BNT / RS;      // 16-byte chunks per thread per slice
   static_assert(TM >= 1 && TN >= 1 && CB >= 1, "tile shape");
-  __shared__ __attribute__((aligned(16))) _Float16 sA[2 * BMT * kBK2];
-  __shared__ __attribute__((aligned(16))) _Float16 sB[2 * BNT * kBK2];
+  __shared__ __attribute__((aligned(16))) _Float16 sAB[2 * (BMT + BNT) * kBK2];
+  _Float16 *const sA = sAB;
+  _Float16 *const sB = sAB + 2 * BMT * kBK2;
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int wm = wave / WGN, wn = wave % WGN;
   const int hi = lane >> 5, l32 = lane & 31;
@@ -394,12 +521,31 @@ __global__ __launch_bounds__(64 * NW) void k_gemm_big(GemmP p) {
     }
   }
 
-  // epilogue, one 32 x 32 tile at a time
+  if constexpr (EPI == G_QKV && BMT * BNT <= (BMT + BNT) * kBK2) {
+    // the block tile goes through LDS (the operand buffers, free after the
+    // last barrier), so the RoPE / KV-store stores are 16-byte row pieces
+    // and the transposed binary16 V mirror is written along positions
+    float *T = (float *)sAB;
+    __syncthreads();  // (every wavefront is past its last operand read)
 #pragma unroll
-  for (int i = 0; i < TM; ++i)
+    for (int i = 0; i < TM; ++i)
 #pragma unroll
-    for (int j = 0; j < TN; ++j)
-      tile_epilogue<EPI>(p, acc[i][j], m0 + wm * WTM + i * 32, n0 + wn * WTN + j * 32 + l32);
+      for (int j = 0; j < TN; ++j)
+#pragma unroll
+        for (int r = 0; r < 16; ++r) {
+          const int row = wm * WTM + i * 32 + 8 * (r >> 2) + 4 * hi + (r & 3);
+          T[qkv_tile_idx<BNT>(row, wn * WTN + j * 32 + l32)] = acc[i][j][r];
+        }
+    __syncthreads();
+    qkv_epilogue_lds<BMT, BNT, NT>(p, T, m0, n0);
+  } else {
+    // epilogue, one 32 x 32 tile at a time
+#pragma unroll
+    for (int i = 0; i < TM; ++i)
+#pragma unroll
+      for (int j = 0; j < TN; ++j)
+        tile_epilogue<EPI>(p, acc[i][j], m0 + wm * WTM + i * 32, n0 + wn * WTN + j * 32 + l32);
+  }
 }
 
 template <int EPI, int BMT, int BNT, int WGM, int FB = 0, int NW = 4, int S = 1>
@@ -420,6 +566,10 @@ static void launch_big(GemmP p, int splits, hipStream_t st) {
 // TFLOP/s on a 2048 x 37888 x 3584 GEMM), 128 x 256 (850) and 128 x 128 (740).
 template <int EPI>
 static void launch_large_m(const GemmP &p, hipStream_t st) {
+  if constexpr (EPI == G_QKV) {  // (its LDS-staged epilogue fits a 128 x 128 tile)
+    launch_big<EPI, 128, 128, 2, 0, 8>(p, 1, st);
+    return;
+  }
   if (p.K < 2048) {
     launch_big<EPI, 128, 128, 2, 0, 8>(p, 1, st);
     return;
