@@ -594,16 +594,28 @@ __global__ __launch_bounds__(64 * G * S) void k_attn_prefill(AttnPreP p) {
 
   // tile loads: chunk c of the K tile is key c / (HD/8), d-chunk c % (HD/8);
   // chunk c of the V^T tile is d c / (KT/8), key-chunk c % (KT/8)
+  // (addresses as a block-uniform base plus a 32-bit lane offset: the base
+  // stays in scalar registers, so the loop-invariant part costs one vector
+  // register per load instead of a 64-bit pointer)
   h8 rk[CPT], rv[CPT];
+  const char *kgb = (const char *)kg, *vgb = (const char *)vg;
+  unsigned ko[CPT], vo[CPT];
+#pragma unroll
+  for (int i = 0; i < CPT; ++i) {
+    const int c = min(tid + i * nthr, KCH - 1);
+    const int kk = c / (HD / 8), kc = c - kk * (HD / 8);
+    ko[i] = (unsigned)((kk * HD + kc * 8) * 2);
+    const int dd = c / (KT / 8), vc = c - dd * (KT / 8);
+    vo[i] = (unsigned)((dd * p.ldp + vc * 8) * 2);
+  }
   auto gload = [&](int kt) {
+    const unsigned kadv = (unsigned)(kt * KT * HD * 2), vadv = (unsigned)(kt * KT * 2);
 #pragma unroll
     for (int i = 0; i < CPT; ++i) {
       const int c = tid + i * nthr;
       if (c < KCH) {
-        const int kk = c / (HD / 8), kc = c - kk * (HD / 8);
-        rk[i] = *(const h8 *)(kg + (size_t)(kt * KT + kk) * HD + kc * 8);
-        const int dd = c / (KT / 8), vc = c - dd * (KT / 8);
-        rv[i] = *(const h8 *)(vg + (size_t)dd * p.ldp + kt * KT + vc * 8);
+        rk[i] = *(const h8 *)(kgb + (ko[i] + kadv));
+        rv[i] = *(const h8 *)(vgb + (vo[i] + vadv));
       }
     }
   };
