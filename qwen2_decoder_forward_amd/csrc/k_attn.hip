@@ -447,8 +447,10 @@ void attn_decode(const Dims &d, int layer, const KVCache &kv, const float *q, in
 // transposed as [d][pos]: the MFMA operand layouts; written by every K/V
 // store, and by k_kv_f16 after a direct write of the f32 cache).  One block
 // per (32-query tile, KV head) with one wavefront per query head of the
-// group, so each K / V tile in LDS serves the whole group.  Per 64-key tile
-// and 32-key half:
+// group (G = group size), so each K / V tile in LDS serves the whole group;
+// short prompts (fewer than 128 such blocks) instead run one block per query
+// head (G = 1, blockIdx.z = head within the group), trading repeated K / V
+// tile loads for seven times the blocks.  Per 64-key tile and 32-key half:
 //   S^T[key, query] = K (A: 32 keys x 16 d) * Q^T (B: 16 d x 32 queries)
 // so each lane owns one query column and 16 of the half's keys (the other 16
 // sit in lane ^ 32): the online-softmax max and sum need one cross-lane step,
@@ -549,7 +551,7 @@ __global__ __launch_bounds__(64 * G * S) void k_attn_prefill(AttnPreP p) {
   const int tid = threadIdx.x - half * NTHR, nthr = NTHR;  // index within the half
   const int tile = gridDim.x - 1 - blockIdx.x;  // longest tiles first
   const int g = blockIdx.y;
-  const int h = g * G + hw;
+  const int h = g * p.d.group + blockIdx.z * G + hw;  // (blockIdx.z: G-head share of the group)
   const int r0 = tile * 32;
   const int M = p.M;
   const int last_row = min(r0 + 31, M - 1);
@@ -760,6 +762,12 @@ static void attn_prefill_g(const AttnPreP &p, dim3 grid, hipStream_t st) {
 template <int HD>
 static void attn_prefill_hd(const AttnPreP &p, hipStream_t st) {
   const dim3 grid((p.M + 31) / 32, p.d.nkv);
+  if ((int)(grid.x * grid.y) < 128) {
+    // few query tiles (short prompts): one query head per block, so the
+    // group's heads run on separate CUs (each block loads its group's K / V)
+    attn_prefill_g<HD, 1>(p, dim3(grid.x, grid.y, p.d.group), st);
+    return;
+  }
   switch (p.d.group) {  // the group size is a compile-time constant of the kernel
     case 1: attn_prefill_g<HD, 1>(p, grid, st); break;
     case 2: attn_prefill_g<HD, 2>(p, grid, st); break;
