@@ -607,10 +607,10 @@ static void launch_large_m(const GemmP &p, hipStream_t st) {
 // The four partial tiles are summed through LDS, wavefront t finishing
 // tile t.  A block may also take only a share of K (split-K, residual
 // GEMMs only: raw partial sums, folded in by the next RMSNorm).
-template <int EPI, int TM>
-__global__ __launch_bounds__(256) void k_gemm_skinny(GemmP p) {
+template <int EPI, int TM, int NWS = 4>
+__global__ __launch_bounds__(64 * NWS) void k_gemm_skinny(GemmP p) {
   constexpr int U = TM >= 4 ? 4 : 8;  // MFMA steps of loads in flight per wavefront
-  __shared__ f16x sRed[4][TM][64];
+  __shared__ f16x sRed[NWS][TM][64];
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int hi = lane >> 5, l32 = lane & 31;
   const int M = p.M, N = p.N, K = p.K;
@@ -619,7 +619,7 @@ __global__ __launch_bounds__(256) void k_gemm_skinny(GemmP p) {
   // K steps of this block, then of this wavefront
   const int steps = K / 16;
   const int bs0 = blockIdx.z * p.k_steps, bs1 = min(steps, bs0 + p.k_steps);
-  const int per = (bs1 - bs0 + 3) / 4;
+  const int per = (bs1 - bs0 + NWS - 1) / NWS;
   const int s0 = bs0 + wave * per, s1 = min(bs1, s0 + per);
 
   const _Float16 *Ap[TM];
@@ -653,10 +653,32 @@ __global__ __launch_bounds__(256) void k_gemm_skinny(GemmP p) {
 #pragma unroll
   for (int i = 0; i < TM; ++i) sRed[wave][i][lane] = acc[i];
   __syncthreads();
+  if constexpr (EPI == G_QKV && TM == 1 && NWS == 8) {
+    // every wavefront finishes two of the tile's 16 accumulator rows, so the
+    // RoPE / KV-store epilogue runs on all eight wavefronts
+    const int n = n0 + l32;
+    int m[2];
+    bool ok[2];
+    float a[2], b[2];
+#pragma unroll
+    for (int u = 0; u < 2; ++u) {
+      const int r = 2 * wave + u;
+      float x = sRed[0][0][lane][r];
+#pragma unroll
+      for (int w = 1; w < NWS; ++w) x += sRed[w][0][lane][r];
+      a[u] = x;
+      b[u] = __shfl_xor(x, 1, 64);  // the pair partner (column n + 1)
+      const int mm = m0 + 8 * (r >> 2) + 4 * hi + (r & 3);
+      ok[u] = mm < M && n < N && (n & 1) == 0;
+      m[u] = min(mm, M - 1);
+    }
+    qkv_store_rows<2, 2>(p.d, p.qkv, m, min(n & ~1, N - 2), a, b, ok);
+    return;
+  }
   if (wave >= TM) return;
   f16x v = sRed[0][wave][lane];
 #pragma unroll
-  for (int w = 1; w < 4; ++w) v += sRed[w][wave][lane];
+  for (int w = 1; w < NWS; ++w) v += sRed[w][wave][lane];
 
   tile_epilogue<EPI>(p, v, m0 + wave * 32, n0 + l32);
 }
@@ -690,6 +712,12 @@ static int launch_skinny(GemmP p, const Workspace &wsp, hipStream_t st) {
   const int splits = (steps + p.k_steps - 1) / p.k_steps;
   p.ws = splits > 1 ? wsp.buf : nullptr;
   dim3 grid(nt, (p.M + 32 * best_tm - 1) / (32 * best_tm), splits);
+  if (EPI == G_QKV && best_tm == 1) {
+    // (no K split across blocks for QKV: eight wavefronts split the block's
+    // K range, so each one's share of steps goes out in one batch of loads)
+    hipLaunchKernelGGL((k_gemm_skinny<EPI, 1, 8>), grid, dim3(512), 0, st, p);
+    return 0;
+  }
   switch (best_tm) {
     case 4: hipLaunchKernelGGL((k_gemm_skinny<EPI, 4>), grid, dim3(256), 0, st, p); break;
     case 2: hipLaunchKernelGGL((k_gemm_skinny<EPI, 2>), grid, dim3(256), 0, st, p); break;

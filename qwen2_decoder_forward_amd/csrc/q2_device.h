@@ -183,15 +183,15 @@ __device__ __forceinline__ void pin_regs(T (&a)[N]) {
 // pair (n even, n + 1 < nqkv).  Every load of the NE rows (position and
 // sequence slot, then cos / sin at those positions) is issued before any
 // store, so the loads cost two memory round trips in all.  The stores go
-// out in groups of four rows whose values and addresses are all computed
+// out in groups of GS rows whose values and addresses are all computed
 // first: a register written after a store that reads it makes the compiler
 // wait for that store to complete (s_waitcnt vmcnt), so this bounds those
 // waits to one per group.  Rows with ok[] false store nothing.
-template <int NE>
+template <int NE, int GS = 4>
 __device__ __forceinline__ void qkv_store_rows(const Dims &d, const QkvEpi &e, const int (&m)[NE],
                                                int n, const float (&a)[NE], const float (&b)[NE],
                                                const bool (&ok)[NE]) {
-  static_assert(NE % 4 == 0, "groups of four rows");
+  static_assert(NE % GS == 0, "groups of GS rows");
   unsigned pos[NE], seq[NE];
 #pragma unroll
   for (int k = 0; k < NE; ++k) {
@@ -219,12 +219,12 @@ __device__ __forceinline__ void qkv_store_rows(const Dims &d, const QkvEpi &e, c
   const size_t g = (size_t)(is_k ? head - d.nh : head - d.nh - d.nkv);
   const size_t s16 = is_k ? (size_t)half : (size_t)half * e.kv.ldp;  // mirror partner distance
 #pragma unroll
-  for (int k0 = 0; k0 < NE; k0 += 4) {
-    float xs[4], ys[4];
-    float *p0[4], *p1[4];
-    _Float16 *q0[4], *q1[4];
+  for (int k0 = 0; k0 < NE; k0 += GS) {
+    float xs[GS], ys[GS];
+    float *p0[GS], *p1[GS];
+    _Float16 *q0[GS], *q1[GS];
 #pragma unroll
-    for (int u = 0; u < 4; ++u) {
+    for (int u = 0; u < GS; ++u) {
       const int k = k0 + u;
       const float x0 = a[k] + bias[0], y0 = b[k] + bias[1];
       xs[u] = x0 * cs[k] - y0 * sn[k];
@@ -248,7 +248,7 @@ __device__ __forceinline__ void qkv_store_rows(const Dims &d, const QkvEpi &e, c
     pin_regs(q0);
     pin_regs(q1);
 #pragma unroll
-    for (int u = 0; u < 4; ++u) {
+    for (int u = 0; u < GS; ++u) {
       if (!ok[k0 + u]) continue;
       *p0[u] = xs[u];
       *p1[u] = ys[u];
