@@ -694,7 +694,7 @@ static int launch_skinny(GemmP p, const Workspace &wsp, hipStream_t st) {
   double best_cost = 1e30;
   for (int tm = 4; tm >= 1; tm >>= 1) {
     const int mt = (p.M + 32 * tm - 1) / (32 * tm);
-    const int max_sp = (EPI == G_RESID && wsp.buf) ? 16 : 1;
+    const int max_sp = (EPI == G_RESID && wsp.buf) ? kMaxSplits : 1;
     for (int sp = 1; sp <= max_sp; ++sp) {
       if ((size_t)sp * p.M * p.N * 4 > wsp.bytes && sp > 1) break;
       const int ks = (steps + sp - 1) / sp;
@@ -734,7 +734,7 @@ template <int EPI, int BMT, int BNT, int WGM, int S, int FB = 0, int NW = 4>
 static int launch_ring(GemmP p, int splits, const Workspace &wsp, hipStream_t st) {
   const int nk = p.K / kBK2;
   if (EPI != G_RESID || !wsp.buf) splits = 1;
-  splits = max(1, min(splits, min(16, nk)));
+  splits = max(1, min(splits, min(kMaxSplits, nk)));
   while (splits > 1 && (size_t)splits * p.M * p.N * 4 > wsp.bytes) --splits;
   p.ws = splits > 1 ? wsp.buf : nullptr;
   const int ks = (nk + splits - 1) / splits;
@@ -767,7 +767,7 @@ static int launch_tiles(GemmP p, const Workspace &wsp, hipStream_t st) {
   if (EPI == G_RESID && p.K >= 2048 && wsp.buf) {
     const int blocks = ((p.N + 31) / 32) * ((p.M + 127) / 128);
     splits = (256 + blocks - 1) / blocks;
-    splits = min(splits, min(16, nk));
+    splits = min(splits, min(kMaxSplits, nk));
     const size_t per = (size_t)p.M * p.N * 4;
     splits = min(splits, (int)(wsp.bytes / per));
     if (splits < 1) splits = 1;

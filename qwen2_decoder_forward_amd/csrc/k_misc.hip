@@ -51,7 +51,15 @@ __global__ __launch_bounds__(256) void k_rmsnorm_rows(float *h, int ldh, const f
     if (k < H) {
       v[c] = *(const f4 *)(row + k);
       if (splits > 0) {
-        for (int z = 0; z < splits; ++z) v[c] += *(const f4 *)(part + ((size_t)z * M + m) * H + k);
+        // every partial set's load in flight at once (set index clamped,
+        // the sets past `splits` masked), then the sum in set order
+        f4 pz[kMaxSplits];
+#pragma unroll
+        for (int z = 0; z < kMaxSplits; ++z)
+          pz[z] = *(const f4 *)(part + ((size_t)min(z, splits - 1) * M + m) * H + k);
+#pragma unroll
+        for (int z = 0; z < kMaxSplits; ++z)
+          if (z < splits) v[c] += pz[z];
         *(f4 *)(row + k) = v[c];
       }
       ss += v[c].x * v[c].x + v[c].y * v[c].y + v[c].z * v[c].z + v[c].w * v[c].w;

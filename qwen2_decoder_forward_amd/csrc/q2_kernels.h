@@ -98,6 +98,7 @@ struct Workspace {
   float *buf;
   size_t bytes;
 };
+constexpr int kMaxSplits = 16;  // split-K partial-sum sets a residual GEMM may leave
 void gemm_qkv(const Dims &d, const LayerW &w, const _Float16 *x, int lda, int M,
               const QkvEpi &e, const Workspace &ws, hipStream_t st);
 // Returns the number of split-K partial-sum sets left in ws.buf ([z][M][N]);
