@@ -56,17 +56,36 @@ __global__ __launch_bounds__(256) void k_attn_decode(AttnDecP p) {
   const float *vbase = p.kv.v + p.kv.off(p.d, p.layer, seq, g, kb);
   const float *qrow = p.q + (size_t)m * p.ldq + (size_t)g * G * HD;
 
-  for (int i = tid * 4; i < nk * HD; i += 1024) {
-    const f4 kv4 = *(const f4 *)(kbase + i);
-    const f4 vv4 = *(const f4 *)(vbase + i);
-    const int r = i / HD, cc = i - r * HD;
-    sK[r * KS + cc + 0] = kv4.x;
-    sK[r * KS + cc + 1] = kv4.y;
-    sK[r * KS + cc + 2] = kv4.z;
-    sK[r * KS + cc + 3] = kv4.w;
-    *(f4 *)(sV + i) = vv4;
+  // the q loads, then every K / V load of the thread, in flight at once
+  // (elements past the chunk's nk keys re-read its last key, never used)
+  constexpr int QPT = (G * HD + 255) / 256;
+  float qr[QPT];
+#pragma unroll
+  for (int u = 0; u < QPT; ++u) qr[u] = qrow[min(tid + 256 * u, G * HD - 1)];
+  constexpr int LPT = (C * HD + 1023) / 1024;  // 16-byte loads per thread and tensor
+  f4 kr[LPT], vr[LPT];
+#pragma unroll
+  for (int u = 0; u < LPT; ++u) {
+    const int i = min(tid * 4 + 1024 * u, nk * HD - 4);
+    kr[u] = *(const f4 *)(kbase + i);
+    vr[u] = *(const f4 *)(vbase + i);
   }
-  for (int i = tid; i < G * HD; i += 256) sQ[i] = qrow[i] * p.scale;
+  __builtin_amdgcn_sched_barrier(0);  // (all loads issued before the first LDS write)
+#pragma unroll
+  for (int u = 0; u < LPT; ++u) {
+    const int i = tid * 4 + 1024 * u;
+    if (i < C * HD) {
+      const int r = i / HD, cc = i - r * HD;
+      sK[r * KS + cc + 0] = kr[u].x;
+      sK[r * KS + cc + 1] = kr[u].y;
+      sK[r * KS + cc + 2] = kr[u].z;
+      sK[r * KS + cc + 3] = kr[u].w;
+      *(f4 *)(sV + i) = vr[u];
+    }
+  }
+#pragma unroll
+  for (int u = 0; u < QPT; ++u)
+    if (tid + 256 * u < G * HD) sQ[tid + 256 * u] = qr[u] * p.scale;
   __syncthreads();
 
   const int j = lane;
