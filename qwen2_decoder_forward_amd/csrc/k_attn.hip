@@ -16,10 +16,10 @@ namespace q2 {
 // `group` query heads of the KV head.  Scores: thread t takes key t % 64 for
 // heads t / 64 and t / 64 + 4, so each head's 64 scores sit in one wavefront
 // and its max and exp-sum are wave reductions.  P.V: thread (head, d) sums
-// over the chunk's keys.  A single-chunk call writes the normalised output;
-// otherwise every block writes its chunk's (max, exp-sum, un-normalised
-// output) record and the records are merged (k_attn_merge, or the prologue
-// of the WO GEMV).  No block waits on another.
+// over 4 dims of the chunk's keys.  A single-chunk call writes the
+// normalised output; otherwise every block writes its chunk's (un-normalised
+// output, max, exp-sum) record and k_attn_merge combines the records.  No
+// block waits on another.
 struct AttnDecP {
   Dims d;
   int layer;
@@ -38,8 +38,10 @@ template <int HD, int G, bool DIRECT>
 __global__ __launch_bounds__(256) void k_attn_decode(AttnDecP p) {
   constexpr int C = kChunkKeys;
   static_assert(C == 64, "one wavefront per head's chunk scores");
-  constexpr int KS = HD + 1;  // padded K row: conflict-free row walk
-  __shared__ float sK[C * KS];
+  // padded K row: rows start 4 banks apart, so the 16-byte row walks of 16
+  // consecutive lanes (keys) touch distinct bank groups
+  constexpr int KS = HD + 4;
+  __shared__ __attribute__((aligned(16))) float sK[C * KS];
   __shared__ __attribute__((aligned(16))) float sV[C * HD];
   __shared__ __attribute__((aligned(16))) float sQ[G * HD];
   __shared__ float sP[G * C];
@@ -76,10 +78,7 @@ __global__ __launch_bounds__(256) void k_attn_decode(AttnDecP p) {
     const int i = tid * 4 + 1024 * u;
     if (i < C * HD) {
       const int r = i / HD, cc = i - r * HD;
-      sK[r * KS + cc + 0] = kr[u].x;
-      sK[r * KS + cc + 1] = kr[u].y;
-      sK[r * KS + cc + 2] = kr[u].z;
-      sK[r * KS + cc + 3] = kr[u].w;
+      *(f4 *)(sK + r * KS + cc) = kr[u];
       *(f4 *)(sV + i) = vr[u];
     }
   }
@@ -95,8 +94,15 @@ __global__ __launch_bounds__(256) void k_attn_decode(AttnDecP p) {
     if (h < G) {  // uniform across the wave
       float a = 0.f;
       if (j < nk) {
-#pragma unroll 16
-        for (int dd = 0; dd < HD; ++dd) a = fmaf(sQ[h * HD + dd], sK[j * KS + dd], a);
+#pragma unroll
+        for (int d4 = 0; d4 < HD; d4 += 4) {
+          const f4 qq = *(const f4 *)(sQ + h * HD + d4);
+          const f4 kk = *(const f4 *)(sK + j * KS + d4);
+          a = fmaf(qq.x, kk.x, a);
+          a = fmaf(qq.y, kk.y, a);
+          a = fmaf(qq.z, kk.z, a);
+          a = fmaf(qq.w, kk.w, a);
+        }
       }
       const float s = j < nk ? a : kNegInf;
       const float mx = wave_max(s);
@@ -111,25 +117,27 @@ __global__ __launch_bounds__(256) void k_attn_decode(AttnDecP p) {
   }
   __syncthreads();
 
-  const int rec = G * (HD + 2);
+  constexpr int rec = attn_rec_floats(G, HD);
   float *part = p.part.buf + (((size_t)m * p.d.nkv + g) * p.part.n_chunks + c) * rec;
-  for (int idx = tid; idx < G * HD; idx += 256) {
-    const int h = idx / HD, dd = idx - h * HD;
-    float acc = 0.f;
+  // P.V: thread (head, 4 dims), 16-byte V reads
+  for (int idx = tid; idx < G * HD / 4; idx += 256) {
+    const int h = idx / (HD / 4), d4 = 4 * (idx - h * (HD / 4));
+    f4 acc = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll 8
-    for (int jj = 0; jj < nk; ++jj) acc = fmaf(sP[h * C + jj], sV[jj * HD + dd], acc);
+    for (int jj = 0; jj < nk; ++jj) acc += sP[h * C + jj] * *(const f4 *)(sV + jj * HD + d4);
+    const int o = h * HD + d4;
     if (DIRECT) {
-      const float v = acc / sL[h];
-      const size_t oi = (size_t)m * p.ldo + (size_t)g * G * HD + idx;
-      if (p.o32) p.o32[oi] = v;
-      if (p.o16) p.o16[oi] = (_Float16)v;
+      const f4 v = acc / sL[h];
+      const size_t oi = (size_t)m * p.ldo + (size_t)g * G * HD + o;
+      if (p.o32) *(f4 *)(p.o32 + oi) = v;
+      if (p.o16) *(h4 *)(p.o16 + oi) = (h4){(_Float16)v.x, (_Float16)v.y, (_Float16)v.z, (_Float16)v.w};
     } else {
-      part[2 * G + idx] = acc;
+      *(f4 *)(part + o) = acc;
     }
   }
   if (!DIRECT && tid < G) {
-    part[tid] = sM[tid];
-    part[G + tid] = sL[tid];
+    part[G * HD + tid] = sM[tid];
+    part[G * HD + G + tid] = sL[tid];
   }
 }
 
@@ -151,11 +159,12 @@ __global__ __launch_bounds__(256) void k_attn_merge(AttnDecP p) {
   const int tid = threadIdx.x;
   const int P = p.rows.pos[m] + 1;
   const int nch = (P + kChunkKeys - 1) / kChunkKeys;
-  const int rec = G * (HD + 2);
+  const int rec = attn_rec_floats(G, HD);
   const float *base = p.part.buf + ((size_t)m * p.d.nkv + g) * p.part.n_chunks * rec;
+  const int om = G * HD, ol = G * HD + G;  // offsets of the maxima and the exp-sums
 
   float mx = kNegInf;
-  for (int c = tid; c < nch; c += 256) mx = fmaxf(mx, base[(size_t)c * rec + hg]);
+  for (int c = tid; c < nch; c += 256) mx = fmaxf(mx, base[(size_t)c * rec + om + hg]);
   sRed[tid] = mx;
   __syncthreads();
   for (int o = 128; o > 0; o >>= 1) {
@@ -167,9 +176,9 @@ __global__ __launch_bounds__(256) void k_attn_merge(AttnDecP p) {
   float l = 0.f;
   for (int c = tid; c < nch; c += 256) {
     const float *r = base + (size_t)c * rec;
-    const float wgt = __expf(r[hg] - M);
+    const float wgt = __expf(r[om + hg] - M);
     sW[c] = wgt;
-    l = fmaf(r[G + hg], wgt, l);
+    l = fmaf(r[ol + hg], wgt, l);
   }
   sRed[tid] = l;
   __syncthreads();
@@ -181,7 +190,7 @@ __global__ __launch_bounds__(256) void k_attn_merge(AttnDecP p) {
 
   const int dd = tid % HD, part = tid / HD;
   float acc = 0.f;
-  const float *ob = base + 2 * G + (size_t)hg * HD + dd;
+  const float *ob = base + (size_t)hg * HD + dd;
 #pragma unroll 4
   for (int c = part; c < nch; c += PARTS) acc = fmaf(ob[(size_t)c * rec], sW[c], acc);
   sAcc[part][dd] = acc;

@@ -123,8 +123,14 @@ void embed_rows(const uint16_t *E, int H, int V, const int *const *tokens, int t
 // Attention.
 constexpr int kChunkKeys = 64;  // keys per block of the decode attention
 constexpr int kMaxMergeChunks = 2048;  // chunks the merge kernel holds: n_ctx <= 131072
+// A chunk record holds, for the group's query heads, the un-normalised
+// outputs o[group][hd], then the maxima m[group] and exp-sums l[group],
+// padded to a multiple of 4 floats (16-byte aligned records).
+__host__ __device__ constexpr int attn_rec_floats(int group, int hd) {
+  return (group * (hd + 2) + 3) / 4 * 4;
+}
 struct AttnPartials {
-  float *buf;    // [rows][nkv][n_chunks][group][hd + 2]: (max, exp-sum, o) per head
+  float *buf;    // [rows][nkv][n_chunks] records of attn_rec_floats(group, hd)
   int n_chunks;  // chunk slots per row: ceil(n_ctx / kChunkKeys)
 };
 // Split-KV attention, one row per query token (decode and short prefills).

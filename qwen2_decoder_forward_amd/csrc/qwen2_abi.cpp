@@ -314,7 +314,7 @@ int qwen2_load(const qwen2_hparams *hp, const qwen2_weights *w, void *stream, qw
     Slot s_h = take(R * H * 4), s_q = take(R * nhd * 4), s_x16 = take(R * H * 2),
          s_a16 = take(R * Ip * 2), s_o32 = take(D * nhd * 4), s_a32 = take(D * Ip * 4),
          s_norm = take(D * H * 4), s_io = take(kSlotBytes + 3 * c->io_cap * 4),
-         s_part = take((size_t)D * d.nkv * c->part.n_chunks * d.group * (d.hd + 2) * 4),
+         s_part = take((size_t)D * d.nkv * c->part.n_chunks * q2::attn_rec_floats(d.group, d.hd) * 4),
          s_best = take(D * 8), s_bad = take(4), s_splitk = take(kSplitKBytes);
     c->sarena_bytes = cur;
     LTRY([&]() -> int {
