@@ -292,11 +292,11 @@ __global__ __launch_bounds__(256) void k_attn_wo(AttnWoP p) {
   // values (a load the compiler can tie to a condition is moved into a
   // branch, and its value is then copied at the branch join, which waits for
   // it on the spot): WO rows past the chunk are never stored, keys past the
-  // position get a -inf score and a zero weight.  The first row's position,
+  // position re-read the last visible key (a cache hit) and get a -inf
+  // score and a zero weight.  The first row's position,
   // sequence slot and q go out before the WO slice, so the K / V loads that
   // depend on them do not wait for the slice (vector loads complete in order).
   const int d_lane = lane % LD, ph = lane / LD;
-  const int last = p.d.n_ctx - 1;
   int pos = (int)vload(p.rows.pos, 0), seq = (int)vload(p.rows.seq, 0);
   float qraw = p.q[(size_t)head * HD + (tid < HD ? tid : 0)];
   __builtin_amdgcn_sched_barrier(0);  // (keeps this issue order)
@@ -327,13 +327,13 @@ __global__ __launch_bounds__(256) void k_attn_wo(AttnWoP p) {
 #pragma unroll
       for (int i = 0; i < KPT; ++i) {
         const int ci = tid + 256 * i, j = ci / C4;
-        kr[i] = kbase[(size_t)min(t0 + j, last) * C4 + (ci - j * C4)];
+        kr[i] = kbase[(size_t)min(t0 + j, P - 1) * C4 + (ci - j * C4)];
       }
       f4 v[KPL];
 #pragma unroll
       for (int i = 0; i < KPL; ++i) {
         const int jj = t0 + KW * w + ph + PH * i;
-        v[i] = *(const f4 *)(vbase + (size_t)min(jj, last) * HD + 4 * d_lane);
+        v[i] = *(const f4 *)(vbase + (size_t)min(jj, P - 1) * HD + 4 * d_lane);
       }
       const float qv = tid < HD ? qraw * p.scale : 0.f;
       __syncthreads();  // the previous tile's (or row's) LDS reads are done
