@@ -705,14 +705,18 @@ __global__ __launch_bounds__(64 * G * S) void k_attn_prefill(AttnPreP p) {
         for (int r = 0; r < 16; ++r) mt = fmaxf(mt, s[hf][r]);
       mt = fmaxf(mt, __shfl_xor(mt, 32, 64));
       const float m_new = fmaxf(m_run, mt);
-      const float alpha = exp2f(m_run - m_new);
+      // (a query that has seen no visible key yet, e.g. in the second half's
+      // keys when its position lies before them, keeps m = -inf: subtract 0
+      // then, so its weights are exp2(-inf) = 0 instead of NaN)
+      const float m_sub = m_new == kNegInf ? 0.f : m_new;
+      const float alpha = exp2f(m_run - m_sub);
       float ls = 0.f;
       h8 pb[2][2];
 #pragma unroll
       for (int hf = 0; hf < 2; ++hf)
 #pragma unroll
         for (int r = 0; r < 16; ++r) {
-          const float e = exp2f(s[hf][r] - m_new);
+          const float e = exp2f(s[hf][r] - m_sub);
           ls += e;
           pb[hf][r >> 3][r & 7] = (_Float16)e;
         }

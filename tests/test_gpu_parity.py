@@ -74,6 +74,20 @@ def test_tiny_positions_with_gaps_and_continuation(tiny_w):
     p.close()
 
 
+def test_mfma_prefill_rows_far_apart(tiny_w):
+    """One prefill pass (MFMA path) whose rows 0..30 sit at positions 0..30
+    and whose last row sits at position 4000: the attention's second key
+    half (keys from 2048 on) is invisible to the first 31 rows, which must
+    contribute zero weight there (not NaN)."""
+    p = Pair(TINY, tiny_w, n_ctx=4200)
+    pos = list(range(31)) + [4000]
+    lg, _, r = p.prefill(0, syn.make_prompt(TINY, 32, 11), pos)
+    assert np.all(np.isfinite(lg))
+    check(lg, r.logits[0], TOL, "prefill with rows 0..30 and 4000")
+    check(p.hidden(0, 1), r.layer_output, TOL, "layer_output")
+    p.close()
+
+
 def test_hard_error_at_n_ctx_leaves_cache_unchanged(tiny_w):
     import qwen2_decoder_forward_amd as q
     p = Pair(TINY, tiny_w, n_ctx=16)
