@@ -6,6 +6,8 @@
 // the KV slots 0..p of its own sequence (full causal attention, no window).
 // Both kernels load each K/V tile once per KV head and share it across the
 // whole query group.
+#include <algorithm>
+
 #include "q2_device.h"
 
 namespace q2 {
@@ -545,6 +547,11 @@ struct AttnPreP {
   _Float16 *o16;
   int ldo;
   float qscale;  // head_dim^-0.5 * log2(e): scores in base 2
+  // causal balance: query tiles split_from .. n_tiles-1 run as two blocks
+  // each (first / second half of their key tiles) whose softmax states go to
+  // part and are combined by k_attn_prefill_merge
+  int n_tiles, split_from;
+  float *part;  // [split tile][piece][query head][32 rows][hd + 4]: o, max, sum (base 2), pad
 };
 
 // S = 2 (head_dim <= 64): two wavefronts per query head; the block's two
@@ -577,8 +584,21 @@ __global__ __launch_bounds__(64 * G * S) void k_attn_prefill(AttnPreP p) {
   const int lane = threadIdx.x & 63, w = threadIdx.x >> 6;
   const int half = w / G, hw = w - half * G;
   const int tid = threadIdx.x - half * NTHR, nthr = NTHR;  // index within the half
-  const int tile = gridDim.x - 1 - blockIdx.x;  // longest tiles first
-  const int g = blockIdx.y;
+  // longest work first: the split tiles' two pieces (descending tiles),
+  // then the whole tiles (descending)
+  // (the KV head is the grid's fastest index, so the dispatch order is
+  // longest-first across the KV heads too)
+  const int n_split = p.n_tiles - p.split_from;
+  const int wi = blockIdx.y;  // work index
+  int tile, piece;
+  if (wi < 2 * n_split) {
+    tile = p.n_tiles - 1 - wi / 2;
+    piece = wi & 1;
+  } else {
+    tile = p.split_from - 1 - (wi - 2 * n_split);
+    piece = -1;
+  }
+  const int g = blockIdx.x;
   const int h = g * p.d.group + blockIdx.z * G + hw;  // (blockIdx.z: G-head share of the group)
   const int r0 = tile * 32;
   const int M = p.M;
@@ -618,9 +638,15 @@ __global__ __launch_bounds__(64 * G * S) void k_attn_prefill(AttnPreP p) {
   const _Float16 *kg = p.k16 + (size_t)g * p.gstride;
   const _Float16 *vg = p.v16t + (size_t)g * p.gstride;
   const int ntiles = kmax / KT + 1;
-  const int n0 = (ntiles + S - 1) / S;              // tiles of the first half (>= 1)
-  const int kt0 = half * n0;                         // this half's first tile
-  const int cnt = min(ntiles, kt0 + n0) - kt0;       // and its tile count (may be 0)
+  int kb = 0, ke = ntiles;  // this block's key tiles (a split piece takes half)
+  if (piece >= 0) {
+    const int ph = (ntiles + 1) / 2;
+    kb = piece ? ph : 0;
+    ke = piece ? ntiles : ph;
+  }
+  const int n0 = (ke - kb + S - 1) / S;              // tiles of the first half
+  const int kt0 = kb + half * n0;                    // this half's first tile
+  const int cnt = max(0, min(ke, kt0 + n0) - kt0);   // and its tile count (may be 0)
 
   // tile loads: chunk c of the K tile is key c / (HD/8), d-chunk c % (HD/8);
   // chunk c of the V^T tile is d c / (KT/8), key-chunk c % (KT/8)
@@ -760,15 +786,33 @@ __global__ __launch_bounds__(64 * G * S) void k_attn_prefill(AttnPreP p) {
     if (half == 1) return;
     const float *x = xb + (size_t)hw * NF * 64 + lane;
     const float m1 = x[0], l1 = x[64];
-    const float mm = fmaxf(m_run, m1);  // (the first half always saw key 0: finite)
-    const float a0 = exp2f(m_run - mm), a1 = exp2f(m1 - mm);
+    const float mm = fmaxf(m_run, m1);
+    const float mm_sub = mm == kNegInf ? 0.f : mm;  // (no visible key in either half)
+    const float a0 = exp2f(m_run - mm_sub), a1 = exp2f(m1 - mm_sub);
     l_run = l_run * a0 + l1 * a1;
+    m_run = mm;
 #pragma unroll
     for (int t = 0; t < DT; ++t)
 #pragma unroll
       for (int r = 0; r < 16; ++r) o[t][r] = o[t][r] * a0 + x[(2 + t * 16 + r) * 64] * a1;
   }
 
+  if (piece >= 0) {  // a split piece: its (un-normalised) state for the merge
+    float *pr = p.part + ((((size_t)(tile - p.split_from) * 2 + piece) * p.d.nh + h) * 32 +
+                          (lane & 31)) * (HD + 4);
+#pragma unroll
+    for (int t = 0; t < DT; ++t)
+#pragma unroll
+      for (int rq = 0; rq < 4; ++rq) {
+        const int d0 = t * 32 + 8 * rq + 4 * hi;
+        if (d0 < HD) *(f4 *)(pr + d0) = (f4){o[t][4 * rq], o[t][4 * rq + 1], o[t][4 * rq + 2], o[t][4 * rq + 3]};
+      }
+    if (hi == 0) {
+      pr[HD] = m_run;
+      pr[HD + 1] = l_run;
+    }
+    return;
+  }
   if (!qvalid) return;
   const float inv_l = 1.0f / l_run;
   _Float16 *orow = p.o16 + (size_t)qrow * p.ldo + (size_t)h * HD;
@@ -785,6 +829,28 @@ __global__ __launch_bounds__(64 * G * S) void k_attn_prefill(AttnPreP p) {
     }
 }
 
+// Combines the two pieces of each split query tile: O = (e^(m0-M) o0 +
+// e^(m1-M) o1) / (e^(m0-M) l0 + e^(m1-M) l1), M the larger maximum (states
+// in base 2).  One block per (split tile, query head).
+template <int HD>
+__global__ __launch_bounds__(256) void k_attn_prefill_merge(AttnPreP p) {
+  const int u = blockIdx.x, h = blockIdx.y;
+  const int r0 = (p.split_from + u) * 32;
+  const float *a = p.part + (((size_t)u * 2 + 0) * p.d.nh + h) * 32 * (HD + 4);
+  const float *b = p.part + (((size_t)u * 2 + 1) * p.d.nh + h) * 32 * (HD + 4);
+  for (int idx = threadIdx.x; idx < 32 * HD; idx += 256) {
+    const int q = idx / HD, dd = idx - q * HD;
+    if (r0 + q >= p.M) break;  // (rows past M come last)
+    const float *x = a + q * (HD + 4), *y = b + q * (HD + 4);
+    const float m0 = x[HD], m1 = y[HD];
+    const float mm = fmaxf(m0, m1);
+    const float sub = mm == kNegInf ? 0.f : mm;
+    const float w0 = exp2f(m0 - sub), w1 = exp2f(m1 - sub);
+    const float o = (x[dd] * w0 + y[dd] * w1) / (x[HD + 1] * w0 + y[HD + 1] * w1);
+    p.o16[(size_t)(r0 + q) * p.ldo + (size_t)h * HD + dd] = (_Float16)o;
+  }
+}
+
 template <int HD, int G>
 static void attn_prefill_g(const AttnPreP &p, dim3 grid, hipStream_t st) {
   constexpr int S = HD <= 64 ? 2 : 1;  // (hd 128 needs more registers than 2 halves allow)
@@ -793,11 +859,26 @@ static void attn_prefill_g(const AttnPreP &p, dim3 grid, hipStream_t st) {
 
 template <int HD>
 static void attn_prefill_hd(const AttnPreP &p, hipStream_t st) {
-  const dim3 grid((p.M + 31) / 32, p.d.nkv);
+  const int n_split = p.n_tiles - p.split_from;
+  const dim3 grid(p.d.nkv, p.n_tiles + n_split);
+  if (n_split > 0) {
+    switch (p.d.group) {
+      case 7: attn_prefill_g<HD, 7>(p, grid, st); break;
+      case 8: attn_prefill_g<HD, 8>(p, grid, st); break;
+      case 4: attn_prefill_g<HD, 4>(p, grid, st); break;
+      case 2: attn_prefill_g<HD, 2>(p, grid, st); break;
+      case 1: attn_prefill_g<HD, 1>(p, grid, st); break;
+      case 3: attn_prefill_g<HD, 3>(p, grid, st); break;
+      case 5: attn_prefill_g<HD, 5>(p, grid, st); break;
+      default: attn_prefill_g<HD, 6>(p, grid, st); break;
+    }
+    hipLaunchKernelGGL((k_attn_prefill_merge<HD>), dim3(n_split, p.d.nh), dim3(256), 0, st, p);
+    return;
+  }
   if ((int)(grid.x * grid.y) < 128) {
     // few query tiles (short prompts): one query head per block, so the
     // group's heads run on separate CUs (each block loads its group's K / V)
-    attn_prefill_g<HD, 1>(p, dim3(grid.x, grid.y, p.d.group), st);
+    attn_prefill_g<HD, 1>(p, dim3(grid.x, grid.y, p.d.group), st);  // (z: head in the group)
     return;
   }
   switch (p.d.group) {  // the group size is a compile-time constant of the kernel
@@ -813,12 +894,27 @@ static void attn_prefill_hd(const AttnPreP &p, hipStream_t st) {
 }
 
 void attn_prefill(const Dims &d, int layer, const KVCache &kv, const float *q, int ldq,
-                  RowInfo rows, int M, int seq, int kmax, _Float16 *o16, int ldo, hipStream_t st) {
-  (void)kmax;  // (read on the device from the rows' positions)
+                  RowInfo rows, int M, int seq, const int *host_pos, const Workspace &ws,
+                  _Float16 *o16, int ldo, hipStream_t st) {
   const size_t b16 = kv.off16(d, layer, seq, 0);
-  const AttnPreP p{d, q, ldq, rows, M, kv.k16 + b16, kv.v16t + b16,
-                   (size_t)kv.ldp * d.hd, kv.ldp, o16, ldo,
-                   (1.0f / sqrtf((float)d.hd)) * 1.4426950408889634f};
+  AttnPreP p{d, q, ldq, rows, M, kv.k16 + b16, kv.v16t + b16,
+             (size_t)kv.ldp * d.hd, kv.ldp, o16, ldo,
+             (1.0f / sqrtf((float)d.hd)) * 1.4426950408889634f, 0, 0, ws.buf};
+  // Causal balance: with one block per (query tile, KV head) the last tile's
+  // block has the most key tiles; tiles with more than half of the largest
+  // count (and at least 8 key tiles) are split in two, so no block has more
+  // than about half of the longest tile's work.  Positions are strictly
+  // increasing, so the key-tile count grows with the tile index.
+  const int T = (M + 31) / 32;
+  p.n_tiles = p.split_from = T;
+  auto ntiles = [&](int t) { return host_pos[std::min(32 * t + 31, M - 1)] / kPreKeys + 1; };
+  if (T * d.nkv >= 128 && ntiles(T - 1) >= 8) {
+    const int lim = (ntiles(T - 1) + 1) / 2;
+    int sf = T;
+    while (sf > 0 && ntiles(sf - 1) > lim) --sf;
+    const size_t need = (size_t)(T - sf) * 2 * d.nh * 32 * (d.hd + 4) * sizeof(float);
+    if (ws.buf && need <= ws.bytes) p.split_from = sf;
+  }
   switch (d.hd) {
     case 16: attn_prefill_hd<16>(p, st); break;
     case 64: attn_prefill_hd<64>(p, st); break;

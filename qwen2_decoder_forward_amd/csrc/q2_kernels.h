@@ -151,10 +151,12 @@ constexpr int wo_loads_per_wave(int hd) { return hd == 64 ? 2 : 8; }
 void attn_wo_fused(const Dims &d, int layer, const KVCache &kv, const float *q, int ldq,
                    RowInfo rows, int M, const uint16_t *wo, float *h, int ldh, hipStream_t st);
 // Causal flash attention over MFMA for one prefill pass of M rows of
-// sequence `seq` (positions strictly increasing, the last one kmax), on the
-// binary16 mirror of the cache.
+// sequence `seq` (positions strictly increasing; host_pos = their host copy,
+// which sizes the work split), on the binary16 mirror of the cache.  Long
+// passes use `ws` for the split query tiles' partial softmax states.
 void attn_prefill(const Dims &d, int layer, const KVCache &kv, const float *q, int ldq,
-                  RowInfo rows, int M, int seq, int kmax, _Float16 *o16, int ldo, hipStream_t st);
+                  RowInfo rows, int M, int seq, const int *host_pos, const Workspace &ws,
+                  _Float16 *o16, int ldo, hipStream_t st);
 // Rewrites the binary16 mirror of positions pos0 .. pos0+n-1 of (layer, seq)
 // from the f32 cache (after a direct write of the f32 cache).
 void kv_mirror(const Dims &d, const KVCache &kv, int layer, int seq, int pos0, int n,

@@ -495,8 +495,8 @@ void prefill_pass(qwen2_ctx *c, int M, int off, const int *pos, const int *seq, 
       TIMED(QWEN2_OP_GATEUP, q2::gemv_swiglu(d, w, c->h, M, c->a32, d.I_pad, eps, st));
       TIMED(QWEN2_OP_DOWN, q2::gemv_resid(w.wd, d.H, d.I_pad, c->a32, d.I_pad, M, c->h, d.H, st));
     } else {
-      TIMED(QWEN2_OP_ATTN, q2::attn_prefill(d, l, kv, c->q32, nhd, rows, M, seq_id,
-                                            host_pos[M - 1], c->x16, nhd, st));
+      TIMED(QWEN2_OP_ATTN, q2::attn_prefill(d, l, kv, c->q32, nhd, rows, M, seq_id, host_pos,
+                                            c->splitk, c->x16, nhd, st));
       TIMED(QWEN2_OP_WO, pending = q2::gemm_resid(w.wo, d.H, nhd, c->x16, nhd, M, c->h, d.H,
                                                   c->splitk, st));
       TIMED(QWEN2_OP_NORM, q2::rmsnorm_rows_f16(c->h, d.H, w.ffn_norm, d.H, M, eps, c->x16, d.H,

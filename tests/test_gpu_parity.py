@@ -51,11 +51,13 @@ def test_tiny_kv_cache_matches_oracle(tiny_w):
     p.close()
 
 
-@pytest.mark.parametrize("n", [9, 40, 100, 600, 1100])
+@pytest.mark.parametrize("n", [9, 40, 100, 600, 1100, 2100])
 def test_tiny_mfma_prefill_path(tiny_w, n):
     """Prompts longer than 8 rows take the MFMA GEMM + flash-attention path
     (f16 operands): ragged 32-row tiles, hd = 16; from 512 rows on the
-    large-tile GEMM (128-row tiles, a ragged last band at 1100)."""
+    large-tile GEMM (128-row tiles, a ragged last band at 1100); at 2100 rows
+    the attention splits its longest query tiles' key ranges over two blocks
+    and merges their softmax states."""
     p = Pair(TINY, tiny_w, n_ctx=max(128, n + 8))
     run_chain(p, syn.make_prompt(TINY, n, 3), 3, TOL, f"tiny-mfma-{n}")
     p.close()
