@@ -735,24 +735,29 @@ __global__ __launch_bounds__(64 * G * S) void k_attn_prefill(AttnPreP p) {
       // keys when its position lies before them, keeps m = -inf: subtract 0
       // then, so its weights are exp2(-inf) = 0 instead of NaN)
       const float m_sub = m_new == kNegInf ? 0.f : m_new;
-      const float alpha = exp2f(m_run - m_sub);
+      // the hardware 2^x (v_exp_f32): every argument is <= 0, and results
+      // below 2^-126 (weights that cannot matter) flush to zero
+      const float alpha = __builtin_amdgcn_exp2f(m_run - m_sub);
       float ls = 0.f;
       h8 pb[2][2];
 #pragma unroll
       for (int hf = 0; hf < 2; ++hf)
 #pragma unroll
         for (int r = 0; r < 16; ++r) {
-          const float e = exp2f(s[hf][r] - m_sub);
+          const float e = __builtin_amdgcn_exp2f(s[hf][r] - m_sub);
           ls += e;
           pb[hf][r >> 3][r & 7] = (_Float16)e;
         }
       ls += __shfl_xor(ls, 32, 64);
       l_run = l_run * alpha + ls;
       m_run = m_new;
+      const bool rescale = __any(alpha != 1.0f);  // (skipped while no maximum moved)
 #pragma unroll
       for (int t = 0; t < DT; ++t) {
+        if (rescale) {
 #pragma unroll
-        for (int r = 0; r < 16; ++r) o[t][r] *= alpha;
+          for (int r = 0; r < 16; ++r) o[t][r] *= alpha;
+        }
         const _Float16 *vr = sv + (t * 32 + (lane & 31)) * VP;
 #pragma unroll
         for (int hf = 0; hf < 2; ++hf) {
