@@ -49,15 +49,14 @@ __global__ __launch_bounds__(256) void k_gemm_lmhead(GemmP p) {
   const int M = p.M, N = p.N, K = p.K;
   const int hi = lane >> 5, l32 = lane & 31;
 
-  // each thread moves two 16-byte chunks of A and two of W per K slice
+  // each thread moves two 16-byte chunks of A and two of W per K slice;
+  // rows past M or N are clamped to the last row (their results are never
+  // stored), so every load is unconditional
   const int cr0 = tid >> 2, cr1 = (tid + 256) >> 2, ck = (tid & 3) * 8;
-  const bool a0ok = m0 + cr0 < M, a1ok = m0 + cr1 < M;
-  const bool w0ok = n0 + cr0 < N, w1ok = n0 + cr1 < N;
-  const _Float16 *Ap0 = p.A + (size_t)(a0ok ? m0 + cr0 : 0) * p.lda + ck;
-  const _Float16 *Ap1 = p.A + (size_t)(a1ok ? m0 + cr1 : 0) * p.lda + ck;
-  const _Float16 *Wp0 = p.W + (size_t)(w0ok ? n0 + cr0 : 0) * K + ck;
-  const _Float16 *Wp1 = p.W + (size_t)(w1ok ? n0 + cr1 : 0) * K + ck;
-  const h8 zero = {0, 0, 0, 0, 0, 0, 0, 0};
+  const _Float16 *Ap0 = p.A + (size_t)min(m0 + cr0, M - 1) * p.lda + ck;
+  const _Float16 *Ap1 = p.A + (size_t)min(m0 + cr1, M - 1) * p.lda + ck;
+  const _Float16 *Wp0 = p.W + (size_t)min(n0 + cr0, N - 1) * K + ck;
+  const _Float16 *Wp1 = p.W + (size_t)min(n0 + cr1, N - 1) * K + ck;
 
   f16x acc[2][2];
 #pragma unroll
@@ -69,37 +68,38 @@ __global__ __launch_bounds__(256) void k_gemm_lmhead(GemmP p) {
 
   // K slices kt0 .. kt0 + nk - 1; a ring of kStages register sets keeps the
   // global loads of the next kStages - 1 slices in flight while one slice is
-  // multiplied out of LDS.
+  // multiplied out of LDS.  Every stage issues the same loads (past the last
+  // slice they re-read it) in a fixed order, so the count of outstanding
+  // loads at the loop head stays exact instead of draining the ring.
   const int kt0 = blockIdx.z * p.k_steps;
   const int nk = min(K / BK - kt0, p.k_steps);
   h8 ra[kStages][2], rw[kStages][2];
+  auto gl = [&](int st, int kt) {
+    const int ko = (kt0 + min(kt, nk - 1)) * BK;
+    ra[st][0] = *(const h8 *)(Ap0 + ko);
+    ra[st][1] = *(const h8 *)(Ap1 + ko);
+    rw[st][0] = *(const h8 *)(Wp0 + ko);
+    rw[st][1] = *(const h8 *)(Wp1 + ko);
+  };
 #pragma unroll
   for (int st = 0; st < kStages; ++st) {
-    const int ko = (kt0 + st) * BK;
-    const bool ok = st < nk;
-    ra[st][0] = ok && a0ok ? *(const h8 *)(Ap0 + ko) : zero;
-    ra[st][1] = ok && a1ok ? *(const h8 *)(Ap1 + ko) : zero;
-    rw[st][0] = ok && w0ok ? *(const h8 *)(Wp0 + ko) : zero;
-    rw[st][1] = ok && w1ok ? *(const h8 *)(Wp1 + ko) : zero;
+    gl(st, st);
+    __builtin_amdgcn_sched_barrier(0);
   }
   for (int kb = 0; kb < nk; kb += kStages) {
 #pragma unroll
     for (int st = 0; st < kStages; ++st) {
       const int kt = kb + st;
+      // (stages past the last slice still write, wait and load, and only
+      // skip the multiply, so the loop has no branch around a load)
+      *(h8 *)(sA + cr0 * LDT + ck) = ra[st][0];
+      *(h8 *)(sA + cr1 * LDT + ck) = ra[st][1];
+      *(h8 *)(sW + cr0 * LDT + ck) = rw[st][0];
+      *(h8 *)(sW + cr1 * LDT + ck) = rw[st][1];
+      __syncthreads();
+      gl(st, kt + kStages);
+      __builtin_amdgcn_sched_barrier(0);
       if (kt < nk) {  // uniform across the block
-        *(h8 *)(sA + cr0 * LDT + ck) = ra[st][0];
-        *(h8 *)(sA + cr1 * LDT + ck) = ra[st][1];
-        *(h8 *)(sW + cr0 * LDT + ck) = rw[st][0];
-        *(h8 *)(sW + cr1 * LDT + ck) = rw[st][1];
-        __syncthreads();
-        const int kn = kt + kStages;
-        if (kn < nk) {
-          const int ko = (kt0 + kn) * BK;
-          ra[st][0] = a0ok ? *(const h8 *)(Ap0 + ko) : zero;
-          ra[st][1] = a1ok ? *(const h8 *)(Ap1 + ko) : zero;
-          rw[st][0] = w0ok ? *(const h8 *)(Wp0 + ko) : zero;
-          rw[st][1] = w1ok ? *(const h8 *)(Wp1 + ko) : zero;
-        }
 #pragma unroll
         for (int s = 0; s < 2; ++s) {
           h8 af[2], bf[2];
@@ -115,8 +115,8 @@ __global__ __launch_bounds__(256) void k_gemm_lmhead(GemmP p) {
             for (int j = 0; j < 2; ++j)
               acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_f16(af[i], bf[j], acc[i][j], 0, 0, 0);
         }
-        __syncthreads();
       }
+      __syncthreads();
     }
   }
 
