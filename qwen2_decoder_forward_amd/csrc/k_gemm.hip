@@ -7,8 +7,10 @@
 //   SWIGLU a = silu(gate) * up   (pair-packed gate/up rows, f16 out)
 //   LMHEAD logits + per-row greedy argmax key
 // k_gemm_big (QKV, RESID, SWIGLU) uses 64-wide K slices double-buffered in
-// LDS; k_gemm_lmhead (the lm_head over the vocabulary, M <= a few hundred
-// rows) uses 128 x 128 x 32 tiles staged through registers.
+// LDS, staged through registers; k_gemm_xl (the long-K residual and SwiGLU
+// GEMMs of many rows) loads 256 x 256 x 64 tiles straight into LDS;
+// k_gemm_lmhead (the lm_head over the vocabulary, M <= a few hundred rows)
+// uses 128 x 128 x 32 tiles staged through registers.
 // MFMA 32x32 layout: lane l supplies A[l%32][8*(l/32)..+8] and
 // B[8*(l/32)..+8][l%32]; it receives D[8*(r/4) + 4*(l/32) + r%4][l%32].
 #include "q2_device.h"
@@ -548,6 +550,195 @@ __global__ __launch_bounds__(64 * NW) void k_gemm_big(GemmP p) {
   }
 }
 
+// ------------------------------------------------- large-M, MFMA-bound core
+// 256 x 256 block tile, four wavefronts in a 2 x 2 arrangement, each owning
+// 128 x 128 of the output as 4 x 4 MFMA tiles (256 accumulators per lane,
+// held in the accumulation registers).  Per 64-wide K slice a wavefront
+// reads 32 KB of operand fragments from LDS for 64 MFMAs, a third of what
+// the 128 x 128 tile with eight wavefronts reads per MFMA.
+// The operand slices go from global memory straight into LDS
+// (global_load_lds_dwordx4: lane i's 16 bytes land at byte 16 i of the
+// instruction's 1 KB destination), in two stages.  The LDS layout is the
+// one of k_gemm_big (chunk slot s of row r holds logical chunk
+// s ^ ((r >> 1) & 7)); as the destination of a lane is fixed, the swizzle is
+// applied on the source side: each lane loads the logical chunk its slot
+// holds.  The loads are counted by vmcnt like any global load; the waits
+// for them are explicit.
+// Tile order: the grid is 1-D over tiles numbered with M fastest; blocks are
+// dealt round-robin over the 8 XCDs, and XCD x takes the x-th contiguous
+// eighth of that order, so each XCD streams a band of weight columns once
+// while the activations (a few MB) are read by every XCD.
+constexpr int kXT = 256;
+
+// s_waitcnt vmcnt(N) with expcnt and lgkmcnt at their maxima (no wait)
+template <int N>
+__device__ __forceinline__ void wait_vmcnt() {
+  static_assert(N >= 0 && N < 64, "vmcnt range");
+  __builtin_amdgcn_s_waitcnt((N & 15) | (7 << 4) | (15 << 8) | ((N >> 4) << 14));
+}
+
+// 16 bytes per lane from base + voff into LDS at byte lds + 16 * lane.
+// Written as asm: the compiler models this load as a possible LDS access
+// of unknown order and then turns every LDS-read wait behind it into
+// lgkmcnt(0), which would also wait for the fragment reads just issued.
+// The hardware counts it in vmcnt only; the waits for it are explicit.  (An
+// M0 write needs one wait state before the load that reads it.)
+__device__ __forceinline__ void lds_dma16(const void *base, unsigned voff, unsigned lds) {
+  asm volatile("s_mov_b32 m0, %2\n\ts_nop 0\n\tglobal_load_lds_dwordx4 %0, %1"
+               :
+               : "v"(voff), "s"(base), "s"(lds)
+               : "memory", "m0");
+}
+
+// BK: K slice width (32 or 64), NST: LDS stages (NST - 1 slices in flight).
+template <int EPI, int BK, int NST>
+__global__ __launch_bounds__(256) void k_gemm_xl(GemmP p) {
+  constexpr int CPR = BK / 8;         // 16-byte chunks per tile row
+  constexpr int RPI = 64 / CPR;       // tile rows one 1 KB load instruction fills
+  constexpr int LPO = kXT / RPI / 4;  // load instructions per wavefront per operand
+  constexpr int LPT = 2 * LPO;        // ... per slice
+  constexpr int KS = BK / 16;         // MFMA steps per slice
+  constexpr int SA = kXT * BK;        // halves of one operand slice
+  constexpr int SST = 2 * SA;         // halves of one stage
+  static_assert(KS % 2 == 0 && LPT <= 16, "slice shape");
+  // Bank spread: a 16-byte LDS access serves 16 lanes (256 B, the 64 banks)
+  // at a time; rows r .. r + 15 at one logical chunk must land in 16
+  // distinct 16-byte bank groups.  256 B hold 16 / CPR rows, so chunk slot
+  // s of row r holds logical chunk s ^ ((r / (16 / CPR)) % CPR).
+  auto swz = [](int r) { return (r / (16 / CPR)) & (CPR - 1); };
+  __shared__ __attribute__((aligned(1024))) _Float16 sm[NST * SST];  // [stage][A | W][row][BK]
+  const int tid = threadIdx.x, lane = tid & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int wm = wave >> 1, wn = wave & 1;
+  const int hi = lane >> 5, l32 = lane & 31;
+  const int M = p.M, N = p.N, K = p.K;
+
+  const int MB = (M + kXT - 1) / kXT;
+  const int nb = gridDim.x, bid = blockIdx.x;
+  int tile = bid;
+  if ((nb & 7) == 0) tile = (bid & 7) * (nb >> 3) + (bid >> 3);
+  const int m0 = (tile % MB) * kXT, n0 = (tile / MB) * kXT;
+
+  // load instruction j of wavefront w fills tile rows RPI (LPO w + j) .. +RPI
+  unsigned offA[LPO], offB[LPO];
+#pragma unroll
+  for (int j = 0; j < LPO; ++j) {
+    const int r = RPI * (LPO * wave + j) + lane / CPR;
+    const int c = (lane % CPR) ^ swz(r);
+    offA[j] = ((unsigned)min(m0 + r, M - 1) * (unsigned)p.lda + 8u * c) * 2u;
+    offB[j] = ((unsigned)min(n0 + r, N - 1) * (unsigned)K + 8u * c) * 2u;
+  }
+  const int kz0 = blockIdx.z * p.k_steps;  // split K: blockIdx.z takes p.k_steps slices
+  const int nk = min(K / BK - kz0, p.k_steps);
+  const char *Ab = (const char *)p.A + (size_t)kz0 * BK * 2;
+  const char *Wb = (const char *)p.W + (size_t)kz0 * BK * 2;
+  // load q (A rows, then W rows) of slice kt (clamped: the padding requests
+  // past the end re-read the last slice, so every iteration issues the same
+  // loads) into stage st
+  const unsigned lds0 = (unsigned)(size_t)(__attribute__((address_space(3))) _Float16 *)sm;
+  auto gload = [&](int q, int kt, int st) {
+    const unsigned ko = (unsigned)min(kt, nk - 1) * (BK * 2);
+    const unsigned dst =
+        lds0 + 2u * (st * SST + (q < LPO ? 0 : SA) + (wave * LPO + (q % LPO)) * 512);
+    lds_dma16(q < LPO ? Ab + ko : Wb + ko, q < LPO ? offA[q] : offB[q - LPO], dst);
+  };
+
+  // fragment reads: rows wm * 128 + 32 i + l32 of A and wn * 128 + 32 j + l32
+  // of W (their swizzle depends on l32 only), logical chunk 2 ks + hi of the
+  // 16-wide step ks
+  const int f = swz(l32);
+  const int ra = (wm * 128 + l32) * BK, rb = (wn * 128 + l32) * BK;
+  auto frag = [&](int st, int ks, h8 (&af)[4], h8 (&bf)[4]) {
+    const int co = ((2 * ks + hi) ^ f) << 3;
+    const _Float16 *a = sm + st * SST + ra + co;
+    const _Float16 *b = sm + st * SST + SA + rb + co;
+#pragma unroll
+    for (int i = 0; i < 4; ++i) af[i] = *(const h8 *)(a + i * 32 * BK);
+#pragma unroll
+    for (int j = 0; j < 4; ++j) bf[j] = *(const h8 *)(b + j * 32 * BK);
+  };
+  f16x acc[4][4];
+#pragma unroll
+  for (int i = 0; i < 4; ++i)
+#pragma unroll
+    for (int j = 0; j < 4; ++j)
+#pragma unroll
+      for (int r = 0; r < 16; ++r) acc[i][j][r] = 0.f;
+  // the 16 MFMAs of one step; with LD, load q of slice kt_ld goes out after
+  // MFMA q (the address arithmetic and issue overlap the matrix pipe)
+  auto mfma = [&](const h8 (&af)[4], const h8 (&bf)[4], bool LD, int kt_ld, int st_ld) {
+#pragma unroll
+    for (int q = 0; q < 16; ++q) {
+      acc[q >> 2][q & 3] =
+          __builtin_amdgcn_mfma_f32_32x32x16_f16(af[q >> 2], bf[q & 3], acc[q >> 2][q & 3], 0, 0, 0);
+      if (LD && q < LPT) gload(q, kt_ld, st_ld);
+    }
+  };
+  // (program order is kept: each phase's LDS reads must be in flight while
+  // the previous phase's MFMAs run, which the scheduler would not arrange)
+#define XL_PHASE __builtin_amdgcn_sched_barrier(0)
+
+  // Iteration kt multiplies slice kt (stage kt % NST) and requests slice
+  // kt + NST - 1 into the stage slice kt - 1 occupied (its reads ended
+  // before the barrier that closed iteration kt - 1), from inside its first
+  // MFMA step.  The fragments of step s + 1 are read while step s is
+  // multiplied.  Before its last step it waits for its own loads of slice
+  // kt + 1 (the NST - 2 newer slices may stay in flight), meets the barrier
+  // (everyone's loads of slice kt + 1 have landed) and reads that slice's
+  // first step.
+  h8 a0[4], b0[4], a1[4], b1[4];
+#pragma unroll
+  for (int s = 0; s < NST - 1; ++s)
+#pragma unroll
+    for (int q = 0; q < LPT; ++q) gload(q, s, s);
+  wait_vmcnt<(NST - 2) * LPT>();
+  __syncthreads();
+  frag(0, 0, a0, b0);
+  int cur = 0, nxt = 1, ld = NST - 1;  // stages of slices kt, kt + 1, kt + NST - 1
+  for (int kt = 0; kt < nk; ++kt) {
+#pragma unroll
+    for (int ks = 0; ks < KS; ++ks) {
+      XL_PHASE;
+      if (ks + 1 < KS) {
+        if (ks & 1)
+          frag(cur, ks + 1, a0, b0);
+        else
+          frag(cur, ks + 1, a1, b1);
+      } else {
+        wait_vmcnt<(NST - 2) * LPT>();
+        __syncthreads();
+        XL_PHASE;
+        frag(nxt, 0, a0, b0);
+      }
+      XL_PHASE;
+      if (ks & 1)
+        mfma(a1, b1, false, 0, 0);
+      else
+        mfma(a0, b0, ks == 0, kt + NST - 1, ld);
+    }
+    cur = nxt;
+    nxt = nxt + 1 == NST ? 0 : nxt + 1;
+    ld = ld + 1 == NST ? 0 : ld + 1;
+  }
+  XL_PHASE;
+
+  // One 32 x 32 tile at a time, its sums copied out of the accumulation
+  // registers right before use (the copies are explicit: left to the
+  // compiler, all 256 are made at the loop exit, which needs more
+  // registers than there are and spills them to scratch).
+#pragma unroll
+  for (int i = 0; i < 4; ++i)
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+      f16x v;
+#pragma unroll
+      for (int r = 0; r < 16; ++r) asm volatile("v_accvgpr_read_b32 %0, %1" : "=v"(v[r]) : "a"(acc[i][j][r]));
+      tile_epilogue<EPI>(p, v, m0 + wm * 128 + i * 32, n0 + wn * 128 + j * 32 + l32);
+      XL_PHASE;
+    }
+#undef XL_PHASE
+}
+
 template <int EPI, int BMT, int BNT, int WGM, int FB = 0, int NW = 4, int S = 1>
 static void launch_big(GemmP p, int splits, hipStream_t st) {
   const int nk = p.K / kBK2;
@@ -558,21 +749,55 @@ static void launch_big(GemmP p, int splits, hipStream_t st) {
   hipLaunchKernelGGL((k_gemm_big<EPI, BMT, BNT, WGM, FB, NW, S>), grid, dim3(64 * NW), 0, st, p);
 }
 
-// Tile of a large-M GEMM (all with 8 wavefronts, 2 along M x 4 along N).
-// Short K (< 2048, the 0.5B shape's 896): 128 x 128 (measured 381-643
-// TFLOP/s on the 4096-row 0.5B projections, against 304-590 with 4
+// Large-M GEMM with long K (>= 2048, M >= 1024), residual and SwiGLU
+// epilogues: k_gemm_xl.  Measured against the best k_gemm_big tile on the
+// hd-128 shapes: gate/up 2048 x 37888 x 3584 635 -> 572 us, down
+// 2048 x 3584 x 18944 (split in two) 351 -> 271 us, WO 2048 x 3584 x 3584
+// (two splits) 71 -> 63 us.  Residual GEMMs with fewer tiles than CUs split
+// K so that about 256 blocks run; their partial sums go to the workspace
+// (at most 256 / tiles sets of M x N, i.e. <= 64 MB) and are folded in by
+// the next RMSNorm.  Returns the number of pending partial-sum sets (0:
+// applied).
+template <int EPI>
+static int launch_xl(GemmP p, const Workspace &wsp, hipStream_t st) {
+  constexpr int BK = 64;
+  const int nk = p.K / BK;
+  const int tiles = ((p.M + kXT - 1) / kXT) * ((p.N + kXT - 1) / kXT);
+  int splits = 1;
+  if (EPI == G_RESID && wsp.buf && tiles < 256) {
+    splits = min(256 / tiles, min(kMaxSplits, nk));
+    splits = min(splits, (int)(wsp.bytes / ((size_t)p.M * p.N * 4)));
+    if (splits < 1) splits = 1;
+  }
+  p.k_steps = (nk + splits - 1) / splits;
+  splits = (nk + p.k_steps - 1) / p.k_steps;
+  p.ws = splits > 1 ? wsp.buf : nullptr;
+  hipLaunchKernelGGL((k_gemm_xl<EPI, BK, 2>), dim3(tiles, 1, splits), dim3(256), 0, st, p);
+  return splits > 1 ? splits : 0;
+}
+
+// Tile of the other large-M GEMMs (all with 8 wavefronts, 2 along M x 4
+// along N).  Short K (< 2048, the 0.5B shape's 896): 128 x 128 (measured
+// 381-643 TFLOP/s on the 4096-row 0.5B projections, against 304-590 with 4
 // wavefronts).  Long K: the tile whose measured per-CU rate times the number
 // of rounds of blocks over the 256 CUs is cheapest, among 256 x 256 (910
 // TFLOP/s on a 2048 x 37888 x 3584 GEMM), 128 x 256 (850) and 128 x 128 (740).
 template <int EPI>
-static void launch_large_m(const GemmP &p, hipStream_t st) {
+static int launch_large_m(const GemmP &p, const Workspace &wsp, hipStream_t st) {
   if constexpr (EPI == G_QKV) {  // (its LDS-staged epilogue fits a 128 x 128 tile)
     launch_big<EPI, 128, 128, 2, 0, 8>(p, 1, st);
-    return;
+    return 0;
+  } else {
+    // (residual GEMMs with fewer than 96 tiles would need more than two
+    // partial-sum sets, whose folding costs the next RMSNorm more than the
+    // split saves: 0.5B down)
+    const int tiles = ((p.M + kXT - 1) / kXT) * ((p.N + kXT - 1) / kXT);
+    if (p.K >= 2048 && p.M >= 1024 && (EPI == G_SWIGLU || tiles >= 96))
+      return launch_xl<EPI>(p, wsp, st);
   }
   if (p.K < 2048) {
     launch_big<EPI, 128, 128, 2, 0, 8>(p, 1, st);
-    return;
+    return 0;
   }
   struct Cand { int bm, bn; double rate; };
   const Cand cand[3] = {{256, 256, 910.0}, {128, 256, 850.0}, {128, 128, 740.0}};
@@ -592,6 +817,7 @@ static void launch_large_m(const GemmP &p, hipStream_t st) {
     launch_big<EPI, 128, 256, 2, 1, 8>(p, 1, st);
   else
     launch_big<EPI, 128, 128, 2, 0, 8>(p, 1, st);
+  return 0;
 }
 
 // ------------------------------------------------------ skinny projections
@@ -750,10 +976,7 @@ static int launch_ring(GemmP p, int splits, const Workspace &wsp, hipStream_t st
 // pending (0 when the result was applied directly).
 template <int EPI>
 static int launch_tiles(GemmP p, const Workspace &wsp, hipStream_t st) {
-  if (p.M >= kBigM) {
-    launch_large_m<EPI>(p, st);
-    return 0;
-  }
+  if (p.M >= kBigM) return launch_large_m<EPI>(p, wsp, st);
   if (p.K <= 1024 && p.N <= 2048) return launch_skinny<EPI>(p, wsp, st);
   // gate/up of up to 128 rows: a ring of two K slices in flight and the
   // next step's LDS fragments read ahead (measured on the 0.5B gate/up

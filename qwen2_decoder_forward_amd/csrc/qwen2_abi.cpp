@@ -25,7 +25,7 @@ constexpr int kGemvRows = 8;      // rows up to this use the f32 GEMV path
 constexpr int kMaxPassRows = 4096;  // rows per prefill pass
 constexpr int kProfMax = 16384;     // timed launches between two reads
 constexpr size_t kSlotBytes = 64;   // pointer slots at the head of a staged call
-constexpr size_t kSplitKBytes = 48ull << 20;  // split-K partial sums
+constexpr size_t kSplitKBytes = 64ull << 20;  // split-K partial sums (large-M residual GEMMs: <= 256 x 256 x 256 x 4 B)
 
 thread_local std::string g_load_error;
 
