@@ -729,7 +729,7 @@ __global__ __launch_bounds__(64 * G * S) void k_attn_prefill(AttnPreP p) {
       for (int hf = 0; hf < 2; ++hf)
 #pragma unroll
         for (int r = 0; r < 16; ++r) mt = fmaxf(mt, s[hf][r]);
-      mt = fmaxf(mt, __shfl_xor(mt, 32, 64));
+      mt = max32(mt);
       const float m_new = fmaxf(m_run, mt);
       // (a query that has seen no visible key yet, e.g. in the second half's
       // keys when its position lies before them, keeps m = -inf: subtract 0
@@ -748,7 +748,7 @@ __global__ __launch_bounds__(64 * G * S) void k_attn_prefill(AttnPreP p) {
           ls += e;
           pb[hf][r >> 3][r & 7] = (_Float16)e;
         }
-      ls += __shfl_xor(ls, 32, 64);
+      ls = sum32(ls);
       l_run = l_run * alpha + ls;
       m_run = m_new;
       const bool rescale = __any(alpha != 1.0f);  // (skipped while no maximum moved)

@@ -23,16 +23,41 @@ __device__ __forceinline__ float dpp(float v) {
                                                             0xF, 0xF, true));
 }
 
+// The two values a lane pair (l, l ^ 16) or (l, l ^ 32) holds, in both lanes
+// of the pair: v_permlane16_swap / v_permlane32_swap with the same register
+// as both operands return the even and the odd row (half) of the pair.
+// They run on the VALU, against an LDS round trip for a shuffle.
+__device__ __forceinline__ void pair16(float v, float &a, float &b) {
+  const auto r = __builtin_amdgcn_permlane16_swap(__float_as_uint(v), __float_as_uint(v), true, false);
+  a = __uint_as_float(r[0]);
+  b = __uint_as_float(r[1]);
+}
+__device__ __forceinline__ void pair32(float v, float &a, float &b) {
+  const auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(v), __float_as_uint(v), true, false);
+  a = __uint_as_float(r[0]);
+  b = __uint_as_float(r[1]);
+}
+__device__ __forceinline__ float sum32(float v) {  // v[l] + v[l ^ 32]
+  float a, b;
+  pair32(v, a, b);
+  return a + b;
+}
+__device__ __forceinline__ float max32(float v) {  // max(v[l], v[l ^ 32])
+  float a, b;
+  pair32(v, a, b);
+  return fmaxf(a, b);
+}
+
 // Sum over the 64 lanes, result in every lane: four DPP steps combine each
-// row of 16 lanes, two shuffles combine the four rows.
+// row of 16 lanes, two lane-pair swaps combine the four rows.
 __device__ __forceinline__ float wave_sum(float v) {
   v += dpp<0xB1>(v);
   v += dpp<0x4E>(v);
   v += dpp<0x141>(v);
   v += dpp<0x140>(v);
-  v += __shfl_xor(v, 16, 64);
-  v += __shfl_xor(v, 32, 64);
-  return v;
+  float a, b;
+  pair16(v, a, b);
+  return sum32(a + b);
 }
 
 __device__ __forceinline__ float wave_max(float v) {
@@ -40,9 +65,9 @@ __device__ __forceinline__ float wave_max(float v) {
   v = fmaxf(v, dpp<0x4E>(v));
   v = fmaxf(v, dpp<0x141>(v));
   v = fmaxf(v, dpp<0x140>(v));
-  v = fmaxf(v, __shfl_xor(v, 16, 64));
-  v = fmaxf(v, __shfl_xor(v, 32, 64));
-  return v;
+  float a, b;
+  pair16(v, a, b);
+  return max32(fmaxf(a, b));
 }
 
 __device__ __forceinline__ unsigned long long shfl_xor_u64(unsigned long long v, int o) {
