@@ -79,12 +79,16 @@ def test_batched_decode_64_sequences_at_1024(w05):
     p.close()
 
 
-def test_hd128_full_width_two_layers_prompt_2048():
+@pytest.mark.parametrize("n", [2048, 2100])
+def test_hd128_full_width_two_layers_prompt(n):
+    """The 2048-token workload prompt, and 2100 rows: a ragged last row tile
+    (52 of 256 rows) in the 256 x 256 GEMM tiles of WO / down (two K splits)
+    and gate/up."""
     G2 = syn.model_shape("qwen2-hd128", n_layer=2)
-    say("[hd128-L2] drawing weights")
+    say(f"[hd128-L2-{n}] drawing weights")
     w = syn.make_weights(G2)
     p = Pair(G2, w, n_ctx=4096)
-    run_chain(p, syn.make_prompt(G2, 2048), 2, TOL, "hd128-L2")
+    run_chain(p, syn.make_prompt(G2, n), 2, TOL, f"hd128-L2-{n}")
     p.close()
 
 
