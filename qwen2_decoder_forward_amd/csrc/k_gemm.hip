@@ -40,6 +40,7 @@ struct GemmP {
   ArgmaxEpi am;
   float *ws;      // split-K: raw partial sums [splits][M][N] (RESID only)
   int k_steps;    // K slices per block (per split)
+  int atomic_out; // split-K residual: partial sums added into h with float atomics
 };
 
 __global__ __launch_bounds__(256) void k_gemm_lmhead(GemmP p) {
@@ -167,8 +168,11 @@ __global__ __launch_bounds__(256) void k_gemm_lmhead(GemmP p) {
 // whose column is n.  Every load (the residual rows, the QKV epilogue's
 // tables) is issued before the first store, so the tile costs one or two
 // memory round trips: a load after a store to a possibly aliasing address
-// would wait for it.  Split-K residual blocks (p.ws) store raw partial sums
-// [split][M][N], folded in by the next RMSNorm.
+// would wait for it.  Split-K residual blocks (p.ws) either add their
+// partial sums into h with float atomics (p.atomic_out: GEMMs of fewer than
+// 512 rows, where the adds are few; their order varies from run to run by
+// an ulp) or store them raw, [split][M][N], for the next RMSNorm to fold in
+// (the large-M GEMMs, whose millions of adds would cost more than the fold).
 template <int EPI>
 __device__ __forceinline__ void tile_epilogue(const GemmP &p, const f16x &v, int mt0, int n) {
   const int lane = threadIdx.x & 63, hi = lane >> 5;
@@ -181,7 +185,11 @@ __device__ __forceinline__ void tile_epilogue(const GemmP &p, const f16x &v, int
     ok[r] = m[r] < M && n < N;
     m[r] = min(m[r], M - 1);
   }
-  if (EPI == G_RESID && p.ws) {
+  if (EPI == G_RESID && p.ws && p.atomic_out) {
+#pragma unroll
+    for (int r = 0; r < 16; ++r)
+      if (ok[r]) atomicAdd(p.h + (size_t)m[r] * p.ldh + n, v[r]);
+  } else if (EPI == G_RESID && p.ws) {
 #pragma unroll
     for (int r = 0; r < 16; ++r)
       if (ok[r]) p.ws[((size_t)blockIdx.z * M + m[r]) * N + n] = v[r];
@@ -910,8 +918,10 @@ __global__ __launch_bounds__(64 * NWS) void k_gemm_skinny(GemmP p) {
 }
 
 // Launch shape of a skinny GEMM: rows per block 32 TM (TM = 4, 2, 1) and,
-// for residual GEMMs, K splits; the choice minimises the bytes the busiest
-// CU loads (A and W of its blocks), with blocks dealt evenly over 256 CUs.
+// for residual GEMMs, K splits (added into h with float atomics); the
+// choice minimises the bytes the busiest CU loads (A and W of its blocks),
+// with blocks dealt evenly over 256 CUs, plus a charge per split (the extra
+// adds).
 template <int EPI>
 static int launch_skinny(GemmP p, const Workspace &wsp, hipStream_t st) {
   const int steps = p.K / 16;
@@ -937,6 +947,7 @@ static int launch_skinny(GemmP p, const Workspace &wsp, hipStream_t st) {
   p.k_steps = (steps + best_sp - 1) / best_sp;
   const int splits = (steps + p.k_steps - 1) / p.k_steps;
   p.ws = splits > 1 ? wsp.buf : nullptr;
+  p.atomic_out = 1;  // (the split sums go straight into h)
   dim3 grid(nt, (p.M + 32 * best_tm - 1) / (32 * best_tm), splits);
   if (EPI == G_QKV && best_tm == 1) {
     // (no K split across blocks for QKV: eight wavefronts split the block's
@@ -949,7 +960,7 @@ static int launch_skinny(GemmP p, const Workspace &wsp, hipStream_t st) {
     case 2: hipLaunchKernelGGL((k_gemm_skinny<EPI, 2>), grid, dim3(256), 0, st, p); break;
     default: hipLaunchKernelGGL((k_gemm_skinny<EPI, 1>), grid, dim3(256), 0, st, p); break;
   }
-  return splits > 1 ? splits : 0;
+  return 0;
 }
 
 // Mid-M launch (8 < M < kBigM): tile BMT x BNT with NW wavefronts, S K
@@ -972,8 +983,11 @@ static int launch_ring(GemmP p, int splits, const Workspace &wsp, hipStream_t st
 
 // K % 64 == 0.  Many rows: launch_large_m.  Fewer rows: the weights
 // dominate and the K loop is latency-bound, so the tiles keep a ring of K
-// slices in flight.  Returns the number of split-K partial-sum sets left
-// pending (0 when the result was applied directly).
+// slices in flight, and long-K residual GEMMs split K over about 256 blocks
+// whose sums are added into h atomically (0.5B 128-token prefill 1.24 ->
+// 1.20 ms against split sums folded in by the next RMSNorm).  Returns the
+// number of split-K partial-sum sets left pending in the workspace (0 when
+// the result was applied directly).
 template <int EPI>
 static int launch_tiles(GemmP p, const Workspace &wsp, hipStream_t st) {
   if (p.M >= kBigM) return launch_large_m<EPI>(p, wsp, st);
@@ -989,17 +1003,16 @@ static int launch_tiles(GemmP p, const Workspace &wsp, hipStream_t st) {
   int splits = 1;
   if (EPI == G_RESID && p.K >= 2048 && wsp.buf) {
     const int blocks = ((p.N + 31) / 32) * ((p.M + 127) / 128);
-    splits = (256 + blocks - 1) / blocks;
+    splits = max(1, 256 / blocks);
     splits = min(splits, min(kMaxSplits, nk));
     const size_t per = (size_t)p.M * p.N * 4;
     splits = min(splits, (int)(wsp.bytes / per));
     if (splits < 1) splits = 1;
   }
   p.ws = splits > 1 ? wsp.buf : nullptr;
-  const int ks = (nk + splits - 1) / splits;
-  const int used = (nk + ks - 1) / ks;  // launch_big's effective split count
+  p.atomic_out = 1;  // (few rows: the split sums go straight into h)
   launch_big<EPI, 128, 32, 4>(p, splits, st);
-  return used > 1 ? used : 0;
+  return 0;
 }
 
 // Every projection but the lm_head runs on the tile kernels (K is a

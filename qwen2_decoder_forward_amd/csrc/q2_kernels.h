@@ -92,8 +92,10 @@ void gemv_lmhead(const Dims &d, const uint16_t *W, const float *norm_w, const fl
 void argmax_finalize(const ArgmaxEpi &e, int M, hipStream_t st);
 
 // MFMA GEMM family (rows M > 8): A f16 [M, lda], W f16 [N, K], K % 32 == 0.
-// GEMMs with few output tiles (small M) split K over blocks; the f32 partial
-// sums go to a context-owned workspace and a small kernel applies the op.
+// Residual GEMMs with few output tiles split K over blocks: with fewer than
+// 512 rows the blocks add their f32 partial sums into h with float atomics;
+// with more, the partial sums go to a context-owned workspace and the next
+// RMSNorm folds them in.
 struct Workspace {
   float *buf;
   size_t bytes;
