@@ -172,7 +172,8 @@ __global__ __launch_bounds__(256) void k_gemm_lmhead(GemmP p) {
 // partial sums into h with float atomics (p.atomic_out: GEMMs of fewer than
 // 512 rows, where the adds are few; their order varies from run to run by
 // an ulp) or store them raw, [split][M][N], for the next RMSNorm to fold in
-// (the large-M GEMMs, whose millions of adds would cost more than the fold).
+// (the large-M GEMMs, whose millions of adds cost more than the fold:
+// hd-128 2048-row prefill 32.7 -> 34.5 ms with atomics).
 template <int EPI>
 __device__ __forceinline__ void tile_epilogue(const GemmP &p, const f16x &v, int mt0, int n) {
   const int lane = threadIdx.x & 63, hi = lane >> 5;
