@@ -19,11 +19,11 @@ namespace q2 {
 
 enum { G_QKV = 0, G_RESID = 1, G_SWIGLU = 2, G_LMHEAD = 3 };
 
-// k_gemm_lmhead: block tile 128 x 128 x 32, four wavefronts in a 2 x 2
-// arrangement, each owning 64 x 64 (2 x 2 MFMA tiles); a ring of kStages
-// register sets keeps the global loads of the next slices in flight while
-// one slice is multiplied out of LDS.
-constexpr int BM = 128, BN = 128, BK = 32, LDT = BK + 8;
+// k_gemm_lmhead: block tile LBM x 128 x 32 (LBM = 64 or 128 rows), four
+// wavefronts in a 2 x 2 arrangement, each owning (LBM / 2) x 64 (LBM / 64 x
+// 2 MFMA tiles); a ring of kStages register sets keeps the global loads of
+// the next slices in flight while one slice is multiplied out of LDS.
+constexpr int BN = 128, BK = 32, LDT = BK + 8;
 constexpr int kStages = 4;  // K slices in flight per block
 
 struct GemmP {
@@ -43,27 +43,30 @@ struct GemmP {
   int atomic_out; // split-K residual: partial sums added into h with float atomics
 };
 
+template <int LBM>
 __global__ __launch_bounds__(256) void k_gemm_lmhead(GemmP p) {
-  __shared__ __attribute__((aligned(16))) _Float16 sA[BM * LDT];
+  constexpr int TMW = LBM / 64;  // MFMA tiles per wavefront along M
+  constexpr int WTM = LBM / 2;   // wavefront tile rows
+  __shared__ __attribute__((aligned(16))) _Float16 sA[LBM * LDT];
   __shared__ __attribute__((aligned(16))) _Float16 sW[BN * LDT];
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int wm = wave >> 1, wn = wave & 1;
-  const int m0 = blockIdx.y * BM, n0 = blockIdx.x * BN;
+  const int m0 = blockIdx.y * LBM, n0 = blockIdx.x * BN;
   const int M = p.M, N = p.N, K = p.K;
   const int hi = lane >> 5, l32 = lane & 31;
 
-  // each thread moves two 16-byte chunks of A and two of W per K slice;
+  // each thread moves LBM / 64 16-byte chunks of A and two of W per K slice;
   // rows past M or N are clamped to the last row (their results are never
   // stored), so every load is unconditional
   const int cr0 = tid >> 2, cr1 = (tid + 256) >> 2, ck = (tid & 3) * 8;
   const _Float16 *Ap0 = p.A + (size_t)min(m0 + cr0, M - 1) * p.lda + ck;
-  const _Float16 *Ap1 = p.A + (size_t)min(m0 + cr1, M - 1) * p.lda + ck;
+  const _Float16 *Ap1 = p.A + (size_t)min(m0 + (LBM == 128 ? cr1 : cr0), M - 1) * p.lda + ck;
   const _Float16 *Wp0 = p.W + (size_t)min(n0 + cr0, N - 1) * K + ck;
   const _Float16 *Wp1 = p.W + (size_t)min(n0 + cr1, N - 1) * K + ck;
 
-  f16x acc[2][2];
+  f16x acc[TMW][2];
 #pragma unroll
-  for (int i = 0; i < 2; ++i)
+  for (int i = 0; i < TMW; ++i)
 #pragma unroll
     for (int j = 0; j < 2; ++j)
 #pragma unroll
@@ -80,7 +83,7 @@ __global__ __launch_bounds__(256) void k_gemm_lmhead(GemmP p) {
   auto gl = [&](int st, int kt) {
     const int ko = (kt0 + min(kt, nk - 1)) * BK;
     ra[st][0] = *(const h8 *)(Ap0 + ko);
-    ra[st][1] = *(const h8 *)(Ap1 + ko);
+    if (LBM == 128) ra[st][1] = *(const h8 *)(Ap1 + ko);
     rw[st][0] = *(const h8 *)(Wp0 + ko);
     rw[st][1] = *(const h8 *)(Wp1 + ko);
   };
@@ -96,7 +99,7 @@ __global__ __launch_bounds__(256) void k_gemm_lmhead(GemmP p) {
       // (stages past the last slice still write, wait and load, and only
       // skip the multiply, so the loop has no branch around a load)
       *(h8 *)(sA + cr0 * LDT + ck) = ra[st][0];
-      *(h8 *)(sA + cr1 * LDT + ck) = ra[st][1];
+      if (LBM == 128) *(h8 *)(sA + cr1 * LDT + ck) = ra[st][1];
       *(h8 *)(sW + cr0 * LDT + ck) = rw[st][0];
       *(h8 *)(sW + cr1 * LDT + ck) = rw[st][1];
       __syncthreads();
@@ -105,15 +108,15 @@ __global__ __launch_bounds__(256) void k_gemm_lmhead(GemmP p) {
       if (kt < nk) {  // uniform across the block
 #pragma unroll
         for (int s = 0; s < 2; ++s) {
-          h8 af[2], bf[2];
+          h8 af[TMW], bf[2];
 #pragma unroll
-          for (int i = 0; i < 2; ++i)
-            af[i] = *(const h8 *)(sA + (wm * 64 + i * 32 + l32) * LDT + s * 16 + hi * 8);
+          for (int i = 0; i < TMW; ++i)
+            af[i] = *(const h8 *)(sA + (wm * WTM + i * 32 + l32) * LDT + s * 16 + hi * 8);
 #pragma unroll
           for (int j = 0; j < 2; ++j)
             bf[j] = *(const h8 *)(sW + (wn * 64 + j * 32 + l32) * LDT + s * 16 + hi * 8);
 #pragma unroll
-          for (int i = 0; i < 2; ++i)
+          for (int i = 0; i < TMW; ++i)
 #pragma unroll
             for (int j = 0; j < 2; ++j)
               acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_f16(af[i], bf[j], acc[i][j], 0, 0, 0);
@@ -124,14 +127,14 @@ __global__ __launch_bounds__(256) void k_gemm_lmhead(GemmP p) {
   }
 
   // ------------------------------------------ epilogue: logits + argmax key
-  __shared__ unsigned long long sBest[2][BM];
+  __shared__ unsigned long long sBest[2][LBM];
   float *logits = *p.am.logits;
-  unsigned long long kb[2][16];
+  unsigned long long kb[TMW][16];
 #pragma unroll
-  for (int i = 0; i < 2; ++i)
+  for (int i = 0; i < TMW; ++i)
 #pragma unroll
     for (int r = 0; r < 16; ++r) {
-      const int m = m0 + wm * 64 + i * 32 + 8 * (r >> 2) + 4 * hi + (r & 3);
+      const int m = m0 + wm * WTM + i * 32 + 8 * (r >> 2) + 4 * hi + (r & 3);
       unsigned long long b = 0ull;
 #pragma unroll
       for (int j = 0; j < 2; ++j) {
@@ -152,12 +155,12 @@ __global__ __launch_bounds__(256) void k_gemm_lmhead(GemmP p) {
     }
   if (l32 == 0) {
 #pragma unroll
-    for (int i = 0; i < 2; ++i)
+    for (int i = 0; i < TMW; ++i)
 #pragma unroll
-      for (int r = 0; r < 16; ++r) sBest[wn][wm * 64 + i * 32 + 8 * (r >> 2) + 4 * hi + (r & 3)] = kb[i][r];
+      for (int r = 0; r < 16; ++r) sBest[wn][wm * WTM + i * 32 + 8 * (r >> 2) + 4 * hi + (r & 3)] = kb[i][r];
   }
   __syncthreads();
-  if (tid < BM && m0 + tid < M) {
+  if (tid < LBM && m0 + tid < M) {
     const unsigned long long b = sBest[0][tid] > sBest[1][tid] ? sBest[0][tid] : sBest[1][tid];
     atomicMax(&p.am.best[m0 + tid], b);
   }
@@ -1024,7 +1027,6 @@ static int launch(GemmP p, const Workspace &wsp, hipStream_t st) {
   return launch_tiles<EPI>(p, wsp, st);
 }
 
-static dim3 grid_for(int M, int N) { return dim3((N + BN - 1) / BN, (M + BM - 1) / BM); }
 
 static GemmP base(const _Float16 *A, int lda, int M, const uint16_t *W, int N, int K) {
   GemmP p{};
@@ -1066,7 +1068,12 @@ void gemm_lmhead(const Dims &d, const uint16_t *W, const _Float16 *x, int lda, i
   GemmP p = base(x, lda, M, W, d.V, d.H);
   p.am = e;
   p.k_steps = d.H / BK;
-  hipLaunchKernelGGL(k_gemm_lmhead, grid_for(M, d.V), dim3(256), 0, st, p);
+  // (64-row tiles up to 64 rows: a 128-row tile would load and multiply
+  // every A row twice)
+  if (M <= 64)
+    hipLaunchKernelGGL(k_gemm_lmhead<64>, dim3((d.V + BN - 1) / BN, 1), dim3(256), 0, st, p);
+  else
+    hipLaunchKernelGGL(k_gemm_lmhead<128>, dim3((d.V + BN - 1) / BN, (M + 127) / 128), dim3(256), 0, st, p);
   argmax_finalize(e, M, st);
 }
 
