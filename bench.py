@@ -35,16 +35,19 @@ MFMA_F16_PEAK_TFS = 2500.0  # MI355X dense f16 MFMA
 # WRITE_SIZE passes, scaled by what the counters read for a 256 MiB copy
 # (profiles/qwen2.5-0.5b_gateup_gemv_hbm_traffic.md); valid only while the
 # kernel source is the one the counters were taken on.
-GATEUP_TRAFFIC_BYTES = 17585594
-GATEUP_TRAFFIC_SRC_SHA = "d5d78a6b2fc5478e"
+GATEUP_TRAFFIC_BYTES = 17569237
+GATEUP_TRAFFIC_SRC_SHA = "46f060f0a93c23d1"
 
 
 def gateup_traffic(shape):
     import hashlib
-    src = os.path.join(os.path.dirname(os.path.abspath(__file__)), "qwen2_decoder_forward_amd",
-                       "csrc", "k_gemv.hip")
-    with open(src, "rb") as f:
-        sha = hashlib.sha256(f.read()).hexdigest()[:16]
+    h = hashlib.sha256()
+    for name in ("k_gemv.hip", "q2_device.h"):  # the kernel and the device helpers it inlines
+        src = os.path.join(os.path.dirname(os.path.abspath(__file__)), "qwen2_decoder_forward_amd",
+                           "csrc", name)
+        with open(src, "rb") as f:
+            h.update(f.read())
+    sha = h.hexdigest()[:16]
     if sha != GATEUP_TRAFFIC_SRC_SHA or shape.name != "qwen2.5-0.5b":
         return None
     return GATEUP_TRAFFIC_BYTES
