@@ -435,6 +435,137 @@ void attn_wo_fused(const Dims &d, int layer, const KVCache &kv, const float *q, 
   }
 }
 
+// ------------------------------------- chunk-record merge fused with WO
+// Longer contexts on the decode path: after k_attn_decode has left its
+// chunk records, one block per (WO row chunk, query head) merges the head's
+// records into its attention output (as k_attn_merge does) and multiplies it
+// by its slice of WO, adding the partial row sums into the residual with
+// float atomics (as k_attn_wo).  This replaces the merge kernel and the WO
+// GEMV, one kernel boundary fewer per layer.  The WO slice is loaded first,
+// so its latency overlaps the merge.
+struct MergeWoP {
+  Dims d;
+  AttnPartials part;
+  RowInfo rows;
+  int M;
+  const _Float16 *wo;
+  float *h;
+  int ldh;
+  int rows_per_block;
+};
+
+template <int HD, int MT>
+__global__ __launch_bounds__(256) void k_merge_wo(MergeWoP p) {
+  constexpr int PARTS = 256 / HD;          // thread groups splitting the chunks
+  constexpr int LPR = HD / 8;              // lanes per WO row segment (8 halves each)
+  constexpr int RPI = 64 / LPR;            // WO rows per wavefront load
+  constexpr int WI = wo_loads_per_wave(HD);  // WO loads per wavefront
+  __shared__ float sW[kMaxMergeChunks];
+  __shared__ float sRed[2][4];
+  __shared__ float sAcc[PARTS][HD];
+  __shared__ __attribute__((aligned(16))) float sO[MT * HD];
+  const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
+  const int rc = blockIdx.x, head = blockIdx.y;
+  const int G = p.d.group, g = head / G, hg = head - g * G;
+  const int H = p.d.H, nhd = p.d.nh * HD;
+
+  const int r0 = rc * p.rows_per_block;
+  const int rend = min(H, r0 + p.rows_per_block);
+  const int kc = lane % LPR;
+  h8 wreg[WI];
+#pragma unroll
+  for (int i = 0; i < WI; ++i) {
+    const int row = r0 + (w * WI + i) * RPI + lane / LPR;
+    wreg[i] = __builtin_nontemporal_load(
+        (const h8 *)(p.wo + (size_t)min(row, H - 1) * nhd + (size_t)head * HD + kc * 8));
+  }
+
+  const int rec = attn_rec_floats(G, HD);
+  const int om = G * HD, ol = G * HD + G;  // offsets of the maxima and the exp-sums
+  const int M_rows = MT == 1 ? 1 : p.M;
+  for (int m = 0; m < M_rows; ++m) {
+    const int P = p.rows.pos[m] + 1;
+    const int nch = (P + kChunkKeys - 1) / kChunkKeys;
+    const float *base = p.part.buf + ((size_t)m * p.d.nkv + g) * p.part.n_chunks * rec;
+    float mx = kNegInf;
+    for (int c = tid; c < nch; c += 256) mx = fmaxf(mx, base[(size_t)c * rec + om + hg]);
+    mx = wave_max(mx);
+    __syncthreads();  // (the previous row's reads of sW, sAcc and sRed are done)
+    if (lane == 0) sRed[0][w] = mx;
+    __syncthreads();
+    const float Mx = fmaxf(fmaxf(sRed[0][0], sRed[0][1]), fmaxf(sRed[0][2], sRed[0][3]));
+    float l = 0.f;
+    for (int c = tid; c < nch; c += 256) {
+      const float *r = base + (size_t)c * rec;
+      const float wgt = __expf(r[om + hg] - Mx);
+      sW[c] = wgt;
+      l = fmaf(r[ol + hg], wgt, l);
+    }
+    l = wave_sum(l);
+    if (lane == 0) sRed[1][w] = l;
+    __syncthreads();
+    const float L = (sRed[1][0] + sRed[1][1]) + (sRed[1][2] + sRed[1][3]);
+    const int dd = tid % HD, part = tid / HD;
+    float acc = 0.f;
+    const float *ob = base + (size_t)hg * HD + dd;
+#pragma unroll 4
+    for (int c = part; c < nch; c += PARTS) acc = fmaf(ob[(size_t)c * rec], sW[c], acc);
+    sAcc[part][dd] = acc;
+    __syncthreads();
+    if (tid < HD) {
+      float v = 0.f;
+#pragma unroll
+      for (int q = 0; q < PARTS; ++q) v += sAcc[q][tid];
+      sO[m * HD + tid] = v / L;
+    }
+  }
+  __syncthreads();
+
+  // WO slice times the head outputs; partial row sums added into the residual
+#pragma unroll
+  for (int i = 0; i < WI; ++i) {
+    const int row = r0 + (w * WI + i) * RPI + lane / LPR;
+#pragma unroll
+    for (int m = 0; m < MT; ++m) {
+      if (m < p.M) {
+        const f4 o0 = *(const f4 *)(sO + m * HD + kc * 8);
+        const f4 o1 = *(const f4 *)(sO + m * HD + kc * 8 + 4);
+        float a = (float)wreg[i][0] * o0.x;
+        a = fmaf((float)wreg[i][1], o0.y, a);
+        a = fmaf((float)wreg[i][2], o0.z, a);
+        a = fmaf((float)wreg[i][3], o0.w, a);
+        a = fmaf((float)wreg[i][4], o1.x, a);
+        a = fmaf((float)wreg[i][5], o1.y, a);
+        a = fmaf((float)wreg[i][6], o1.z, a);
+        a = fmaf((float)wreg[i][7], o1.w, a);
+        a = group_sum<LPR>(a);
+        if (kc == 0 && row < rend) atomicAdd(p.h + (size_t)m * p.ldh + row, a);
+      }
+    }
+  }
+}
+
+template <int HD>
+static void merge_wo_hd(const MergeWoP &p, int grid_x, hipStream_t st) {
+  dim3 grid(grid_x, p.d.nh);
+  if (p.M <= 1)
+    hipLaunchKernelGGL((k_merge_wo<HD, 1>), grid, dim3(256), 0, st, p);
+  else
+    hipLaunchKernelGGL((k_merge_wo<HD, 8>), grid, dim3(256), 0, st, p);
+}
+
+void merge_wo(const Dims &d, const AttnPartials &part, RowInfo rows, int M, const uint16_t *wo,
+              float *h, int ldh, hipStream_t st) {
+  const int rpb = 4 * wo_loads_per_wave(d.hd) * (64 / (d.hd / 8));  // WO rows per block
+  const MergeWoP p{d, part, rows, M, (const _Float16 *)wo, h, ldh, rpb};
+  const int gx = (d.H + rpb - 1) / rpb;
+  switch (d.hd) {
+    case 16: merge_wo_hd<16>(p, gx, st); break;
+    case 64: merge_wo_hd<64>(p, gx, st); break;
+    default: merge_wo_hd<128>(p, gx, st); break;
+  }
+}
+
 template <int HD, int G>
 static void attn_decode_g(const AttnDecP &p, int M, int n_chunks, bool merge, hipStream_t st) {
   if (n_chunks <= 1) {

@@ -152,6 +152,11 @@ constexpr int kFusedKeys = 1024;
 constexpr int wo_loads_per_wave(int hd) { return hd == 64 ? 2 : 8; }
 void attn_wo_fused(const Dims &d, int layer, const KVCache &kv, const float *q, int ldq,
                    RowInfo rows, int M, const uint16_t *wo, float *h, int ldh, hipStream_t st);
+// The chunk records of attn_decode (merge = false) of M <= 8 rows merged
+// and multiplied by WO, the partial row sums added into h with float
+// atomics: per (WO row chunk, query head) block as in attn_wo_fused.
+void merge_wo(const Dims &d, const AttnPartials &p, RowInfo rows, int M, const uint16_t *wo,
+              float *h, int ldh, hipStream_t st);
 // Causal flash attention over MFMA for one prefill pass of M rows of
 // sequence `seq` (positions strictly increasing; host_pos = their host copy,
 // which sizes the work split), on the binary16 mirror of the cache.  Long

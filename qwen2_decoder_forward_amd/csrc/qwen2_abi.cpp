@@ -419,7 +419,8 @@ struct OpTimer {
 // Attention then WO + residual on the GEMV path (M <= 8 rows, q in q32,
 // output added to rows h).  Short contexts run one fused kernel (head
 // attention times a WO slice, atomically added to h); longer ones run the
-// chunked attention with its merge kernel, then the WO GEMV.
+// chunked attention, then one kernel that merges its chunk records and
+// multiplies by WO the same way.
 void attn_wo_gemv(qwen2_ctx *c, int l, const float *q, q2::RowInfo rows, int M, int n_chunks,
                   float *h, hipStream_t st) {
   const Dims &d = c->d;
@@ -430,9 +431,9 @@ void attn_wo_gemv(qwen2_ctx *c, int l, const float *q, q2::RowInfo rows, int M, 
     TIMED(QWEN2_OP_ATTN, q2::attn_wo_fused(d, l, kv, q, nhd, rows, M, w.wo, h, d.H, st));
     return;
   }
-  TIMED(QWEN2_OP_ATTN, q2::attn_decode(d, l, kv, q, nhd, rows, M, n_chunks, true, c->part,
-                                       c->o32, nullptr, nhd, st));
-  TIMED(QWEN2_OP_WO, q2::gemv_resid(w.wo, d.H, nhd, c->o32, nhd, M, h, d.H, st));
+  TIMED(QWEN2_OP_ATTN, q2::attn_decode(d, l, kv, q, nhd, rows, M, n_chunks, false, c->part,
+                                       nullptr, nullptr, nhd, st));
+  TIMED(QWEN2_OP_WO, q2::merge_wo(d, c->part, rows, M, w.wo, h, d.H, st));
 }
 
 q2::QkvEpi qkv_epi(qwen2_ctx *c, int l, const int *pos, const int *seq) {
