@@ -147,8 +147,11 @@ void attn_decode(const Dims &d, int layer, const KVCache &kv, const float *q, in
 // into h with float atomics.  A block's WO chunk is 4 wavefronts x
 // wo_loads_per_wave(hd) loads x 512 / hd rows: hd 64 takes 64-row chunks, so
 // 14 heads x 14 chunks of the 0.5B shape spread the (repeated) K/V reads of
-// a head over 196 blocks (measured faster than 32, 128 or 256 rows).
-constexpr int kFusedKeys = 1024;
+// a head over 196 blocks (measured faster than 32, 128 or 256 rows).  Every
+// block reads all of its head's keys, so from about 512 positions on the
+// chunked attention with merge_wo is faster (0.5B decode at positions
+// 400 / 700: 1,857 / 1,631 tok/s fused against 1,782 / 1,729 chunked).
+constexpr int kFusedKeys = 512;
 constexpr int wo_loads_per_wave(int hd) { return hd == 64 ? 2 : 8; }
 void attn_wo_fused(const Dims &d, int layer, const KVCache &kv, const float *q, int ldq,
                    RowInfo rows, int M, const uint16_t *wo, float *h, int ldh, hipStream_t st);
