@@ -149,7 +149,8 @@ __global__ __launch_bounds__(256) void k_attn_decode(AttnDecP p) {
 // per thread) and kept in LDS, then each output dimension is summed over the
 // chunks by HD-thread groups that split the chunk range, and the groups'
 // sums are added through LDS.  (A thread per output walking every chunk in
-// turn took 60 us per layer at 4096 positions.)
+// turn took 60 us per layer at 4096 positions.)  k_merge_wo merges the same
+// way.
 template <int HD>
 __global__ __launch_bounds__(256) void k_attn_merge(AttnDecP p) {
   constexpr int PARTS = 256 / HD;  // thread groups splitting the chunks
@@ -164,37 +165,44 @@ __global__ __launch_bounds__(256) void k_attn_merge(AttnDecP p) {
   const int rec = attn_rec_floats(G, HD);
   const float *base = p.part.buf + ((size_t)m * p.d.nkv + g) * p.part.n_chunks * rec;
   const int om = G * HD, ol = G * HD + G;  // offsets of the maxima and the exp-sums
+  const int lane = tid & 63, w = tid >> 6;
 
+  // The first CB chunks of each thread group's share are loaded together
+  // with the maxima and exp-sums, all at clamped chunks (a load tied to a
+  // condition is waited for on the spot): one memory round trip for up to
+  // PARTS CB chunks; longer rows read the rest after.
+  constexpr int CB = HD >= 64 ? 32 : 8;
+  const int dd = tid % HD, part = tid / HD;
+  const float *ob = base + (size_t)hg * HD + dd;
+  const float mc = base[(size_t)min(tid, nch - 1) * rec + om + hg];
+  const float lc = base[(size_t)min(tid, nch - 1) * rec + ol + hg];
+  float ov[CB];
+#pragma unroll
+  for (int i = 0; i < CB; ++i) ov[i] = ob[(size_t)min(part + PARTS * i, nch - 1) * rec];
   float mx = kNegInf;
-  for (int c = tid; c < nch; c += 256) mx = fmaxf(mx, base[(size_t)c * rec + om + hg]);
-  sRed[tid] = mx;
+  for (int c = tid; c < nch; c += 256) mx = fmaxf(mx, c == tid ? mc : base[(size_t)c * rec + om + hg]);
+  mx = wave_max(mx);
+  if (lane == 0) sRed[w] = mx;
   __syncthreads();
-  for (int o = 128; o > 0; o >>= 1) {
-    if (tid < o) sRed[tid] = fmaxf(sRed[tid], sRed[tid + o]);
-    __syncthreads();
-  }
-  const float M = sRed[0];
-  __syncthreads();
+  const float M = fmaxf(fmaxf(sRed[0], sRed[1]), fmaxf(sRed[2], sRed[3]));
   float l = 0.f;
   for (int c = tid; c < nch; c += 256) {
     const float *r = base + (size_t)c * rec;
-    const float wgt = __expf(r[om + hg] - M);
+    const float wgt = __expf((c == tid ? mc : r[om + hg]) - M);
     sW[c] = wgt;
-    l = fmaf(r[ol + hg], wgt, l);
+    l = fmaf(c == tid ? lc : r[ol + hg], wgt, l);
   }
-  sRed[tid] = l;
+  l = wave_sum(l);
+  if (lane == 0) sRed[4 + w] = l;
   __syncthreads();
-  for (int o = 128; o > 0; o >>= 1) {
-    if (tid < o) sRed[tid] += sRed[tid + o];
-    __syncthreads();
-  }
-  const float L = sRed[0];
+  const float L = (sRed[4] + sRed[5]) + (sRed[6] + sRed[7]);
 
-  const int dd = tid % HD, part = tid / HD;
   float acc = 0.f;
-  const float *ob = base + (size_t)hg * HD + dd;
+#pragma unroll
+  for (int i = 0; i < CB; ++i)
+    if (part + PARTS * i < nch) acc = fmaf(ov[i], sW[part + PARTS * i], acc);
 #pragma unroll 4
-  for (int c = part; c < nch; c += PARTS) acc = fmaf(ob[(size_t)c * rec], sW[c], acc);
+  for (int c = part + PARTS * CB; c < nch; c += PARTS) acc = fmaf(ob[(size_t)c * rec], sW[c], acc);
   sAcc[part][dd] = acc;
   __syncthreads();
   if (tid < HD) {
@@ -482,13 +490,26 @@ __global__ __launch_bounds__(256) void k_merge_wo(MergeWoP p) {
 
   const int rec = attn_rec_floats(G, HD);
   const int om = G * HD, ol = G * HD + G;  // offsets of the maxima and the exp-sums
+  // The first CB chunks of each thread group's share are loaded together
+  // with the maxima and exp-sums (one memory round trip for up to PARTS CB
+  // chunks: 64 at hd 128, 128 at hd 64); longer rows read the rest after.
+  constexpr int CB = HD >= 64 ? 32 : 8;
+  const int dd = tid % HD, part = tid / HD;
   const int M_rows = MT == 1 ? 1 : p.M;
   for (int m = 0; m < M_rows; ++m) {
     const int P = p.rows.pos[m] + 1;
     const int nch = (P + kChunkKeys - 1) / kChunkKeys;
     const float *base = p.part.buf + ((size_t)m * p.d.nkv + g) * p.part.n_chunks * rec;
+    const float *ob = base + (size_t)hg * HD + dd;
+    // (unconditional loads at clamped chunks: a load tied to a condition is
+    // waited for on the spot; only chunks < nch are used)
     float mx = kNegInf;
-    for (int c = tid; c < nch; c += 256) mx = fmaxf(mx, base[(size_t)c * rec + om + hg]);
+    const float mc = base[(size_t)min(tid, nch - 1) * rec + om + hg];
+    const float lc = base[(size_t)min(tid, nch - 1) * rec + ol + hg];
+    float ov[CB];
+#pragma unroll
+    for (int i = 0; i < CB; ++i) ov[i] = ob[(size_t)min(part + PARTS * i, nch - 1) * rec];
+    for (int c = tid; c < nch; c += 256) mx = fmaxf(mx, c == tid ? mc : base[(size_t)c * rec + om + hg]);
     mx = wave_max(mx);
     __syncthreads();  // (the previous row's reads of sW, sAcc and sRed are done)
     if (lane == 0) sRed[0][w] = mx;
@@ -497,19 +518,20 @@ __global__ __launch_bounds__(256) void k_merge_wo(MergeWoP p) {
     float l = 0.f;
     for (int c = tid; c < nch; c += 256) {
       const float *r = base + (size_t)c * rec;
-      const float wgt = __expf(r[om + hg] - Mx);
+      const float wgt = __expf((c == tid ? mc : r[om + hg]) - Mx);
       sW[c] = wgt;
-      l = fmaf(r[ol + hg], wgt, l);
+      l = fmaf(c == tid ? lc : r[ol + hg], wgt, l);
     }
     l = wave_sum(l);
     if (lane == 0) sRed[1][w] = l;
     __syncthreads();
     const float L = (sRed[1][0] + sRed[1][1]) + (sRed[1][2] + sRed[1][3]);
-    const int dd = tid % HD, part = tid / HD;
     float acc = 0.f;
-    const float *ob = base + (size_t)hg * HD + dd;
+#pragma unroll
+    for (int i = 0; i < CB; ++i)
+      if (part + PARTS * i < nch) acc = fmaf(ov[i], sW[part + PARTS * i], acc);
 #pragma unroll 4
-    for (int c = part; c < nch; c += PARTS) acc = fmaf(ob[(size_t)c * rec], sW[c], acc);
+    for (int c = part + PARTS * CB; c < nch; c += PARTS) acc = fmaf(ob[(size_t)c * rec], sW[c], acc);
     sAcc[part][dd] = acc;
     __syncthreads();
     if (tid < HD) {
