@@ -314,7 +314,7 @@ def main():
         "decode_hbm_frac": dec_gbs / HBM_PEAK_GBS,
         "wall_s_timed": wall,
         "roofline": {
-            "kernel": "k_gemv<1,4,EPI_SWIGLU> (RMSNorm + gate/up + SwiGLU, decode M=1)",
+            "kernel": "k_gemv1<4,2,EPI_SWIGLU> (RMSNorm + gate/up + SwiGLU, decode M=1)",
             "bound": "hbm", "achieved": achieved, "peak": HBM_PEAK_GBS, "unit": "GB/s",
             "frac": achieved / HBM_PEAK_GBS, "traffic": gateup_traffic(shape),
             "bytes_per_launch": gu_bytes, "avg_launch_us": gu_avg_s * 1e6, "launches_timed": reps,
