@@ -111,6 +111,14 @@ int qwen2_check_hparams(const qwen2_hparams *hp);
 int qwen2_check_prefill(const qwen2_hparams *hp, int32_t seq, const int32_t *tokens,
                         const int32_t *positions, int32_t n);
 
+/* Host-side validation of a batched prefill, as qwen2_prefill_batch performs
+ * it.  Order: E_ARG (n_batch <= 0, a null pointer, a length <= 0, more than
+ * 2^31 - 1 rows), E_SEQ (range, then repeats), then each sequence in turn as
+ * qwen2_check_prefill checks it. */
+int qwen2_check_prefill_batch(const qwen2_hparams *hp, int32_t n_batch, const int32_t *seq_ids,
+                              const int32_t *lens, const int32_t *tokens,
+                              const int32_t *positions);
+
 /* Host-side validation of a decode batch, as qwen2_decode performs it.
  * Order: E_ARG, E_SEQ (range, then repeats), E_POS. */
 int qwen2_check_decode(const qwen2_hparams *hp, int32_t n_batch, const int32_t *seq_ids,
@@ -138,6 +146,29 @@ int qwen2_load(const qwen2_hparams *hp, const qwen2_weights *w, void *stream, qw
 int qwen2_prefill(qwen2_ctx *ctx, int32_t seq, const int32_t *tokens, const int32_t *positions,
                   int32_t n, float *logits_dev, int32_t *argmax_dev, void *stream);
 
+/* Runs the prompts (or continuations) of n_batch distinct sequences in one
+ * call (positions are data, so prefill, decode and continuation are one
+ * computation: minfer page, section 6).  The rows of all sequences share each projection's matrix product
+ * (passes of up to max_rows rows; a sequence may straddle two passes) and
+ * attention runs per sequence, so each sequence gets what qwen2_prefill on
+ * its own rows gives, up to rounding order.
+ *   seq_ids    host [n_batch] distinct slots in [0, n_seq)
+ *   lens       host [n_batch] rows of each sequence, each > 0
+ *   tokens, positions  host [sum of lens]: the rows of sequence b follow
+ *              those of sequence b - 1; within a sequence the rules of
+ *              qwen2_prefill hold (positions strictly increasing, each in
+ *              [0, n_ctx), K/V stored before any row attends)
+ *   logits_dev device [n_batch, n_vocab] f32 or NULL: row b is the last
+ *              row of sequence b
+ *   argmax_dev device [n_batch] int32 or NULL
+ * Every check (qwen2_check_prefill_batch) precedes any device work, so a
+ * rejected call leaves the cache untouched.  Afterwards qwen2_read_hidden
+ * returns n_batch rows.  Asynchronous on `stream`; the host arrays may be
+ * reused on return. */
+int qwen2_prefill_batch(qwen2_ctx *ctx, int32_t n_batch, const int32_t *seq_ids,
+                        const int32_t *lens, const int32_t *tokens, const int32_t *positions,
+                        float *logits_dev, int32_t *argmax_dev, void *stream);
+
 /* One decode step for n_batch distinct sequences (row b belongs to
  * seq_ids[b] at positions[b]).
  *   seq_ids, positions  host [n_batch]
@@ -152,7 +183,8 @@ int qwen2_decode(qwen2_ctx *ctx, int32_t n_batch, const int32_t *seq_ids, const 
                  const int32_t *positions, float *logits_dev, int32_t *argmax_dev, void *stream);
 
 /* Copies the read-out rows of the last prefill/decode (1 row after a
- * prefill, n_batch rows after a decode) to out_dev [rows, n_embd] f32.
+ * prefill, n_batch rows after a batched prefill or a decode) to out_dev
+ * [rows, n_embd] f32.
  * which = 0: the last layer's layer_output; 1: final_norm_output (nnterp
  * names).  Enqueued on `stream`. */
 int qwen2_read_hidden(qwen2_ctx *ctx, int32_t which, float *out_dev, void *stream);

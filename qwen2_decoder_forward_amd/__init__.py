@@ -16,8 +16,9 @@ import numpy as np
 
 __all__ = [
     "Hparams", "LayerWeights", "Weights", "Info", "Qwen2Error", "CODES", "lib", "LIB_PATH",
-    "qwen2_check_hparams", "qwen2_check_prefill", "qwen2_check_decode", "qwen2_load",
-    "qwen2_prefill", "qwen2_decode", "qwen2_read_hidden", "qwen2_kv_read", "qwen2_kv_write",
+    "qwen2_check_hparams", "qwen2_check_prefill", "qwen2_check_prefill_batch",
+    "qwen2_check_decode", "qwen2_load", "qwen2_prefill", "qwen2_prefill_batch", "qwen2_decode",
+    "qwen2_read_hidden", "qwen2_kv_read", "qwen2_kv_write",
     "qwen2_sync_status", "qwen2_info", "qwen2_last_error", "qwen2_strerror", "qwen2_free",
     "qwen2_prof_enable", "qwen2_prof_read", "qwen2_prof_repeat", "OPS", "make_hparams", "Model",
 ]
@@ -81,9 +82,11 @@ def lib() -> C.CDLL:
         sig = {
             "qwen2_check_hparams": (i32, [C.POINTER(Hparams)]),
             "qwen2_check_prefill": (i32, [C.POINTER(Hparams), i32, PI32, PI32, i32]),
+            "qwen2_check_prefill_batch": (i32, [C.POINTER(Hparams), i32, PI32, PI32, PI32, PI32]),
             "qwen2_check_decode": (i32, [C.POINTER(Hparams), i32, PI32, PI32]),
             "qwen2_load": (i32, [C.POINTER(Hparams), C.POINTER(Weights), vp, C.POINTER(vp)]),
             "qwen2_prefill": (i32, [vp, i32, PI32, PI32, i32, vp, vp, vp]),
+            "qwen2_prefill_batch": (i32, [vp, i32, PI32, PI32, PI32, PI32, vp, vp, vp]),
             "qwen2_decode": (i32, [vp, i32, PI32, vp, PI32, vp, vp, vp]),
             "qwen2_read_hidden": (i32, [vp, i32, vp, vp]),
             "qwen2_kv_read": (i32, [vp, i32, i32, i32, i32, vp, vp, vp]),
@@ -154,6 +157,27 @@ def qwen2_check_prefill(hp: Hparams, seq: int, tokens, positions) -> int:
     return lib().qwen2_check_prefill(C.byref(hp), seq, _p(t, PI32), _p(p, PI32), len(t))
 
 
+def _batch(seq_ids, tokens, positions):
+    """Flattens per-sequence lists into (seq_ids, lens, tokens, positions)."""
+    s = _i32(seq_ids)
+    if len(tokens) != len(s) or len(positions) != len(s):
+        raise ValueError("one token list and one position list per sequence")
+    t = [_i32(x) for x in tokens]
+    p = [_i32(x) for x in positions]
+    if any(len(a) != len(b) for a, b in zip(t, p)):
+        raise ValueError("tokens and positions of a sequence differ in length")
+    lens = np.array([len(a) for a in t], dtype=np.int32)
+    cat = lambda xs: np.ascontiguousarray(np.concatenate(xs) if xs else np.zeros(0, np.int32))
+    return s, lens, cat(t), cat(p)
+
+
+def qwen2_check_prefill_batch(hp: Hparams, seq_ids, tokens, positions) -> int:
+    """tokens, positions: one array per sequence."""
+    s, n, t, p = _batch(seq_ids, tokens, positions)
+    return lib().qwen2_check_prefill_batch(C.byref(hp), len(s), _p(s, PI32), _p(n, PI32),
+                                           _p(t, PI32), _p(p, PI32))
+
+
 def qwen2_check_decode(hp: Hparams, seq_ids, positions) -> int:
     s, p = _i32(seq_ids), _i32(positions)
     return lib().qwen2_check_decode(C.byref(hp), len(s), _p(s, PI32), _p(p, PI32))
@@ -191,6 +215,15 @@ def qwen2_prefill(ctx: int, seq: int, tokens, positions, logits=None, argmax=Non
     t, p = _i32(tokens), _i32(positions)
     _check(lib().qwen2_prefill(ctx, seq, _p(t, PI32), _p(p, PI32), len(t), _ptr(logits),
                                _ptr(argmax), _stream(stream)), ctx)
+
+
+def qwen2_prefill_batch(ctx: int, seq_ids, tokens, positions, logits=None, argmax=None,
+                        stream=None) -> None:
+    """tokens, positions: one array per sequence; logits [len(seq_ids), V]."""
+    s, n, t, p = _batch(seq_ids, tokens, positions)
+    _check(lib().qwen2_prefill_batch(ctx, len(s), _p(s, PI32), _p(n, PI32), _p(t, PI32),
+                                     _p(p, PI32), _ptr(logits), _ptr(argmax), _stream(stream)),
+           ctx)
 
 
 def qwen2_decode(ctx: int, seq_ids, tokens_dev, positions, logits=None, argmax=None,
@@ -263,6 +296,9 @@ class Model:
 
     def prefill(self, seq, tokens, positions, logits=None, argmax=None, stream=None):
         qwen2_prefill(self.ctx, seq, tokens, positions, logits, argmax, stream)
+
+    def prefill_batch(self, seq_ids, tokens, positions, logits=None, argmax=None, stream=None):
+        qwen2_prefill_batch(self.ctx, seq_ids, tokens, positions, logits, argmax, stream)
 
     def decode(self, seq_ids, tokens_dev, positions, logits=None, argmax=None, stream=None):
         qwen2_decode(self.ctx, seq_ids, tokens_dev, positions, logits, argmax, stream)

@@ -1,4 +1,4 @@
-// Embedding gather and row RMSNorm.
+// Embedding gather, row RMSNorm and row copies.
 #include "q2_device.h"
 
 namespace q2 {
@@ -87,6 +87,23 @@ void rmsnorm_rows_f16(float *h, int ldh, const float *w, int H, int M, float eps
                       int ldx, float *y32, const float *part, int splits, hipStream_t st) {
   hipLaunchKernelGGL(k_rmsnorm_rows, dim3(M), dim3(256), 0, st, h, ldh, w, H, M, eps, x, ldx,
                      y32, part, splits);
+}
+
+// dst[dst_rows[i]] = src[src_rows[i]] for i < k, ncols floats per row
+// (ncols a multiple of 4, row strides multiples of 4): one block per pair.
+__global__ __launch_bounds__(256) void k_copy_rows(const float *src, int lds, const int *src_rows,
+                                                   float *dst, int ldd, const int *dst_rows,
+                                                   int ncols) {
+  const float *s = src + (size_t)src_rows[blockIdx.x] * lds;
+  float *o = dst + (size_t)dst_rows[blockIdx.x] * ldd;
+  for (int k = threadIdx.x * 4; k < ncols; k += 256 * 4) *(f4 *)(o + k) = *(const f4 *)(s + k);
+}
+
+void copy_rows(const float *src, int lds, const int *src_rows, float *dst, int ldd,
+               const int *dst_rows, int k, int ncols, hipStream_t st) {
+  if (k <= 0) return;
+  hipLaunchKernelGGL(k_copy_rows, dim3(k), dim3(256), 0, st, src, lds, src_rows, dst, ldd,
+                     dst_rows, ncols);
 }
 
 }  // namespace q2

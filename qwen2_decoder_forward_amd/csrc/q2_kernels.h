@@ -121,6 +121,10 @@ void rmsnorm_rows_f16(float *h, int ldh, const float *w, int H, int M, float eps
 // [0, V) reads row 0 and sets *bad_flag to 1.
 void embed_rows(const uint16_t *E, int H, int V, const int *const *tokens, int tok_off, int M,
                 float *h, unsigned int *bad_flag, hipStream_t st);
+// dst[dst_rows[i]] = src[src_rows[i]] (ncols floats) for the k listed pairs;
+// the row lists live on the device.
+void copy_rows(const float *src, int lds, const int *src_rows, float *dst, int ldd,
+               const int *dst_rows, int k, int ncols, hipStream_t st);
 
 // Attention.
 constexpr int kChunkKeys = 64;  // keys per block of the decode attention

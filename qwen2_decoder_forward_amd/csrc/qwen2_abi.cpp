@@ -305,7 +305,7 @@ int qwen2_load(const qwen2_hparams *hp, const qwen2_weights *w, void *stream, qw
   c->rows_cap = std::max(c->max_rows, d.n_seq);
   c->dec_rows = std::max(d.n_seq, kGemvRows);
   c->part.n_chunks = (d.n_ctx + q2::kChunkKeys - 1) / q2::kChunkKeys;
-  c->io_cap = (size_t)std::max(d.n_ctx, d.n_seq);
+  c->io_cap = (size_t)std::max(d.n_ctx, c->max_rows + d.n_seq);
   const char *ng = getenv("QWEN2_NO_GRAPH");
   c->use_graphs = !(ng && ng[0] == '1');
   {
@@ -466,9 +466,17 @@ void tail_row(qwen2_ctx *c, int r, const int *pos, const int *seq, int last_pos,
   c->last_rows = 1;
 }
 
-// One pass of at most max_rows rows; `last` marks the pass that reads out.
-void prefill_pass(qwen2_ctx *c, int M, int off, const int *pos, const int *seq, int seq_id,
-                  bool last, const int32_t *host_pos, hipStream_t st) {
+// A run of rows of one sequence inside a prefill pass.
+struct Seg {
+  int r0, n, seq;
+};
+
+// One pass of at most max_rows rows (runs of rows of one or more sequences,
+// `segs`), up to and including the last layer's Q/K/V: every row's K/V is
+// then stored and, with the last layer's input norm having folded every
+// pending partial sum, h and q32 hold each row's last-layer input and query.
+void prefill_pass(qwen2_ctx *c, int M, int off, const int *pos, const int *seq,
+                  const std::vector<Seg> &segs, const int32_t *host_pos, hipStream_t st) {
   const Dims &d = c->d;
   const float eps = c->hp.rms_eps;
   const int nhd = d.nh * d.hd;
@@ -476,7 +484,9 @@ void prefill_pass(qwen2_ctx *c, int M, int off, const int *pos, const int *seq, 
   const q2::RowInfo rows{pos, seq};
   TIMED(QWEN2_OP_EMBED, q2::embed_rows(c->tok_embd, d.H, d.V, &dev_slots(c)->tokens, off, M,
                                        c->h, c->bad_flag, st));
-  const int n_chunks = chunks_for(host_pos[M - 1]);
+  int max_pos = 0;
+  for (const Seg &g : segs) max_pos = std::max(max_pos, (int)host_pos[g.r0 + g.n - 1]);
+  const int n_chunks = chunks_for(max_pos);
   const bool gemv = M <= kGemvRows;
   int pending = 0;  // split-K partial sums of the last residual GEMM not yet in h
   for (int l = 0; l < d.L; ++l) {
@@ -490,14 +500,17 @@ void prefill_pass(qwen2_ctx *c, int M, int off, const int *pos, const int *seq, 
       pending = 0;
       TIMED(QWEN2_OP_QKV, q2::gemm_qkv(d, w, c->x16, d.H, M, e, c->splitk, st));
     }
-    if (l == d.L - 1) break;  // the last layer continues on the last row only
+    if (l == d.L - 1) break;  // the last layer goes on for read-out rows only
     if (gemv) {
       attn_wo_gemv(c, l, c->q32, rows, M, n_chunks, c->h, st);
       TIMED(QWEN2_OP_GATEUP, q2::gemv_swiglu(d, w, c->h, M, c->a32, d.I_pad, eps, st));
       TIMED(QWEN2_OP_DOWN, q2::gemv_resid(w.wd, d.H, d.I_pad, c->a32, d.I_pad, M, c->h, d.H, st));
     } else {
-      TIMED(QWEN2_OP_ATTN, q2::attn_prefill(d, l, kv, c->q32, nhd, rows, M, seq_id, host_pos,
-                                            c->splitk, c->x16, nhd, st));
+      for (const Seg &g : segs)
+        TIMED(QWEN2_OP_ATTN,
+              q2::attn_prefill(d, l, kv, c->q32 + (size_t)g.r0 * nhd, nhd,
+                               q2::RowInfo{pos + g.r0, seq + g.r0}, g.n, g.seq, host_pos + g.r0,
+                               c->splitk, c->x16 + (size_t)g.r0 * nhd, nhd, st));
       TIMED(QWEN2_OP_WO, pending = q2::gemm_resid(w.wo, d.H, nhd, c->x16, nhd, M, c->h, d.H,
                                                   c->splitk, st));
       TIMED(QWEN2_OP_NORM, q2::rmsnorm_rows_f16(c->h, d.H, w.ffn_norm, d.H, M, eps, c->x16, d.H,
@@ -507,47 +520,40 @@ void prefill_pass(qwen2_ctx *c, int M, int off, const int *pos, const int *seq, 
                                                     d.H, c->splitk, st));
     }
   }
-  // (the last layer's QKV norm above folded every pending partial sum)
-  if (last) tail_row(c, M - 1, pos, seq, host_pos[M - 1], st);
 }
 
-// Every kernel of one decode step for B rows (replayed from a graph).
-void decode_launches(qwen2_ctx *c, int B, int n_chunks, const int *dpos, const int *dseq,
-                     hipStream_t st) {
+// Attention onwards of layer l for B rows of independent positions (their
+// K/V stored, queries in q32 rows 0..B-1, residual stream in h rows
+// 0..B-1).  Returns the split-K partial-sum sets left pending in h.
+int rows_rest(qwen2_ctx *c, int l, int B, int n_chunks, q2::RowInfo rows, hipStream_t st) {
   const Dims &d = c->d;
   const float eps = c->hp.rms_eps;
   const int nhd = d.nh * d.hd;
-  const q2::KVCache kv = kv_of(c);
-  const q2::RowInfo rows{dpos, dseq};
-  TIMED(QWEN2_OP_EMBED, q2::embed_rows(c->tok_embd, d.H, d.V, &dev_slots(c)->tokens, 0, B, c->h,
-                                       c->bad_flag, st));
-  const bool gemv = B <= kGemvRows;
-  int pending = 0;  // split-K partial sums of the last residual GEMM not yet in h
-  for (int l = 0; l < d.L; ++l) {
-    const LayerW &w = c->layers[l];
-    const q2::QkvEpi e = qkv_epi(c, l, dpos, dseq);
-    if (gemv) {
-      TIMED(QWEN2_OP_QKV, q2::gemv_qkv(d, w, c->h, B, e, eps, st));
-      attn_wo_gemv(c, l, c->q32, rows, B, n_chunks, c->h, st);
-      TIMED(QWEN2_OP_GATEUP, q2::gemv_swiglu(d, w, c->h, B, c->a32, d.I_pad, eps, st));
-      TIMED(QWEN2_OP_DOWN, q2::gemv_resid(w.wd, d.H, d.I_pad, c->a32, d.I_pad, B, c->h, d.H, st));
-    } else {
-      TIMED(QWEN2_OP_NORM, q2::rmsnorm_rows_f16(c->h, d.H, w.attn_norm, d.H, B, eps, c->x16, d.H,
-                                                nullptr, c->splitk.buf, pending, st));
-      pending = 0;
-      TIMED(QWEN2_OP_QKV, q2::gemm_qkv(d, w, c->x16, d.H, B, e, c->splitk, st));
-      TIMED(QWEN2_OP_ATTN, q2::attn_decode(d, l, kv, c->q32, nhd, rows, B, n_chunks, true,
-                                           c->part, nullptr, c->x16, nhd, st));
-      TIMED(QWEN2_OP_WO, pending = q2::gemm_resid(w.wo, d.H, nhd, c->x16, nhd, B, c->h, d.H,
-                                                  c->splitk, st));
-      TIMED(QWEN2_OP_NORM, q2::rmsnorm_rows_f16(c->h, d.H, w.ffn_norm, d.H, B, eps, c->x16, d.H,
-                                                nullptr, c->splitk.buf, pending, st));
-      TIMED(QWEN2_OP_GATEUP, q2::gemm_swiglu(d, w, c->x16, d.H, B, c->a16, d.I_pad, c->splitk, st));
-      TIMED(QWEN2_OP_DOWN, pending = q2::gemm_resid(w.wd, d.H, d.I_pad, c->a16, d.I_pad, B, c->h,
-                                                    d.H, c->splitk, st));
-    }
+  const LayerW &w = c->layers[l];
+  if (B <= kGemvRows) {
+    attn_wo_gemv(c, l, c->q32, rows, B, n_chunks, c->h, st);
+    TIMED(QWEN2_OP_GATEUP, q2::gemv_swiglu(d, w, c->h, B, c->a32, d.I_pad, eps, st));
+    TIMED(QWEN2_OP_DOWN, q2::gemv_resid(w.wd, d.H, d.I_pad, c->a32, d.I_pad, B, c->h, d.H, st));
+    return 0;
   }
-  if (gemv) {
+  int pending;
+  TIMED(QWEN2_OP_ATTN, q2::attn_decode(d, l, kv_of(c), c->q32, nhd, rows, B, n_chunks, true,
+                                       c->part, nullptr, c->x16, nhd, st));
+  TIMED(QWEN2_OP_WO, pending = q2::gemm_resid(w.wo, d.H, nhd, c->x16, nhd, B, c->h, d.H,
+                                              c->splitk, st));
+  TIMED(QWEN2_OP_NORM, q2::rmsnorm_rows_f16(c->h, d.H, w.ffn_norm, d.H, B, eps, c->x16, d.H,
+                                            nullptr, c->splitk.buf, pending, st));
+  TIMED(QWEN2_OP_GATEUP, q2::gemm_swiglu(d, w, c->x16, d.H, B, c->a16, d.I_pad, c->splitk, st));
+  TIMED(QWEN2_OP_DOWN, pending = q2::gemm_resid(w.wd, d.H, d.I_pad, c->a16, d.I_pad, B, c->h,
+                                                d.H, c->splitk, st));
+  return pending;
+}
+
+// Final norm, lm_head and argmax of h rows 0..B-1 into the staged slots.
+void rows_head(qwen2_ctx *c, int B, int pending, hipStream_t st) {
+  const Dims &d = c->d;
+  const float eps = c->hp.rms_eps;
+  if (B <= kGemvRows) {
     TIMED(QWEN2_OP_LMHEAD, q2::gemv_lmhead(d, c->lm_head, c->out_norm, c->h, B, c->normed,
                                            argmax_epi(c), eps, st));
   } else {
@@ -555,6 +561,30 @@ void decode_launches(qwen2_ctx *c, int B, int n_chunks, const int *dpos, const i
                                               c->normed, c->splitk.buf, pending, st));
     TIMED(QWEN2_OP_LMHEAD, q2::gemm_lmhead(d, c->lm_head, c->x16, d.H, B, argmax_epi(c), st));
   }
+}
+
+// Every kernel of one decode step for B rows (replayed from a graph).
+void decode_launches(qwen2_ctx *c, int B, int n_chunks, const int *dpos, const int *dseq,
+                     hipStream_t st) {
+  const Dims &d = c->d;
+  const float eps = c->hp.rms_eps;
+  const q2::RowInfo rows{dpos, dseq};
+  TIMED(QWEN2_OP_EMBED, q2::embed_rows(c->tok_embd, d.H, d.V, &dev_slots(c)->tokens, 0, B, c->h,
+                                       c->bad_flag, st));
+  int pending = 0;  // split-K partial sums of the last residual GEMM not yet in h
+  for (int l = 0; l < d.L; ++l) {
+    const LayerW &w = c->layers[l];
+    const q2::QkvEpi e = qkv_epi(c, l, dpos, dseq);
+    if (B <= kGemvRows) {
+      TIMED(QWEN2_OP_QKV, q2::gemv_qkv(d, w, c->h, B, e, eps, st));
+    } else {
+      TIMED(QWEN2_OP_NORM, q2::rmsnorm_rows_f16(c->h, d.H, w.attn_norm, d.H, B, eps, c->x16, d.H,
+                                                nullptr, c->splitk.buf, pending, st));
+      TIMED(QWEN2_OP_QKV, q2::gemm_qkv(d, w, c->x16, d.H, B, e, c->splitk, st));
+    }
+    pending = rows_rest(c, l, B, n_chunks, rows, st);
+  }
+  rows_head(c, B, pending, st);
 }
 
 }  // namespace
@@ -576,8 +606,78 @@ int qwen2_prefill(qwen2_ctx *c, int32_t seq, const int32_t *tokens, const int32_
   if (rc) return rc;
   for (int off = 0; off < n; off += c->max_rows) {
     const int M = std::min(c->max_rows, n - off);
-    prefill_pass(c, M, off, df[1] + off, df[2] + off, seq, off + M == n, positions + off, st);
+    prefill_pass(c, M, off, df[1] + off, df[2] + off, {Seg{0, M, seq}}, positions + off, st);
+    if (off + M == n) tail_row(c, M - 1, df[1] + off, df[2] + off, positions[n - 1], st);
   }
+  HIP_TRY(c, hipGetLastError());
+  return QWEN2_OK;
+}
+
+int qwen2_prefill_batch(qwen2_ctx *c, int32_t nb, const int32_t *seq_ids, const int32_t *lens,
+                        const int32_t *tokens, const int32_t *positions, float *logits_dev,
+                        int32_t *argmax_dev, void *stream) {
+  if (!c) return QWEN2_E_ARG;
+  std::string msg;
+  int rc = q2::check_prefill_batch(&c->hp, nb, seq_ids, lens, tokens, positions, &msg);
+  if (rc) return set_err(c, rc, msg);
+  hipStream_t st = (hipStream_t)stream;
+  const Dims &d = c->d;
+  const int nhd = d.nh * d.hd;
+  std::vector<int> end(nb);  // one past each sequence's last row
+  int total = 0;
+  for (int b = 0; b < nb; ++b) end[b] = total += lens[b];
+  // Passes of up to max_rows consecutive rows; a sequence may straddle two.
+  // At the end of each pass the residual rows and queries of the sequences
+  // whose last row it holds are set aside (normed, o32: row b for sequence
+  // b), and one read-out of all nb rows follows the last pass.
+  std::vector<int32_t> f_tok, f_pos, f_seq;
+  int b = 0;
+  for (int off = 0; off < total; off += c->max_rows) {
+    const int M = std::min(c->max_rows, total - off);
+    std::vector<Seg> segs;
+    std::vector<int32_t> src, dst;
+    for (int r = off; r < off + M;) {
+      while (end[b] <= r) ++b;
+      const int stop = std::min(end[b], off + M);
+      segs.push_back(Seg{r - off, stop - r, seq_ids[b]});
+      if (stop == end[b]) {
+        src.push_back(stop - 1 - off);
+        dst.push_back(b);
+      }
+      r = stop;
+    }
+    const int k = (int)src.size();
+    f_tok.assign(tokens + off, tokens + off + M);
+    f_pos.assign(positions + off, positions + off + M);
+    f_seq.clear();
+    for (const Seg &g : segs) f_seq.insert(f_seq.end(), g.n, g.seq);
+    f_tok.insert(f_tok.end(), src.begin(), src.end());
+    f_pos.insert(f_pos.end(), dst.begin(), dst.end());
+    f_seq.resize(M + k, 0);
+    const int32_t *fields[3] = {f_tok.data(), f_pos.data(), f_seq.data()};
+    int *df[3];
+    const CallSlots slots{(const int *)(c->io + kSlotBytes), nullptr, nullptr};
+    rc = stage_call(c, st, slots, M + k, 3, fields, df);
+    if (rc) return rc;
+    prefill_pass(c, M, 0, df[1], df[2], segs, positions + off, st);
+    q2::copy_rows(c->h, d.H, df[0] + M, c->normed, d.H, df[1] + M, k, d.H, st);
+    q2::copy_rows(c->q32, nhd, df[0] + M, c->o32, nhd, df[1] + M, k, nhd, st);
+  }
+  // read-out: the last layer from attention on, for the last row of each sequence
+  std::vector<int32_t> t_pos(nb), t_seq(seq_ids, seq_ids + nb);
+  for (int i = 0; i < nb; ++i) t_pos[i] = positions[end[i] - 1];
+  const int32_t *fields[2] = {t_pos.data(), t_seq.data()};
+  int *df[2];
+  const CallSlots slots{nullptr, logits_dev, argmax_dev};
+  rc = stage_call(c, st, slots, nb, 2, fields, df);
+  if (rc) return rc;
+  HIP_TRY(c, hipMemcpyAsync(c->h, c->normed, (size_t)nb * d.H * 4, hipMemcpyDeviceToDevice, st));
+  HIP_TRY(c, hipMemcpyAsync(c->q32, c->o32, (size_t)nb * nhd * 4, hipMemcpyDeviceToDevice, st));
+  const int n_chunks = chunks_for(*std::max_element(t_pos.begin(), t_pos.end()));
+  const int pending = rows_rest(c, d.L - 1, nb, n_chunks, q2::RowInfo{df[0], df[1]}, st);
+  rows_head(c, nb, pending, st);
+  c->last_h = c->h;
+  c->last_rows = nb;
   HIP_TRY(c, hipGetLastError());
   return QWEN2_OK;
 }

@@ -91,6 +91,34 @@ int check_decode(const qwen2_hparams *hp, int32_t n_batch, const int32_t *seq_id
   return QWEN2_OK;
 }
 
+int check_prefill_batch(const qwen2_hparams *hp, int32_t n_batch, const int32_t *seq_ids,
+                        const int32_t *lens, const int32_t *tokens, const int32_t *positions,
+                        std::string *msg) {
+  if (!hp || n_batch <= 0 || !seq_ids || !lens || !tokens || !positions)
+    return fail(msg, QWEN2_E_ARG, "empty prefill batch or null pointer");
+  int64_t total = 0;
+  for (int32_t b = 0; b < n_batch; ++b) {
+    if (lens[b] <= 0) return fail(msg, QWEN2_E_ARG, "sequence %lld of the batch has no rows", b);
+    total += lens[b];
+  }
+  if (total > INT32_MAX) return fail(msg, QWEN2_E_ARG, "more than 2^31 - 1 rows in one batch");
+  for (int32_t b = 0; b < n_batch; ++b)
+    if (seq_ids[b] < 0 || seq_ids[b] >= hp->n_seq)
+      return fail(msg, QWEN2_E_SEQ, "sequence %lld not in [0, %lld)", seq_ids[b], hp->n_seq);
+  std::vector<char> seen(hp->n_seq, 0);
+  for (int32_t b = 0; b < n_batch; ++b) {
+    if (seen[seq_ids[b]]) return fail(msg, QWEN2_E_SEQ, "sequence %lld repeated in one batch", seq_ids[b]);
+    seen[seq_ids[b]] = 1;
+  }
+  int64_t off = 0;
+  for (int32_t b = 0; b < n_batch; ++b) {
+    int rc = check_prefill(hp, seq_ids[b], tokens + off, positions + off, lens[b], msg);
+    if (rc) return rc;
+    off += lens[b];
+  }
+  return QWEN2_OK;
+}
+
 }  // namespace q2
 
 extern "C" {
@@ -102,6 +130,14 @@ int qwen2_check_prefill(const qwen2_hparams *hp, int32_t seq, const int32_t *tok
   int rc = q2::check_hparams(hp, nullptr);
   if (rc) return rc;
   return q2::check_prefill(hp, seq, tokens, positions, n, nullptr);
+}
+
+int qwen2_check_prefill_batch(const qwen2_hparams *hp, int32_t n_batch, const int32_t *seq_ids,
+                              const int32_t *lens, const int32_t *tokens,
+                              const int32_t *positions) {
+  int rc = q2::check_hparams(hp, nullptr);
+  if (rc) return rc;
+  return q2::check_prefill_batch(hp, n_batch, seq_ids, lens, tokens, positions, nullptr);
 }
 
 int qwen2_check_decode(const qwen2_hparams *hp, int32_t n_batch, const int32_t *seq_ids,

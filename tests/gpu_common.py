@@ -65,6 +65,15 @@ class Pair:
         torch.cuda.synchronize()
         return self.logits[0].cpu().numpy(), int(self.ids[0].item()), r
 
+    def prefill_batch(self, seqs, toks, poss):
+        """One batched call on the GPU; the oracle runs each sequence's prefill
+        on its own (a batch is defined as those independent prefills)."""
+        B = len(seqs)
+        self.m.prefill_batch(seqs, toks, poss, self.logits[:B], self.ids[:B])
+        rs = [self.o.prefill(s, t, p) for s, t, p in zip(seqs, toks, poss)]
+        torch.cuda.synchronize()
+        return self.logits[:B].cpu().numpy(), self.ids[:B].cpu().numpy(), rs
+
     def decode(self, seqs, toks, pos):
         B = len(seqs)
         tdev = torch.tensor(np.asarray(toks, np.int32), device=DEV)

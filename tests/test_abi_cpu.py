@@ -85,6 +85,43 @@ def test_validation_matches_oracle():
         assert got == want, (seqs, pos, got, want)
 
 
+def test_batch_validation():
+    """A batched prefill is valid exactly when its slots are distinct and each
+    sequence would pass qwen2_check_prefill on its own; errors report in the
+    header's order (arguments, slots, then sequence by sequence)."""
+    shape = syn.MODELS["tiny"]
+    hp = hp_for(shape)  # n_ctx 16, n_seq 2
+    V = shape.n_vocab
+    cases = [
+        (([0, 1], [[1, 2], [3]], [[0, 1], [5]]), "OK"),
+        (([1], [[1]], [[15]]), "OK"),
+        (([], [], []), "E_ARG"),
+        (([0, 1], [[1], []], [[0], []]), "E_ARG"),          # an empty sequence
+        (([0, 0], [[1], [2]], [[0], [1]]), "E_SEQ"),        # repeated slot
+        (([0, 2], [[1], [2]], [[0], [1]]), "E_SEQ"),        # slot out of range
+        (([0, 0], [[V], [2]], [[0], [1]]), "E_SEQ"),        # slots before tokens
+        (([0, 1], [[1], [V]], [[0], [1]]), "E_TOKEN"),
+        (([0, 1], [[1], [2]], [[0], [16]]), "E_POS"),
+        (([0, 1], [[1, 2], [2]], [[3, 3], [1]]), "E_ORDER"),
+        (([1, 0], [[1, V], [2]], [[0, 1], [-1]]), "E_TOKEN"),  # the first bad sequence reports
+        (([1, 0], [[1, 2], [V]], [[1, 0], [1]]), "E_ORDER"),
+    ]
+    for (seqs, toks, pos), want in cases:
+        got = q.CODES[q.qwen2_check_prefill_batch(hp, seqs, toks, pos)]
+        assert got == want, (seqs, toks, pos, got, want)
+    # when every slot is distinct, the batch's verdict is that of the first
+    # failing sequence checked alone
+    rng = np.random.default_rng(5)
+    for _ in range(200):
+        nb = int(rng.integers(1, 3))
+        seqs = list(rng.permutation(2)[:nb])
+        toks = [list(rng.integers(-1, V + 1, rng.integers(1, 4))) for _ in range(nb)]
+        pos = [sorted(rng.integers(-1, 17, len(t))) for t in toks]
+        singles = [q.CODES[q.qwen2_check_prefill(hp, s, t, p)] for s, t, p in zip(seqs, toks, pos)]
+        want = next((c for c in singles if c != "OK"), "OK")
+        assert q.CODES[q.qwen2_check_prefill_batch(hp, seqs, toks, pos)] == want
+
+
 @pytest.mark.parametrize("change,ok", [
     ({}, True),
     ({"n_head_kv": 3}, False),             # n_head % n_head_kv

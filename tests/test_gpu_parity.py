@@ -170,6 +170,86 @@ def test_multi_pass_prefill(tiny_w):
     p.close()
 
 
+def _check_batch(p, seqs, toks, poss, tol, what):
+    lg, ids, rs = p.prefill_batch(seqs, toks, poss)
+    h = p.hidden(0, len(seqs))
+    for b, r in enumerate(rs):
+        check(lg[b], r.logits[0], tol, f"{what}: logits of sequence {seqs[b]}")
+        check_id(ids[b], r.logits[0], r.argmax[0], f"{what}: id of sequence {seqs[b]}")
+        check(h[b], r.layer_output[0], tol, f"{what}: layer_output of sequence {seqs[b]}")
+
+
+def test_prefill_batch_gemv_rows(tiny_w):
+    """A batched prefill of 6 rows in all (the f32 GEMV path and a 3-row
+    read-out): a continuation after an earlier prefill, gapped positions and
+    a one-row sequence, in an order unlike the slot order."""
+    p = Pair(TINY, tiny_w, n_ctx=64, n_seq=4)
+    p.prefill(2, syn.make_prompt(TINY, 5, 21), np.arange(5))
+    seqs = [2, 0, 3]
+    toks = [syn.make_prompt(TINY, 2, 22), syn.make_prompt(TINY, 3, 23), [7]]
+    poss = [[5, 6], [0, 3, 9], [0]]
+    _check_batch(p, seqs, toks, poss, TOL_F32, "batch-gemv")
+    # the cache now continues with a decode of every sequence
+    lg, ids, r = p.decode(seqs, [1, 2, 3], [7, 10, 1])
+    for b in range(3):
+        check(lg[b], r.logits[b], TOL_F32, f"decode after the batch, row {b}")
+    p.close()
+
+
+@pytest.mark.parametrize("lens", [[1, 40, 2, 33, 9, 1, 64, 5, 17, 3, 8, 31],
+                                  [300, 1, 700, 45]])
+def test_prefill_batch_mfma_rows(tiny_w, lens):
+    """Batched prefills on the MFMA path: one-row, ragged and multi-tile
+    sequences sharing each GEMM; 12 read-out rows take the MFMA read-out,
+    4 the GEMV one; some sequences continue an earlier prefill."""
+    B = len(lens)
+    p = Pair(TINY, tiny_w, n_ctx=1024, n_seq=16)
+    start = [0] * B
+    for b in range(0, B, 3):
+        start[b] = 11 + b
+        p.prefill(b, syn.make_prompt(TINY, start[b], 40 + b), np.arange(start[b]))
+    seqs = list(range(B))[::-1]
+    toks = [syn.make_prompt(TINY, lens[s], 60 + s) for s in seqs]
+    poss = [np.arange(start[s], start[s] + lens[s]) for s in seqs]
+    _check_batch(p, seqs, toks, poss, TOL, f"batch-mfma-{B}")
+    p.close()
+
+
+def test_prefill_batch_straddles_passes(tiny_w):
+    """5,030 rows in all: the 4,096-row first pass ends inside the second
+    sequence, whose rows continue in the next pass."""
+    p = Pair(TINY, tiny_w, n_ctx=4096, n_seq=3)
+    lens = [3000, 2000, 30]
+    seqs = [1, 0, 2]
+    toks = [syn.make_prompt(TINY, n, 80 + i) for i, n in enumerate(lens)]
+    poss = [np.arange(n) for n in lens]
+    _check_batch(p, seqs, toks, poss, TOL, "batch-passes")
+    p.close()
+
+
+def test_prefill_batch_rejects_before_any_work(tiny_w):
+    """A repeated slot or a bad position anywhere in the batch fails the whole
+    call before anything is enqueued: the cache keeps its contents."""
+    import qwen2_decoder_forward_amd as q
+    p = Pair(TINY, tiny_w, n_ctx=64, n_seq=3)
+    p.prefill(0, [1, 2, 3], [0, 1, 2])
+    nkv, hd = TINY.n_head_kv, TINY.head_dim
+    k0 = torch.empty((nkv, 64, hd), device=DEV)
+    v0 = torch.empty((nkv, 64, hd), device=DEV)
+    p.m.kv_read(0, 0, 0, 64, k0, v0)
+    for seqs, toks, poss, code in [([0, 0], [[4], [5]], [[3], [4]], "E_SEQ"),
+                                   ([0, 1], [[4], [5, 6]], [[3], [0, 64]], "E_POS")]:
+        with pytest.raises(q.Qwen2Error) as ei:
+            p.m.prefill_batch(seqs, toks, poss, p.logits[:2], p.ids[:2])
+        assert ei.value.name == code
+    k1 = torch.empty_like(k0)
+    v1 = torch.empty_like(v0)
+    p.m.kv_read(0, 0, 0, 64, k1, v1)
+    torch.cuda.synchronize()
+    assert torch.equal(k0, k1) and torch.equal(v0, v1)
+    p.close()
+
+
 HD128 = dataclasses.replace(syn.MODELS["qwen2-hd128"], name="hd128-narrow", n_layer=2,
                             n_embd=896, n_head=7, n_head_kv=1, n_ff=640, n_vocab=4096)
 
