@@ -209,13 +209,25 @@ def main():
     pos_prompt = np.arange(n, dtype=np.int32)
 
     if batched:
-        # setup (untimed): every sequence slot holds a prefix of n tokens
+        # setup (outside the decode timing): every sequence slot holds a
+        # prefix of n tokens, written one sequence per call and by one
+        # batched call, each twice (the same values, up to rounding order)
         prompts = [syn.make_prompt(shape, n, 100 + j) for j in range(n_seq)]
-        for j in range(n_seq):
-            model.prefill(j, prompts[j], pos_prompt, None, None)
-        torch.cuda.synchronize()
-        log(f"[{wl.name}] {n_seq} prefixes of {n} tokens prefilled")
         seqs = list(range(n_seq))
+        setup = {}
+        for kind in ("per_sequence", "batched") * 2:  # the second round counts
+            torch.cuda.synchronize()
+            t_setup = time.perf_counter()
+            if kind == "batched":
+                model.prefill_batch(seqs, prompts, [pos_prompt] * n_seq)
+            else:
+                for j in range(n_seq):
+                    model.prefill(j, prompts[j], pos_prompt, None, None)
+            torch.cuda.synchronize()
+            setup[kind] = n_seq * n / (time.perf_counter() - t_setup)
+        log(f"[{wl.name}] {n_seq} prefixes of {n} tokens prefilled: "
+            f"{setup['per_sequence']:.0f} tok/s one sequence per call, "
+            f"{setup['batched']:.0f} tok/s in one batched call")
         toks = torch.tensor(syn.make_prompt(shape, n_seq, 999), dtype=torch.int32, device=dev)
         logits = torch.empty((n_seq, V), dtype=torch.float32, device=dev)
         ids = torch.zeros(n_seq, dtype=torch.int32, device=dev)
@@ -322,6 +334,8 @@ def main():
         },
         "cpu_baseline": None,
     }
+    if batched:
+        out["setup_prefill_tok_s"] = setup
     if not batched:
         out["prefill_tok_s"] = n / (prefill_ms / 1e3)
         out["prefill_ms"] = prefill_ms

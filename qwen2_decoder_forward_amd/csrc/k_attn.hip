@@ -688,24 +688,34 @@ void kv_mirror(const Dims &d, const KVCache &kv, int layer, int seq, int pos0, i
   }
 }
 
+// One sequence's share of a prefill-attention launch: rows r0 .. r0+M-1 of
+// the pass, its (layer, sequence) block of the mirror, and its work split.
+struct PreSeg {
+  int r0, M;
+  // causal balance: query tiles split_from .. n_tiles-1 run as two blocks
+  // each (first / second half of their key tiles) whose softmax states go to
+  // part (from split record part0 on) and are combined by k_attn_prefill_merge
+  int n_tiles, split_from, part0;
+  size_t kv_off;  // element offset of the sequence's KV head 0 in either mirror
+};
+constexpr int kPreSegs = 8;  // sequences per launch
+
 struct AttnPreP {
   Dims d;
   const float *q;
   int ldq;
   RowInfo rows;
-  int M;
-  const _Float16 *k16, *v16t;  // (layer, seq, KV head 0) blocks of the mirror
+  const _Float16 *k16, *v16t;  // the layer's mirrors (sequence offsets in seg)
   size_t gstride;              // elements between KV heads in either mirror
   int ldp;
   _Float16 *o16;
   int ldo;
   float qscale;  // head_dim^-0.5 * log2(e): scores in base 2
-  // causal balance: query tiles split_from .. n_tiles-1 run as two blocks
-  // each (first / second half of their key tiles) whose softmax states go to
-  // part and are combined by k_attn_prefill_merge
-  int n_tiles, split_from;
-  float *part;  // [split tile][piece][query head][32 rows][hd + 4]: o, max, sum (base 2), pad
+  float *part;   // [split record][piece][query head][32 rows][hd + 4]: o, max, sum (base 2), pad
+  int n_seg;     // sequences in this launch; block row y is work item y / n_seg of sequence y % n_seg
+  PreSeg seg[kPreSegs];
 };
+
 
 // S = 2 (head_dim <= 64): two wavefronts per query head; the block's two
 // halves take the first and the second half of the key tiles, each with its
@@ -741,26 +751,31 @@ __global__ __launch_bounds__(64 * G * S) void k_attn_prefill(AttnPreP p) {
   // then the whole tiles (descending)
   // (the KV head is the grid's fastest index, so the dispatch order is
   // longest-first across the KV heads too)
-  const int n_split = p.n_tiles - p.split_from;
-  const int wi = blockIdx.y;  // work index
+  // (the sequences of the launch interleave, so equal work ranks of all
+  // sequences dispatch together)
+  const PreSeg &sg = p.seg[blockIdx.y % p.n_seg];
+  const int wi = blockIdx.y / p.n_seg;  // work index within the sequence
+  const int n_split = sg.n_tiles - sg.split_from;
+  if (wi >= sg.n_tiles + n_split) return;  // (a shorter sequence: no work)
   int tile, piece;
   if (wi < 2 * n_split) {
-    tile = p.n_tiles - 1 - wi / 2;
+    tile = sg.n_tiles - 1 - wi / 2;
     piece = wi & 1;
   } else {
-    tile = p.split_from - 1 - (wi - 2 * n_split);
+    tile = sg.split_from - 1 - (wi - 2 * n_split);
     piece = -1;
   }
+  const int *pos = p.rows.pos + sg.r0;
   const int g = blockIdx.x;
   const int h = g * p.d.group + blockIdx.z * G + hw;  // (blockIdx.z: G-head share of the group)
   const int r0 = tile * 32;
-  const int M = p.M;
+  const int M = sg.M;
   const int last_row = min(r0 + 31, M - 1);
-  const int kmax = p.rows.pos[last_row];
+  const int kmax = pos[last_row];
   const int qrow = r0 + (lane & 31);
   const bool qvalid = qrow < M;
-  const int qpos = qvalid ? p.rows.pos[qrow] : kmax;
-  const int qpos_min = p.rows.pos[r0];  // keys <= this are visible to every row
+  const int qpos = qvalid ? pos[qrow] : kmax;
+  const int qpos_min = pos[r0];  // keys <= this are visible to every row
   const int hi = lane >> 5;
   _Float16(&hK)[2][KT * KP] = sK[half];
   _Float16(&hV)[2][DV * VP] = sV[half];
@@ -774,7 +789,7 @@ __global__ __launch_bounds__(64 * G * S) void k_attn_prefill(AttnPreP p) {
 
   h8 qf[KSTEPS];
   {
-    const float *qp = p.q + (size_t)(qvalid ? qrow : last_row) * p.ldq + (size_t)h * HD;
+    const float *qp = p.q + (size_t)(sg.r0 + (qvalid ? qrow : last_row)) * p.ldq + (size_t)h * HD;
 #pragma unroll
     for (int s = 0; s < KSTEPS; ++s)
 #pragma unroll
@@ -788,8 +803,8 @@ __global__ __launch_bounds__(64 * G * S) void k_attn_prefill(AttnPreP p) {
     for (int r = 0; r < 16; ++r) o[t][r] = 0.f;
   float m_run = kNegInf, l_run = 0.f;
 
-  const _Float16 *kg = p.k16 + (size_t)g * p.gstride;
-  const _Float16 *vg = p.v16t + (size_t)g * p.gstride;
+  const _Float16 *kg = p.k16 + sg.kv_off + (size_t)g * p.gstride;
+  const _Float16 *vg = p.v16t + sg.kv_off + (size_t)g * p.gstride;
   const int ntiles = kmax / KT + 1;
   int kb = 0, ke = ntiles;  // this block's key tiles (a split piece takes half)
   if (piece >= 0) {
@@ -956,7 +971,7 @@ __global__ __launch_bounds__(64 * G * S) void k_attn_prefill(AttnPreP p) {
   }
 
   if (piece >= 0) {  // a split piece: its (un-normalised) state for the merge
-    float *pr = p.part + ((((size_t)(tile - p.split_from) * 2 + piece) * p.d.nh + h) * 32 +
+    float *pr = p.part + ((((size_t)(sg.part0 + tile - sg.split_from) * 2 + piece) * p.d.nh + h) * 32 +
                           (lane & 31)) * (HD + 4);
 #pragma unroll
     for (int t = 0; t < DT; ++t)
@@ -973,7 +988,7 @@ __global__ __launch_bounds__(64 * G * S) void k_attn_prefill(AttnPreP p) {
   }
   if (!qvalid) return;
   const float inv_l = 1.0f / l_run;
-  _Float16 *orow = p.o16 + (size_t)qrow * p.ldo + (size_t)h * HD;
+  _Float16 *orow = p.o16 + (size_t)(sg.r0 + qrow) * p.ldo + (size_t)h * HD;
 #pragma unroll
   for (int t = 0; t < DT; ++t)
 #pragma unroll
@@ -992,20 +1007,23 @@ __global__ __launch_bounds__(64 * G * S) void k_attn_prefill(AttnPreP p) {
 // in base 2).  One block per (split tile, query head).
 template <int HD>
 __global__ __launch_bounds__(256) void k_attn_prefill_merge(AttnPreP p) {
-  const int u = blockIdx.x, h = blockIdx.y;
-  const int r0 = (p.split_from + u) * 32;
+  const int u = blockIdx.x, h = blockIdx.y;  // (u: split record, over all sequences)
+  int si = 0;
+  while (si + 1 < p.n_seg && u >= p.seg[si + 1].part0) ++si;
+  const PreSeg &sg = p.seg[si];
+  const int r0 = (sg.split_from + u - sg.part0) * 32;
   const float *a = p.part + (((size_t)u * 2 + 0) * p.d.nh + h) * 32 * (HD + 4);
   const float *b = p.part + (((size_t)u * 2 + 1) * p.d.nh + h) * 32 * (HD + 4);
   for (int idx = threadIdx.x; idx < 32 * HD; idx += 256) {
     const int q = idx / HD, dd = idx - q * HD;
-    if (r0 + q >= p.M) break;  // (rows past M come last)
+    if (r0 + q >= sg.M) break;  // (rows past M come last)
     const float *x = a + q * (HD + 4), *y = b + q * (HD + 4);
     const float m0 = x[HD], m1 = y[HD];
     const float mm = fmaxf(m0, m1);
     const float sub = mm == kNegInf ? 0.f : mm;
     const float w0 = exp2f(m0 - sub), w1 = exp2f(m1 - sub);
     const float o = (x[dd] * w0 + y[dd] * w1) / (x[HD + 1] * w0 + y[HD + 1] * w1);
-    p.o16[(size_t)(r0 + q) * p.ldo + (size_t)h * HD + dd] = (_Float16)o;
+    p.o16[(size_t)(sg.r0 + r0 + q) * p.ldo + (size_t)h * HD + dd] = (_Float16)o;
   }
 }
 
@@ -1016,9 +1034,8 @@ static void attn_prefill_g(const AttnPreP &p, dim3 grid, hipStream_t st) {
 }
 
 template <int HD>
-static void attn_prefill_hd(const AttnPreP &p, hipStream_t st) {
-  const int n_split = p.n_tiles - p.split_from;
-  const dim3 grid(p.d.nkv, p.n_tiles + n_split);
+static void attn_prefill_hd(const AttnPreP &p, int items, int work, int n_split, hipStream_t st) {
+  const dim3 grid(p.d.nkv, items * p.n_seg);
   if (n_split > 0) {
     switch (p.d.group) {
       case 7: attn_prefill_g<HD, 7>(p, grid, st); break;
@@ -1033,7 +1050,7 @@ static void attn_prefill_hd(const AttnPreP &p, hipStream_t st) {
     hipLaunchKernelGGL((k_attn_prefill_merge<HD>), dim3(n_split, p.d.nh), dim3(256), 0, st, p);
     return;
   }
-  if ((int)(grid.x * grid.y) < 128) {
+  if (p.d.nkv * work < 128) {
     // few query tiles (short prompts): one query head per block, so the
     // group's heads run on separate CUs (each block loads its group's K / V)
     attn_prefill_g<HD, 1>(p, dim3(grid.x, grid.y, p.d.group), st);  // (z: head in the group)
@@ -1051,33 +1068,83 @@ static void attn_prefill_hd(const AttnPreP &p, hipStream_t st) {
   }
 }
 
-void attn_prefill(const Dims &d, int layer, const KVCache &kv, const float *q, int ldq,
-                  RowInfo rows, int M, int seq, const int *host_pos, const Workspace &ws,
-                  _Float16 *o16, int ldo, hipStream_t st) {
-  const size_t b16 = kv.off16(d, layer, seq, 0);
-  AttnPreP p{d, q, ldq, rows, M, kv.k16 + b16, kv.v16t + b16,
-             (size_t)kv.ldp * d.hd, kv.ldp, o16, ldo,
-             (1.0f / sqrtf((float)d.hd)) * 1.4426950408889634f, 0, 0, ws.buf};
+// Up to kPreSegs sequences in one launch.
+static void attn_prefill_launch(const Dims &d, int layer, const KVCache &kv, const float *q,
+                                int ldq, RowInfo rows, const PrefillSeg *segs, int n,
+                                const int *host_pos, const Workspace &ws, _Float16 *o16,
+                                int ldo, hipStream_t st) {
+  AttnPreP p{};
+  p.d = d;
+  p.q = q;
+  p.ldq = ldq;
+  p.rows = rows;
+  const size_t b16 = kv.off16(d, layer, 0, 0);
+  p.k16 = kv.k16 + b16;
+  p.v16t = kv.v16t + b16;
+  p.gstride = (size_t)kv.ldp * d.hd;
+  p.ldp = kv.ldp;
+  p.o16 = o16;
+  p.ldo = ldo;
+  p.qscale = (1.0f / sqrtf((float)d.hd)) * 1.4426950408889634f;
+  p.part = ws.buf;
+  p.n_seg = n;
   // Causal balance: with one block per (query tile, KV head) the last tile's
   // block has the most key tiles; tiles with more than half of the largest
-  // count (and at least 8 key tiles) are split in two, so no block has more
-  // than about half of the longest tile's work.  Positions are strictly
-  // increasing, so the key-tile count grows with the tile index.
-  const int T = (M + 31) / 32;
-  p.n_tiles = p.split_from = T;
-  auto ntiles = [&](int t) { return host_pos[std::min(32 * t + 31, M - 1)] / kPreKeys + 1; };
-  if (T * d.nkv >= 128 && ntiles(T - 1) >= 8) {
-    const int lim = (ntiles(T - 1) + 1) / 2;
-    int sf = T;
-    while (sf > 0 && ntiles(sf - 1) > lim) --sf;
-    const size_t need = (size_t)(T - sf) * 2 * d.nh * 32 * (d.hd + 4) * sizeof(float);
-    if (ws.buf && need <= ws.bytes) p.split_from = sf;
+  // count over the launch (and at least 8 key tiles) are split in two, so no
+  // block has more than about half of the longest tile's work.  Positions
+  // increase within a sequence, so the key-tile count grows with the tile
+  // index and a sequence's split tiles are its last ones.
+  auto ntiles = [&](const PrefillSeg &g, int t) {
+    return host_pos[g.r0 + std::min(32 * t + 31, g.n - 1)] / kPreKeys + 1;
+  };
+  int total_tiles = 0, kmax = 0;
+  for (int i = 0; i < n; ++i) {
+    const int T = (segs[i].n + 31) / 32;
+    PreSeg &sg = p.seg[i];
+    sg.r0 = segs[i].r0;
+    sg.M = segs[i].n;
+    sg.n_tiles = sg.split_from = T;
+    sg.kv_off = kv.off16(d, layer, segs[i].seq, 0) - b16;
+    total_tiles += T;
+    kmax = std::max(kmax, ntiles(segs[i], T - 1));
+  }
+  if (total_tiles * d.nkv >= 128 && kmax >= 8) {
+    const int lim = (kmax + 1) / 2;
+    int n_split = 0;
+    for (int i = 0; i < n; ++i) {
+      int sf = p.seg[i].n_tiles;
+      while (sf > 0 && ntiles(segs[i], sf - 1) > lim) --sf;
+      n_split += p.seg[i].n_tiles - sf;
+    }
+    const size_t need = (size_t)n_split * 2 * d.nh * 32 * (d.hd + 4) * sizeof(float);
+    if (ws.buf && need <= ws.bytes)
+      for (int i = 0; i < n; ++i) {
+        int sf = p.seg[i].n_tiles;
+        while (sf > 0 && ntiles(segs[i], sf - 1) > lim) --sf;
+        p.seg[i].split_from = sf;
+      }
+  }
+  int items = 0, work = 0, n_split = 0;  // (items: the most work items of one sequence)
+  for (int i = 0; i < n; ++i) {
+    PreSeg &sg = p.seg[i];
+    sg.part0 = n_split;
+    n_split += sg.n_tiles - sg.split_from;
+    items = std::max(items, 2 * sg.n_tiles - sg.split_from);
+    work += 2 * sg.n_tiles - sg.split_from;
   }
   switch (d.hd) {
-    case 16: attn_prefill_hd<16>(p, st); break;
-    case 64: attn_prefill_hd<64>(p, st); break;
-    default: attn_prefill_hd<128>(p, st); break;
+    case 16: attn_prefill_hd<16>(p, items, work, n_split, st); break;
+    case 64: attn_prefill_hd<64>(p, items, work, n_split, st); break;
+    default: attn_prefill_hd<128>(p, items, work, n_split, st); break;
   }
+}
+
+void attn_prefill(const Dims &d, int layer, const KVCache &kv, const float *q, int ldq,
+                  RowInfo rows, const PrefillSeg *segs, int n_segs, const int *host_pos,
+                  const Workspace &ws, _Float16 *o16, int ldo, hipStream_t st) {
+  for (int i = 0; i < n_segs; i += kPreSegs)
+    attn_prefill_launch(d, layer, kv, q, ldq, rows, segs + i, std::min(kPreSegs, n_segs - i),
+                        host_pos, ws, o16, ldo, st);
 }
 
 }  // namespace q2

@@ -164,13 +164,18 @@ void attn_wo_fused(const Dims &d, int layer, const KVCache &kv, const float *q, 
 // atomics: per (WO row chunk, query head) block as in attn_wo_fused.
 void merge_wo(const Dims &d, const AttnPartials &p, RowInfo rows, int M, const uint16_t *wo,
               float *h, int ldh, hipStream_t st);
-// Causal flash attention over MFMA for one prefill pass of M rows of
-// sequence `seq` (positions strictly increasing; host_pos = their host copy,
-// which sizes the work split), on the binary16 mirror of the cache.  Long
-// passes use `ws` for the split query tiles' partial softmax states.
+// Causal flash attention over MFMA for one prefill pass, on the binary16
+// mirror of the cache.  The pass's rows are runs of one sequence each
+// (segs: rows r0 .. r0+n-1 of sequence seq, positions strictly increasing
+// within a run); host_pos is the host copy of the pass's positions, which
+// sizes the work split.  Up to 8 runs share a launch.  Long passes use `ws`
+// for the split query tiles' partial softmax states.
+struct PrefillSeg {
+  int r0, n, seq;
+};
 void attn_prefill(const Dims &d, int layer, const KVCache &kv, const float *q, int ldq,
-                  RowInfo rows, int M, int seq, const int *host_pos, const Workspace &ws,
-                  _Float16 *o16, int ldo, hipStream_t st);
+                  RowInfo rows, const PrefillSeg *segs, int n_segs, const int *host_pos,
+                  const Workspace &ws, _Float16 *o16, int ldo, hipStream_t st);
 // Rewrites the binary16 mirror of positions pos0 .. pos0+n-1 of (layer, seq)
 // from the f32 cache (after a direct write of the f32 cache).
 void kv_mirror(const Dims &d, const KVCache &kv, int layer, int seq, int pos0, int n,

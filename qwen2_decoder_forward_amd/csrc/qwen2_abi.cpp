@@ -301,7 +301,8 @@ int qwen2_load(const qwen2_hparams *hp, const qwen2_weights *w, void *stream, qw
   }
 
   // ---- scratch
-  c->max_rows = std::min(d.n_ctx, kMaxPassRows);
+  // one sequence never has more than n_ctx rows; a batch of several may
+  c->max_rows = d.n_seq > 1 ? kMaxPassRows : std::min(d.n_ctx, kMaxPassRows);
   c->rows_cap = std::max(c->max_rows, d.n_seq);
   c->dec_rows = std::max(d.n_seq, kGemvRows);
   c->part.n_chunks = (d.n_ctx + q2::kChunkKeys - 1) / q2::kChunkKeys;
@@ -467,9 +468,7 @@ void tail_row(qwen2_ctx *c, int r, const int *pos, const int *seq, int last_pos,
 }
 
 // A run of rows of one sequence inside a prefill pass.
-struct Seg {
-  int r0, n, seq;
-};
+using Seg = q2::PrefillSeg;
 
 // One pass of at most max_rows rows (runs of rows of one or more sequences,
 // `segs`), up to and including the last layer's Q/K/V: every row's K/V is
@@ -506,11 +505,9 @@ void prefill_pass(qwen2_ctx *c, int M, int off, const int *pos, const int *seq,
       TIMED(QWEN2_OP_GATEUP, q2::gemv_swiglu(d, w, c->h, M, c->a32, d.I_pad, eps, st));
       TIMED(QWEN2_OP_DOWN, q2::gemv_resid(w.wd, d.H, d.I_pad, c->a32, d.I_pad, M, c->h, d.H, st));
     } else {
-      for (const Seg &g : segs)
-        TIMED(QWEN2_OP_ATTN,
-              q2::attn_prefill(d, l, kv, c->q32 + (size_t)g.r0 * nhd, nhd,
-                               q2::RowInfo{pos + g.r0, seq + g.r0}, g.n, g.seq, host_pos + g.r0,
-                               c->splitk, c->x16 + (size_t)g.r0 * nhd, nhd, st));
+      TIMED(QWEN2_OP_ATTN, q2::attn_prefill(d, l, kv, c->q32, nhd, rows, segs.data(),
+                                            (int)segs.size(), host_pos, c->splitk, c->x16, nhd,
+                                            st));
       TIMED(QWEN2_OP_WO, pending = q2::gemm_resid(w.wo, d.H, nhd, c->x16, nhd, M, c->h, d.H,
                                                   c->splitk, st));
       TIMED(QWEN2_OP_NORM, q2::rmsnorm_rows_f16(c->h, d.H, w.ffn_norm, d.H, M, eps, c->x16, d.H,
