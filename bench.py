@@ -35,8 +35,8 @@ MFMA_F16_PEAK_TFS = 2500.0  # MI355X dense f16 MFMA
 # WRITE_SIZE passes, scaled by what the counters read for a 256 MiB copy
 # (profiles/qwen2.5-0.5b_gateup_gemv_hbm_traffic.md); valid only while the
 # kernel source is the one the counters were taken on.
-GATEUP_TRAFFIC_BYTES = 17569214
-GATEUP_TRAFFIC_SRC_SHA = "5892b713360143a9"
+GATEUP_TRAFFIC_BYTES = 17577429
+GATEUP_TRAFFIC_SRC_SHA = "da50443ef03e3b10"
 
 
 def gateup_traffic(shape):
@@ -298,6 +298,19 @@ def main():
     gu_bytes = gateup_bytes(shape)
     achieved = gu_bytes / gu_avg_s / 1e9
 
+    # next_token_probs of the read-out rows (softmax over the vocabulary):
+    # average of 100 back-to-back calls on the last step's logits
+    prob_rows = n_seq if batched else 1
+    probs = torch.empty((prob_rows, V), dtype=torch.float32, device=dev)
+    model.next_token_probs(logits, prob_rows, probs)
+    torch.cuda.synchronize()
+    ev_k[0].record(stream)
+    for _ in range(100):
+        model.next_token_probs(logits, prob_rows, probs)
+    ev_k[1].record(stream)
+    torch.cuda.synchronize()
+    probs_us = ev_k[0].elapsed_time(ev_k[1]) / 100 * 1e3
+
     fl = prefill_gemm_flops(shape, n)
     prefill_flops = sum(fl.values()) + attn_prefill_flops(shape, n)
     prefill_bytes = wb["f16"] + wb["f32"] + n * kv_pos
@@ -325,6 +338,8 @@ def main():
         "decode_hbm_gbs": dec_gbs,
         "decode_hbm_frac": dec_gbs / HBM_PEAK_GBS,
         "wall_s_timed": wall,
+        "next_token_probs_us": probs_us,
+        "next_token_probs_rows": prob_rows,
         "roofline": {
             "kernel": "k_gemv1<4,2,EPI_SWIGLU> (RMSNorm + gate/up + SwiGLU, decode M=1)",
             "bound": "hbm", "achieved": achieved, "peak": HBM_PEAK_GBS, "unit": "GB/s",
@@ -350,6 +365,8 @@ def main():
             f"{out['prefill_mfma_frac'] * 100:.1f}% MFMA)")
     log(f"[{wl.name}] decode {dec_tok_s:.1f} tok/s ({decode_ms:.3f} ms, {dec_gbs:.0f} GB/s), "
         f"gate/up GEMV {gu_avg_s * 1e6:.2f} us = {achieved:.0f} GB/s")
+    log(f"[{wl.name}] next_token_probs of {prob_rows} row(s) x {V}: {probs_us:.2f} us "
+        f"({8 * V * prob_rows / (probs_us * 1e3):.0f} GB/s of logits in + probabilities out)")
     if "prefill_ops" in out:
         log(f"[{wl.name}] prefill ops: " + ", ".join(
             f"{k} {v['mfma_frac'] * 100:.1f}%" for k, v in out["prefill_ops"].items()))

@@ -182,6 +182,30 @@ int qwen2_prefill_batch(qwen2_ctx *ctx, int32_t n_batch, const int32_t *seq_ids,
 int qwen2_decode(qwen2_ctx *ctx, int32_t n_batch, const int32_t *seq_ids, const int32_t *tokens_dev,
                  const int32_t *positions, float *logits_dev, int32_t *argmax_dev, void *stream);
 
+/* next_token_probs (nnterp page, the standardized tap list: the next-token
+ * distribution at the last position): the softmax of each of `rows` rows of
+ * logits_dev [rows, n_vocab] f32 (as written by a prefill or decode) into
+ * probs_dev [rows, n_vocab] f32, p = e^(x - max) / sum e^(x - max).
+ * rows in [1, max(n_seq, 8)], else E_ARG.  Enqueued on `stream`; uses a
+ * context-owned partial-sum buffer, so calls on one context must not
+ * overlap. */
+int qwen2_next_token_probs(qwen2_ctx *ctx, const float *logits_dev, int32_t rows,
+                           float *probs_dev, void *stream);
+
+/* Stop ids as data (eos and im_end, minfer page, section 5; the Qwen2.5
+ * ids are 151643 and 151645): up to 8 ids in [0, n_vocab); n = 0 clears
+ * them (the default).  From then on every greedy read-out (prefill, batched
+ * prefill, decode) whose id is one of them latches, for its sequence slot,
+ * the smallest such read-out position, so a loop that runs ahead on the
+ * device can be cut back afterwards.  E_ARG for n outside [0, 8], E_TOKEN for
+ * an id out of range.  Synchronous: call it while no call that reads the
+ * table is in flight. */
+int qwen2_set_stop_ids(qwen2_ctx *ctx, const int32_t *ids, int32_t n);
+
+/* Copies the latched stop positions to out_dev [n_seq] int32 (-1: no stop
+ * id read out yet) and, if clear != 0, resets them.  Enqueued on `stream`. */
+int qwen2_read_stops(qwen2_ctx *ctx, int32_t *out_dev, int32_t clear, void *stream);
+
 /* Copies the read-out rows of the last prefill/decode (1 row after a
  * prefill, n_batch rows after a batched prefill or a decode) to out_dev
  * [rows, n_embd] f32.

@@ -29,6 +29,11 @@ What it computes (plain definition, written out step by step):
   projection"; xinfer Module 7, section 7.3), and greedy argmax on the
   device side of the pages' engines (xinfer 7.3) taken here as the lowest
   index of the largest logit.
+* next_token_probs: the next-token distribution at a read-out position, the
+  softmax of that row's logits (nnterp page, standardized tap list).
+* Stop ids are data (eos and im_end, minfer page, section 5): a greedy
+  read-out whose id is one of them marks its sequence as stopped at that
+  read-out position; the earliest such position is kept.
 
 Precision: activations are stored as float32 between operations (the CPU
 reference and activations are f32 in the xinfer Module 7, section 7.4 dtype
@@ -189,6 +194,24 @@ def softmax(s: np.ndarray) -> np.ndarray:
     s = np.asarray(s, dtype=f64)
     e = np.exp(s - np.max(s, axis=-1, keepdims=True))
     return e / np.sum(e, axis=-1, keepdims=True)
+
+
+def next_token_probs(logits: np.ndarray) -> np.ndarray:
+    """The next-token distribution of each read-out row: softmax over the
+    vocabulary of its logits (float64, rounded to float32)."""
+    return softmax(logits).astype(f32)
+
+
+def stop_positions(n_seq: int, readouts, stop_ids) -> np.ndarray:
+    """readouts: (sequence slot, read-out position, greedy id) triples in any
+    order.  Returns, per slot, the smallest read-out position whose id is a
+    stop id, or -1 when there is none."""
+    stops = set(int(t) for t in stop_ids)
+    out = np.full(n_seq, -1, dtype=np.int64)
+    for seq, pos, tok in readouts:
+        if int(tok) in stops and (out[seq] < 0 or pos < out[seq]):
+            out[seq] = pos
+    return out
 
 
 def silu(z: np.ndarray) -> np.ndarray:

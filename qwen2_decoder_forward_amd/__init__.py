@@ -18,7 +18,8 @@ __all__ = [
     "Hparams", "LayerWeights", "Weights", "Info", "Qwen2Error", "CODES", "lib", "LIB_PATH",
     "qwen2_check_hparams", "qwen2_check_prefill", "qwen2_check_prefill_batch",
     "qwen2_check_decode", "qwen2_load", "qwen2_prefill", "qwen2_prefill_batch", "qwen2_decode",
-    "qwen2_read_hidden", "qwen2_kv_read", "qwen2_kv_write",
+    "qwen2_read_hidden", "qwen2_kv_read", "qwen2_kv_write", "qwen2_next_token_probs",
+    "qwen2_set_stop_ids", "qwen2_read_stops",
     "qwen2_sync_status", "qwen2_info", "qwen2_last_error", "qwen2_strerror", "qwen2_free",
     "qwen2_prof_enable", "qwen2_prof_read", "qwen2_prof_repeat", "OPS", "make_hparams", "Model",
 ]
@@ -89,6 +90,9 @@ def lib() -> C.CDLL:
             "qwen2_prefill_batch": (i32, [vp, i32, PI32, PI32, PI32, PI32, vp, vp, vp]),
             "qwen2_decode": (i32, [vp, i32, PI32, vp, PI32, vp, vp, vp]),
             "qwen2_read_hidden": (i32, [vp, i32, vp, vp]),
+            "qwen2_next_token_probs": (i32, [vp, vp, i32, vp, vp]),
+            "qwen2_set_stop_ids": (i32, [vp, PI32, i32]),
+            "qwen2_read_stops": (i32, [vp, vp, i32, vp]),
             "qwen2_kv_read": (i32, [vp, i32, i32, i32, i32, vp, vp, vp]),
             "qwen2_kv_write": (i32, [vp, i32, i32, i32, i32, vp, vp, vp]),
             "qwen2_sync_status": (i32, [vp, vp]),
@@ -237,6 +241,20 @@ def qwen2_read_hidden(ctx: int, which: int, out, stream=None) -> None:
     _check(lib().qwen2_read_hidden(ctx, which, _ptr(out), _stream(stream)), ctx)
 
 
+def qwen2_next_token_probs(ctx: int, logits, rows: int, probs, stream=None) -> None:
+    _check(lib().qwen2_next_token_probs(ctx, _ptr(logits), rows, _ptr(probs), _stream(stream)),
+           ctx)
+
+
+def qwen2_set_stop_ids(ctx: int, ids) -> None:
+    a = _i32(ids)
+    _check(lib().qwen2_set_stop_ids(ctx, _p(a, PI32), len(a)), ctx)
+
+
+def qwen2_read_stops(ctx: int, out, clear: bool = False, stream=None) -> None:
+    _check(lib().qwen2_read_stops(ctx, _ptr(out), int(bool(clear)), _stream(stream)), ctx)
+
+
 def qwen2_kv_read(ctx: int, layer: int, seq: int, pos0: int, n: int, k, v, stream=None) -> None:
     _check(lib().qwen2_kv_read(ctx, layer, seq, pos0, n, _ptr(k), _ptr(v), _stream(stream)), ctx)
 
@@ -305,6 +323,15 @@ class Model:
 
     def read_hidden(self, which, out, stream=None):
         qwen2_read_hidden(self.ctx, which, out, stream)
+
+    def next_token_probs(self, logits, rows, probs, stream=None):
+        qwen2_next_token_probs(self.ctx, logits, rows, probs, stream)
+
+    def set_stop_ids(self, ids):
+        qwen2_set_stop_ids(self.ctx, ids)
+
+    def read_stops(self, out, clear=False, stream=None):
+        qwen2_read_stops(self.ctx, out, clear, stream)
 
     def kv_read(self, layer, seq, pos0, n, k, v, stream=None):
         qwen2_kv_read(self.ctx, layer, seq, pos0, n, k, v, stream)

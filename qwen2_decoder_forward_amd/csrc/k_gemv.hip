@@ -508,19 +508,6 @@ __global__ __launch_bounds__(256) void k_lmhead(GemvP p) {
   }
 }
 
-// The greedy result: index of each row's packed maximum, which is then
-// cleared for the next call.  Runs after the lm_head kernel (the kernel
-// boundary orders the atomics before these reads).
-__global__ void k_argmax_finalize(unsigned long long *best, int M, int *const *out) {
-  const int m = blockIdx.x * blockDim.x + threadIdx.x;
-  if (m < M) {
-    const unsigned long long b = best[m];
-    best[m] = 0ull;
-    int *o = *out;
-    if (o) o[m] = argmax_index(b);
-  }
-}
-
 // ------------------------------------------------------------------ launch
 template <int EPI>
 constexpr bool kResidEpi() { return EPI == EPI_RESID; }
@@ -626,10 +613,6 @@ void gemv_lmhead(const Dims &d, const uint16_t *W, const float *norm_w, const fl
     launch<4, EPI_LMHEAD>(p, 4096, st);
   }
   argmax_finalize(e, M, st);
-}
-
-void argmax_finalize(const ArgmaxEpi &e, int M, hipStream_t st) {
-  hipLaunchKernelGGL(k_argmax_finalize, dim3((M + 255) / 256), dim3(256), 0, st, e.best, M, e.out);
 }
 
 }  // namespace q2

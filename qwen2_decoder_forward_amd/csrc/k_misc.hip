@@ -1,4 +1,5 @@
-// Embedding gather, row RMSNorm and row copies.
+// Embedding gather, row RMSNorm, row copies, the greedy read-out's index and
+// stop-id latch, and the next-token distribution.
 #include "q2_device.h"
 
 namespace q2 {
@@ -104,6 +105,120 @@ void copy_rows(const float *src, int lds, const int *src_rows, float *dst, int l
   if (k <= 0) return;
   hipLaunchKernelGGL(k_copy_rows, dim3(k), dim3(256), 0, st, src, lds, src_rows, dst, ldd,
                      dst_rows, ncols);
+}
+
+// The greedy result: index of each row's packed maximum, which is then
+// cleared for the next call.  Runs after the lm_head kernel (the kernel
+// boundary orders its atomics before these reads).  When the id is one of
+// the stop ids, the row's sequence slot keeps the smallest such read-out
+// position.
+__global__ void k_argmax_finalize(ArgmaxEpi e, int M) {
+  const int m = blockIdx.x * blockDim.x + threadIdx.x;
+  if (m < M) {
+    const unsigned long long b = e.best[m];
+    e.best[m] = 0ull;
+    const int id = argmax_index(b);
+    int *o = *e.out;
+    if (o) o[m] = id;
+    const int n_stop = e.stop[0];
+    for (int i = 0; i < n_stop; ++i)
+      if (id == e.stop[1 + i]) {
+        atomicMin(e.stop_pos + e.rows.seq[m], (unsigned)e.rows.pos[m]);
+        break;
+      }
+  }
+}
+
+void argmax_finalize(const ArgmaxEpi &e, int M, hipStream_t st) {
+  hipLaunchKernelGGL(k_argmax_finalize, dim3((M + 255) / 256), dim3(256), 0, st, e, M);
+}
+
+// out[s] = latched stop position of slot s (-1: none); with `clear` the
+// latch is reset.
+__global__ void k_read_stops(unsigned *stop_pos, int n, int *out, int clear) {
+  const int s = blockIdx.x * blockDim.x + threadIdx.x;
+  if (s < n) {
+    out[s] = (int)stop_pos[s];  // (~0u reads as -1)
+    if (clear) stop_pos[s] = ~0u;
+  }
+}
+
+void read_stops(unsigned *stop_pos, int n, int *out, int clear, hipStream_t st) {
+  hipLaunchKernelGGL(k_read_stops, dim3((n + 255) / 256), dim3(256), 0, st, stop_pos, n, out,
+                     clear);
+}
+
+// Next-token distribution p = softmax(logits row), in two launches over
+// kProbBlocks blocks per row.  First: each block's maximum m_b and
+// s_b = sum over its columns of e^(x - m_b), as an online (max, sum) per
+// thread, then combined over the block.
+__device__ __forceinline__ void ms_combine(float &m, float &s, float m2, float s2) {
+  const float mm = fmaxf(m, m2);
+  if (mm == kNegInf) return;  // (both empty)
+  s = s * expf(m - mm) + s2 * expf(m2 - mm);
+  m = mm;
+}
+
+__global__ __launch_bounds__(256) void k_softmax_part(const float *logits, int V, float2 *part) {
+  const int b = blockIdx.x, row = blockIdx.y;
+  const int chunk = (V + kProbBlocks - 1) / kProbBlocks;
+  const int c0 = b * chunk, c1 = min(V, c0 + chunk);
+  const float *x = logits + (size_t)row * V;
+  float m = kNegInf, s = 0.f;
+  for (int i = c0 + (int)threadIdx.x; i < c1; i += 256) {
+    const float v = x[i];
+    if (v > m) {
+      s = s * expf(m - v) + 1.f;
+      m = v;
+    } else {
+      s += expf(v - m);
+    }
+  }
+  // combine over the wavefront, then over the 4 wavefronts
+  for (int off = 32; off > 0; off >>= 1) {
+    const float m2 = __shfl_xor(m, off), s2 = __shfl_xor(s, off);
+    ms_combine(m, s, m2, s2);
+  }
+  __shared__ float2 sw[4];
+  const int w = threadIdx.x >> 6;
+  if ((threadIdx.x & 63) == 0) sw[w] = make_float2(m, s);
+  __syncthreads();
+  if (threadIdx.x == 0) {
+    for (int i = 1; i < 4; ++i) ms_combine(m, s, sw[i].x, sw[i].y);
+    part[(size_t)row * kProbBlocks + b] = make_float2(m, s);
+  }
+}
+
+// Second: every block combines its row's kProbBlocks partials into the row
+// maximum M and S = sum of e^(x - M), and writes e^(x - M) / S for its columns.
+__global__ __launch_bounds__(256) void k_softmax_norm(const float *logits, int V,
+                                                      const float2 *part, float *probs) {
+  const int b = blockIdx.x, row = blockIdx.y;
+  __shared__ float2 sms;
+  if (threadIdx.x < 64) {
+    const float2 q = part[(size_t)row * kProbBlocks + threadIdx.x];  // (kProbBlocks = 64)
+    float m = q.x, s = q.y;
+    for (int off = 32; off > 0; off >>= 1) {
+      const float m2 = __shfl_xor(m, off), s2 = __shfl_xor(s, off);
+      ms_combine(m, s, m2, s2);
+    }
+    if (threadIdx.x == 0) sms = make_float2(m, s);
+  }
+  __syncthreads();
+  const float M = sms.x, inv = 1.0f / sms.y;
+  const int chunk = (V + kProbBlocks - 1) / kProbBlocks;
+  const int c0 = b * chunk, c1 = min(V, c0 + chunk);
+  const float *x = logits + (size_t)row * V;
+  float *y = probs + (size_t)row * V;
+  for (int i = c0 + (int)threadIdx.x; i < c1; i += 256) y[i] = expf(x[i] - M) * inv;
+}
+
+void softmax_rows(const float *logits, int rows, int V, float2 *part, float *probs,
+                  hipStream_t st) {
+  static_assert(kProbBlocks == 64, "one partial per lane of the combining wavefront");
+  const dim3 grid(kProbBlocks, rows);
+  hipLaunchKernelGGL(k_softmax_part, grid, dim3(256), 0, st, logits, V, part);
+  hipLaunchKernelGGL(k_softmax_norm, grid, dim3(256), 0, st, logits, V, part, probs);
 }
 
 }  // namespace q2

@@ -72,7 +72,11 @@ struct ArgmaxEpi {
   float *const *logits;      // -> [M, V] f32 or null
   unsigned long long *best;  // [M]
   int *const *out;           // -> [M] int32 or null
+  RowInfo rows;              // position and sequence slot of each read-out row
+  const int *stop;           // [1 + kMaxStopIds]: count, then the stop ids
+  unsigned *stop_pos;        // [n_seq]: smallest read-out position whose id was a stop id (~0u: none)
 };
+constexpr int kMaxStopIds = 8;
 
 // ---------------------------------------------------------------- launchers
 // GEMV family (rows M <= 8, f32 activations, f16 weights streamed once).
@@ -87,9 +91,16 @@ void gemv_swiglu(const Dims &d, const LayerW &w, const float *h, int M, float *a
 void gemv_lmhead(const Dims &d, const uint16_t *W, const float *norm_w, const float *h, int M,
                  float *normed_out, const ArgmaxEpi &e, float eps, hipStream_t st);
 
-// Writes the index of each row's packed maximum and clears it; launched after
-// an lm_head kernel.
+// Writes the index of each row's packed maximum and clears it, and latches
+// stop ids; launched after an lm_head kernel.
 void argmax_finalize(const ArgmaxEpi &e, int M, hipStream_t st);
+// out[s] = the latched stop position of slot s, -1 for none (reset with clear).
+void read_stops(unsigned *stop_pos, int n, int *out, int clear, hipStream_t st);
+// probs[r] = softmax(logits[r]) for rows r < rows, over V columns; part holds
+// rows * kProbBlocks (max, sum) pairs.
+constexpr int kProbBlocks = 64;
+void softmax_rows(const float *logits, int rows, int V, float2 *part, float *probs,
+                  hipStream_t st);
 
 // MFMA GEMM family (rows M > 8): A f16 [M, lda], W f16 [N, K], K % 32 == 0.
 // Residual GEMMs with few output tiles split K over blocks: with fewer than

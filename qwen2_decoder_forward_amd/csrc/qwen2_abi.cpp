@@ -68,6 +68,9 @@ struct qwen2_ctx {
   q2::Workspace splitk{};  // split-K partial sums of the small-M GEMMs
   unsigned long long *best = nullptr;
   unsigned int *bad_flag = nullptr;
+  int *stop_ids = nullptr;     // [1 + kMaxStopIds]: count, then the ids
+  unsigned *stop_pos = nullptr;  // [n_seq] latched stop positions (~0u: none)
+  float2 *prob_part = nullptr;   // [dec_rows][kProbBlocks] softmax partials
   // captured decode steps, keyed by (batch size, attention splits)
   std::map<std::pair<int, int>, hipGraphExec_t> graphs;
   hipStream_t cap_stream = nullptr;  // captures only (never runs work)
@@ -316,11 +319,14 @@ int qwen2_load(const qwen2_hparams *hp, const qwen2_weights *w, void *stream, qw
          s_a16 = take(R * Ip * 2), s_o32 = take(D * nhd * 4), s_a32 = take(D * Ip * 4),
          s_norm = take(D * H * 4), s_io = take(kSlotBytes + 3 * c->io_cap * 4),
          s_part = take((size_t)D * d.nkv * c->part.n_chunks * q2::attn_rec_floats(d.group, d.hd) * 4),
-         s_best = take(D * 8), s_bad = take(4), s_splitk = take(kSplitKBytes);
+         s_best = take(D * 8), s_bad = take(4), s_splitk = take(kSplitKBytes),
+         s_stop = take((1 + q2::kMaxStopIds) * 4), s_stop_pos = take((size_t)d.n_seq * 4),
+         s_prob = take(D * q2::kProbBlocks * sizeof(float2));
     c->sarena_bytes = cur;
     LTRY([&]() -> int {
       HIP_TRY(c, hipMalloc(&c->sarena, c->sarena_bytes));
       HIP_TRY(c, hipMemset(c->sarena, 0, c->sarena_bytes));
+      HIP_TRY(c, hipMemset(c->sarena + s_stop_pos.off, 0xFF, (size_t)d.n_seq * 4));
       return 0;
     }());
     char *S = c->sarena;
@@ -336,6 +342,9 @@ int qwen2_load(const qwen2_hparams *hp, const qwen2_weights *w, void *stream, qw
     c->best = (unsigned long long *)(S + s_best.off);
     c->splitk = q2::Workspace{(float *)(S + s_splitk.off), kSplitKBytes};
     c->bad_flag = (unsigned *)(S + s_bad.off);
+    c->stop_ids = (int *)(S + s_stop.off);
+    c->stop_pos = (unsigned *)(S + s_stop_pos.off);
+    c->prob_part = (float2 *)(S + s_prob.off);
   }
   LTRY([&]() -> int {
     HIP_TRY(c, hipHostMalloc((void **)&c->pinned, kRing * (kSlotBytes + 3 * c->io_cap * 4),
@@ -386,9 +395,10 @@ const CallSlots *dev_slots(qwen2_ctx *c) { return (const CallSlots *)c->io; }
 
 q2::KVCache kv_of(const qwen2_ctx *c) { return q2::KVCache{c->kc, c->vc, c->kc16, c->vc16t, c->ldp}; }
 
-q2::ArgmaxEpi argmax_epi(qwen2_ctx *c) {
+q2::ArgmaxEpi argmax_epi(qwen2_ctx *c, q2::RowInfo rows) {
   const CallSlots *ds = dev_slots(c);
-  return q2::ArgmaxEpi{(float *const *)&ds->logits, c->best, (int *const *)&ds->argmax};
+  return q2::ArgmaxEpi{(float *const *)&ds->logits, c->best, (int *const *)&ds->argmax, rows,
+                       c->stop_ids, c->stop_pos};
 }
 
 int chunks_for(int max_pos) { return (max_pos + q2::kChunkKeys) / q2::kChunkKeys; }
@@ -462,7 +472,8 @@ void tail_row(qwen2_ctx *c, int r, const int *pos, const int *seq, int last_pos,
   TIMED(QWEN2_OP_GATEUP, q2::gemv_swiglu(d, w, hr, 1, c->a32, d.I_pad, c->hp.rms_eps, st));
   TIMED(QWEN2_OP_DOWN, q2::gemv_resid(w.wd, d.H, d.I_pad, c->a32, d.I_pad, 1, hr, d.H, st));
   TIMED(QWEN2_OP_LMHEAD, q2::gemv_lmhead(d, c->lm_head, c->out_norm, hr, 1, c->normed,
-                                         argmax_epi(c), c->hp.rms_eps, st));
+                                         argmax_epi(c, q2::RowInfo{pos + r, seq + r}),
+                                         c->hp.rms_eps, st));
   c->last_h = hr;
   c->last_rows = 1;
 }
@@ -547,16 +558,17 @@ int rows_rest(qwen2_ctx *c, int l, int B, int n_chunks, q2::RowInfo rows, hipStr
 }
 
 // Final norm, lm_head and argmax of h rows 0..B-1 into the staged slots.
-void rows_head(qwen2_ctx *c, int B, int pending, hipStream_t st) {
+void rows_head(qwen2_ctx *c, int B, q2::RowInfo rows, int pending, hipStream_t st) {
   const Dims &d = c->d;
   const float eps = c->hp.rms_eps;
   if (B <= kGemvRows) {
     TIMED(QWEN2_OP_LMHEAD, q2::gemv_lmhead(d, c->lm_head, c->out_norm, c->h, B, c->normed,
-                                           argmax_epi(c), eps, st));
+                                           argmax_epi(c, rows), eps, st));
   } else {
     TIMED(QWEN2_OP_NORM, q2::rmsnorm_rows_f16(c->h, d.H, c->out_norm, d.H, B, eps, c->x16, d.H,
                                               c->normed, c->splitk.buf, pending, st));
-    TIMED(QWEN2_OP_LMHEAD, q2::gemm_lmhead(d, c->lm_head, c->x16, d.H, B, argmax_epi(c), st));
+    TIMED(QWEN2_OP_LMHEAD, q2::gemm_lmhead(d, c->lm_head, c->x16, d.H, B, argmax_epi(c, rows),
+                                           st));
   }
 }
 
@@ -581,7 +593,7 @@ void decode_launches(qwen2_ctx *c, int B, int n_chunks, const int *dpos, const i
     }
     pending = rows_rest(c, l, B, n_chunks, rows, st);
   }
-  rows_head(c, B, pending, st);
+  rows_head(c, B, rows, pending, st);
 }
 
 }  // namespace
@@ -671,8 +683,9 @@ int qwen2_prefill_batch(qwen2_ctx *c, int32_t nb, const int32_t *seq_ids, const 
   HIP_TRY(c, hipMemcpyAsync(c->h, c->normed, (size_t)nb * d.H * 4, hipMemcpyDeviceToDevice, st));
   HIP_TRY(c, hipMemcpyAsync(c->q32, c->o32, (size_t)nb * nhd * 4, hipMemcpyDeviceToDevice, st));
   const int n_chunks = chunks_for(*std::max_element(t_pos.begin(), t_pos.end()));
-  const int pending = rows_rest(c, d.L - 1, nb, n_chunks, q2::RowInfo{df[0], df[1]}, st);
-  rows_head(c, nb, pending, st);
+  const q2::RowInfo tail{df[0], df[1]};
+  const int pending = rows_rest(c, d.L - 1, nb, n_chunks, tail, st);
+  rows_head(c, nb, tail, pending, st);
   c->last_h = c->h;
   c->last_rows = nb;
   HIP_TRY(c, hipGetLastError());
@@ -718,6 +731,39 @@ int qwen2_decode(qwen2_ctx *c, int32_t B, const int32_t *seq_ids, const int32_t 
     it = c->graphs.emplace(key, ge).first;
   }
   HIP_TRY(c, hipGraphLaunch(it->second, st));
+  return QWEN2_OK;
+}
+
+int qwen2_next_token_probs(qwen2_ctx *c, const float *logits_dev, int32_t rows, float *probs_dev,
+                           void *stream) {
+  if (!c) return QWEN2_E_ARG;
+  if (!logits_dev || !probs_dev) return set_err(c, QWEN2_E_ARG, "null logits or probs");
+  if (rows < 1 || rows > c->dec_rows)
+    return set_err(c, QWEN2_E_ARG, "rows must be in [1, max(n_seq, 8)]");
+  hipStream_t st = (hipStream_t)stream;
+  q2::softmax_rows(logits_dev, rows, c->d.V, c->prob_part, probs_dev, st);
+  HIP_TRY(c, hipGetLastError());
+  return QWEN2_OK;
+}
+
+int qwen2_set_stop_ids(qwen2_ctx *c, const int32_t *ids, int32_t n) {
+  if (!c) return QWEN2_E_ARG;
+  if (n < 0 || n > q2::kMaxStopIds || (n > 0 && !ids))
+    return set_err(c, QWEN2_E_ARG, "between 0 and 8 stop ids");
+  int32_t t[1 + q2::kMaxStopIds] = {n};
+  for (int i = 0; i < n; ++i) {
+    if (ids[i] < 0 || ids[i] >= c->d.V) return set_err(c, QWEN2_E_TOKEN, "stop id outside [0, n_vocab)");
+    t[1 + i] = ids[i];
+  }
+  HIP_TRY(c, hipMemcpy(c->stop_ids, t, sizeof t, hipMemcpyHostToDevice));
+  return QWEN2_OK;
+}
+
+int qwen2_read_stops(qwen2_ctx *c, int32_t *out_dev, int32_t clear, void *stream) {
+  if (!c) return QWEN2_E_ARG;
+  if (!out_dev) return set_err(c, QWEN2_E_ARG, "null out_dev");
+  q2::read_stops(c->stop_pos, c->d.n_seq, out_dev, clear != 0, (hipStream_t)stream);
+  HIP_TRY(c, hipGetLastError());
   return QWEN2_OK;
 }
 

@@ -41,6 +41,17 @@ def check_id(gpu_id, ref_logits, ref_id, what):
     return False
 
 
+def check_probs(got, logits, what):
+    """next_token_probs against the oracle's softmax of the same logits:
+    |p - ref| <= 1e-5 ref + 1e-38 element by element (f32 exponentials of
+    arguments down to about -100), and each row sums to 1 within 1e-5."""
+    ref = O.next_token_probs(logits).astype(np.float64)
+    got = np.asarray(got, np.float64)
+    bad = np.abs(got - ref) > 1e-5 * ref + 1e-38
+    assert not bad.any(), f"{what}: {int(bad.sum())} probabilities off, e.g. {got[bad][:3]} vs {ref[bad][:3]}"
+    assert np.all(np.abs(got.sum(-1) - 1) < 1e-5), f"{what}: rows sum to {got.sum(-1)}"
+
+
 class Pair:
     """A GPU context and an oracle over the same weights."""
 

@@ -10,7 +10,7 @@ if not torch.cuda.is_available():
     pytest.skip("no GPU", allow_module_level=True)
 
 import qwen2_synth as syn  # noqa: E402
-from gpu_common import DEV, Pair, check, check_id, run_chain, say  # noqa: E402
+from gpu_common import DEV, Pair, check, check_id, check_probs, run_chain, say  # noqa: E402
 
 pytestmark = pytest.mark.gpu
 
@@ -31,6 +31,38 @@ def test_0_5b_weight_store_and_kv_sizes(w05):
     assert info.weight_bytes_f16 == 987_922_432          # ~942 MiB of f16 weights
     assert info.kv_bytes_per_pos == 24_576               # 24 KB of f32 K/V per position
     assert info.kv_bytes == 96 * 2 ** 20                 # n_ctx 4096 -> 96 MiB
+    m.close()
+
+
+def test_0_5b_next_token_probs_and_stop_ids(w05):
+    """The 151,936-entry distribution of a prefill read-out and of a 3-row
+    decode against the oracle's softmax of the same logits; the eos / im_end
+    ids as stop ids (a random-init model rarely produces them: the latch must
+    then stay at -1, else hold the read-out position)."""
+    import qwen2_decoder_forward_amd as q
+    from oracle import qwen2_oracle as O
+    m = q.Model(S, w05, n_ctx=256, n_seq=3)
+    m.set_stop_ids([151643, 151645])
+    V = S.n_vocab
+    logits = torch.empty((3, V), dtype=torch.float32, device=DEV)
+    probs = torch.empty((3, V), dtype=torch.float32, device=DEV)
+    ids = torch.zeros(3, dtype=torch.int32, device=DEV)
+    for s_ in range(3):
+        m.prefill(s_, syn.make_prompt(S, 16, 70 + s_), np.arange(16), logits[s_], ids[s_:s_ + 1])
+    m.next_token_probs(logits, 3, probs)
+    torch.cuda.synchronize()
+    check_probs(probs.cpu().numpy(), logits.cpu().numpy(), "0.5B prefill read-outs")
+    first = ids.cpu().numpy().copy()
+    m.decode([2, 0, 1], ids[[2, 0, 1]].contiguous(), [16, 16, 16], logits, ids)
+    m.next_token_probs(logits, 3, probs)
+    stops = torch.empty(3, dtype=torch.int32, device=DEV)
+    m.read_stops(stops)
+    torch.cuda.synchronize()
+    check_probs(probs.cpu().numpy(), logits.cpu().numpy(), "0.5B 3-row decode")
+    dec = ids.cpu().numpy()
+    reads = [(s_, 15, int(first[s_])) for s_ in range(3)]
+    reads += [(s_, 16, int(dec[b])) for b, s_ in enumerate([2, 0, 1])]
+    assert list(stops.cpu().numpy()) == list(O.stop_positions(3, reads, [151643, 151645]))
     m.close()
 
 

@@ -15,7 +15,7 @@ if not torch.cuda.is_available():
     pytest.skip("no GPU", allow_module_level=True)
 
 import qwen2_synth as syn  # noqa: E402
-from gpu_common import DEV, Pair, check, check_id, run_chain, say  # noqa: E402
+from gpu_common import DEV, Pair, check, check_id, check_probs, run_chain, say  # noqa: E402
 
 pytestmark = pytest.mark.gpu
 
@@ -247,6 +247,89 @@ def test_prefill_batch_rejects_before_any_work(tiny_w):
     p.m.kv_read(0, 0, 0, 64, k1, v1)
     torch.cuda.synchronize()
     assert torch.equal(k0, k1) and torch.equal(v0, v1)
+    p.close()
+
+
+def test_next_token_probs(tiny_w):
+    """Softmax of the read-out logits: one row after a prefill, 12 after a
+    batched decode, and rows of wide-range logits written directly (large
+    negative gaps, ties)."""
+    p = Pair(TINY, tiny_w, n_ctx=64, n_seq=12)
+    V = TINY.n_vocab
+    probs = torch.empty((12, V), dtype=torch.float32, device=DEV)
+    lg, _, r = p.prefill(0, syn.make_prompt(TINY, 6, 3), np.arange(6))
+    p.m.next_token_probs(p.logits, 1, probs)
+    torch.cuda.synchronize()
+    check_probs(probs[:1].cpu().numpy(), lg[None], "after a prefill")
+    seqs = list(range(12))
+    for s_ in seqs[1:]:
+        p.prefill(s_, syn.make_prompt(TINY, 3, 30 + s_), np.arange(3))
+    lg, _, r = p.decode(seqs, list(range(12)), [6] + [3] * 11)
+    p.m.next_token_probs(p.logits, 12, probs)
+    torch.cuda.synchronize()
+    check_probs(probs.cpu().numpy(), lg, "after a 12-row decode")
+    x = torch.randn((5, V), generator=torch.Generator().manual_seed(9)) * 40
+    x[1] = 0.0
+    x[2, ::3] = -200.0
+    x[3, 7] = 500.0
+    p.logits[:5].copy_(x.to(DEV))
+    p.m.next_token_probs(p.logits, 5, probs)
+    torch.cuda.synchronize()
+    check_probs(probs[:5].cpu().numpy(), x.numpy(), "direct logits")
+    p.close()
+
+
+def test_stop_ids_latch_earliest_position(tiny_w):
+    """Stop ids are data: every greedy read-out (decode on both paths, prefill,
+    batched prefill) whose id is a stop id marks its slot; the earliest
+    read-out position is kept, compared exactly with the oracle's definition
+    applied to the ids this run produced."""
+    import qwen2_decoder_forward_amd as q
+    from oracle import qwen2_oracle as O
+    p = Pair(TINY, tiny_w, n_ctx=64, n_seq=12)
+    m = p.m
+    stops_out = torch.empty(12, dtype=torch.int32, device=DEV)
+    # a first greedy chain without stop ids, to pick ids that will recur
+    ids = torch.zeros(13, dtype=torch.int32, device=DEV)
+    m.prefill(0, syn.make_prompt(TINY, 5, 8), np.arange(5), None, ids[0:1])
+    for k in range(12):
+        m.decode([0], ids[k:k + 1], [5 + k], None, ids[k + 1:k + 2])
+    first = ids.cpu().numpy()
+    stop = [int(first[4]), int(first[9]), TINY.n_vocab - 1]
+    m.set_stop_ids(stop)
+    m.read_stops(stops_out, clear=True)
+    reads = []
+    # slot 1: the same prompt, a greedy chain on the GEMV path
+    ids.zero_()
+    m.prefill(1, syn.make_prompt(TINY, 5, 8), np.arange(5), None, ids[0:1])
+    for k in range(12):
+        m.decode([1], ids[k:k + 1], [5 + k], None, ids[k + 1:k + 2])
+    got = ids.cpu().numpy()
+    reads += [(1, 4 + k, int(got[k])) for k in range(13)]
+    # a batched prefill of 10 slots (MFMA read-out), then a 10-row decode step
+    slots = list(range(2, 12))
+    toks = [syn.make_prompt(TINY, 2 + j % 3, 50 + j) for j in range(10)]
+    poss = [np.arange(len(t)) for t in toks]
+    bids = torch.zeros(10, dtype=torch.int32, device=DEV)
+    m.prefill_batch(slots, toks, poss, None, bids)
+    b0 = bids.cpu().numpy()
+    reads += [(s_, len(t) - 1, int(b0[j])) for j, (s_, t) in enumerate(zip(slots, toks))]
+    m.decode(slots, bids, [len(t) for t in toks], None, bids)
+    b1 = bids.cpu().numpy()
+    reads += [(s_, len(t), int(b1[j])) for j, (s_, t) in enumerate(zip(slots, toks))]
+    m.read_stops(stops_out)
+    torch.cuda.synchronize()
+    want = O.stop_positions(12, reads, stop)
+    assert list(stops_out.cpu().numpy()) == list(want), (list(stops_out.cpu().numpy()), list(want))
+    assert (want >= 0).any()  # the chain repeats its first run, so a stop id recurs
+    m.read_stops(stops_out, clear=True)
+    m.read_stops(stops_out)
+    torch.cuda.synchronize()
+    assert (stops_out.cpu().numpy() == -1).all()
+    with pytest.raises(q.Qwen2Error):
+        m.set_stop_ids([TINY.n_vocab])
+    with pytest.raises(q.Qwen2Error):
+        m.set_stop_ids(list(range(9)))
     p.close()
 
 

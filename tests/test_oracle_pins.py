@@ -154,6 +154,40 @@ def test_softmax_rows_sum_to_one_and_mask():
     assert np.all(p[:, 50:] == 0)
 
 
+def test_next_token_probs_closed_forms():
+    """Two logits give the logistic function of their difference; equal
+    logits give the uniform distribution; adding a constant changes nothing;
+    the largest logit keeps the largest probability; torch's softmax (an
+    independent routine) agrees."""
+    d = np.array([-4.0, -0.5, 0.0, 2.0, 30.0])
+    two = np.stack([d, np.zeros_like(d)], -1)
+    p = O.next_token_probs(two)
+    np.testing.assert_allclose(p[:, 0], 1 / (1 + np.exp(-d)), rtol=2e-7)
+    np.testing.assert_allclose(O.next_token_probs(np.full((1, 7), 3.5)), 1 / 7, rtol=1e-7)
+    rng = np.random.default_rng(6)
+    x = (rng.standard_normal((3, 1000)) * 8).astype(np.float32)
+    np.testing.assert_array_equal(O.next_token_probs(x), O.next_token_probs(x.astype(np.float64) + 1e3))
+    assert np.array_equal(np.argmax(O.next_token_probs(x), -1), np.argmax(x, -1))
+    ref = torch.softmax(torch.tensor(x, dtype=torch.float64), -1).numpy()
+    np.testing.assert_allclose(O.next_token_probs(x), ref, rtol=1e-6, atol=1e-30)
+
+
+def test_stop_positions_brute_force():
+    """The earliest read-out position per slot whose id is a stop id,
+    against a scan over every (slot, position) on small random histories."""
+    rng = np.random.default_rng(7)
+    for _ in range(50):
+        n_seq = int(rng.integers(1, 4))
+        stop = list(rng.integers(0, 6, rng.integers(0, 3)))
+        reads = [(int(rng.integers(0, n_seq)), int(rng.integers(0, 20)), int(rng.integers(0, 6)))
+                 for _ in range(rng.integers(0, 12))]
+        got = O.stop_positions(n_seq, reads, stop)
+        for s_ in range(n_seq):
+            hits = [p for p in range(20) for (q, pp, t) in reads if q == s_ and pp == p and t in stop]
+            assert got[s_] == (min(hits) if hits else -1)
+    assert list(O.stop_positions(2, [(0, 5, 9), (0, 3, 9), (1, 4, 8)], [9])) == [3, -1]
+
+
 def test_silu_closed_form():
     z = np.array([-3.0, 0.0, 1.5])
     np.testing.assert_allclose(O.silu(z), z * (1 / (1 + np.exp(-z))), rtol=1e-15)
