@@ -55,8 +55,9 @@ enum {
  * QwenConfig of xinfer Module 7, section 7.1).
  * Supported: n_embd == n_head * head_dim, n_embd % 64 == 0, n_embd <= 5120,
  * n_ctx <= 131072, n_head % n_head_kv == 0 with n_head / n_head_kv <= 8,
- * head_dim in {16, 64, 128}, rope_style == 0 (NonInterleaved, the Qwen2
- * convention of the minfer page, section 3), rope_theta > 0,
+ * head_dim in {16, 64, 128}, rope_style 0 (NonInterleaved: dimension d pairs
+ * with d + head_dim/2, the Qwen2 convention) or 1 (Interleaved: 2d pairs with
+ * 2d + 1), a model-level flag (minfer page, section 3), rope_theta > 0,
  * rope_freq_scale > 0, rms_eps >= 0, every size > 0. */
 typedef struct qwen2_hparams {
   int32_t n_layer, n_embd, n_head, n_head_kv, head_dim, n_ff, n_vocab;
@@ -64,7 +65,7 @@ typedef struct qwen2_hparams {
                          section 6), not the model's training context */
   int32_t n_seq;      /* independent sequence slots in the KV cache */
   int32_t tied;       /* 1: lm_head is the token embedding (xinfer 7.3) */
-  int32_t rope_style; /* 0 = NonInterleaved; anything else is rejected */
+  int32_t rope_style; /* 0 = NonInterleaved, 1 = Interleaved; else rejected */
   float rope_theta;   /* RoPE base; angle = pos * freq_scale * theta^(-2d/head_dim) */
   float rope_freq_scale;
   float rms_eps;      /* y = w * x / sqrt(mean(x^2) + rms_eps) */

@@ -116,6 +116,9 @@ class Hparams:
     rope_theta: float
     rms_eps: float
     rope_freq_scale: float = 1.0
+    # RoPE pairing is a model-level flag (minfer page, section 3): 0 =
+    # NonInterleaved (the Qwen2 family), 1 = Interleaved (Llama style)
+    rope_style: int = 0
 
     def validate(self) -> None:
         if min(self.n_layer, self.n_embd, self.n_head, self.n_head_kv,
@@ -130,6 +133,8 @@ class Hparams:
             raise OracleError("E_HPARAMS", "n_head % n_head_kv != 0")
         if self.head_dim % 2:
             raise OracleError("E_HPARAMS", "RoPE pairs need an even head_dim")
+        if self.rope_style not in (0, 1):
+            raise OracleError("E_HPARAMS", "rope_style is 0 (NonInterleaved) or 1 (Interleaved)")
 
 
 # --------------------------------------------------------------------------
@@ -176,8 +181,9 @@ def rope_rotate_half(x: np.ndarray, phi: np.ndarray) -> np.ndarray:
 
 
 def rope_interleaved(x: np.ndarray, phi: np.ndarray) -> np.ndarray:
-    """Llama-style Interleaved RoPE (pairs (2d, 2d+1)).  Not Qwen2's
-    convention (minfer page, section 3); kept only as a negative test."""
+    """Llama-style Interleaved RoPE: dimension 2d pairs with 2d + 1, rotated
+    by phi[:, d].  Not the Qwen2 family's convention, but a model-level flag
+    (minfer page, section 3)."""
     x = np.asarray(x, dtype=f64)
     a, b = x[..., 0::2], x[..., 1::2]
     c = np.cos(phi)[:, None, :]
@@ -387,8 +393,9 @@ class Qwen2Oracle:
             q = linear(x, L["wq"], L["bq"], self._w64((l, "wq"), L["wq"]))
             k = linear(x, L["wk"], L["bk"], self._w64((l, "wk"), L["wk"]))
             v = linear(x, L["wv"], L["bv"], self._w64((l, "wv"), L["wv"]))
-            q = rope_rotate_half(q.reshape(n, nh, hd), phi)
-            k = rope_rotate_half(k.reshape(n, nkv, hd), phi)
+            rope = rope_interleaved if self.hp.rope_style == 1 else rope_rotate_half
+            q = rope(q.reshape(n, nh, hd), phi)
+            k = rope(k.reshape(n, nkv, hd), phi)
             v = v.reshape(n, nkv, hd)
             # KV store of every row first, then attention.
             for i in range(n):
@@ -433,9 +440,9 @@ class Qwen2Oracle:
                       final_norm_output=y, taps=T)
 
 
-def hparams_for(shape, n_ctx: int, n_seq: int = 1) -> Hparams:
+def hparams_for(shape, n_ctx: int, n_seq: int = 1, rope_style: int = 0) -> Hparams:
     """Hparams from a ``qwen2_synth.ModelShape`` plus the cache sizes."""
     return Hparams(n_layer=shape.n_layer, n_embd=shape.n_embd, n_head=shape.n_head,
                    n_head_kv=shape.n_head_kv, head_dim=shape.head_dim, n_ff=shape.n_ff,
                    n_vocab=shape.n_vocab, n_ctx=n_ctx, n_seq=n_seq, tied=shape.tied,
-                   rope_theta=shape.rope_theta, rms_eps=shape.rms_eps)
+                   rope_theta=shape.rope_theta, rms_eps=shape.rms_eps, rope_style=rope_style)

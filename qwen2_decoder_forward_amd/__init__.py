@@ -308,8 +308,9 @@ def qwen2_free(ctx: int) -> None:
 class Model:
     """A loaded context with its hparams (convenience over the calls above)."""
 
-    def __init__(self, shape, weights: dict, n_ctx: int, n_seq: int = 1, stream=None):
-        self.hp = make_hparams(shape, n_ctx, n_seq)
+    def __init__(self, shape, weights: dict, n_ctx: int, n_seq: int = 1, stream=None,
+                 rope_style: int = 0):
+        self.hp = make_hparams(shape, n_ctx, n_seq, rope_style)
         self.ctx = qwen2_load(self.hp, weights, stream)
 
     def prefill(self, seq, tokens, positions, logits=None, argmax=None, stream=None):

@@ -149,9 +149,9 @@ void read_stops(unsigned *stop_pos, int n, int *out, int clear, hipStream_t st) 
 }
 
 // Next-token distribution p = softmax(logits row), in two launches over
-// kProbBlocks blocks per row.  First: each block's maximum m_b and
-// s_b = sum over its columns of e^(x - m_b), as an online (max, sum) per
-// thread, then combined over the block.
+// kProbBlocks blocks per row (one per CU for a single row).  First: each
+// block's maximum m_b and s_b = sum over its columns of e^(x - m_b), as an
+// online (max, sum) per thread, then combined over the block.
 __device__ __forceinline__ void ms_combine(float &m, float &s, float m2, float s2) {
   const float mm = fmaxf(m, m2);
   if (mm == kNegInf) return;  // (both empty)
@@ -189,23 +189,26 @@ __global__ __launch_bounds__(256) void k_softmax_part(const float *logits, int V
   }
 }
 
-// Second: every block combines its row's kProbBlocks partials into the row
-// maximum M and S = sum of e^(x - M), and writes e^(x - M) / S for its columns.
+// Second: every block combines its row's kProbBlocks partials (one per
+// thread) into the row maximum M and S = sum of e^(x - M), and writes
+// e^(x - M) / S for its columns.
 __global__ __launch_bounds__(256) void k_softmax_norm(const float *logits, int V,
                                                       const float2 *part, float *probs) {
   const int b = blockIdx.x, row = blockIdx.y;
-  __shared__ float2 sms;
-  if (threadIdx.x < 64) {
-    const float2 q = part[(size_t)row * kProbBlocks + threadIdx.x];  // (kProbBlocks = 64)
+  __shared__ float2 sw[4];
+  {
+    const float2 q = part[(size_t)row * kProbBlocks + threadIdx.x];  // (kProbBlocks = 256)
     float m = q.x, s = q.y;
     for (int off = 32; off > 0; off >>= 1) {
       const float m2 = __shfl_xor(m, off), s2 = __shfl_xor(s, off);
       ms_combine(m, s, m2, s2);
     }
-    if (threadIdx.x == 0) sms = make_float2(m, s);
+    if ((threadIdx.x & 63) == 0) sw[threadIdx.x >> 6] = make_float2(m, s);
   }
   __syncthreads();
-  const float M = sms.x, inv = 1.0f / sms.y;
+  float M = sw[0].x, S = sw[0].y;
+  for (int i = 1; i < 4; ++i) ms_combine(M, S, sw[i].x, sw[i].y);
+  const float inv = 1.0f / S;
   const int chunk = (V + kProbBlocks - 1) / kProbBlocks;
   const int c0 = b * chunk, c1 = min(V, c0 + chunk);
   const float *x = logits + (size_t)row * V;
@@ -215,10 +218,36 @@ __global__ __launch_bounds__(256) void k_softmax_norm(const float *logits, int V
 
 void softmax_rows(const float *logits, int rows, int V, float2 *part, float *probs,
                   hipStream_t st) {
-  static_assert(kProbBlocks == 64, "one partial per lane of the combining wavefront");
+  static_assert(kProbBlocks == 256, "one partial per thread of the combining block");
   const dim3 grid(kProbBlocks, rows);
   hipLaunchKernelGGL(k_softmax_part, grid, dim3(256), 0, st, logits, V, part);
   hipLaunchKernelGGL(k_softmax_norm, grid, dim3(256), 0, st, logits, V, part, probs);
+}
+
+// Interleaved-RoPE models hold K with dimension 2j at j and 2j+1 at j + hd/2.
+// to_pairs: natural [rows, hd] -> that order; else back.  One thread per
+// (row, j).
+__global__ void k_pair_order(const float *src, float *dst, int rows, int hd, int to_pairs) {
+  const int half = hd / 2;
+  const int i = blockIdx.x * blockDim.x + threadIdx.x;
+  if (i < rows * half) {
+    const int r = i / half, j = i - r * half;
+    const float *s = src + (size_t)r * hd;
+    float *o = dst + (size_t)r * hd;
+    if (to_pairs) {
+      o[j] = s[2 * j];
+      o[j + half] = s[2 * j + 1];
+    } else {
+      o[2 * j] = s[j];
+      o[2 * j + 1] = s[j + half];
+    }
+  }
+}
+
+void pair_order(const float *src, float *dst, int rows, int hd, bool to_pairs, hipStream_t st) {
+  const int n = rows * (hd / 2);
+  hipLaunchKernelGGL(k_pair_order, dim3((n + 255) / 256), dim3(256), 0, st, src, dst, rows, hd,
+                     (int)to_pairs);
 }
 
 }  // namespace q2

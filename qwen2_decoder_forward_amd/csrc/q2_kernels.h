@@ -94,11 +94,14 @@ void gemv_lmhead(const Dims &d, const uint16_t *W, const float *norm_w, const fl
 // Writes the index of each row's packed maximum and clears it, and latches
 // stop ids; launched after an lm_head kernel.
 void argmax_finalize(const ArgmaxEpi &e, int M, hipStream_t st);
+// Between natural K rows [rows, hd] and the rotation-pair order an
+// Interleaved-RoPE model keeps in its cache (2j -> j, 2j+1 -> j + hd/2).
+void pair_order(const float *src, float *dst, int rows, int hd, bool to_pairs, hipStream_t st);
 // out[s] = the latched stop position of slot s, -1 for none (reset with clear).
 void read_stops(unsigned *stop_pos, int n, int *out, int clear, hipStream_t st);
 // probs[r] = softmax(logits[r]) for rows r < rows, over V columns; part holds
 // rows * kProbBlocks (max, sum) pairs.
-constexpr int kProbBlocks = 64;
+constexpr int kProbBlocks = 256;
 void softmax_rows(const float *logits, int rows, int V, float2 *part, float *probs,
                   hipStream_t st);
 

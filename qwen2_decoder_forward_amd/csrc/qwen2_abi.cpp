@@ -125,8 +125,15 @@ void release(qwen2_ctx *c) {
   delete c;
 }
 
-// Packs the fused QKV rows: for every head of [q | k | v], packed rows
-// (2j, 2j+1) = natural rows (j, j + hd/2).
+// Packs the fused QKV rows.  The kernels rotate packed row pair (2j, 2j+1)
+// of a head by RoPE angle j and write the pair to dimensions j and j + hd/2
+// of the q row or KV slot.  NonInterleaved (and every v head): packed rows
+// (2j, 2j+1) = natural rows (j, j + hd/2), so dimensions keep their order.
+// Interleaved q and k heads: packed rows (2j, 2j+1) = natural rows (2j,
+// 2j+1), the pair the Interleaved style rotates by angle j; q and k then
+// hold the same permutation of their dimensions (2j -> j, 2j+1 -> j + hd/2),
+// which leaves every q.k product, and so the attention, unchanged.  The
+// cache's K copies (qwen2_kv_read / kv_write) undo and apply it.
 template <typename T>
 void pack_qkv(const qwen2_hparams &hp, const T *q, const T *k, const T *v, size_t rowlen,
               std::vector<T> &out) {
@@ -134,19 +141,21 @@ void pack_qkv(const qwen2_hparams &hp, const T *q, const T *k, const T *v, size_
   const int nh = hp.n_head, nkv = hp.n_head_kv;
   out.assign((size_t)(nh + 2 * nkv) * hd * rowlen, T(0));
   size_t dst_row = 0;
-  auto put_heads = [&](const T *src, int heads) {
+  auto put_heads = [&](const T *src, int heads, bool interleaved) {
     for (int hh = 0; hh < heads; ++hh)
       for (int j = 0; j < half; ++j) {
         for (int part = 0; part < 2; ++part) {
-          const size_t srow = (size_t)hh * hd + j + part * half;
+          const int dim = interleaved ? 2 * j + part : j + part * half;
+          const size_t srow = (size_t)hh * hd + dim;
           memcpy(&out[dst_row * rowlen], src + srow * rowlen, rowlen * sizeof(T));
           ++dst_row;
         }
       }
   };
-  put_heads(q, nh);
-  put_heads(k, nkv);
-  put_heads(v, nkv);
+  const bool il = hp.rope_style == 1;
+  put_heads(q, nh, il);
+  put_heads(k, nkv, il);
+  put_heads(v, nkv, false);
 }
 
 }  // namespace
@@ -785,16 +794,19 @@ static int kv_copy(qwen2_ctx *c, int32_t layer, int32_t seq, int32_t pos0, int32
     return set_err(c, QWEN2_E_POS, "kv range outside [0, n_ctx)");
   const q2::KVCache kv = kv_of(c);
   const size_t bytes = (size_t)n * c->d.hd * 4;
+  const bool il = c->hp.rope_style == 1;  // K held in rotation-pair order (see pack_qkv)
   for (int g = 0; g < c->d.nkv; ++g) {
     float *ck = c->kc + kv.off(c->d, layer, seq, g, pos0);
     float *cv = c->vc + kv.off(c->d, layer, seq, g, pos0);
     float *bk = k + (size_t)g * n * c->d.hd, *bv = v + (size_t)g * n * c->d.hd;
     hipStream_t st = (hipStream_t)stream;
     if (to_cache) {
-      HIP_TRY(c, hipMemcpyAsync(ck, bk, bytes, hipMemcpyDeviceToDevice, st));
+      if (il) q2::pair_order(bk, ck, n, c->d.hd, true, st);
+      else HIP_TRY(c, hipMemcpyAsync(ck, bk, bytes, hipMemcpyDeviceToDevice, st));
       HIP_TRY(c, hipMemcpyAsync(cv, bv, bytes, hipMemcpyDeviceToDevice, st));
     } else {
-      HIP_TRY(c, hipMemcpyAsync(bk, ck, bytes, hipMemcpyDeviceToDevice, st));
+      if (il) q2::pair_order(ck, bk, n, c->d.hd, false, st);
+      else HIP_TRY(c, hipMemcpyAsync(bk, ck, bytes, hipMemcpyDeviceToDevice, st));
       HIP_TRY(c, hipMemcpyAsync(bv, cv, bytes, hipMemcpyDeviceToDevice, st));
     }
   }

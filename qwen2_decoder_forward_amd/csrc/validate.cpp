@@ -43,8 +43,8 @@ int check_hparams(const qwen2_hparams *hp, std::string *msg) {
     return fail(msg, QWEN2_E_HPARAMS, "n_embd %lld > 5120 is not supported", hp->n_embd);
   if (hp->n_ctx > 131072)  // the decode attention merges at most 2048 64-key chunks
     return fail(msg, QWEN2_E_HPARAMS, "n_ctx %lld > 131072 is not supported", hp->n_ctx);
-  if (hp->rope_style != 0)
-    return fail(msg, QWEN2_E_HPARAMS, "rope_style %lld: only 0 (NonInterleaved) is supported",
+  if (hp->rope_style != 0 && hp->rope_style != 1)
+    return fail(msg, QWEN2_E_HPARAMS, "rope_style %lld: 0 (NonInterleaved) or 1 (Interleaved)",
                 hp->rope_style);
   if (!(hp->rope_theta > 0.f) || !(hp->rope_freq_scale > 0.f) || !(hp->rms_eps >= 0.f))
     return fail(msg, QWEN2_E_HPARAMS, "rope_theta, rope_freq_scale must be > 0, rms_eps >= 0");

@@ -55,11 +55,12 @@ def check_probs(got, logits, what):
 class Pair:
     """A GPU context and an oracle over the same weights."""
 
-    def __init__(self, shape, weights, n_ctx, n_seq=1, cache_decoded=False):
+    def __init__(self, shape, weights, n_ctx, n_seq=1, cache_decoded=False, rope_style=0):
         self.shape = shape
         self.w = weights
-        self.m = q.Model(shape, weights, n_ctx, n_seq)
-        self.o = O.Qwen2Oracle(O.hparams_for(shape, n_ctx, n_seq), weights, cache_decoded)
+        self.m = q.Model(shape, weights, n_ctx, n_seq, rope_style=rope_style)
+        self.o = O.Qwen2Oracle(O.hparams_for(shape, n_ctx, n_seq, rope_style), weights,
+                               cache_decoded)
         self.V, self.H = shape.n_vocab, shape.n_embd
         self.logits = torch.empty((max(n_seq, 1), self.V), dtype=torch.float32, device=DEV)
         self.ids = torch.zeros(max(n_seq, 1), dtype=torch.int32, device=DEV)

@@ -140,8 +140,11 @@ def test_hparams_checks(change, ok):
 
 def test_rope_style_and_bad_scalars_rejected():
     hp = hp_for(syn.MODELS["tiny"])
-    hp.rope_style = 1
-    assert q.CODES[q.qwen2_check_hparams(hp)] == "E_HPARAMS"
+    hp.rope_style = 1  # Interleaved: a model-level flag
+    assert q.CODES[q.qwen2_check_hparams(hp)] == "OK"
+    for bad in (2, -1):
+        hp.rope_style = bad
+        assert q.CODES[q.qwen2_check_hparams(hp)] == "E_HPARAMS"
     hp = hp_for(syn.MODELS["tiny"])
     hp.rope_theta = 0.0
     assert q.CODES[q.qwen2_check_hparams(hp)] == "E_HPARAMS"

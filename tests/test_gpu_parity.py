@@ -250,6 +250,32 @@ def test_prefill_batch_rejects_before_any_work(tiny_w):
     p.close()
 
 
+def test_interleaved_rope_model(tiny_w):
+    """rope_style 1 (Interleaved, a model-level flag): prompt 8 and greedy
+    steps on the f32 path, a 40-row MFMA prefill, and the K cache read back
+    in natural dimension order, all against the oracle run with the same
+    flag (whose interleaved rotation differs from the default one)."""
+    p = Pair(TINY, tiny_w, n_ctx=64, rope_style=1)
+    run_chain(p, syn.make_prompt(TINY, 8, 4), 4, TOL_F32, "interleaved")
+    nkv, hd = TINY.n_head_kv, TINY.head_dim
+    for l in range(TINY.n_layer):
+        k = torch.empty((nkv, 12, hd), device=DEV)
+        v = torch.empty((nkv, 12, hd), device=DEV)
+        p.m.kv_read(l, 0, 0, 12, k, v)
+        torch.cuda.synchronize()
+        check(k.cpu().numpy(), p.o.k_cache[0][l][:, :12], TOL_F32, f"interleaved K layer {l}")
+        check(v.cpu().numpy(), p.o.v_cache[0][l][:, :12], TOL_F32, f"interleaved V layer {l}")
+        # a write of what was read leaves the cache (and the next step) unchanged
+        p.m.kv_write(l, 0, 0, 12, k, v)
+    lg, _, r = p.decode([0], [3], [12])
+    check(lg[0], r.logits[0], TOL_F32, "interleaved decode after a K round trip")
+    p.close()
+    p = Pair(TINY, tiny_w, n_ctx=128, rope_style=1)
+    lg, gid, r = p.prefill(0, syn.make_prompt(TINY, 40, 6), np.arange(40))
+    check(lg, r.logits[0], TOL, "interleaved 40-row prefill")
+    p.close()
+
+
 def test_next_token_probs(tiny_w):
     """Softmax of the read-out logits: one row after a prefill, 12 after a
     batched decode, and rows of wide-range logits written directly (large
@@ -344,6 +370,36 @@ def test_hd128_untied_group7(n):
     w = syn.make_weights(HD128)
     p = Pair(HD128, w, n_ctx=256)
     run_chain(p, syn.make_prompt(HD128, n), 4, TOL if n > 8 else TOL_F32 * 10, f"hd128-{n}")
+    p.close()
+
+
+# Head layouts of the family at their real widths (two layers, a small FFN
+# and vocabulary): 12/2 and 16/2 heads of 128 (groups 6 and 8), 40/8 (group
+# 5, the widest hidden size the decode GEMVs take), multi-head attention
+# (n_head_kv = n_head, Qwen1.5) and the two other RoPE bases.
+FAMILY = {
+    "heads12-2": dict(n_embd=1536, n_head=12, n_head_kv=2, head_dim=128),
+    "heads16-2": dict(n_embd=2048, n_head=16, n_head_kv=2, head_dim=128),
+    "heads40-8": dict(n_embd=5120, n_head=40, n_head_kv=8, head_dim=128),
+    "mha8-theta1e4": dict(n_embd=512, n_head=8, n_head_kv=8, head_dim=64, rope_theta=1e4),
+    "theta1e7": dict(n_embd=896, n_head=14, n_head_kv=2, head_dim=64, rope_theta=1e7),
+}
+
+
+@pytest.mark.parametrize("name", list(FAMILY))
+def test_family_head_shapes(name):
+    """Prompt 5 (f32 path) with greedy steps, then a 40-row prompt (MFMA
+    path), against the oracle."""
+    shape = dataclasses.replace(syn.MODELS["qwen2-hd128"], name=name, n_layer=2, n_ff=512,
+                                n_vocab=2048, **FAMILY[name])
+    w = syn.make_weights(shape)
+    p = Pair(shape, w, n_ctx=128)
+    run_chain(p, syn.make_prompt(shape, 5), 3, TOL_F32 * 10, f"{name}-5")
+    p.close()
+    p = Pair(shape, w, n_ctx=128)
+    lg, gid, r = p.prefill(0, syn.make_prompt(shape, 40, 2), np.arange(40))
+    check(lg, r.logits[0], TOL, f"{name} 40-row prefill")
+    check_id(gid, r.logits[0], r.argmax[0], f"{name} 40-row prefill")
     p.close()
 
 

@@ -145,6 +145,25 @@ def test_interleaved_rope_differs():
     assert np.max(np.abs(O.rope_interleaved(x, phi) - O.rope_rotate_half(x, phi))) > 1e-2
 
 
+def test_interleaved_rope_closed_form_and_pair_order():
+    """Interleaved RoPE turns each pair (x[2d], x[2d+1]) by phi[d] (the 2-D
+    rotation written out), and equals rotate_half applied after moving
+    dimension 2d to d and 2d+1 to d + hd/2, then moved back."""
+    rng = np.random.default_rng(8)
+    x = rng.standard_normal((3, 2, 8)).astype(np.float32)
+    phi = O.rope_angles(np.array([0, 5, 77]), 8, 1e4)
+    got = O.rope_interleaved(x, phi)
+    for n in range(3):
+        for d in range(4):
+            c, s = np.cos(phi[n, d]), np.sin(phi[n, d])
+            a, b = x[n, :, 2 * d].astype(np.float64), x[n, :, 2 * d + 1].astype(np.float64)
+            np.testing.assert_allclose(got[n, :, 2 * d], a * c - b * s, rtol=1e-6, atol=1e-7)
+            np.testing.assert_allclose(got[n, :, 2 * d + 1], b * c + a * s, rtol=1e-6, atol=1e-7)
+    perm = np.concatenate([np.arange(0, 8, 2), np.arange(1, 8, 2)])  # new dim j <- old perm[j]
+    back = np.argsort(perm)
+    np.testing.assert_array_equal(O.rope_rotate_half(x[..., perm], phi)[..., back], got)
+
+
 def test_softmax_rows_sum_to_one_and_mask():
     rng = np.random.default_rng(5)
     s = rng.standard_normal((6, 100)) * 30
