@@ -22,7 +22,8 @@ namespace {
 
 constexpr int kRing = 4;          // pinned staging slots for per-call row data
 constexpr int kGemvRows = 8;      // rows up to this use the f32 GEMV path
-constexpr int kMaxPassRows = 4096;  // rows per prefill pass
+constexpr int kMaxPassRows = 4096;   // rows per prefill pass of one sequence
+constexpr int kMaxBatchRows = 8192;  // rows per pass of a multi-sequence context
 constexpr int kProfMax = 16384;     // timed launches between two reads
 constexpr size_t kSlotBytes = 64;   // pointer slots at the head of a staged call
 constexpr size_t kSplitKBytes = 64ull << 20;  // split-K partial sums (large-M residual GEMMs: <= 256 x 256 x 256 x 4 B)
@@ -314,7 +315,7 @@ int qwen2_load(const qwen2_hparams *hp, const qwen2_weights *w, void *stream, qw
 
   // ---- scratch
   // one sequence never has more than n_ctx rows; a batch of several may
-  c->max_rows = d.n_seq > 1 ? kMaxPassRows : std::min(d.n_ctx, kMaxPassRows);
+  c->max_rows = d.n_seq > 1 ? kMaxBatchRows : std::min(d.n_ctx, kMaxPassRows);
   c->rows_cap = std::max(c->max_rows, d.n_seq);
   c->dec_rows = std::max(d.n_seq, kGemvRows);
   c->part.n_chunks = (d.n_ctx + q2::kChunkKeys - 1) / q2::kChunkKeys;

@@ -216,10 +216,11 @@ def test_prefill_batch_mfma_rows(tiny_w, lens):
 
 
 def test_prefill_batch_straddles_passes(tiny_w):
-    """5,030 rows in all: the 4,096-row first pass ends inside the second
-    sequence, whose rows continue in the next pass."""
-    p = Pair(TINY, tiny_w, n_ctx=4096, n_seq=3)
-    lens = [3000, 2000, 30]
+    """9,030 rows in all: the 8,192-row first pass of a multi-sequence
+    context ends inside the second sequence, whose rows continue in the next
+    pass."""
+    p = Pair(TINY, tiny_w, n_ctx=8192, n_seq=3)
+    lens = [6000, 3000, 30]
     seqs = [1, 0, 2]
     toks = [syn.make_prompt(TINY, n, 80 + i) for i, n in enumerate(lens)]
     poss = [np.arange(n) for n in lens]
