@@ -148,8 +148,9 @@ void read_stops(unsigned *stop_pos, int n, int *out, int clear, hipStream_t st) 
                      clear);
 }
 
-// Next-token distribution p = softmax(logits row), in two launches over
-// kProbBlocks blocks per row (one per CU for a single row).  First: each
+// Next-token distribution p = softmax(logits row), in two launches over nb
+// blocks per row (nb <= kProbBlocks: one per CU for a single row, fewer
+// per row as rows are added, so that blocks stay busy).  First: each
 // block's maximum m_b and s_b = sum over its columns of e^(x - m_b), as an
 // online (max, sum) per thread, then combined over the block.
 __device__ __forceinline__ void ms_combine(float &m, float &s, float m2, float s2) {
@@ -161,7 +162,7 @@ __device__ __forceinline__ void ms_combine(float &m, float &s, float m2, float s
 
 __global__ __launch_bounds__(256) void k_softmax_part(const float *logits, int V, float2 *part) {
   const int b = blockIdx.x, row = blockIdx.y;
-  const int chunk = (V + kProbBlocks - 1) / kProbBlocks;
+  const int chunk = (V + gridDim.x - 1) / gridDim.x;
   const int c0 = b * chunk, c1 = min(V, c0 + chunk);
   const float *x = logits + (size_t)row * V;
   float m = kNegInf, s = 0.f;
@@ -185,7 +186,7 @@ __global__ __launch_bounds__(256) void k_softmax_part(const float *logits, int V
   __syncthreads();
   if (threadIdx.x == 0) {
     for (int i = 1; i < 4; ++i) ms_combine(m, s, sw[i].x, sw[i].y);
-    part[(size_t)row * kProbBlocks + b] = make_float2(m, s);
+    part[(size_t)row * gridDim.x + b] = make_float2(m, s);
   }
 }
 
@@ -197,8 +198,12 @@ __global__ __launch_bounds__(256) void k_softmax_norm(const float *logits, int V
   const int b = blockIdx.x, row = blockIdx.y;
   __shared__ float2 sw[4];
   {
-    const float2 q = part[(size_t)row * kProbBlocks + threadIdx.x];  // (kProbBlocks = 256)
-    float m = q.x, s = q.y;
+    float m = kNegInf, s = 0.f;  // (threads past nb hold an empty partial)
+    if (threadIdx.x < gridDim.x) {
+      const float2 q = part[(size_t)row * gridDim.x + threadIdx.x];
+      m = q.x;
+      s = q.y;
+    }
     for (int off = 32; off > 0; off >>= 1) {
       const float m2 = __shfl_xor(m, off), s2 = __shfl_xor(s, off);
       ms_combine(m, s, m2, s2);
@@ -209,7 +214,7 @@ __global__ __launch_bounds__(256) void k_softmax_norm(const float *logits, int V
   float M = sw[0].x, S = sw[0].y;
   for (int i = 1; i < 4; ++i) ms_combine(M, S, sw[i].x, sw[i].y);
   const float inv = 1.0f / S;
-  const int chunk = (V + kProbBlocks - 1) / kProbBlocks;
+  const int chunk = (V + gridDim.x - 1) / gridDim.x;
   const int c0 = b * chunk, c1 = min(V, c0 + chunk);
   const float *x = logits + (size_t)row * V;
   float *y = probs + (size_t)row * V;
@@ -218,8 +223,9 @@ __global__ __launch_bounds__(256) void k_softmax_norm(const float *logits, int V
 
 void softmax_rows(const float *logits, int rows, int V, float2 *part, float *probs,
                   hipStream_t st) {
-  static_assert(kProbBlocks == 256, "one partial per thread of the combining block");
-  const dim3 grid(kProbBlocks, rows);
+  static_assert(kProbBlocks == 256, "at most one partial per thread of the combining block");
+  const int nb = std::max(16, std::min(kProbBlocks, 1024 / rows));
+  const dim3 grid(nb, rows);
   hipLaunchKernelGGL(k_softmax_part, grid, dim3(256), 0, st, logits, V, part);
   hipLaunchKernelGGL(k_softmax_norm, grid, dim3(256), 0, st, logits, V, part, probs);
 }
