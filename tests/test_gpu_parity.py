@@ -303,6 +303,11 @@ def test_next_token_probs(tiny_w):
     p.m.next_token_probs(p.logits, 5, probs)
     torch.cuda.synchronize()
     check_probs(probs[:5].cpu().numpy(), x.numpy(), "direct logits")
+    import qwen2_decoder_forward_amd as q
+    for rows in (0, 13):  # rows must be in [1, max(n_seq, 8)] = [1, 12]
+        with pytest.raises(q.Qwen2Error) as e:
+            p.m.next_token_probs(p.logits, rows, probs)
+        assert e.value.name == "E_ARG"
     p.close()
 
 
@@ -357,6 +362,14 @@ def test_stop_ids_latch_earliest_position(tiny_w):
         m.set_stop_ids([TINY.n_vocab])
     with pytest.raises(q.Qwen2Error):
         m.set_stop_ids(list(range(9)))
+    # no stop ids: nothing latches
+    m.set_stop_ids([])
+    ids.zero_()
+    for k in range(4):
+        m.decode([1], ids[k:k + 1], [20 + k], None, ids[k + 1:k + 2])
+    m.read_stops(stops_out)
+    torch.cuda.synchronize()
+    assert (stops_out.cpu().numpy() == -1).all()
     p.close()
 
 
