@@ -1093,7 +1093,10 @@ static void attn_prefill_launch(const Dims &d, int layer, const KVCache &kv, con
   // count over the launch (and at least 8 key tiles) are split in two, so no
   // block has more than about half of the longest tile's work.  Positions
   // increase within a sequence, so the key-tile count grows with the tile
-  // index and a sequence's split tiles are its last ones.
+  // index and a sequence's split tiles are its last ones.  With 512 or more
+  // blocks (two per CU) the CUs already balance long and short tiles, and
+  // the split's merge would only add work (batched 0.5B prefill, 8 x 1024
+  // rows per launch: 714 K -> 775 K tok/s without it).
   auto ntiles = [&](const PrefillSeg &g, int t) {
     return host_pos[g.r0 + std::min(32 * t + 31, g.n - 1)] / kPreKeys + 1;
   };
@@ -1108,7 +1111,7 @@ static void attn_prefill_launch(const Dims &d, int layer, const KVCache &kv, con
     total_tiles += T;
     kmax = std::max(kmax, ntiles(segs[i], T - 1));
   }
-  if (total_tiles * d.nkv >= 128 && kmax >= 8) {
+  if (total_tiles * d.nkv >= 128 && total_tiles * d.nkv < 512 && kmax >= 8) {
     const int lim = (kmax + 1) / 2;
     int n_split = 0;
     for (int i = 0; i < n; ++i) {
