@@ -171,7 +171,7 @@ def main():
     ap.add_argument("--cpu-seconds", type=float, default=15.0)
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--workload", default="0.5b",
-                    help="0.5b (the benchmark line, default), 0.5b-long, 0.5b-batched, hd128, tiny")
+                    help="0.5b (the benchmark line, default), 0.5b-long, 0.5b-batched, hd128, 1.5b-heads, tiny")
     ap.add_argument("--pmc-pass", action="store_true",
                     help="only the launches a rocprofv3 --pmc counter pass reads: a plain 256 MiB "
                          "device copy (calibration), then 48 launches of the gate/up GEMV")

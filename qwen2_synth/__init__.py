@@ -86,6 +86,11 @@ MODELS: Dict[str, ModelShape] = {
     # Qwen2-7B-like shape: hd 128, group 7, untied lm_head.
     "qwen2-hd128": ModelShape("qwen2-hd128", 28, 3584, 28, 4, 128, 18944,
                               152064, False, 1e6, 1e-6, 3),
+    # The 12-over-2 head layout of 1.5B (nnterp page, "Grouped-query
+    # attention": head_dim 128, so hidden 1536); the pages give no layer count
+    # or FFN width for it: 28 layers and FFN 8960, tied lm_head.
+    "qwen2.5-1.5b-heads": ModelShape("qwen2.5-1.5b-heads", 28, 1536, 12, 2, 128, 8960,
+                                     151936, True, 1e6, 1e-6, 4),
 }
 
 
@@ -111,6 +116,9 @@ WORKLOADS: Dict[str, Workload] = {
                              "Qwen2.5-0.5B shape: 64 sequences with a 1024-token prefix, one decode step each"),
     "hd128": Workload("hd128", "qwen2-hd128", 2048, 128, 4096, 1,
                       "Qwen2-7B-like shape (hd 128, untied): prompt 2048, 128 greedy steps, n_ctx 4096"),
+    "1.5b-heads": Workload("1.5b-heads", "qwen2.5-1.5b-heads", 512, 128, 4096, 1,
+                           "12/2 heads of 128 (the 1.5B layout), 28 layers, FFN 8960: prompt 512, "
+                           "128 greedy steps, n_ctx 4096"),
 }
 
 
