@@ -537,6 +537,8 @@ static void launch(GemvP &p, int max_grid, hipStream_t st) {
     // 18944: 24.6 -> 23.0 us)
     if (kc <= 2 || (kResidEpi<E1>() && kc > 10))
       hipLaunchKernelGGL((k_gemv1<R, 2, E1>), dim3(grid), dim3(256), 0, st, p);
+    else if (kc <= 4)
+      hipLaunchKernelGGL((k_gemv1<R, 4, E1>), dim3(grid), dim3(256), 0, st, p);
     else if (kc <= 8)
       hipLaunchKernelGGL((k_gemv1<R, 8, E1>), dim3(grid), dim3(256), 0, st, p);
     else
