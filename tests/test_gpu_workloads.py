@@ -8,7 +8,9 @@
 * the hd-128 / group-7 / untied shape at full width (2 layers) with a
   2048-token prompt against the oracle, and the full 28-layer model checked
   for properties that hold at any size (prefill of n+1 tokens = prefill of n
-  then one decode step; argmax = lowest index of the largest logit).
+  then one decode step; argmax = lowest index of the largest logit);
+* the 1.5B head layout (12/2 heads of 128) at full width (2 layers) with the
+  512-token workload prompt against the oracle.
 """
 import numpy as np
 import pytest
@@ -89,6 +91,20 @@ def test_hd128_full_width_two_layers_prompt(n):
     w = syn.make_weights(G2)
     p = Pair(G2, w, n_ctx=4096)
     run_chain(p, syn.make_prompt(G2, n), 2, TOL, f"hd128-L2-{n}")
+    p.close()
+
+
+@pytest.mark.parametrize("n", [512, 530])
+def test_1_5b_layout_full_width_two_layers_prompt(n):
+    """The 1.5B head layout (12/2 heads of 128, hidden 1536, FFN 8960, the
+    151,936-entry tied vocabulary) at two layers: the 512-token workload
+    prompt on the large-tile GEMMs and 530 rows (a ragged last row tile),
+    then greedy steps on the 4-chunk decode GEMVs."""
+    S15 = syn.model_shape("qwen2.5-1.5b-heads", n_layer=2)
+    say(f"[1.5b-L2-{n}] drawing weights")
+    w = syn.make_weights(S15)
+    p = Pair(S15, w, n_ctx=1024)
+    run_chain(p, syn.make_prompt(S15, n), 2, TOL, f"1.5b-L2-{n}")
     p.close()
 
 
