@@ -92,8 +92,7 @@ class Pair:
         self.m.decode(seqs, tdev, pos, self.logits[:B], self.ids[:B])
         r = self.o.decode(seqs, toks, pos)
         torch.cuda.synchronize()
-        # device-side flags (bad token id; a timed-out wait inside an
-        # overlapped decode step) must be clear
+        # the device-side bad-token flag must be clear
         assert self.m.sync_status() == 0
         return self.logits[:B].cpu().numpy(), self.ids[:B].cpu().numpy(), r
 

@@ -293,6 +293,49 @@ def test_oracle_matches_brute_force(kv):
         assert r.argmax[0] == int(np.argmax(ref[i]))
 
 
+@pytest.mark.parametrize("kv", [2, 4, 1])
+def test_interleaved_model_matches_brute_force(kv):
+    """The model-level Interleaved flag (minfer page, section 3) wired through
+    the whole oracle: q and k both rotated in 2d / 2d+1 pairs, v not at all,
+    on GQA, MHA and MQA layouts, prefill then cached decode steps."""
+    shape = syn.MODELS["tiny"] if kv == 2 else tiny_variant(n_head_kv=kv)
+    w = syn.make_weights(shape)
+    orc = O.Qwen2Oracle(O.hparams_for(shape, 64, 1, rope_style=1), w)
+    toks = syn.make_prompt(shape, 14, 9)
+    ref, outs = brute_force(shape, w, toks, interleaved=True)
+    r = orc.prefill(0, toks[:9], np.arange(9))
+    assert rel_err(r.logits[0], ref[8]) < 1e-6
+    assert rel_err(r.layer_output[0], outs[-1][8]) < 1e-6
+    for i in range(9, 14):
+        r = orc.decode([0], [toks[i]], [i])
+        assert rel_err(r.logits[0], ref[i]) < 1e-6, i
+        assert r.argmax[0] == int(np.argmax(ref[i]))
+    # and the flag matters: the NonInterleaved brute force disagrees
+    ref_ni, _ = brute_force(shape, w, toks, interleaved=False)
+    assert rel_err(r.logits[0], ref_ni[13]) > 1e-3
+
+
+def test_interleaved_pin_catches_a_half_wired_flag(monkeypatch):
+    """Planted mistake: the Interleaved pairing applied to q but the
+    NonInterleaved one to k.  The model-level pin above must reject it."""
+    shape = syn.MODELS["tiny"]
+    w = syn.make_weights(shape)
+    toks = syn.make_prompt(shape, 10, 9)
+    ref, _ = brute_force(shape, w, toks, interleaved=True)
+    calls = {"n": 0}
+    real = O.rope_interleaved
+
+    def q_only(x, phi):
+        calls["n"] += 1
+        return real(x, phi) if calls["n"] % 2 == 1 else O.rope_rotate_half(x, phi)
+
+    monkeypatch.setattr(O, "rope_interleaved", q_only)
+    orc = O.Qwen2Oracle(O.hparams_for(shape, 64, 1, rope_style=1), w)
+    r = orc.prefill(0, toks, np.arange(10))
+    assert calls["n"] == 2 * shape.n_layer
+    assert rel_err(r.logits[0], ref[9]) > 1e-3
+
+
 def test_wrong_rope_style_is_detected_by_brute_force():
     shape = syn.MODELS["tiny"]
     orc, w = build(shape)
