@@ -4,8 +4,16 @@
 // KV head j serves query heads 7j..7j+6, nnterp Qwen2 page, "Grouped-query
 // attention"); scores are scaled by head_dim^-0.5; a row at position p sees
 // the KV slots 0..p of its own sequence (full causal attention, no window).
-// Both kernels load each K/V tile once per KV head and share it across the
-// whole query group.
+//
+// Which kernels share a KV head's K / V across its query group:
+//  * k_attn_decode (chunked decode attention) and k_attn_prefill (MFMA
+//    prefill attention) load each K / V tile once per KV head and use it for
+//    every query head of the group (k_attn_prefill's short-prompt form runs
+//    one head per block instead, so the group's heads spread over CUs);
+//  * k_attn_wo1 and k_attn_wo (attention fused with WO, short contexts) do
+//    not: a block serves one (WO row chunk, query head) pair and reads that
+//    head's K / V itself.  Their cost is the per-block K / V fetch and the
+//    kernel's fixed latency, not the total K / V traffic (see k_attn_wo1).
 #include <algorithm>
 
 #include "q2_device.h"
@@ -240,6 +248,12 @@ struct AttnWoP {
   int ldh;
   int rows_per_block;
   float scale;
+  // One-row calls (k_attn_wo1): K and V of KV head 0 of the row's (layer,
+  // sequence) block (head g starts g * n_ctx * HD floats later) and the
+  // number of key slots nk1 its loads cover (the row's position < nk1 <=
+  // n_ctx), known on the host; the position itself is read on the device.
+  const float *kb1, *vb1;
+  int nk1;
 };
 
 template <int N>
@@ -266,7 +280,7 @@ __global__ __launch_bounds__(256) void k_attn_wo(AttnWoP p) {
   constexpr int KPL = KW / PH;
   constexpr int LPR = HD / 8;              // lanes per WO row segment (8 halves each)
   constexpr int RPI = 64 / LPR;            // WO rows per wavefront load
-  constexpr int WI = wo_loads_per_wave(HD);  // WO loads per wavefront
+  constexpr int WI = wo_loads_fused(HD);  // WO loads per wavefront
   // K tile in LDS, 16-byte chunk c of key row j stored at chunk c ^ (j % C4):
   // a lane walking its own row meets a different bank group than its
   // neighbours, so the row reads are conflict-free without padding.
@@ -421,20 +435,197 @@ __global__ __launch_bounds__(256) void k_attn_wo(AttnWoP p) {
   }
 }
 
+// Sum of v over the lanes l with the same l % N (N a power of two, 4..32):
+// the other lanes of the wavefront hold other keys' partial sums for the
+// same dimensions.
+template <int N>
+__device__ __forceinline__ float across_groups(float v) {
+  if (N < 16) {  // (only head_dim 16: 4 lanes per key)
+    for (int o = N; o < 16; o <<= 1) v += __shfl_xor(v, o, 64);
+  }
+  if (N < 32) {
+    float a, b;
+    pair16(v, a, b);
+    v = a + b;
+  }
+  return sum32(v);
+}
+
+// One row (batch-1 decode, a prefill's last row): one block per (WO row
+// chunk, query head), as k_attn_wo, with a shorter critical path.  The
+// host gives the row's K / V block and a key bound nk1, so every load of
+// the block (q, the WO slice, the position and the K / V of its first key
+// tile) is issued at once, before any of them is waited for.  A key's
+// score is computed where its K row lands: HD / 4 lanes hold 4 dimensions
+// each and combine their partial dot products with DPP, so K never goes
+// through LDS; softmax and P.V stay in registers, and the four wavefronts
+// meet twice per call (the tile maximum, then the outputs).  Keys past the
+// position get a -inf score and a zero V (a select, so whatever a slot past
+// the position holds cannot reach the sums).
+template <int HD>
+__global__ __launch_bounds__(256) void k_attn_wo1(AttnWoP p) {
+  constexpr int LPK = HD / 4;             // lanes per key (4 dims, one 16-byte load, each)
+  constexpr int KPI = 64 / LPK;           // keys per wavefront load
+  constexpr int NI = HD == 16 ? 8 : 16;   // K (and V) loads per lane and key tile
+  constexpr int KPW = NI * KPI;           // keys per wavefront and tile
+  constexpr int TK = 4 * KPW;             // keys per tile: 256 (hd 64), 128 (hd 128), 512 (hd 16)
+  constexpr int LPR = HD / 8;             // lanes per WO row segment (8 halves each)
+  constexpr int RPI = 64 / LPR;           // WO rows per wavefront load
+  constexpr int WI = wo_loads_fused(HD);  // WO loads per wavefront
+  __shared__ float sM[2][4];
+  __shared__ float sL[4];
+  __shared__ __attribute__((aligned(16))) float sO[4][HD];
+
+  const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
+  const int rc = blockIdx.x, head = blockIdx.y;
+  const int G = p.d.group, H = p.d.H, nhd = p.d.nh * HD;
+  const int g = head / G;
+  const int dc = lane % LPK, kg = lane / LPK;
+  {  // the kernel arguments the loads need, in the first scalar-load batch
+    const int *rp = p.rows.pos;
+    const float *qp = p.q, *kp = p.kb1, *vp = p.vb1;
+    const _Float16 *wp = p.wo;
+    asm volatile("" ::"s"(rp), "s"(qp), "s"(kp), "s"(vp), "s"(wp));
+    asm volatile("" ::"s"(G), "s"(H), "s"(p.d.nh), "s"(p.d.n_ctx), "s"(p.nk1),
+                 "s"(p.rows_per_block), "s"(p.scale));
+  }
+  const unsigned pos = vload(p.rows.pos, 0);
+  const f4 q4 = *(const f4 *)(p.q + (size_t)head * HD + 4 * dc);
+  const int r0 = rc * p.rows_per_block;
+  const int rend = min(H, r0 + p.rows_per_block);
+  const int kc = lane % LPR;
+  h8 wreg[WI];
+#pragma unroll
+  for (int i = 0; i < WI; ++i) {
+    const int row = r0 + (w * WI + i) * RPI + lane / LPR;
+    wreg[i] = __builtin_nontemporal_load(
+        (const h8 *)(p.wo + (size_t)min(row, H - 1) * nhd + (size_t)head * HD + kc * 8));
+  }
+  const float *kb = p.kb1 + (size_t)g * p.d.n_ctx * HD + 4 * dc;
+  const float *vb = p.vb1 + (size_t)g * p.d.n_ctx * HD + 4 * dc;
+  const int klast = p.nk1 - 1;
+
+  float m_run = kNegInf, l_run = 0.f;
+  f4 o = {0.f, 0.f, 0.f, 0.f};
+  int t0 = 0, tile = 0;
+  unsigned pos_t;
+  do {
+    f4 kr[NI], vr[NI];
+#pragma unroll
+    for (int i = 0; i < NI; ++i) {
+      const int key = min(t0 + w * KPW + i * KPI + kg, klast);
+      kr[i] = *(const f4 *)(kb + (size_t)key * HD);
+    }
+#pragma unroll
+    for (int i = 0; i < NI; ++i) {
+      const int key = min(t0 + w * KPW + i * KPI + kg, klast);
+      vr[i] = *(const f4 *)(vb + (size_t)key * HD);
+    }
+    __builtin_amdgcn_sched_barrier(0);  // (every load of the tile issued before any use)
+    // The position, passed through an empty asm here: otherwise the
+    // compiler derives the trip count from it before the loop, which waits
+    // for its load ahead of the K / V loads.
+    pos_t = pos;
+    asm volatile("" : "+v"(pos_t));
+    // scores of this lane group's NI keys (each in all LPK lanes of the group)
+    float sc[NI];
+    float mt = kNegInf;
+#pragma unroll
+    for (int i = 0; i < NI; ++i) {
+      float a = q4.x * kr[i].x;
+      a = fmaf(q4.y, kr[i].y, a);
+      a = fmaf(q4.z, kr[i].z, a);
+      a = fmaf(q4.w, kr[i].w, a);
+      a = group_sum<LPK < 16 ? LPK : 16>(a);
+      if (LPK == 32) {  // (a key's 32 lanes: rows l and l ^ 16 of a half)
+        float x, y;
+        pair16(a, x, y);
+        a = x + y;
+      }
+      const unsigned key = (unsigned)(t0 + w * KPW + i * KPI + kg);
+      sc[i] = key <= pos_t ? a * p.scale : kNegInf;
+      mt = fmaxf(mt, sc[i]);
+    }
+    mt = wave_max(mt);
+    if (lane == 0) sM[tile & 1][w] = mt;
+    __syncthreads();
+    const float mx = fmaxf(fmaxf(sM[tile & 1][0], sM[tile & 1][1]),
+                           fmaxf(sM[tile & 1][2], sM[tile & 1][3]));
+    const float m_new = fmaxf(m_run, mx);  // (finite: key t0 <= pos is in every tile)
+    const float alpha = __expf(m_run - m_new);
+    float lt = 0.f;
+    f4 ot = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+    for (int i = 0; i < NI; ++i) {
+      const float e = __expf(sc[i] - m_new);
+      const unsigned key = (unsigned)(t0 + w * KPW + i * KPI + kg);
+      const f4 vv = key <= pos_t ? vr[i] : (f4){0.f, 0.f, 0.f, 0.f};
+      lt += e;
+      ot += e * vv;
+    }
+    l_run = l_run * alpha + lt;
+    o = o * alpha + ot;
+    m_run = m_new;
+    t0 += TK;
+    ++tile;
+  } while ((unsigned)t0 <= pos_t);
+
+  // this wavefront's sums over all its keys, then over the four wavefronts
+  o.x = across_groups<LPK>(o.x);
+  o.y = across_groups<LPK>(o.y);
+  o.z = across_groups<LPK>(o.z);
+  o.w = across_groups<LPK>(o.w);
+  l_run = across_groups<LPK>(l_run);
+  if (kg == 0) *(f4 *)&sO[w][4 * dc] = o;
+  if (lane == 0) sL[w] = l_run;
+  __syncthreads();
+  const float inv = 1.0f / ((sL[0] + sL[1]) + (sL[2] + sL[3]));
+  f4 o0 = *(const f4 *)&sO[0][kc * 8], o1 = *(const f4 *)&sO[0][kc * 8 + 4];
+#pragma unroll
+  for (int ww = 1; ww < 4; ++ww) {
+    o0 += *(const f4 *)&sO[ww][kc * 8];
+    o1 += *(const f4 *)&sO[ww][kc * 8 + 4];
+  }
+  o0 *= inv;
+  o1 *= inv;
+
+  // WO slice times the head output; partial row sums added into the residual
+#pragma unroll
+  for (int i = 0; i < WI; ++i) {
+    const int row = r0 + (w * WI + i) * RPI + lane / LPR;
+    float a = (float)wreg[i][0] * o0.x;
+    a = fmaf((float)wreg[i][1], o0.y, a);
+    a = fmaf((float)wreg[i][2], o0.z, a);
+    a = fmaf((float)wreg[i][3], o0.w, a);
+    a = fmaf((float)wreg[i][4], o1.x, a);
+    a = fmaf((float)wreg[i][5], o1.y, a);
+    a = fmaf((float)wreg[i][6], o1.z, a);
+    a = fmaf((float)wreg[i][7], o1.w, a);
+    a = group_sum<LPR>(a);
+    if (kc == 0 && row < rend) atomicAdd(p.h + row, a);
+  }
+}
+
 template <int HD>
 static void attn_wo_hd(const AttnWoP &p, int grid_x, hipStream_t st) {
   dim3 grid(grid_x, p.d.nh);
   if (p.M <= 1)
-    hipLaunchKernelGGL((k_attn_wo<HD, 1>), grid, dim3(256), 0, st, p);
+    hipLaunchKernelGGL((k_attn_wo1<HD>), grid, dim3(256), 0, st, p);
   else
     hipLaunchKernelGGL((k_attn_wo<HD, 8>), grid, dim3(256), 0, st, p);
 }
 
 void attn_wo_fused(const Dims &d, int layer, const KVCache &kv, const float *q, int ldq,
-                   RowInfo rows, int M, const uint16_t *wo, float *h, int ldh, hipStream_t st) {
-  const int rpb = 4 * wo_loads_per_wave(d.hd) * (64 / (d.hd / 8));  // WO rows per block
+                   RowInfo rows, int M, int seq1, int nk1, const uint16_t *wo, float *h, int ldh,
+                   hipStream_t st) {
+  const int rpb = 4 * wo_loads_fused(d.hd) * (64 / (d.hd / 8));  // WO rows per block
   AttnWoP p{d, layer, kv, q, ldq, rows, M, (const _Float16 *)wo, h, ldh, rpb,
-            1.0f / sqrtf((float)d.hd)};
+            1.0f / sqrtf((float)d.hd), nullptr, nullptr, 0};
+  if (M <= 1) {
+    p.kb1 = kv.k + kv.off(d, layer, seq1, 0, 0);
+    p.vb1 = kv.v + kv.off(d, layer, seq1, 0, 0);
+    p.nk1 = nk1;
+  }
   const int gx = (d.H + rpb - 1) / rpb;
   switch (d.hd) {
     case 16: attn_wo_hd<16>(p, gx, st); break;

@@ -169,10 +169,15 @@ void attn_decode(const Dims &d, int layer, const KVCache &kv, const float *q, in
 // block reads all of its head's keys, so from about 512 positions on the
 // chunked attention with merge_wo is faster (0.5B decode at positions
 // 400 / 700: 1,857 / 1,631 tok/s fused against 1,782 / 1,729 chunked).
+// One-row calls (M = 1) give the row's sequence slot seq1 and a key bound
+// nk1 (position < nk1 <= n_ctx) from the host: the kernel then addresses
+// K / V without waiting for the row data it reads on the device.
 constexpr int kFusedKeys = 512;
 constexpr int wo_loads_per_wave(int hd) { return hd == 64 ? 2 : 8; }
+constexpr int wo_loads_fused(int hd) { return hd == 64 ? 2 : 8; }  // (attn_wo_fused's blocks)
 void attn_wo_fused(const Dims &d, int layer, const KVCache &kv, const float *q, int ldq,
-                   RowInfo rows, int M, const uint16_t *wo, float *h, int ldh, hipStream_t st);
+                   RowInfo rows, int M, int seq1, int nk1, const uint16_t *wo, float *h, int ldh,
+                   hipStream_t st);
 // The chunk records of attn_decode (merge = false) of M <= 8 rows merged
 // and multiplied by WO, the partial row sums added into h with float
 // atomics: per (WO row chunk, query head) block as in attn_wo_fused.

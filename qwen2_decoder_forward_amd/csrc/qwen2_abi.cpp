@@ -6,8 +6,9 @@
 #include <string.h>
 
 #include <algorithm>
-#include <map>
+#include <list>
 #include <string>
+#include <tuple>
 #include <utility>
 #include <vector>
 
@@ -27,6 +28,8 @@ constexpr int kMaxBatchRows = 8192;  // rows per pass of a multi-sequence contex
 constexpr int kProfMax = 16384;     // timed launches between two reads
 constexpr size_t kSlotBytes = 64;   // pointer slots at the head of a staged call
 constexpr size_t kSplitKBytes = 64ull << 20;  // split-K partial sums (large-M residual GEMMs: <= 256 x 256 x 256 x 4 B)
+constexpr size_t kMaxGraphs = 32;   // captured decode steps kept per context
+using GraphKey = std::tuple<int, int, int>;  // (rows, attention chunks, slot of a one-row step)
 
 thread_local std::string g_load_error;
 
@@ -72,8 +75,9 @@ struct qwen2_ctx {
   int *stop_ids = nullptr;     // [1 + kMaxStopIds]: count, then the ids
   unsigned *stop_pos = nullptr;  // [n_seq] latched stop positions (~0u: none)
   float2 *prob_part = nullptr;   // [dec_rows][kProbBlocks] softmax partials
-  // captured decode steps, keyed by (batch size, attention splits)
-  std::map<std::pair<int, int>, hipGraphExec_t> graphs;
+  // captured decode steps, keyed by (batch size, attention chunks, slot of
+  // a one-row step), least recently used first; at most kMaxGraphs live
+  std::list<std::pair<GraphKey, hipGraphExec_t>> graphs;
   hipStream_t cap_stream = nullptr;  // captures only (never runs work)
   bool use_graphs = true;
   // pinned staging ring
@@ -438,18 +442,22 @@ struct OpTimer {
   } while (0)
 
 // Attention then WO + residual on the GEMV path (M <= 8 rows, q in q32,
-// output added to rows h).  Short contexts run one fused kernel (head
+// output added to rows h).  seq1: the sequence slot of a one-row call
+// (unused otherwise).  Short contexts run one fused kernel (head
 // attention times a WO slice, atomically added to h); longer ones run the
 // chunked attention, then one kernel that merges its chunk records and
 // multiplies by WO the same way.
 void attn_wo_gemv(qwen2_ctx *c, int l, const float *q, q2::RowInfo rows, int M, int n_chunks,
-                  float *h, hipStream_t st) {
+                  int seq1, float *h, hipStream_t st) {
   const Dims &d = c->d;
   const LayerW &w = c->layers[l];
   const int nhd = d.nh * d.hd;
   const q2::KVCache kv = kv_of(c);
   if (n_chunks * q2::kChunkKeys <= q2::kFusedKeys) {
-    TIMED(QWEN2_OP_ATTN, q2::attn_wo_fused(d, l, kv, q, nhd, rows, M, w.wo, h, d.H, st));
+    // one row: its slot and a key bound past its position, from the host
+    const int nk1 = std::min(n_chunks * q2::kChunkKeys, d.n_ctx);
+    TIMED(QWEN2_OP_ATTN, q2::attn_wo_fused(d, l, kv, q, nhd, rows, M, seq1, nk1, w.wo, h, d.H,
+                                           st));
     return;
   }
   TIMED(QWEN2_OP_ATTN, q2::attn_decode(d, l, kv, q, nhd, rows, M, n_chunks, false, c->part,
@@ -471,14 +479,15 @@ q2::QkvEpi qkv_epi(qwen2_ctx *c, int l, const int *pos, const int *seq) {
 
 // The last layer of a prefill pass after its K/V are stored: only the last
 // row goes on (attention, WO, FFN, final norm, lm_head, argmax).
-void tail_row(qwen2_ctx *c, int r, const int *pos, const int *seq, int last_pos, hipStream_t st) {
+void tail_row(qwen2_ctx *c, int r, const int *pos, const int *seq, int last_pos, int host_seq,
+              hipStream_t st) {
   const Dims &d = c->d;
   const int l = d.L - 1;
   const LayerW &w = c->layers[l];
   const int nhd = d.nh * d.hd;
   float *hr = c->h + (size_t)r * d.H;
   attn_wo_gemv(c, l, c->q32 + (size_t)r * nhd, q2::RowInfo{pos + r, seq + r}, 1,
-               chunks_for(last_pos), hr, st);
+               chunks_for(last_pos), host_seq, hr, st);
   TIMED(QWEN2_OP_GATEUP, q2::gemv_swiglu(d, w, hr, 1, c->a32, d.I_pad, c->hp.rms_eps, st));
   TIMED(QWEN2_OP_DOWN, q2::gemv_resid(w.wd, d.H, d.I_pad, c->a32, d.I_pad, 1, hr, d.H, st));
   TIMED(QWEN2_OP_LMHEAD, q2::gemv_lmhead(d, c->lm_head, c->out_norm, hr, 1, c->normed,
@@ -522,7 +531,7 @@ void prefill_pass(qwen2_ctx *c, int M, int off, const int *pos, const int *seq,
     }
     if (l == d.L - 1) break;  // the last layer goes on for read-out rows only
     if (gemv) {
-      attn_wo_gemv(c, l, c->q32, rows, M, n_chunks, c->h, st);
+      attn_wo_gemv(c, l, c->q32, rows, M, n_chunks, segs[0].seq, c->h, st);
       TIMED(QWEN2_OP_GATEUP, q2::gemv_swiglu(d, w, c->h, M, c->a32, d.I_pad, eps, st));
       TIMED(QWEN2_OP_DOWN, q2::gemv_resid(w.wd, d.H, d.I_pad, c->a32, d.I_pad, M, c->h, d.H, st));
     } else {
@@ -542,14 +551,16 @@ void prefill_pass(qwen2_ctx *c, int M, int off, const int *pos, const int *seq,
 
 // Attention onwards of layer l for B rows of independent positions (their
 // K/V stored, queries in q32 rows 0..B-1, residual stream in h rows
-// 0..B-1).  Returns the split-K partial-sum sets left pending in h.
-int rows_rest(qwen2_ctx *c, int l, int B, int n_chunks, q2::RowInfo rows, hipStream_t st) {
+// 0..B-1; seq1 = the slot of a one-row call).  Returns the split-K
+// partial-sum sets left pending in h.
+int rows_rest(qwen2_ctx *c, int l, int B, int n_chunks, q2::RowInfo rows, int seq1,
+              hipStream_t st) {
   const Dims &d = c->d;
   const float eps = c->hp.rms_eps;
   const int nhd = d.nh * d.hd;
   const LayerW &w = c->layers[l];
   if (B <= kGemvRows) {
-    attn_wo_gemv(c, l, c->q32, rows, B, n_chunks, c->h, st);
+    attn_wo_gemv(c, l, c->q32, rows, B, n_chunks, seq1, c->h, st);
     TIMED(QWEN2_OP_GATEUP, q2::gemv_swiglu(d, w, c->h, B, c->a32, d.I_pad, eps, st));
     TIMED(QWEN2_OP_DOWN, q2::gemv_resid(w.wd, d.H, d.I_pad, c->a32, d.I_pad, B, c->h, d.H, st));
     return 0;
@@ -584,7 +595,7 @@ void rows_head(qwen2_ctx *c, int B, q2::RowInfo rows, int pending, hipStream_t s
 
 // Every kernel of one decode step for B rows (replayed from a graph).
 void decode_launches(qwen2_ctx *c, int B, int n_chunks, const int *dpos, const int *dseq,
-                     hipStream_t st) {
+                     int seq1, hipStream_t st) {
   const Dims &d = c->d;
   const float eps = c->hp.rms_eps;
   const q2::RowInfo rows{dpos, dseq};
@@ -601,7 +612,7 @@ void decode_launches(qwen2_ctx *c, int B, int n_chunks, const int *dpos, const i
                                                 nullptr, c->splitk.buf, pending, st));
       TIMED(QWEN2_OP_QKV, q2::gemm_qkv(d, w, c->x16, d.H, B, e, c->splitk, st));
     }
-    pending = rows_rest(c, l, B, n_chunks, rows, st);
+    pending = rows_rest(c, l, B, n_chunks, rows, seq1, st);
   }
   rows_head(c, B, rows, pending, st);
 }
@@ -626,7 +637,7 @@ int qwen2_prefill(qwen2_ctx *c, int32_t seq, const int32_t *tokens, const int32_
   for (int off = 0; off < n; off += c->max_rows) {
     const int M = std::min(c->max_rows, n - off);
     prefill_pass(c, M, off, df[1] + off, df[2] + off, {Seg{0, M, seq}}, positions + off, st);
-    if (off + M == n) tail_row(c, M - 1, df[1] + off, df[2] + off, positions[n - 1], st);
+    if (off + M == n) tail_row(c, M - 1, df[1] + off, df[2] + off, positions[n - 1], seq, st);
   }
   HIP_TRY(c, hipGetLastError());
   return QWEN2_OK;
@@ -694,7 +705,7 @@ int qwen2_prefill_batch(qwen2_ctx *c, int32_t nb, const int32_t *seq_ids, const 
   HIP_TRY(c, hipMemcpyAsync(c->q32, c->o32, (size_t)nb * nhd * 4, hipMemcpyDeviceToDevice, st));
   const int n_chunks = chunks_for(*std::max_element(t_pos.begin(), t_pos.end()));
   const q2::RowInfo tail{df[0], df[1]};
-  const int pending = rows_rest(c, d.L - 1, nb, n_chunks, tail, st);
+  const int pending = rows_rest(c, d.L - 1, nb, n_chunks, tail, nb == 1 ? seq_ids[0] : -1, st);
   rows_head(c, nb, tail, pending, st);
   c->last_h = c->h;
   c->last_rows = nb;
@@ -716,15 +727,22 @@ int qwen2_decode(qwen2_ctx *c, int32_t B, const int32_t *seq_ids, const int32_t 
   rc = stage_call(c, st, slots, B, 2, fields, df);
   if (rc) return rc;
   const int n_chunks = chunks_for(*std::max_element(positions, positions + B));
+  const int seq1 = B == 1 ? seq_ids[0] : -1;  // a one-row step addresses its slot directly
   c->last_h = c->h;
   c->last_rows = B;
   if (!c->use_graphs || c->prof_mask) {
-    decode_launches(c, B, n_chunks, df[0], df[1], st);
+    decode_launches(c, B, n_chunks, df[0], df[1], seq1, st);
     HIP_TRY(c, hipGetLastError());
     return QWEN2_OK;
   }
-  auto key = std::make_pair((int)B, n_chunks);
-  auto it = c->graphs.find(key);
+  // What the captured launches depend on: the row count; the chunk count
+  // (the chunked attention's grid, the one-row fused attention's key bound),
+  // except for the fused attention of 2..8 rows, which reads it on the
+  // device; the slot, for the one-row fused attention only.
+  const bool fused = B <= kGemvRows && n_chunks * q2::kChunkKeys <= q2::kFusedKeys;
+  const GraphKey key{(int)B, fused && B > 1 ? 0 : n_chunks, fused && B == 1 ? seq1 : -1};
+  auto it = std::find_if(c->graphs.begin(), c->graphs.end(),
+                         [&](const std::pair<GraphKey, hipGraphExec_t> &g) { return g.first == key; });
   if (it == c->graphs.end()) {
     hipGraph_t g = nullptr;
     hipGraphExec_t ge = nullptr;
@@ -732,15 +750,24 @@ int qwen2_decode(qwen2_ctx *c, int32_t B, const int32_t *seq_ids, const int32_t 
     // stream, which cannot be captured); the graph then runs on the caller's
     hipStream_t cs = c->cap_stream;
     HIP_TRY(c, hipStreamBeginCapture(cs, hipStreamCaptureModeThreadLocal));
-    decode_launches(c, B, n_chunks, df[0], df[1], cs);
+    decode_launches(c, B, n_chunks, df[0], df[1], seq1, cs);
     hipError_t e1 = hipStreamEndCapture(cs, &g);
     if (e1 != hipSuccess) return set_err(c, QWEN2_E_HIP, std::string("graph capture: ") + hipGetErrorString(e1));
     hipError_t e2 = hipGraphInstantiate(&ge, g, nullptr, nullptr, 0);
     (void)hipGraphDestroy(g);
     if (e2 != hipSuccess) return set_err(c, QWEN2_E_HIP, std::string("graph instantiate: ") + hipGetErrorString(e2));
-    it = c->graphs.emplace(key, ge).first;
+    if (c->graphs.size() >= kMaxGraphs) {
+      // the least recently used graph goes, once no replay of it can still
+      // be in flight on this stream
+      HIP_TRY(c, hipStreamSynchronize(st));
+      (void)hipGraphExecDestroy(c->graphs.back().second);
+      c->graphs.pop_back();
+    }
+    c->graphs.emplace_front(key, ge);
+  } else if (it != c->graphs.begin()) {
+    c->graphs.splice(c->graphs.begin(), c->graphs, it);
   }
-  HIP_TRY(c, hipGraphLaunch(it->second, st));
+  HIP_TRY(c, hipGraphLaunch(c->graphs.front().second, st));
   return QWEN2_OK;
 }
 

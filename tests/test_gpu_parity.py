@@ -443,3 +443,41 @@ def test_graph_replay_matches_direct_launches(tiny_w, monkeypatch):
     lg_direct, ids_direct = chain()
     assert np.array_equal(ids_graph, ids_direct)
     check(lg_graph, lg_direct, 1e-6, "graph vs direct logits")
+
+
+def test_one_row_decode_across_slots_and_graph_eviction(tiny_w):
+    """One-row decode steps address their slot's K/V from the host, and each
+    (slot, chunk count) gets its own captured step: 40 slots decoded one row
+    at a time, in an interleaved order, twice over (more distinct steps than
+    the 32 graphs a context keeps, so evicted graphs are captured again), each
+    step against the oracle.  Before the prompts, every slot's cache is
+    filled with large values at positions 0..63 (through qwen2_kv_write on
+    the GPU and directly on the oracle side): slots past a row's position
+    hold data the attention must mask out, not zeros."""
+    n_slots = 40
+    p = Pair(TINY, tiny_w, n_ctx=64, n_seq=n_slots)
+    nkv, hd, L = TINY.n_head_kv, TINY.head_dim, TINY.n_layer
+    rng = np.random.default_rng(5)
+    junk_k = (rng.standard_normal((nkv, 64, hd)) * 50).astype(np.float32)
+    junk_v = (rng.standard_normal((nkv, 64, hd)) * 50).astype(np.float32)
+    kd, vd = torch.from_numpy(junk_k).to(DEV), torch.from_numpy(junk_v).to(DEV)
+    for s in range(n_slots):
+        Kc, Vc = p.o._cache(s)
+        for l in range(L):
+            p.m.kv_write(l, s, 0, 64, kd, vd)
+            Kc[l][:, :64] = junk_k
+            Vc[l][:, :64] = junk_v
+    torch.cuda.synchronize()
+    lens = [1 + (3 * s) % 6 for s in range(n_slots)]
+    for s in range(n_slots):
+        p.prefill(s, syn.make_prompt(TINY, lens[s], 500 + s), np.arange(lens[s]))
+    order = [(7 * i) % n_slots for i in range(n_slots)]
+    step = 0
+    for rnd in range(2):
+        for s in order:
+            pos = lens[s] + rnd
+            lg, ids, r = p.decode([s], [int(syn.make_prompt(TINY, 1, 900 + step)[0])], [pos])
+            check(lg[0], r.logits[0], TOL_F32, f"slot {s} round {rnd}")
+            check_id(ids[0], r.logits[0], r.argmax[0], f"slot {s} round {rnd}")
+            step += 1
+    p.close()
