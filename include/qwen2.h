@@ -25,6 +25,8 @@
  *  - `stream` is a hipStream_t (NULL = the default stream).  Compute calls
  *    only enqueue work; the caller synchronises the stream before reading
  *    device outputs.
+ *  - Calls on one context share its scratch and KV cache: the caller keeps
+ *    them ordered (one stream, or synchronised between streams).
  *  - Every call returns QWEN2_OK (0) or a negative QWEN2_E_* code.  All
  *    checks that can be done on the host run before anything is enqueued, so
  *    a rejected call changes neither the KV cache nor any other state.
@@ -193,6 +195,20 @@ int qwen2_decode(qwen2_ctx *ctx, int32_t n_batch, const int32_t *seq_ids, const 
 int qwen2_next_token_probs(qwen2_ctx *ctx, const float *logits_dev, int32_t rows,
                            float *probs_dev, void *stream);
 
+/* For callers that cannot allocate device memory (code under HIP graph
+ * capture, tight serving loops, harnesses that forbid hipMalloc): the same
+ * softmax as qwen2_next_token_probs, with no context.  logits_dev [rows,
+ * n_vocab] f32 -> probs_dev [rows, n_vocab] f32, rows in [1, 64], n_vocab >=
+ * 1 (else QWEN2_E_ARG).  Its partial sums live in a fixed 8 KiB device array
+ * inside the library (one per GPU, held until the process ends), so the call
+ * allocates nothing; every call on one GPU shares that array, so calls that
+ * overlap on one GPU (different streams, or threads) race and must be
+ * ordered by the caller.  Enqueued on `stream` on the current device; the
+ * first call on a device also looks up the array's device address
+ * (QWEN2_E_HIP if that fails).  Errors are reported by qwen2_last_error(NULL). */
+int qwen2_next_token_probs_static(const float *logits_dev, int32_t rows, int32_t n_vocab,
+                                  float *probs_dev, void *stream);
+
 /* Stop ids as data (eos and im_end, minfer page, section 5; the Qwen2.5
  * ids are 151643 and 151645): up to 8 ids in [0, n_vocab); n = 0 clears
  * them (the default).  From then on every greedy read-out (prefill, batched
@@ -258,7 +274,9 @@ int qwen2_prof_read(qwen2_ctx *ctx, int32_t op, int32_t *launches, double *total
  * (it writes only a scratch buffer, so the model state is unchanged);
  * anything else is QWEN2_E_ARG. */
 int qwen2_prof_repeat(qwen2_ctx *ctx, int32_t op, int32_t rows, int32_t iters, void *stream);
-const char *qwen2_last_error(const qwen2_ctx *ctx); /* ctx may be NULL: last load error */
+const char *qwen2_last_error(const qwen2_ctx *ctx); /* ctx NULL: the last error of a call
+                                                       without a context (qwen2_load,
+                                                       qwen2_next_token_probs_static) */
 const char *qwen2_strerror(int code);
 
 /* Frees every device allocation of the context (synchronises the device). */

@@ -19,6 +19,7 @@ __all__ = [
     "qwen2_check_hparams", "qwen2_check_prefill", "qwen2_check_prefill_batch",
     "qwen2_check_decode", "qwen2_load", "qwen2_prefill", "qwen2_prefill_batch", "qwen2_decode",
     "qwen2_read_hidden", "qwen2_kv_read", "qwen2_kv_write", "qwen2_next_token_probs",
+    "qwen2_next_token_probs_static",
     "qwen2_set_stop_ids", "qwen2_read_stops",
     "qwen2_sync_status", "qwen2_info", "qwen2_last_error", "qwen2_strerror", "qwen2_free",
     "qwen2_prof_enable", "qwen2_prof_read", "qwen2_prof_repeat", "OPS", "make_hparams", "Model",
@@ -91,6 +92,7 @@ def lib() -> C.CDLL:
             "qwen2_decode": (i32, [vp, i32, PI32, vp, PI32, vp, vp, vp]),
             "qwen2_read_hidden": (i32, [vp, i32, vp, vp]),
             "qwen2_next_token_probs": (i32, [vp, vp, i32, vp, vp]),
+            "qwen2_next_token_probs_static": (i32, [vp, i32, i32, vp, vp]),
             "qwen2_set_stop_ids": (i32, [vp, PI32, i32]),
             "qwen2_read_stops": (i32, [vp, vp, i32, vp]),
             "qwen2_kv_read": (i32, [vp, i32, i32, i32, i32, vp, vp, vp]),
@@ -244,6 +246,12 @@ def qwen2_read_hidden(ctx: int, which: int, out, stream=None) -> None:
 def qwen2_next_token_probs(ctx: int, logits, rows: int, probs, stream=None) -> None:
     _check(lib().qwen2_next_token_probs(ctx, _ptr(logits), rows, _ptr(probs), _stream(stream)),
            ctx)
+
+
+def qwen2_next_token_probs_static(logits, rows: int, n_vocab: int, probs, stream=None) -> None:
+    """The allocation-free form (no context; the library's fixed scratch)."""
+    _check(lib().qwen2_next_token_probs_static(_ptr(logits), rows, n_vocab, _ptr(probs),
+                                               _stream(stream)))
 
 
 def qwen2_set_stop_ids(ctx: int, ids) -> None:

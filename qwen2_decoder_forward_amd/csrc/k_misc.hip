@@ -1,5 +1,9 @@
 // Embedding gather, row RMSNorm, row copies, the greedy read-out's index and
-// stop-id latch, and the next-token distribution.
+// stop-id latch, and the next-token distribution (also its context-free,
+// allocation-free entry point qwen2_next_token_probs_static).
+#include <mutex>
+
+#include "../../include/qwen2.h"
 #include "q2_device.h"
 
 namespace q2 {
@@ -221,10 +225,12 @@ __global__ __launch_bounds__(256) void k_softmax_norm(const float *logits, int V
   for (int i = c0 + (int)threadIdx.x; i < c1; i += 256) y[i] = expf(x[i] - M) * inv;
 }
 
+int softmax_blocks(int rows) { return std::max(16, std::min(kProbBlocks, 1024 / rows)); }
+
 void softmax_rows(const float *logits, int rows, int V, float2 *part, float *probs,
                   hipStream_t st) {
   static_assert(kProbBlocks == 256, "at most one partial per thread of the combining block");
-  const int nb = std::max(16, std::min(kProbBlocks, 1024 / rows));
+  const int nb = softmax_blocks(rows);
   const dim3 grid(nb, rows);
   hipLaunchKernelGGL(k_softmax_part, grid, dim3(256), 0, st, logits, V, part);
   hipLaunchKernelGGL(k_softmax_norm, grid, dim3(256), 0, st, logits, V, part, probs);
@@ -257,3 +263,66 @@ void pair_order(const float *src, float *dst, int rows, int hd, bool to_pairs, h
 }
 
 }  // namespace q2
+
+// ------------------------------------------- next_token_probs with no allocation
+// The softmax partials of qwen2_next_token_probs_static live in this
+// file-scope device array (one copy per GPU, kept until the process ends)
+// instead of a context's scratch.  Host code never passes the array's name
+// to a kernel: on the host it is only a stand-in for the symbol.  Its device
+// address is looked up once per device, with that device current, and kept.
+namespace {
+constexpr int kStaticProbRows = 64;
+constexpr int kStaticPartials = 1024;  // >= rows * softmax_blocks(rows) for rows <= 64
+constexpr int kMaxDevices = 64;
+static __device__ __align__(256) float2 scratch[kStaticPartials];
+std::mutex g_scratch_mu;
+float2 *g_scratch_ptr[kMaxDevices] = {};
+
+int scratch_on(int dev, float2 **out) {
+  std::lock_guard<std::mutex> lock(g_scratch_mu);
+  if (!g_scratch_ptr[dev]) {
+    float2 *ptr = nullptr;
+    const hipError_t e = hipGetSymbolAddress((void **)&ptr, HIP_SYMBOL(scratch));
+    if (e != hipSuccess || !ptr) {
+      q2::set_static_error(std::string("hipGetSymbolAddress(scratch): ") + hipGetErrorString(e));
+      return QWEN2_E_HIP;
+    }
+    g_scratch_ptr[dev] = ptr;
+  }
+  *out = g_scratch_ptr[dev];
+  return QWEN2_OK;
+}
+}  // namespace
+
+extern "C" int qwen2_next_token_probs_static(const float *logits_dev, int32_t rows,
+                                             int32_t n_vocab, float *probs_dev, void *stream) {
+  static_assert(kStaticProbRows * 16 <= kStaticPartials, "rows * blocks per row fit");
+  if (!logits_dev || !probs_dev) {
+    q2::set_static_error("null logits or probs");
+    return QWEN2_E_ARG;
+  }
+  if (rows < 1 || rows > kStaticProbRows || n_vocab < 1) {
+    q2::set_static_error("rows must be in [1, 64] and n_vocab >= 1");
+    return QWEN2_E_ARG;
+  }
+  if (rows * q2::softmax_blocks(rows) > kStaticPartials) {  // (never, by the block count's rule)
+    q2::set_static_error("softmax partials exceed the static scratch");
+    return QWEN2_E_ARG;
+  }
+  int dev = 0;
+  hipError_t e = hipGetDevice(&dev);
+  if (e != hipSuccess || dev < 0 || dev >= kMaxDevices) {
+    q2::set_static_error(std::string("hipGetDevice: ") + hipGetErrorString(e));
+    return QWEN2_E_HIP;
+  }
+  float2 *part = nullptr;
+  const int rc = scratch_on(dev, &part);
+  if (rc) return rc;
+  q2::softmax_rows(logits_dev, rows, n_vocab, part, probs_dev, (hipStream_t)stream);
+  e = hipGetLastError();
+  if (e != hipSuccess) {
+    q2::set_static_error(std::string("softmax launch: ") + hipGetErrorString(e));
+    return QWEN2_E_HIP;
+  }
+  return QWEN2_OK;
+}

@@ -5,6 +5,8 @@
 #include <stddef.h>
 #include <stdint.h>
 
+#include <string>
+
 namespace q2 {
 
 // Model dimensions as the kernels see them.
@@ -102,8 +104,11 @@ void read_stops(unsigned *stop_pos, int n, int *out, int clear, hipStream_t st);
 // probs[r] = softmax(logits[r]) for rows r < rows, over V columns; part holds
 // rows * kProbBlocks (max, sum) pairs.
 constexpr int kProbBlocks = 256;
+int softmax_blocks(int rows);  // blocks per row softmax_rows uses
 void softmax_rows(const float *logits, int rows, int V, float2 *part, float *probs,
                   hipStream_t st);
+// Message for qwen2_last_error(NULL) from a call that has no context.
+void set_static_error(const std::string &msg);
 
 // MFMA GEMM family (rows M > 8): A f16 [M, lda], W f16 [N, K], K % 32 == 0.
 // Residual GEMMs with few output tiles split K over blocks: with fewer than

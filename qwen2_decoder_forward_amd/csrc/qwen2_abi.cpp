@@ -97,6 +97,12 @@ struct qwen2_ctx {
 
 namespace {
 
+}  // namespace
+
+void q2::set_static_error(const std::string &msg) { g_load_error = msg; }
+
+namespace {
+
 int set_err(qwen2_ctx *c, int code, const std::string &m) {
   if (c) c->err = m;
   else g_load_error = m;
