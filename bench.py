@@ -57,12 +57,22 @@ def log(*a):
     print(*a, file=sys.stderr, flush=True)
 
 
+def streamed_f16(shape, wb: dict, rows: int) -> int:
+    """binary16 bytes a pass over `rows` token rows reads: every matrix once
+    (the lm_head included), plus the `rows` gathered embedding rows.  An
+    untied model's embedding table is not streamed, only its rows are
+    gathered, so its V x H table is not counted."""
+    table = 0 if shape.tied else shape.n_vocab * shape.n_embd * 2
+    return wb["f16"] - table + rows * shape.n_embd * 2
+
+
 def decode_bytes(shape, pos: int, wb: dict) -> int:
     """Algorithmic bytes of one batch-1 decode token at position `pos`: every
-    weight once (f16 matrices incl. the tied lm_head, f32 biases and norms)
-    plus the K/V of positions 0..pos read and one position written (f32)."""
+    streamed weight once (f16 matrices incl. the lm_head, the token's
+    embedding row, f32 biases and norms) plus the K/V of positions 0..pos
+    read and one position written (f32)."""
     kv_pos = shape.n_layer * 2 * shape.n_head_kv * shape.head_dim * 4
-    return wb["f16"] + wb["f32"] + kv_pos * (pos + 1) + kv_pos
+    return streamed_f16(shape, wb, 1) + wb["f32"] + kv_pos * (pos + 1) + kv_pos
 
 
 def gateup_bytes(shape) -> int:
@@ -91,8 +101,15 @@ def cpu_baseline(shape, weights, prompt, n_ctx, budget_s):
         steps += 1
     t2 = time.perf_counter()
     threads = max([i.get("num_threads", 1) for i in threadpool_info()] or [1])
+    cpu = "unknown"
+    try:
+        with open("/proc/cpuinfo") as f:
+            cpu = next(l.split(":", 1)[1].strip() for l in f if l.startswith("model name"))
+    except (OSError, StopIteration):
+        pass
     return {
         "value": steps / (t2 - t1), "unit": "tok/s", "cores": int(threads), "kind": "oracle",
+        "cpu_model": cpu,
         "sample": f"NumPy oracle (f32 storage, f64 sums) on the 0.5B workload: prefill of the "
                   f"{n}-token prompt then {steps} greedy decode steps at positions {n}..{n + steps - 1}",
         "prefill_tok_s": n / (t1 - t0), "seconds": t2 - t0,
@@ -143,6 +160,67 @@ def prefill_op_fractions(q, model, shape, prompt, n_ctx):
     return out
 
 
+def trace_summary(path: str) -> None:
+    """Prints, from a rocprofv3 kernel trace (CSV) of a bench.py run, every
+    kernel's average duration over the decode steps' graph replays and, for
+    a kernel also launched back to back (the roofline loop), its average
+    there: a launch whose predecessor and successor are the same kernel
+    belongs to the loop, any other one runs between different kernels."""
+    import csv
+    import statistics as st
+    with open(path) as f:
+        rows = sorted((int(r["Start_Timestamp"]), int(r["End_Timestamp"]), r["Kernel_Name"])
+                      for r in csv.DictReader(f))
+    loop, seq = {}, {}
+    for i, (s0, e0, name) in enumerate(rows):
+        key = name.split("(")[0].replace("void ", "")
+        same = (0 < i < len(rows) - 1 and rows[i - 1][2] == name and rows[i + 1][2] == name)
+        (loop if same else seq).setdefault(key, []).append((e0 - s0) / 1e3)
+    print(f"{'kernel':52s} {'in sequence':>22s} {'back to back':>22s}")
+    for k in sorted(seq, key=lambda k: -sum(seq[k])):
+        a = seq[k]
+        b = loop.get(k, [])
+        bb = f"{len(b):6d} x {st.mean(b):7.2f} us" if b else ""
+        print(f"{k[:52]:52s} {len(a):6d} x {st.mean(a):7.2f} us {bb:>22s}")
+
+
+def counter_summary(path: str, simds: int = 1024, xcds: int = 8) -> None:
+    """Prints, from a rocprofv3 --pmc counter CSV, per kernel: dispatches, the
+    mean of every collected counter per dispatch and, when
+    SQ_VALU_MFMA_BUSY_CYCLES and GRBM_GUI_ACTIVE were collected, the MFMA
+    busy fraction = busy cycles summed over the SIMDs / (GUI-active cycles of
+    one XCD x SIMD count; 256 CUs x 4 SIMDs on the MI355X).  rocprofv3 sums
+    GRBM_GUI_ACTIVE over the 8 XCDs, so one XCD's count is that sum / 8 (the
+    vendor's MfmaUtil metric takes the largest XCD's).  The f16 MFMA flop
+    count is SQ_INSTS_VALU_MFMA_MOPS_F16 x 512."""
+    import csv
+    import collections
+    per = collections.defaultdict(dict)
+    names = {}
+    with open(path) as f:
+        for r in csv.DictReader(f):
+            d = r["Dispatch_Id"]
+            per[d][r["Counter_Name"]] = per[d].get(r["Counter_Name"], 0.0) + float(r["Counter_Value"])
+            names[d] = r["Kernel_Name"].split("(")[0].replace("void ", "")
+    groups = collections.defaultdict(list)
+    for d, c in per.items():
+        groups[names[d]].append(c)
+    counters = sorted({k for c in per.values() for k in c})
+    print(f"{'kernel':48s} {'disp':>5s} " + " ".join(f"{c[:26]:>26s}" for c in counters)
+          + f" {'MFMA busy':>9s} {'f16 MFMA GFLOP':>14s}")
+    for k in sorted(groups, key=lambda k: -sum(c.get("GRBM_GUI_ACTIVE", 0) for c in groups[k])):
+        g = groups[k]
+        mean = {c: sum(x.get(c, 0.0) for x in g) / len(g) for c in counters}
+        util = ""
+        if "SQ_VALU_MFMA_BUSY_CYCLES" in mean and mean.get("GRBM_GUI_ACTIVE"):
+            util = (f"{100 * mean['SQ_VALU_MFMA_BUSY_CYCLES'] / (mean['GRBM_GUI_ACTIVE'] / xcds * simds):8.1f}%")
+        fl = ""
+        if "SQ_INSTS_VALU_MFMA_MOPS_F16" in mean:
+            fl = f"{mean['SQ_INSTS_VALU_MFMA_MOPS_F16'] * 512 / 1e9:14.2f}"
+        print(f"{k[:48]:48s} {len(g):5d} " + " ".join(f"{mean[c]:26.4g}" for c in counters)
+              + f" {util:>9s} {fl:>14s}")
+
+
 def pmc_pass(torch, q, syn):
     """Launches for the HBM traffic counters: torch's copy of a 256 MiB tensor
     (every byte read once and written once: the calibration of FETCH_SIZE and
@@ -172,10 +250,20 @@ def main():
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--workload", default="0.5b",
                     help="0.5b (the benchmark line, default), 0.5b-long, 0.5b-batched, hd128, 1.5b-heads, tiny")
+    ap.add_argument("--trace-summary", metavar="CSV",
+                    help="summarise a rocprofv3 kernel trace of this script (no GPU use)")
+    ap.add_argument("--counter-summary", metavar="CSV",
+                    help="summarise a rocprofv3 --pmc counter CSV of this script (no GPU use)")
     ap.add_argument("--pmc-pass", action="store_true",
                     help="only the launches a rocprofv3 --pmc counter pass reads: a plain 256 MiB "
                          "device copy (calibration), then 48 launches of the gate/up GEMV")
     args = ap.parse_args()
+    if args.trace_summary:
+        trace_summary(args.trace_summary)
+        return
+    if args.counter_summary:
+        counter_summary(args.counter_summary)
+        return
     if args.gpus != 1:
         print(json.dumps({"error": "this implementation runs on one GPU; --gpus must be 1 "
                                    "(figures for several GPUs are not produced)"}))
@@ -273,7 +361,7 @@ def main():
     kv_pos = shape.n_layer * 2 * shape.n_head_kv * shape.head_dim * 4
     if batched:
         dec_tokens = n_seq
-        dec_bytes = wb["f16"] + wb["f32"] + n_seq * kv_pos * (n + 2)
+        dec_bytes = streamed_f16(shape, wb, n_seq) + wb["f32"] + n_seq * kv_pos * (n + 2)
     else:
         dec_tokens = steps_dec
         dec_bytes = sum(decode_bytes(shape, n + s, wb) for s in range(steps_dec))
@@ -281,11 +369,15 @@ def main():
     dec_tok_s = dec_tokens / (decode_ms / 1e3)
 
     # dominant decode kernel: fused RMSNorm + gate/up + SwiGLU GEMV (one launch
-    # per layer and token).  Its average duration is measured with HIP events
-    # on the stream it runs on, around 20 launches per layer that cycle
-    # through the layers (on the 0.5B shape 418 MB of weights, more than the
-    # 256 MB Infinity Cache, so every launch streams its weights from HBM as
-    # in the decode loop).
+    # per layer and token).  Its average duration is measured live with HIP
+    # events on the stream it runs on, around 20 back-to-back launches per
+    # layer that cycle through the layers (on the 0.5B shape 418 MB of
+    # weights, more than the 256 MB Infinity Cache, so every launch streams
+    # its weights from HBM).  Inside the decode graph the same kernel runs
+    # between other kernels; HIP events cannot bracket a node of a graph
+    # replay (an event pair around every direct launch adds its own cost),
+    # so that figure comes from a rocprofv3 kernel trace of this command,
+    # split by `--trace-summary` into the graph replays and this loop.
     reps = 20 * shape.n_layer
     q.qwen2_prof_repeat(model.ctx, "gateup", 1, shape.n_layer)  # warm the launch path
     ev_k = [torch.cuda.Event(enable_timing=True) for _ in range(2)]
@@ -297,6 +389,8 @@ def main():
     gu_avg_s = ev_k[0].elapsed_time(ev_k[1]) / reps / 1e3
     gu_bytes = gateup_bytes(shape)
     achieved = gu_bytes / gu_avg_s / 1e9
+    kc = -(-shape.n_embd // 512)
+    kb = 2 if kc <= 2 else 4 if kc <= 4 else 8 if kc <= 8 else 10
 
     # next_token_probs of the read-out rows (softmax over the vocabulary):
     # average of 100 back-to-back calls on the last step's logits
@@ -313,7 +407,7 @@ def main():
 
     fl = prefill_gemm_flops(shape, n)
     prefill_flops = sum(fl.values()) + attn_prefill_flops(shape, n)
-    prefill_bytes = wb["f16"] + wb["f32"] + n * kv_pos
+    prefill_bytes = streamed_f16(shape, wb, n) + wb["f32"] + n * kv_pos
 
     desc = (f"{wl.description}; model {shape.name}: {shape.n_layer} layers, hidden "
             f"{shape.n_embd}, {shape.n_head}/{shape.n_head_kv} heads, hd {shape.head_dim}, "
@@ -329,7 +423,9 @@ def main():
         "higher_is_better": True,
         "scaling": "weak",
         "vs_baseline": None,
-        "dtype": "f16 weights, f32 activations and accumulation",
+        "dtype": ("f16 weights; decode (rows <= 8): f32 activations, accumulation and KV "
+                  "cache; prefill (rows > 8): f16 activation, K/V-mirror and softmax-weight "
+                  "MFMA operands with f32 accumulation, f32 residual stream and KV cache"),
         "data": "synthetic",
         "config": {"workload": desc, "prompt": n, "decode_steps": steps_dec, "n_ctx": n_ctx,
                    "batch": n_seq},
@@ -341,11 +437,12 @@ def main():
         "next_token_probs_us": probs_us,
         "next_token_probs_rows": prob_rows,
         "roofline": {
-            "kernel": "k_gemv1<4,2,EPI_SWIGLU> (RMSNorm + gate/up + SwiGLU, decode M=1)",
+            "kernel": f"k_gemv1<4, {kb}, 2> (RMSNorm + gate/up + SwiGLU, decode M=1)",
             "bound": "hbm", "achieved": achieved, "peak": HBM_PEAK_GBS, "unit": "GB/s",
             "frac": achieved / HBM_PEAK_GBS, "traffic": gateup_traffic(shape),
             "bytes_per_launch": gu_bytes, "avg_launch_us": gu_avg_s * 1e6, "launches_timed": reps,
-            "timing": "HIP events around back-to-back launches cycling through the layers",
+            "timing": "HIP events around back-to-back launches cycling through the layers "
+                      "(the in-graph duration: rocprofv3 trace, bench.py --trace-summary)",
         },
         "cpu_baseline": None,
     }
