@@ -55,7 +55,7 @@ enum {
 
 /* Model and cache hyperparameters (HParams of the minfer page, section 2;
  * QwenConfig of xinfer Module 7, section 7.1).
- * Supported: n_embd == n_head * head_dim, n_embd % 64 == 0, n_embd <= 5120,
+ * Supported: n_embd == n_head * head_dim, n_embd % 64 == 0, n_embd <= 8192,
  * n_ctx <= 131072, n_head % n_head_kv == 0 with n_head / n_head_kv <= 8,
  * head_dim in {16, 64, 128}, rope_style 0 (NonInterleaved: dimension d pairs
  * with d + head_dim/2, the Qwen2 convention) or 1 (Interleaved: 2d pairs with

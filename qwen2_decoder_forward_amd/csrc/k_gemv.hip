@@ -560,12 +560,20 @@ static GemvP base(const uint16_t *W, int N, int K, const float *x, int ldx, int 
 }
 
 void gemv_qkv(const Dims &d, const LayerW &w, const float *h, int M, const QkvEpi &e,
-              float eps, hipStream_t st) {
+              float eps, float *normed, hipStream_t st) {
   GemvP p = base(w.wqkv, d.nqkv, d.H, h, d.H, M);
-  p.norm_w = w.attn_norm;
-  p.eps = eps;
   p.d = d;
   p.qkv = e;
+  if (d.H > kGemvNormCols) {  // wide rows: norm first, then the multi-batch GEMV
+    rmsnorm_rows_f16(const_cast<float *>(h), d.H, w.attn_norm, d.H, M, eps, nullptr, 0, normed,
+                     nullptr, 0, st);
+    p.x = normed;
+    p.n_groups = (p.N + 4 * 2 - 1) / (4 * 2);
+    hipLaunchKernelGGL((k_gemv<8, 2, 10, EPI_QKV>), dim3(p.n_groups), dim3(256), 0, st, p);
+    return;
+  }
+  p.norm_w = w.attn_norm;
+  p.eps = eps;
   launch<2, EPI_QKV>(p, 1 << 30, st);
 }
 
@@ -581,12 +589,20 @@ void gemv_resid(const uint16_t *W, int N, int K, const float *x, int ldx, int M,
 }
 
 void gemv_swiglu(const Dims &d, const LayerW &w, const float *h, int M, float *a, int lda,
-                 float eps, hipStream_t st) {
+                 float eps, float *normed, hipStream_t st) {
   GemvP p = base(w.wgu, 2 * d.I_pad, d.H, h, d.H, M);
-  p.norm_w = w.ffn_norm;
-  p.eps = eps;
   p.out = a;
   p.ldo = lda;
+  if (d.H > kGemvNormCols) {  // wide rows: norm first, then the multi-batch GEMV
+    rmsnorm_rows_f16(const_cast<float *>(h), d.H, w.ffn_norm, d.H, M, eps, nullptr, 0, normed,
+                     nullptr, 0, st);
+    p.x = normed;
+    p.n_groups = (p.N + 4 * 4 - 1) / (4 * 4);
+    hipLaunchKernelGGL((k_gemv<8, 4, 10, EPI_SWIGLU>), dim3(p.n_groups), dim3(256), 0, st, p);
+    return;
+  }
+  p.norm_w = w.ffn_norm;
+  p.eps = eps;
   launch<4, EPI_SWIGLU>(p, 1 << 30, st);
 }
 
@@ -605,8 +621,15 @@ void gemv_lmhead(const Dims &d, const uint16_t *W, const float *norm_w, const fl
   p.best = e.best;
   p.logits = e.logits;
   p.normed_out = normed_out;
-  const int kc = (d.H + 511) / 512;  // 512-half chunks per row (H <= 5120)
-  if (M <= 1) {  // one row: the persistent kernel (its normed row stays in registers)
+  const int kc = (d.H + 511) / 512;  // 512-half chunks per row
+  if (d.H > kGemvNormCols) {  // wide rows: the final norm first (it also gives the tap)
+    rmsnorm_rows_f16(const_cast<float *>(h), d.H, norm_w, d.H, M, eps, nullptr, 0, normed_out,
+                     nullptr, 0, st);
+    p.x = normed_out;
+    p.norm_w = nullptr;
+    p.normed_out = nullptr;
+    launch<4, EPI_LMHEAD>(p, 4096, st);
+  } else if (M <= 1) {  // one row: the persistent kernel (its normed row stays in registers)
     if (kc <= 2) launch_lmhead<1, 4, 2>(p, st);
     else if (kc <= 4) launch_lmhead<1, 2, 4>(p, st);
     else if (kc <= 8) launch_lmhead<1, 1, 8>(p, st);

@@ -39,12 +39,13 @@ void embed_rows(const uint16_t *E, int H, int V, const int *const *tokens, int t
 // operand) and optionally f32.  When a split-K residual GEMM left `splits`
 // partial sums part[z][m][k] (z < splits), they are first added to the row,
 // which is written back: h[m] += sum_z part[z][m].  Thread t owns 4-float
-// chunks t, t + 256, ... of the row (H <= 5120: at most 5), and issues the
-// loads of its chunk of every partial at once.
+// chunks t, t + 256, ... of the row (H <= 8192: at most 8), and issues the
+// loads of its chunk of every partial at once.  x (f16) may be null when
+// only the f32 copy is wanted.
 __global__ __launch_bounds__(256) void k_rmsnorm_rows(float *h, int ldh, const float *w, int H,
                                                       int M, float eps, _Float16 *x, int ldx,
                                                       float *y32, const float *part, int splits) {
-  constexpr int kMaxChunks = 5;  // 256 threads * 4 floats * 5 = 5120 (the supported maximum)
+  constexpr int kMaxChunks = 8;  // 256 threads * 4 floats * 8 = 8192 (the supported maximum)
   __shared__ float sRed[4];
   const int m = blockIdx.x, tid = threadIdx.x;
   float *row = h + (size_t)m * ldh;
@@ -81,8 +82,10 @@ __global__ __launch_bounds__(256) void k_rmsnorm_rows(float *h, int ldh, const f
     if (k < H) {
       const f4 g = *(const f4 *)(w + k);
       const f4 y = v[c] * inv * g;
-      h4 yh = {(_Float16)y.x, (_Float16)y.y, (_Float16)y.z, (_Float16)y.w};
-      *(h4 *)(x + (size_t)m * ldx + k) = yh;
+      if (x) {
+        h4 yh = {(_Float16)y.x, (_Float16)y.y, (_Float16)y.z, (_Float16)y.w};
+        *(h4 *)(x + (size_t)m * ldx + k) = yh;
+      }
       if (y32) *(f4 *)(y32 + (size_t)m * H + k) = y;
     }
   }

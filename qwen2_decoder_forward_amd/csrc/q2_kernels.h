@@ -83,13 +83,16 @@ constexpr int kMaxStopIds = 8;
 // ---------------------------------------------------------------- launchers
 // GEMV family (rows M <= 8, f32 activations, f16 weights streamed once).
 // y[m, n] = sum_k x'[m, k] W[n, k] with x' = x, or RMSNorm(x) * norm_w when
-// norm_w is given (then K must equal the normed width).
+// norm_w is given (then K must equal the normed width).  Rows wider than
+// kGemvNormCols are normed first by k_rmsnorm_rows into `normed` ([M, H]
+// f32 scratch), then multiplied by the GEMV without its norm prologue.
+constexpr int kGemvNormCols = 10 * 512;
 void gemv_qkv(const Dims &d, const LayerW &w, const float *h, int M, const QkvEpi &e,
-              float eps, hipStream_t st);
+              float eps, float *normed, hipStream_t st);
 void gemv_resid(const uint16_t *W, int N, int K, const float *x, int ldx, int M, float *h,
                 int ldh, hipStream_t st);
 void gemv_swiglu(const Dims &d, const LayerW &w, const float *h, int M, float *a, int lda,
-                 float eps, hipStream_t st);
+                 float eps, float *normed, hipStream_t st);
 void gemv_lmhead(const Dims &d, const uint16_t *W, const float *norm_w, const float *h, int M,
                  float *normed_out, const ArgmaxEpi &e, float eps, hipStream_t st);
 
@@ -133,7 +136,7 @@ void gemm_lmhead(const Dims &d, const uint16_t *W, const _Float16 *x, int lda, i
 
 // RMSNorm of rows into an f16 copy (the MFMA A operand) and, when y32 is
 // given, also into f32 [M, H].  `splits` pending partial-sum sets part[z][M][H]
-// of a residual GEMM are added into h first (H <= 5120).
+// of a residual GEMM are added into h first (H <= 8192); x may be null.
 void rmsnorm_rows_f16(float *h, int ldh, const float *w, int H, int M, float eps, _Float16 *x,
                       int ldx, float *y32, const float *part, int splits, hipStream_t st);
 // Embedding gather h[m] = f32(E[tokens[m]]) without scaling; an id outside

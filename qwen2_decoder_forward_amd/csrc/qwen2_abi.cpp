@@ -494,7 +494,7 @@ void tail_row(qwen2_ctx *c, int r, const int *pos, const int *seq, int last_pos,
   float *hr = c->h + (size_t)r * d.H;
   attn_wo_gemv(c, l, c->q32 + (size_t)r * nhd, q2::RowInfo{pos + r, seq + r}, 1,
                chunks_for(last_pos), host_seq, hr, st);
-  TIMED(QWEN2_OP_GATEUP, q2::gemv_swiglu(d, w, hr, 1, c->a32, d.I_pad, c->hp.rms_eps, st));
+  TIMED(QWEN2_OP_GATEUP, q2::gemv_swiglu(d, w, hr, 1, c->a32, d.I_pad, c->hp.rms_eps, c->normed, st));
   TIMED(QWEN2_OP_DOWN, q2::gemv_resid(w.wd, d.H, d.I_pad, c->a32, d.I_pad, 1, hr, d.H, st));
   TIMED(QWEN2_OP_LMHEAD, q2::gemv_lmhead(d, c->lm_head, c->out_norm, hr, 1, c->normed,
                                          argmax_epi(c, q2::RowInfo{pos + r, seq + r}),
@@ -528,7 +528,7 @@ void prefill_pass(qwen2_ctx *c, int M, int off, const int *pos, const int *seq,
     const LayerW &w = c->layers[l];
     const q2::QkvEpi e = qkv_epi(c, l, pos, seq);
     if (gemv) {
-      TIMED(QWEN2_OP_QKV, q2::gemv_qkv(d, w, c->h, M, e, eps, st));
+      TIMED(QWEN2_OP_QKV, q2::gemv_qkv(d, w, c->h, M, e, eps, c->normed, st));
     } else {
       TIMED(QWEN2_OP_NORM, q2::rmsnorm_rows_f16(c->h, d.H, w.attn_norm, d.H, M, eps, c->x16, d.H,
                                                 nullptr, c->splitk.buf, pending, st));
@@ -538,7 +538,7 @@ void prefill_pass(qwen2_ctx *c, int M, int off, const int *pos, const int *seq,
     if (l == d.L - 1) break;  // the last layer goes on for read-out rows only
     if (gemv) {
       attn_wo_gemv(c, l, c->q32, rows, M, n_chunks, segs[0].seq, c->h, st);
-      TIMED(QWEN2_OP_GATEUP, q2::gemv_swiglu(d, w, c->h, M, c->a32, d.I_pad, eps, st));
+      TIMED(QWEN2_OP_GATEUP, q2::gemv_swiglu(d, w, c->h, M, c->a32, d.I_pad, eps, c->normed, st));
       TIMED(QWEN2_OP_DOWN, q2::gemv_resid(w.wd, d.H, d.I_pad, c->a32, d.I_pad, M, c->h, d.H, st));
     } else {
       TIMED(QWEN2_OP_ATTN, q2::attn_prefill(d, l, kv, c->q32, nhd, rows, segs.data(),
@@ -567,7 +567,7 @@ int rows_rest(qwen2_ctx *c, int l, int B, int n_chunks, q2::RowInfo rows, int se
   const LayerW &w = c->layers[l];
   if (B <= kGemvRows) {
     attn_wo_gemv(c, l, c->q32, rows, B, n_chunks, seq1, c->h, st);
-    TIMED(QWEN2_OP_GATEUP, q2::gemv_swiglu(d, w, c->h, B, c->a32, d.I_pad, eps, st));
+    TIMED(QWEN2_OP_GATEUP, q2::gemv_swiglu(d, w, c->h, B, c->a32, d.I_pad, eps, c->normed, st));
     TIMED(QWEN2_OP_DOWN, q2::gemv_resid(w.wd, d.H, d.I_pad, c->a32, d.I_pad, B, c->h, d.H, st));
     return 0;
   }
@@ -612,7 +612,7 @@ void decode_launches(qwen2_ctx *c, int B, int n_chunks, const int *dpos, const i
     const LayerW &w = c->layers[l];
     const q2::QkvEpi e = qkv_epi(c, l, dpos, dseq);
     if (B <= kGemvRows) {
-      TIMED(QWEN2_OP_QKV, q2::gemv_qkv(d, w, c->h, B, e, eps, st));
+      TIMED(QWEN2_OP_QKV, q2::gemv_qkv(d, w, c->h, B, e, eps, c->normed, st));
     } else {
       TIMED(QWEN2_OP_NORM, q2::rmsnorm_rows_f16(c->h, d.H, w.attn_norm, d.H, B, eps, c->x16, d.H,
                                                 nullptr, c->splitk.buf, pending, st));
@@ -928,7 +928,7 @@ int qwen2_prof_repeat(qwen2_ctx *c, int32_t op, int32_t rows, int32_t iters, voi
   hipStream_t st = (hipStream_t)stream;
   for (int i = 0; i < iters; ++i) {
     const LayerW &w = c->layers[i % c->d.L];
-    q2::gemv_swiglu(c->d, w, c->h, rows, c->a32, c->d.I_pad, c->hp.rms_eps, st);
+    q2::gemv_swiglu(c->d, w, c->h, rows, c->a32, c->d.I_pad, c->hp.rms_eps, c->normed, st);
   }
   HIP_TRY(c, hipGetLastError());
   return QWEN2_OK;

@@ -39,8 +39,8 @@ int check_hparams(const qwen2_hparams *hp, std::string *msg) {
     return fail(msg, QWEN2_E_HPARAMS, "head_dim %lld not in {16, 64, 128}", hp->head_dim);
   if (hp->n_embd % 64)
     return fail(msg, QWEN2_E_HPARAMS, "n_embd %lld is not a multiple of 64", hp->n_embd);
-  if (hp->n_embd > 5120)  // the decode GEMV keeps a whole normed row in registers
-    return fail(msg, QWEN2_E_HPARAMS, "n_embd %lld > 5120 is not supported", hp->n_embd);
+  if (hp->n_embd > 8192)  // (k_rmsnorm_rows: 256 threads x 4 floats x 8 chunks)
+    return fail(msg, QWEN2_E_HPARAMS, "n_embd %lld > 8192 is not supported", hp->n_embd);
   if (hp->n_ctx > 131072)  // the decode attention merges at most 2048 64-key chunks
     return fail(msg, QWEN2_E_HPARAMS, "n_ctx %lld > 131072 is not supported", hp->n_ctx);
   if (hp->rope_style != 0 && hp->rope_style != 1)

@@ -131,6 +131,8 @@ def test_batch_validation():
     ({"n_head": 36, "n_head_kv": 4, "n_embd": 576}, False),  # group 9 > 8
     ({"n_head_kv": 4}, True),              # MHA
     ({"n_head_kv": 1}, True),              # MQA, group 4
+    ({"n_embd": 8192, "n_head": 64, "n_head_kv": 8, "head_dim": 128}, True),   # 64/8 heads (72B)
+    ({"n_embd": 8320, "n_head": 65, "n_head_kv": 5, "head_dim": 128}, False),  # n_embd > 8192
 ])
 def test_hparams_checks(change, ok):
     shape = dataclasses.replace(syn.MODELS["tiny"], **change)

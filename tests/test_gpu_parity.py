@@ -389,12 +389,15 @@ def test_hd128_untied_group7(n):
 
 # Head layouts of the family at their real widths (two layers, a small FFN
 # and vocabulary): 12/2 and 16/2 heads of 128 (groups 6 and 8), 40/8 (group
-# 5, the widest hidden size the decode GEMVs take), multi-head attention
-# (n_head_kv = n_head, Qwen1.5) and the two other RoPE bases.
+# 5, the widest hidden size whose normed row the decode GEMVs keep in
+# registers), 64/8 (hidden 8192: the decode GEMVs norm the row in a
+# separate kernel first), multi-head attention (n_head_kv = n_head, Qwen1.5)
+# and the two other RoPE bases.
 FAMILY = {
     "heads12-2": dict(n_embd=1536, n_head=12, n_head_kv=2, head_dim=128),
     "heads16-2": dict(n_embd=2048, n_head=16, n_head_kv=2, head_dim=128),
     "heads40-8": dict(n_embd=5120, n_head=40, n_head_kv=8, head_dim=128),
+    "heads64-8": dict(n_embd=8192, n_head=64, n_head_kv=8, head_dim=128),
     "mha8-theta1e4": dict(n_embd=512, n_head=8, n_head_kv=8, head_dim=64, rope_theta=1e4),
     "theta1e7": dict(n_embd=896, n_head=14, n_head_kv=2, head_dim=64, rope_theta=1e7),
 }
