@@ -1,7 +1,8 @@
 // Host-side validation of hyperparameters and calls.  No HIP here: these
 // checks run before anything is enqueued, so a rejected call leaves the KV
-// cache and the context unchanged (the minfer page, section 6: a position
-// >= n_ctx is a hard error, "not truncated silently").
+// cache and the context unchanged (the minfer page, section 6 and its
+// troubleshooting list: a position >= n_ctx is rejected with an error, the
+// context is never cut short to fit).
 #include <stdio.h>
 
 #include <string>
