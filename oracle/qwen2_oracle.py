@@ -11,24 +11,24 @@ What it computes (plain definition, written out step by step):
   Q and K, KV store, grouped-query attention (Q K^T scale, softmax, times V),
   WO plus residual, RMSNorm, gate/up, SiLU(gate) * up, down plus residual.
 * Biases on q/k/v only, added before the rotary embedding; no bias on o_proj
-  or the MLP (nnterp Qwen2 encyclopedia page, "Queries, keys and values carry
-  a bias").
+  or the MLP (nnterp Qwen2 encyclopedia page, Notes, the subsection on the
+  q/k/v biases).
 * RoPE in the NonInterleaved / GPT-NeoX rotate_half pairing (minfer page,
   section 3; xinfer Module 7, section 7.2 table): dimension d pairs with
   d + head_dim/2.
 * Query head h reads KV head floor(h / (n_head / n_head_kv)), i.e. KV head j
   serves query heads 7j..7j+6 on the 0.5B shape; score scale head_dim^-0.5
   (nnterp page, "Grouped-query attention").
-* Full causal attention, no sliding window (nnterp page, "The sliding-window
-  keys do nothing").
+* Full causal attention, no sliding window (nnterp page, Notes, the
+  subsection on the sliding-window config keys).
 * Positions are data: a row at position p attends to its sequence's KV slots
   0..p; a position >= n_ctx is a hard error that leaves the cache untouched
   (minfer page, section 6 and troubleshooting item 5).
 * Readout: final RMSNorm, then lm_head (the token embedding when tied), with
-  nothing applied after it (nnterp page, "The readout is the plain
-  projection"; xinfer Module 7, section 7.3), and greedy argmax on the
-  device side of the pages' engines (xinfer 7.3) taken here as the lowest
-  index of the largest logit.
+  nothing applied after it (nnterp page, Notes, the readout subsection;
+  xinfer Module 7, section 7.3), and greedy argmax on the device side of the
+  pages' engines (xinfer 7.3) taken here as the lowest index of the largest
+  logit.
 * next_token_probs: the next-token distribution at a read-out position, the
   softmax of that row's logits (nnterp page, standardized tap list).
 * Stop ids are data (eos and im_end, minfer page, section 5): a greedy
@@ -287,7 +287,7 @@ class Qwen2Oracle:
         return self._dec[key]
 
     def lm_head_bits(self) -> np.ndarray:
-        # W_lm = E when tied (xinfer 7.3; nnterp "The readout ...").
+        # W_lm = E when tied (xinfer 7.3; nnterp Notes, readout subsection).
         return self.w["tok_embd"] if self.hp.tied else self.w["lm_head"]
 
     # ---- cache -------------------------------------------------------------
