@@ -384,15 +384,30 @@ __global__ __launch_bounds__(64 * NW) void k_gemm_big(GemmP p) {
   const int hi = lane >> 5, l32 = lane & 31;
   const int M = p.M, N = p.N, K = p.K;
 
-  // tile order: consecutive blocks of one XCD (blocks are dealt round-robin
-  // over the 8 XCDs) walk the N tiles of one row band, so a band's A rows
-  // stay in that XCD's L2
+  // Tile order.  Blocks are dealt round-robin over the 8 XCDs; XCD x takes
+  // the x-th eighth of the row bands, and walks them in groups of G bands,
+  // N tiles outermost and the group's bands innermost, so the ~32 blocks an
+  // XCD runs at once share G A bands and 32 / G weight tiles in its L2
+  // (rather than one A band and 32 weight tiles: 0.5B 4096-row gate/up and
+  // down about 3 % faster).  Other grids: consecutive blocks of one XCD walk
+  // the N tiles of one row band.
   const int gx = gridDim.x, gy = gridDim.y;
   const int nb = gx * gy;
   const int bid = blockIdx.y * gx + blockIdx.x;
-  int tile = bid;
-  if ((nb & 7) == 0) tile = (bid & 7) * (nb >> 3) + (bid >> 3);
-  const int m0 = (tile / gx) * BMT, n0 = (tile % gx) * BNT;
+  int tm, tn;
+  if ((gy & 7) == 0) {
+    const int xcd = bid & 7, t = bid >> 3, bpx = gy >> 3;
+    const int G = bpx % 4 == 0 ? 4 : bpx % 3 == 0 ? 3 : bpx % 2 == 0 ? 2 : 1;
+    const int grp = t / (G * gx), r = t - grp * (G * gx);
+    tm = xcd * bpx + grp * G + r % G;
+    tn = r / G;
+  } else {
+    int tile = bid;
+    if ((nb & 7) == 0) tile = (bid & 7) * (nb >> 3) + (bid >> 3);
+    tm = tile / gx;
+    tn = tile % gx;
+  }
+  const int m0 = tm * BMT, n0 = tn * BNT;
 
   // global -> register staging: thread t moves chunk (t & 7) of rows (t >> 3) + RS i
   const int cc = tid & 7, r0 = tid >> 3;

@@ -35,53 +35,64 @@ void embed_rows(const uint16_t *E, int H, int V, const int *const *tokens, int t
   hipLaunchKernelGGL(k_embed, dim3(M), dim3(256), 0, st, E, H, V, tokens, tok_off, h, bad_flag);
 }
 
-// One block per row: y = w * x / sqrt(mean(x^2) + eps), stored as f16 (MFMA
-// operand) and optionally f32.  When a split-K residual GEMM left `splits`
-// partial sums part[z][m][k] (z < splits), they are first added to the row,
-// which is written back: h[m] += sum_z part[z][m].  Thread t owns 4-float
-// chunks t, t + 256, ... of the row (H <= 8192: at most 8), and issues the
-// loads of its chunk of every partial at once.  x (f16) may be null when
+// One wavefront per row, four rows per block: y = w * x / sqrt(mean(x^2) +
+// eps), stored as f16 (MFMA operand) and optionally f32.  When a split-K
+// residual GEMM left `splits` partial sums part[z][m][k] (z < splits), they
+// are first added to the row, which is written back: h[m] += sum_z
+// part[z][m].  Lane l owns the 4-float chunks l, l + 64, ... of the row (H
+// <= 8192: at most 32); every load of the lane (row chunks, norm gains,
+// partials) is issued before the first is used, and the row's sum of
+// squares is one wave reduction (no barrier).  x (f16) may be null when
 // only the f32 copy is wanted.
+template <int NCH>
 __global__ __launch_bounds__(256) void k_rmsnorm_rows(float *h, int ldh, const float *w, int H,
                                                       int M, float eps, _Float16 *x, int ldx,
                                                       float *y32, const float *part, int splits) {
-  constexpr int kMaxChunks = 8;  // 256 threads * 4 floats * 8 = 8192 (the supported maximum)
-  __shared__ float sRed[4];
-  const int m = blockIdx.x, tid = threadIdx.x;
+  const int lane = threadIdx.x & 63;
+  const int m = blockIdx.x * 4 + (threadIdx.x >> 6);
+  if (m >= M) return;  // (uniform across the wavefront)
   float *row = h + (size_t)m * ldh;
-  f4 v[kMaxChunks];
-  float ss = 0.f;
+  f4 v[NCH], g[NCH];
 #pragma unroll
-  for (int c = 0; c < kMaxChunks; ++c) {
-    const int k = (tid + c * 256) * 4;
-    if (k < H) {
-      v[c] = *(const f4 *)(row + k);
-      if (splits > 0) {
-        // every partial set's load in flight at once (set index clamped,
-        // the sets past `splits` masked), then the sum in set order
-        f4 pz[kMaxSplits];
+  for (int c = 0; c < NCH; ++c) {
+    const int k = min((lane + c * 64) * 4, H - 4);  // (chunks past H re-read the last, unused)
+    v[c] = *(const f4 *)(row + k);
+    g[c] = *(const f4 *)(w + k);
+  }
+  if (splits > 0) {
+    // two partial sets per round trip (one for the widest rows, whose
+    // chunks fill the registers), summed in set order
+    constexpr int ZB = NCH <= 14 ? 2 : 1;
+    for (int z = 0; z < splits; z += ZB) {
+      f4 pz[ZB][NCH];
 #pragma unroll
-        for (int z = 0; z < kMaxSplits; ++z)
-          pz[z] = *(const f4 *)(part + ((size_t)min(z, splits - 1) * M + m) * H + k);
+      for (int u = 0; u < ZB; ++u) {
+        const float *pr = part + ((size_t)min(z + u, splits - 1) * M + m) * H;
 #pragma unroll
-        for (int z = 0; z < kMaxSplits; ++z)
-          if (z < splits) v[c] += pz[z];
-        *(f4 *)(row + k) = v[c];
+        for (int c = 0; c < NCH; ++c) pz[u][c] = *(const f4 *)(pr + min((lane + c * 64) * 4, H - 4));
       }
-      ss += v[c].x * v[c].x + v[c].y * v[c].y + v[c].z * v[c].z + v[c].w * v[c].w;
+#pragma unroll
+      for (int u = 0; u < ZB; ++u)
+        if (z + u < splits)
+#pragma unroll
+          for (int c = 0; c < NCH; ++c) v[c] += pz[u][c];
+    }
+#pragma unroll
+    for (int c = 0; c < NCH; ++c) {
+      const int k = (lane + c * 64) * 4;
+      if (k < H) *(f4 *)(row + k) = v[c];
     }
   }
-  ss = wave_sum(ss);
-  if ((tid & 63) == 0) sRed[tid >> 6] = ss;
-  __syncthreads();
-  ss = (sRed[0] + sRed[1]) + (sRed[2] + sRed[3]);
-  const float inv = 1.0f / sqrtf(ss / (float)H + eps);
+  float ss = 0.f;
 #pragma unroll
-  for (int c = 0; c < kMaxChunks; ++c) {
-    const int k = (tid + c * 256) * 4;
+  for (int c = 0; c < NCH; ++c)
+    if ((lane + c * 64) * 4 < H) ss += v[c].x * v[c].x + v[c].y * v[c].y + v[c].z * v[c].z + v[c].w * v[c].w;
+  const float inv = 1.0f / sqrtf(wave_sum(ss) / (float)H + eps);
+#pragma unroll
+  for (int c = 0; c < NCH; ++c) {
+    const int k = (lane + c * 64) * 4;
     if (k < H) {
-      const f4 g = *(const f4 *)(w + k);
-      const f4 y = v[c] * inv * g;
+      const f4 y = v[c] * inv * g[c];
       if (x) {
         h4 yh = {(_Float16)y.x, (_Float16)y.y, (_Float16)y.z, (_Float16)y.w};
         *(h4 *)(x + (size_t)m * ldx + k) = yh;
@@ -93,8 +104,20 @@ __global__ __launch_bounds__(256) void k_rmsnorm_rows(float *h, int ldh, const f
 
 void rmsnorm_rows_f16(float *h, int ldh, const float *w, int H, int M, float eps, _Float16 *x,
                       int ldx, float *y32, const float *part, int splits, hipStream_t st) {
-  hipLaunchKernelGGL(k_rmsnorm_rows, dim3(M), dim3(256), 0, st, h, ldh, w, H, M, eps, x, ldx,
-                     y32, part, splits);
+  const dim3 grid((M + 3) / 4);
+  const int nch = (H + 255) / 256;  // 4-float chunks per lane
+  if (nch <= 4)
+    hipLaunchKernelGGL(k_rmsnorm_rows<4>, grid, dim3(256), 0, st, h, ldh, w, H, M, eps, x, ldx,
+                       y32, part, splits);
+  else if (nch <= 8)
+    hipLaunchKernelGGL(k_rmsnorm_rows<8>, grid, dim3(256), 0, st, h, ldh, w, H, M, eps, x, ldx,
+                       y32, part, splits);
+  else if (nch <= 14)
+    hipLaunchKernelGGL(k_rmsnorm_rows<14>, grid, dim3(256), 0, st, h, ldh, w, H, M, eps, x, ldx,
+                       y32, part, splits);
+  else
+    hipLaunchKernelGGL(k_rmsnorm_rows<32>, grid, dim3(256), 0, st, h, ldh, w, H, M, eps, x, ldx,
+                       y32, part, splits);
 }
 
 // dst[dst_rows[i]] = src[src_rows[i]] for i < k, ncols floats per row
