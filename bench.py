@@ -35,8 +35,8 @@ MFMA_F16_PEAK_TFS = 2500.0  # MI355X dense f16 MFMA
 # WRITE_SIZE passes, scaled by what the counters read for a 256 MiB copy
 # (profiles/qwen2.5-0.5b_gateup_gemv_hbm_traffic.md); valid only while the
 # kernel source is the one the counters were taken on.
-GATEUP_TRAFFIC_BYTES = 17585673
-GATEUP_TRAFFIC_SRC_SHA = "2c27861c3ba9c4f2"
+GATEUP_TRAFFIC_BYTES = 17585680
+GATEUP_TRAFFIC_SRC_SHA = "252e5f99aa1e1328"
 
 
 def gateup_traffic(shape):
@@ -206,18 +206,19 @@ def counter_summary(path: str, simds: int = 1024, xcds: int = 8) -> None:
     for d, c in per.items():
         groups[names[d]].append(c)
     counters = sorted({k for c in per.values() for k in c})
-    print(f"{'kernel':48s} {'disp':>5s} " + " ".join(f"{c[:26]:>26s}" for c in counters)
+    print(f"{'kernel':48s} {'disp':>5s} " + " ".join(f"{c[:26]:>26s} {'(max)':>12s}" for c in counters)
           + f" {'MFMA busy':>9s} {'f16 MFMA GFLOP':>14s}")
     for k in sorted(groups, key=lambda k: -sum(c.get("GRBM_GUI_ACTIVE", 0) for c in groups[k])):
         g = groups[k]
         mean = {c: sum(x.get(c, 0.0) for x in g) / len(g) for c in counters}
+        mx = {c: max(x.get(c, 0.0) for x in g) for c in counters}
         util = ""
         if "SQ_VALU_MFMA_BUSY_CYCLES" in mean and mean.get("GRBM_GUI_ACTIVE"):
             util = (f"{100 * mean['SQ_VALU_MFMA_BUSY_CYCLES'] / (mean['GRBM_GUI_ACTIVE'] / xcds * simds):8.1f}%")
         fl = ""
         if "SQ_INSTS_VALU_MFMA_MOPS_F16" in mean:
             fl = f"{mean['SQ_INSTS_VALU_MFMA_MOPS_F16'] * 512 / 1e9:14.2f}"
-        print(f"{k[:48]:48s} {len(g):5d} " + " ".join(f"{mean[c]:26.4g}" for c in counters)
+        print(f"{k[:48]:48s} {len(g):5d} " + " ".join(f"{mean[c]:26.6g} {mx[c]:12.6g}" for c in counters)
               + f" {util:>9s} {fl:>14s}")
 
 
