@@ -809,10 +809,43 @@ static int launch_xl(GemmP p, const Workspace &wsp, hipStream_t st) {
 // wavefronts).  Long K: the tile whose measured per-CU rate times the number
 // of rounds of blocks over the 256 CUs is cheapest, among 256 x 256 (910
 // TFLOP/s on a 2048 x 37888 x 3584 GEMM), 128 x 256 (850) and 128 x 128 (740).
+// A residual GEMM on 128 x 128 tiles whose tiles cannot fill the CUs
+// (fewer than 192) splits K so that about 256 blocks run, the partial sums
+// pending in the workspace for the next RMSNorm (as launch_xl; 1.5B head
+// layout, 512 rows, down 1536 x 8960: 48 tiles).  Returns the pending
+// split count (0: applied).
+template <int EPI>
+static int launch_big_resid(GemmP p, const Workspace &wsp, hipStream_t st) {
+  int splits = 1;
+  const int nk = p.K / kBK2;
+  const int tiles = ((p.M + 127) / 128) * ((p.N + 127) / 128);
+  if (EPI == G_RESID && wsp.buf && tiles < 192) {
+    splits = min(256 / tiles, min(kMaxSplits, nk));
+    splits = min(splits, (int)(wsp.bytes / ((size_t)p.M * p.N * 4)));
+    if (splits < 1) splits = 1;
+  }
+  p.ws = splits > 1 ? wsp.buf : nullptr;
+  p.atomic_out = 0;
+  const int ks = (nk + splits - 1) / splits;
+  const int used = (nk + ks - 1) / ks;
+  launch_big<EPI, 128, 128, 2, 0, 8>(p, splits, st);
+  return used > 1 ? used : 0;
+}
+
 template <int EPI>
 static int launch_large_m(const GemmP &p, const Workspace &wsp, hipStream_t st) {
-  if constexpr (EPI == G_QKV) {  // (its LDS-staged epilogue fits a 128 x 128 tile)
-    launch_big<EPI, 128, 128, 2, 0, 8>(p, 1, st);
+  if constexpr (EPI == G_QKV) {
+    // (its LDS-staged epilogue fits tiles up to 128 x 128) rows per tile:
+    // 128, or fewer when 128-row tiles would leave most CUs idle (about 200
+    // blocks wanted; 1.5B head layout, 512 rows x 2048: 64 tiles of 128 x
+    // 128 against 256 of 32 x 128)
+    const int nt = (p.N + 127) / 128;
+    if (((p.M + 127) / 128) * nt >= 192)
+      launch_big<EPI, 128, 128, 2, 0, 8>(p, 1, st);
+    else if (((p.M + 63) / 64) * nt >= 192)
+      launch_big<EPI, 64, 128, 2, 0, 8>(p, 1, st);
+    else
+      launch_big<EPI, 32, 128, 1, 0, 4>(p, 1, st);
     return 0;
   } else {
     // (residual GEMMs with fewer than 96 tiles would need more than two
@@ -822,10 +855,8 @@ static int launch_large_m(const GemmP &p, const Workspace &wsp, hipStream_t st) 
     if (p.K >= 2048 && p.M >= 1024 && (EPI == G_SWIGLU || tiles >= 96))
       return launch_xl<EPI>(p, wsp, st);
   }
-  if (p.K < 2048) {
-    launch_big<EPI, 128, 128, 2, 0, 8>(p, 1, st);
-    return 0;
-  }
+  if (p.K < 2048 || (EPI == G_RESID && ((p.M + 127) / 128) * ((p.N + 127) / 128) < 192))
+    return launch_big_resid<EPI>(p, wsp, st);
   struct Cand { int bm, bn; double rate; };
   const Cand cand[3] = {{256, 256, 910.0}, {128, 256, 850.0}, {128, 128, 740.0}};
   int best = 2;
