@@ -835,14 +835,30 @@ static int launch_big_resid(GemmP p, const Workspace &wsp, hipStream_t st) {
 template <int EPI>
 static int launch_large_m(const GemmP &p, const Workspace &wsp, hipStream_t st) {
   if constexpr (EPI == G_QKV) {
-    // (its LDS-staged epilogue fits tiles up to 128 x 128) rows per tile:
-    // 128, or fewer when 128-row tiles would leave most CUs idle (about 200
-    // blocks wanted; 1.5B head layout, 512 rows x 2048: 64 tiles of 128 x
-    // 128 against 256 of 32 x 128)
+    // (its LDS-staged epilogue fits tiles up to 128 x 128) Rows per tile:
+    // the one of 128, 64 and 32 with the least rounds of blocks over the 256
+    // CUs times rows per tile over the rate a row of that tile reaches
+    // (relative rates 1, 0.83, 0.59, measured on the hd-128 2048-row QKV).
+    // Measured: 0.5B 4096 rows (288 tiles of 128): 0.78 -> 0.67 ms per
+    // prefill on 64-row tiles; 1.5B head layout, 512 rows x 2048 (64 tiles
+    // of 128): 0.86 -> 0.66 ms on 32-row tiles; hd-128 2048 rows stays on
+    // 128 (32-row tiles: 3.36 -> 4.29 ms).
     const int nt = (p.N + 127) / 128;
-    if (((p.M + 127) / 128) * nt >= 192)
+    const int rows[3] = {128, 64, 32};
+    const double rate[3] = {1.0, 0.83, 0.59};
+    int best = 0;
+    double best_cost = 1e300;
+    for (int i = 0; i < 3; ++i) {
+      const long tiles = (long)((p.M + rows[i] - 1) / rows[i]) * nt;
+      const double cost = (double)((tiles + 255) / 256) * rows[i] / rate[i];
+      if (cost < best_cost * 0.98) {
+        best_cost = cost;
+        best = i;
+      }
+    }
+    if (best == 0)
       launch_big<EPI, 128, 128, 2, 0, 8>(p, 1, st);
-    else if (((p.M + 63) / 64) * nt >= 192)
+    else if (best == 1)
       launch_big<EPI, 64, 128, 2, 0, 8>(p, 1, st);
     else
       launch_big<EPI, 32, 128, 1, 0, 4>(p, 1, st);
