@@ -438,7 +438,7 @@ def main():
         "next_token_probs_us": probs_us,
         "next_token_probs_rows": prob_rows,
         "roofline": {
-            "kernel": f"k_gemv1<4, {kb}, 2> (RMSNorm + gate/up + SwiGLU, decode M=1)",
+            "kernel": f"k_gemv1<2, {kb}, 2> (RMSNorm + gate/up + SwiGLU, decode M=1)",
             "bound": "hbm", "achieved": achieved, "peak": HBM_PEAK_GBS, "unit": "GB/s",
             "frac": achieved / HBM_PEAK_GBS, "traffic": gateup_traffic(shape),
             "bytes_per_launch": gu_bytes, "avg_launch_us": gu_avg_s * 1e6, "launches_timed": reps,

@@ -254,6 +254,7 @@ struct AttnWoP {
   // n_ctx), known on the host; the position itself is read on the device.
   const float *kb1, *vb1;
   int nk1;
+  L2Warm warm;  // one-row calls: producer blocks in grid rows y >= nh
 };
 
 template <int N>
@@ -489,6 +490,10 @@ __global__ __launch_bounds__(256) void k_attn_wo1(AttnWoP p) {
     asm volatile("" ::"s"(G), "s"(H), "s"(p.d.nh), "s"(p.d.n_ctx), "s"(p.nk1),
                  "s"(p.rows_per_block), "s"(p.scale));
   }
+  if (head >= p.d.nh) {  // an L2 warming producer (grid rows past the heads)
+    l2_warm<kWarmStepsAttn>(p.warm, rc + head * (int)gridDim.x);
+    return;
+  }
   const unsigned pos = vload(p.rows.pos, 0);
   const f4 q4 = *(const f4 *)(p.q + (size_t)head * HD + 4 * dc);
   const int r0 = rc * p.rows_per_block;
@@ -609,24 +614,29 @@ __global__ __launch_bounds__(256) void k_attn_wo1(AttnWoP p) {
 template <int HD>
 static void attn_wo_hd(const AttnWoP &p, int grid_x, hipStream_t st) {
   dim3 grid(grid_x, p.d.nh);
-  if (p.M <= 1)
+  if (p.M <= 1) {
+    grid.y += p.warm.n_prod / grid_x;  // (n_prod: whole grid rows)
     hipLaunchKernelGGL((k_attn_wo1<HD>), grid, dim3(256), 0, st, p);
-  else
+  } else {
     hipLaunchKernelGGL((k_attn_wo<HD, 8>), grid, dim3(256), 0, st, p);
+  }
 }
 
 void attn_wo_fused(const Dims &d, int layer, const KVCache &kv, const float *q, int ldq,
                    RowInfo rows, int M, int seq1, int nk1, const uint16_t *wo, float *h, int ldh,
-                   hipStream_t st) {
+                   const uint16_t *warm_wd, hipStream_t st) {
   const int rpb = 4 * wo_loads_fused(d.hd) * (64 / (d.hd / 8));  // WO rows per block
   AttnWoP p{d, layer, kv, q, ldq, rows, M, (const _Float16 *)wo, h, ldh, rpb,
-            1.0f / sqrtf((float)d.hd), nullptr, nullptr, 0};
+            1.0f / sqrtf((float)d.hd), nullptr, nullptr, 0, L2Warm{}};
+  const int gx = (d.H + rpb - 1) / rpb;
   if (M <= 1) {
     p.kb1 = kv.k + kv.off(d, layer, seq1, 0, 0);
     p.vb1 = kv.v + kv.off(d, layer, seq1, 0, 0);
     p.nk1 = nk1;
+    if (warm_wd)  // whole grid rows of producers after the heads' rows
+      p.warm = warm_gemv1(warm_wd, d.H, d.I_pad, down_rows1(d.I_pad), gx * d.nh,
+                          kWarmProdAttn / gx * gx, kWarmStepsAttn);
   }
-  const int gx = (d.H + rpb - 1) / rpb;
   switch (d.hd) {
     case 16: attn_wo_hd<16>(p, gx, st); break;
     case 64: attn_wo_hd<64>(p, gx, st); break;

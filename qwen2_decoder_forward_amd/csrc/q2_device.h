@@ -285,4 +285,44 @@ __device__ __forceinline__ void qkv_store_rows(const Dims &d, const QkvEpi &e, c
   }
 }
 
+
+// A producer block of an L2Warm (linear block id bid) reads its share of the
+// groups the later launch reads on this XCD: the XCD's groups g = x + 8 t
+// are split into contiguous runs of t over the XCD's producers, and the
+// run is read flat, 256 threads x 16 bytes a step, every step issued before
+// any is waited for (steps past the run are skipped, block-uniformly; a
+// thread's part of the last step that falls past the run or the matrix
+// reloads the matrix's first 16 bytes).  The loaded words feed an empty asm
+// only.
+template <int NL>  // at most NL steps per producer (the host plans for that)
+__device__ __forceinline__ void l2_warm(const L2Warm &f, int bid) {
+  const int x = bid & 7;
+  const int first = f.p0 + ((x - f.p0) & 7);  // this XCD's first producer
+  const int n_x = (f.p0 + f.n_prod - first + 7) >> 3;
+  const int j = (bid - first) >> 3;
+  const int T = (f.n_groups - x + 7) >> 3;  // groups the later launch reads on this XCD
+  const int t1 = (int)((long long)(j + 1) * T / n_x);
+  int t = (int)((long long)j * T / n_x), e = threadIdx.x;
+  const int steps = ((t1 - t) * f.group_u4 + 255) >> 8;  // (block-uniform)
+  uint4 v[NL];
+#pragma unroll
+  for (int i = 0; i < NL; ++i) {
+    v[i] = (uint4){0u, 0u, 0u, 0u};
+    if (i < steps) {
+      long long a = (long long)(x + 8 * t) * f.group_u4 + e;
+      if (t >= t1 || a >= f.total_u4) a = 0;
+      v[i] = f.base[a];
+      e += 256;
+      if (e >= f.group_u4) {  // (group_u4 >= 256: at most one group per step)
+        e -= f.group_u4;
+        ++t;
+      }
+    }
+  }
+  unsigned acc = 0;
+#pragma unroll
+  for (int i = 0; i < NL; ++i) acc ^= v[i].x ^ v[i].y ^ v[i].z ^ v[i].w;
+  asm volatile("" ::"v"(acc));
+}
+
 }  // namespace q2

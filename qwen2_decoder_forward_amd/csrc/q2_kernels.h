@@ -66,6 +66,35 @@ struct QkvEpi {
   RopeTable rope;
 };
 
+// Warming of a later launch's weights in the L2 of the XCD that will read
+// them.  Blocks of a launch are dealt to the 8 XCDs round-robin by linear
+// block id (block b runs on XCD b % 8), and each XCD has its own L2, so a
+// one-row GEMV whose block g reads row group g reads it on XCD g % 8.  A
+// launch that leaves CUs idle (the one-row QKV GEMV, the one-row attention)
+// takes extra producer blocks that read, on each XCD, the groups the later
+// GEMV will read there; that GEMV then finds them in its L2.  Performance
+// only: the producers write nothing, and a group they miss is read from HBM.
+struct L2Warm {
+  const uint4 *base;   // the later GEMV's matrix: group g starts at base + g * group_u4
+  long long total_u4;  // its size in 16-byte units
+  int group_u4;        // 16-byte units per group (>= 256)
+  int n_groups;        // groups (the later launch's block g reads group g)
+  int p0, n_prod;      // producer block ids [p0, p0 + n_prod) of the warming launch
+};
+// Producer blocks of the one-row attention, which warms the same layer's
+// down projection, and their step bound (16-byte loads per thread).  More
+// producers than idle CUs keep each one's share small: a CU pulls only about
+// 26 KB per microsecond from HBM (outstanding misses over the latency).
+constexpr int kWarmProdAttn = 256, kWarmStepsAttn = 16;
+// n_prod producers for a later one-row GEMV over W [N, K] with R rows per
+// wave, hosted by a launch whose producer block ids start at p0; none (n_prod
+// = 0 in the result) when it does not pay (weights too large for the L2s)
+// or a producer's share would exceed max_steps steps.
+L2Warm warm_gemv1(const uint16_t *W, int N, int K, int R, int p0, int n_prod, int max_steps);
+// Rows per wave of the one-row gate/up and down GEMVs.
+constexpr int kGateUpRows1 = 2;
+constexpr int down_rows1(int K) { return K >= 2048 ? 1 : 2; }
+
 // Greedy readout: packed (ordered-key, ~index) 64-bit maxima per row, zero
 // between calls (the finalize kernel clears them).  The output pointers are
 // read on the device from a slot the host staged with the call, so a
@@ -183,9 +212,11 @@ void attn_decode(const Dims &d, int layer, const KVCache &kv, const float *q, in
 constexpr int kFusedKeys = 512;
 constexpr int wo_loads_per_wave(int hd) { return hd == 64 ? 2 : 8; }
 constexpr int wo_loads_fused(int hd) { return hd == 64 ? 2 : 8; }  // (attn_wo_fused's blocks)
+// warm_wd: the down projection of the same layer, warmed by producer blocks
+// of the one-row kernel (null: none).
 void attn_wo_fused(const Dims &d, int layer, const KVCache &kv, const float *q, int ldq,
                    RowInfo rows, int M, int seq1, int nk1, const uint16_t *wo, float *h, int ldh,
-                   hipStream_t st);
+                   const uint16_t *warm_wd, hipStream_t st);
 // The chunk records of attn_decode (merge = false) of M <= 8 rows merged
 // and multiplied by WO, the partial row sums added into h with float
 // atomics: per (WO row chunk, query head) block as in attn_wo_fused.
