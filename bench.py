@@ -116,6 +116,49 @@ def cpu_baseline(shape, weights, prompt, n_ctx, budget_s):
     }
 
 
+def measure_ceilings(torch, q, dev, stream) -> dict:
+    """What this device reaches, timed with HIP events in this job: a plain
+    streaming read of an 8 GiB buffer (past the 256 MB Infinity Cache, so HBM;
+    best of three grid sizes, three reads each; a 2 GiB buffer reads about 8 %
+    slower) and a register-only f16 MFMA loop (best of three grid sizes)."""
+    ev = [torch.cuda.Event(enable_timing=True) for _ in range(2)]
+
+    def timed(fn, reps):
+        fn()
+        torch.cuda.synchronize()
+        ev[0].record(stream)
+        for _ in range(reps):
+            fn()
+        ev[1].record(stream)
+        torch.cuda.synchronize()
+        return ev[0].elapsed_time(ev[1]) / reps / 1e3
+
+    nbytes = 8 << 30
+    buf = torch.empty(nbytes, dtype=torch.uint8, device=dev)
+    best_read = (0.0, 0)
+    for nb in (4096, 8192, 16384):
+        out = torch.empty(4 * nb, dtype=torch.int32, device=dev)
+        t = timed(lambda: q.qwen2_probe_read(buf, nbytes, nb, out, stream=stream.cuda_stream), 3)
+        best_read = max(best_read, (nbytes / t / 1e9, nb))
+    del buf
+    iters = 4000
+    best_mfma = (0.0, 0)
+    for nb in (512, 2048, 4096):
+        out = torch.empty(4 * nb, dtype=torch.float32, device=dev)
+        t = timed(lambda: q.qwen2_probe_mfma(iters, nb, out, stream=stream.cuda_stream), 3)
+        flops = nb * 4 * iters * 4 * 2 * 32 * 32 * 16
+        best_mfma = max(best_mfma, (flops / t / 1e12, nb))
+    return {
+        "hbm_read_gbs": best_read[0], "hbm_read_frac_of_peak": best_read[0] / HBM_PEAK_GBS,
+        "hbm_read_blocks": best_read[1], "hbm_read_bytes": nbytes,
+        "mfma_f16_tflops": best_mfma[0], "mfma_frac_of_peak": best_mfma[0] / MFMA_F16_PEAK_TFS,
+        "mfma_blocks": best_mfma[1],
+        "how": "qwen2_probe_read (non-temporal 16-byte loads, 8 in flight per thread) and "
+               "qwen2_probe_mfma (v_mfma_f32_32x32x16_f16, four accumulators per wavefront), "
+               "timed with HIP events in this job",
+    }
+
+
 def prefill_gemm_flops(shape, n: int) -> dict:
     """Dense flops of each projection of a prefill of n rows (the last layer's
     FFN runs on the last row only) and of the lm_head on that row."""
@@ -406,6 +449,8 @@ def main():
     torch.cuda.synchronize()
     probs_us = ev_k[0].elapsed_time(ev_k[1]) / 100 * 1e3
 
+    ceil = measure_ceilings(torch, q, dev, stream)
+
     fl = prefill_gemm_flops(shape, n)
     prefill_flops = sum(fl.values()) + attn_prefill_flops(shape, n)
     prefill_bytes = streamed_f16(shape, wb, n) + wb["f32"] + n * kv_pos
@@ -434,6 +479,7 @@ def main():
         "decode_ms_per_step": decode_ms / (1 if batched else steps_dec),
         "decode_hbm_gbs": dec_gbs,
         "decode_hbm_frac": dec_gbs / HBM_PEAK_GBS,
+        "decode_hbm_frac_of_ceiling": dec_gbs / ceil["hbm_read_gbs"],
         "wall_s_timed": wall,
         "next_token_probs_us": probs_us,
         "next_token_probs_rows": prob_rows,
@@ -441,10 +487,13 @@ def main():
             "kernel": f"k_gemv1<2, {kb}, 2> (RMSNorm + gate/up + SwiGLU, decode M=1)",
             "bound": "hbm", "achieved": achieved, "peak": HBM_PEAK_GBS, "unit": "GB/s",
             "frac": achieved / HBM_PEAK_GBS, "traffic": gateup_traffic(shape),
+            "measured_ceiling": ceil["hbm_read_gbs"],
+            "frac_of_ceiling": achieved / ceil["hbm_read_gbs"],
             "bytes_per_launch": gu_bytes, "avg_launch_us": gu_avg_s * 1e6, "launches_timed": reps,
             "timing": "HIP events around back-to-back launches cycling through the layers "
                       "(the in-graph duration: rocprofv3 trace, bench.py --trace-summary)",
         },
+        "ceilings": ceil,
         "cpu_baseline": None,
     }
     if batched:
@@ -454,6 +503,8 @@ def main():
         out["prefill_ms"] = prefill_ms
         out["prefill_hbm_frac"] = prefill_bytes / (prefill_ms / 1e3) / 1e9 / HBM_PEAK_GBS
         out["prefill_mfma_frac"] = prefill_flops / (prefill_ms / 1e3) / 1e12 / MFMA_F16_PEAK_TFS
+        out["prefill_mfma_frac_of_ceiling"] = (prefill_flops / (prefill_ms / 1e3) / 1e12 /
+                                               ceil["mfma_f16_tflops"])
         if n > 8:
             # a fresh context, so the prefill runs on an empty cache as above
             model.close()
@@ -463,6 +514,9 @@ def main():
             f"{out['prefill_mfma_frac'] * 100:.1f}% MFMA)")
     log(f"[{wl.name}] decode {dec_tok_s:.1f} tok/s ({decode_ms:.3f} ms, {dec_gbs:.0f} GB/s), "
         f"gate/up GEMV {gu_avg_s * 1e6:.2f} us = {achieved:.0f} GB/s")
+    log(f"[{wl.name}] ceilings: HBM read {ceil['hbm_read_gbs']:.0f} GB/s "
+        f"({ceil['hbm_read_frac_of_peak'] * 100:.1f}% of peak), f16 MFMA "
+        f"{ceil['mfma_f16_tflops']:.0f} TFLOP/s ({ceil['mfma_frac_of_peak'] * 100:.1f}% of peak)")
     log(f"[{wl.name}] next_token_probs of {prob_rows} row(s) x {V}: {probs_us:.2f} us "
         f"({8 * V * prob_rows / (probs_us * 1e3):.0f} GB/s of logits in + probabilities out)")
     if "prefill_ops" in out:

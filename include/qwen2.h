@@ -274,9 +274,28 @@ int qwen2_prof_read(qwen2_ctx *ctx, int32_t op, int32_t *launches, double *total
  * (it writes only a scratch buffer, so the model state is unchanged);
  * anything else is QWEN2_E_ARG. */
 int qwen2_prof_repeat(qwen2_ctx *ctx, int32_t op, int32_t rows, int32_t iters, void *stream);
+/* Device ceilings, measured in the same job as a workload so that its rates
+ * can be set against what this device reaches rather than only its spec
+ * peaks (8 TB/s HBM, 2.5 PFLOP/s dense f16 MFMA).  No context; errors are
+ * reported by qwen2_last_error(NULL).  Enqueued on `stream`; the caller
+ * times them with its own events.
+ * qwen2_probe_read: n_blocks blocks of 256 threads read the `bytes` (a
+ * positive multiple of 16) at buf_dev once, with 16-byte non-temporal loads,
+ * and write one fold of the words per wavefront to out_dev [4 n_blocks]
+ * uint32.  A buffer larger than the 256 MB Infinity Cache measures HBM.
+ * qwen2_probe_mfma: n_blocks blocks of four wavefronts, each issuing
+ * 4 iters v_mfma_f32_32x32x16_f16 on register operands (2 * 32 * 32 * 16
+ * flop each), and writing one sum per wavefront to out_dev [4 n_blocks] f32.
+ * QWEN2_E_ARG for a null pointer, bytes not a positive multiple of 16, iters
+ * < 1 or n_blocks outside [1, 65536]. */
+int qwen2_probe_read(const void *buf_dev, size_t bytes, int32_t n_blocks, uint32_t *out_dev,
+                     void *stream);
+int qwen2_probe_mfma(int32_t iters, int32_t n_blocks, float *out_dev, void *stream);
+
 const char *qwen2_last_error(const qwen2_ctx *ctx); /* ctx NULL: the last error of a call
                                                        without a context (qwen2_load,
-                                                       qwen2_next_token_probs_static) */
+                                                       qwen2_next_token_probs_static,
+                                                       qwen2_probe_read, qwen2_probe_mfma) */
 const char *qwen2_strerror(int code);
 
 /* Frees every device allocation of the context (synchronises the device). */

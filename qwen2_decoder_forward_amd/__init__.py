@@ -22,7 +22,8 @@ __all__ = [
     "qwen2_next_token_probs_static",
     "qwen2_set_stop_ids", "qwen2_read_stops",
     "qwen2_sync_status", "qwen2_info", "qwen2_last_error", "qwen2_strerror", "qwen2_free",
-    "qwen2_prof_enable", "qwen2_prof_read", "qwen2_prof_repeat", "OPS", "make_hparams", "Model",
+    "qwen2_prof_enable", "qwen2_prof_read", "qwen2_prof_repeat", "qwen2_probe_read",
+    "qwen2_probe_mfma", "OPS", "make_hparams", "Model",
 ]
 
 LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), "libqwen2_mi355x.so")
@@ -105,6 +106,8 @@ def lib() -> C.CDLL:
             "qwen2_prof_enable": (i32, [vp, C.c_uint32]),
             "qwen2_prof_read": (i32, [vp, i32, PI32, C.POINTER(C.c_double)]),
             "qwen2_prof_repeat": (i32, [vp, i32, i32, i32, vp]),
+            "qwen2_probe_read": (i32, [vp, C.c_size_t, i32, vp, vp]),
+            "qwen2_probe_mfma": (i32, [i32, i32, vp, vp]),
         }
         for name, (res, args) in sig.items():
             f = getattr(L, name)
@@ -252,6 +255,16 @@ def qwen2_next_token_probs_static(logits, rows: int, n_vocab: int, probs, stream
     """The allocation-free form (no context; the library's fixed scratch)."""
     _check(lib().qwen2_next_token_probs_static(_ptr(logits), rows, n_vocab, _ptr(probs),
                                                _stream(stream)))
+
+
+def qwen2_probe_read(buf, nbytes: int, n_blocks: int, out, stream=None) -> None:
+    """Streaming read of nbytes at buf (device ceiling probe; out: [4 n_blocks] int32)."""
+    _check(lib().qwen2_probe_read(_ptr(buf), nbytes, n_blocks, _ptr(out), _stream(stream)))
+
+
+def qwen2_probe_mfma(iters: int, n_blocks: int, out, stream=None) -> None:
+    """Register-only f16 MFMA loop (device ceiling probe; out: [4 n_blocks] f32)."""
+    _check(lib().qwen2_probe_mfma(iters, n_blocks, _ptr(out), _stream(stream)))
 
 
 def qwen2_set_stop_ids(ctx: int, ids) -> None:

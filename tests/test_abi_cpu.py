@@ -158,3 +158,17 @@ def test_rope_style_and_bad_scalars_rejected():
 def test_real_shapes_are_accepted():
     for name in syn.MODELS:
         assert q.qwen2_check_hparams(hp_for(syn.MODELS[name], 4096, 1)) == 0, name
+
+
+def test_probe_arguments_rejected_before_any_launch():
+    """The ceiling probes check their arguments on the host (no device is
+    touched for a rejected call) and report through qwen2_last_error(NULL)."""
+    L = q.lib()
+    out = 4096  # (a non-null stand-in address; never dereferenced here)
+    for buf, nbytes, nb in ((None, 1 << 20, 64), (out, 15, 64), (out, 0, 64), (out, 1 << 20, 0),
+                            (out, 1 << 20, 65537)):
+        assert L.qwen2_probe_read(buf, nbytes, nb, out, None) == -1
+        assert b"qwen2_probe_read" in L.qwen2_last_error(None)
+    for iters, nb, o in ((0, 64, out), (10, 0, out), (10, 64, None), (10, 70000, out)):
+        assert L.qwen2_probe_mfma(iters, nb, o, None) == -1
+        assert b"qwen2_probe_mfma" in L.qwen2_last_error(None)
