@@ -51,6 +51,7 @@ enum {
   QWEN2_E_ORDER = -6,   /* positions of one prefill not strictly increasing */
   QWEN2_E_HIP = -7,     /* a HIP runtime call failed (message has the HIP error) */
   QWEN2_E_OOM = -8,     /* device or host allocation failed */
+  QWEN2_E_DEBUG = -9,   /* a debug check failed (contexts loaded with QWEN2_DEBUG_CHECKS=1) */
 };
 
 /* Model and cache hyperparameters (HParams of the minfer page, section 2;
@@ -132,7 +133,18 @@ int qwen2_check_decode(const qwen2_hparams *hp, int32_t n_batch, const int32_t *
  * may free its copies on return), allocates a zero-filled f32 KV cache
  * [n_layer][n_seq][n_head_kv][n_ctx][head_dim] for K and for V, scratch
  * activations and the RoPE cos/sin table.  Synchronous.  On failure *out is
- * NULL and nothing stays allocated. */
+ * NULL and nothing stays allocated.
+ * Debug checks (the GPU guards of the minfer page, section 7, that fail with
+ * the offending values): with the environment variable QWEN2_DEBUG_CHECKS=1
+ * at load, every prefill, batched prefill and decode of the context also
+ * hashes every KV-cache word (f32 K and V and both binary16 mirrors) outside
+ * the (sequence, position) slots the call may write, before and after the
+ * call, and scans the K / V it wrote, its read-out hidden rows and its
+ * logits (when given) for non-finite values.  Such a call waits for its
+ * stream and returns QWEN2_E_DEBUG, with the place and the value in
+ * qwen2_last_error, if the cache changed outside those slots or a value is
+ * not finite.  Slow (two passes over the whole cache per call); off by
+ * default. */
 int qwen2_load(const qwen2_hparams *hp, const qwen2_weights *w, void *stream, qwen2_ctx **out);
 
 /* Runs the prompt (or a continuation) of one sequence.

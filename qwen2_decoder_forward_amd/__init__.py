@@ -29,7 +29,7 @@ __all__ = [
 LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), "libqwen2_mi355x.so")
 
 CODES = {0: "OK", -1: "E_ARG", -2: "E_HPARAMS", -3: "E_POS", -4: "E_TOKEN", -5: "E_SEQ",
-         -6: "E_ORDER", -7: "E_HIP", -8: "E_OOM"}
+         -6: "E_ORDER", -7: "E_HIP", -8: "E_OOM", -9: "E_DEBUG"}
 
 # op kinds of qwen2_prof_enable / qwen2_prof_read (QWEN2_OP_* in the header)
 OPS = {"embed": 0, "qkv": 1, "attn": 2, "wo": 3, "gateup": 4, "down": 5, "lmhead": 6, "norm": 7}

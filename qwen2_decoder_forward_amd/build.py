@@ -16,7 +16,8 @@ CSRC = os.path.join(PKG, "csrc")
 OBJ = os.path.join(ROOT, "_build", "obj")
 LIB = os.path.join(PKG, "libqwen2_mi355x.so")
 
-SOURCES = ["k_gemv.hip", "k_attn.hip", "k_gemm.hip", "k_misc.hip", "k_probe.hip", "qwen2_abi.cpp",
+SOURCES = ["k_gemv.hip", "k_attn.hip", "k_gemm.hip", "k_misc.hip", "k_probe.hip", "k_debug.hip",
+           "qwen2_abi.cpp",
            "validate.cpp"]
 ARCH = "gfx950"
 # Packed-f32 VALU ops are disabled for every device pass; the compiler then

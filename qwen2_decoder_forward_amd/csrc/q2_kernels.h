@@ -95,6 +95,22 @@ L2Warm warm_gemv1(const uint16_t *W, int N, int K, int R, int p0, int n_prod, in
 constexpr int kGateUpRows1 = 2;
 constexpr int down_rows1(int K) { return K >= 2048 ? 1 : 2; }
 
+// Debug checks of a call (contexts loaded with QWEN2_DEBUG_CHECKS=1).
+// mask [n_seq][n_ctx]: 1 for the slots the call may write.  debug_kv adds a
+// hash of every cache word outside those slots (f32 K and V, both binary16
+// mirrors) into *hash and keeps, in *bad_k / *bad_v, the smallest f32 word
+// index of a non-finite K / V value inside them; debug_nonfinite keeps the
+// smallest index of a non-finite value of x[0 .. n) in *bad.
+struct DebugKv {
+  const unsigned char *mask;
+  int hd, n_ctx, ldp, nkv, n_seq;
+};
+void debug_kv(const DebugKv &a, const float *k, const float *v, const _Float16 *k16,
+              const _Float16 *v16t, size_t f32_words, size_t f16_words,
+              unsigned long long *hash, unsigned long long *bad_k, unsigned long long *bad_v,
+              hipStream_t st);
+void debug_nonfinite(const float *x, size_t n, unsigned long long *bad, hipStream_t st);
+
 // Greedy readout: packed (ordered-key, ~index) 64-bit maxima per row, zero
 // between calls (the finalize kernel clears them).  The output pointers are
 // read on the device from a slot the host staged with the call, so a

@@ -92,6 +92,13 @@ struct qwen2_ctx {
   std::vector<hipEvent_t> prof_ev;  // 2 per timed launch
   int prof_used = 0;
   std::vector<std::pair<int, int>> prof_rec;  // (op, event pair)
+  // debug checks (QWEN2_DEBUG_CHECKS=1 at load): the call's slot mask
+  // [n_seq][n_ctx] and the results [8]: hash before, hash after, first
+  // non-finite K word, V word, logit, hidden value (~0: none), 2 spare
+  bool debug = false;
+  unsigned char *dbg_mask = nullptr;
+  unsigned long long *dbg = nullptr;
+  std::vector<unsigned char> dbg_host;
   std::string err;
 };
 
@@ -127,6 +134,8 @@ void release(qwen2_ctx *c) {
   if (c->vc16t) (void)hipFree(c->vc16t);
   if (c->rope_cos) (void)hipFree(c->rope_cos);
   if (c->sarena) (void)hipFree(c->sarena);
+  if (c->dbg_mask) (void)hipFree(c->dbg_mask);
+  if (c->dbg) (void)hipFree(c->dbg);
   if (c->pinned) (void)hipHostFree(c->pinned);
   for (auto &e : c->ev)
     if (e) (void)hipEventDestroy(e);
@@ -332,6 +341,16 @@ int qwen2_load(const qwen2_hparams *hp, const qwen2_weights *w, void *stream, qw
   c->io_cap = (size_t)std::max(d.n_ctx, c->max_rows + d.n_seq);
   const char *ng = getenv("QWEN2_NO_GRAPH");
   c->use_graphs = !(ng && ng[0] == '1');
+  const char *dc = getenv("QWEN2_DEBUG_CHECKS");
+  c->debug = dc && dc[0] == '1';
+  if (c->debug) {
+    c->dbg_host.assign((size_t)d.n_seq * d.n_ctx, 0);
+    LTRY([&]() -> int {
+      HIP_TRY(c, hipMalloc(&c->dbg_mask, c->dbg_host.size()));
+      HIP_TRY(c, hipMalloc(&c->dbg, 8 * sizeof(unsigned long long)));
+      return 0;
+    }());
+  }
   {
     const size_t R = c->rows_cap, D = c->dec_rows;
     cur = 0;
@@ -623,6 +642,82 @@ void decode_launches(qwen2_ctx *c, int B, int n_chunks, const int *dpos, const i
   rows_head(c, B, rows, pending, st);
 }
 
+// Debug checks (QWEN2_DEBUG_CHECKS=1).  debug_begin marks the (sequence,
+// position) slots a call may write and hashes every other cache word;
+// debug_end hashes them again, scans the K / V the call wrote, its read-out
+// hidden rows and its logits (when given) for non-finite values, waits for
+// the stream, and returns QWEN2_E_DEBUG with the first offending value.
+q2::DebugKv debug_args(qwen2_ctx *c) {
+  const Dims &d = c->d;
+  return q2::DebugKv{c->dbg_mask, d.hd, d.n_ctx, c->ldp, d.nkv, d.n_seq};
+}
+
+void debug_scan_kv(qwen2_ctx *c, unsigned long long *hash, unsigned long long *bk,
+                   unsigned long long *bv, hipStream_t st) {
+  const Dims &d = c->d;
+  const size_t e16 = (size_t)d.L * d.n_seq * d.nkv * c->ldp * d.hd;
+  q2::debug_kv(debug_args(c), c->kc, c->vc, c->kc16, c->vc16t, c->kv_elems, e16 / 2, hash, bk, bv,
+               st);
+}
+
+int debug_begin(qwen2_ctx *c, const std::vector<std::pair<int, int>> &slots, hipStream_t st) {
+  HIP_TRY(c, hipStreamSynchronize(st));  // (the previous check's kernels read the mask)
+  std::fill(c->dbg_host.begin(), c->dbg_host.end(), 0);
+  for (const auto &sp : slots) c->dbg_host[(size_t)sp.first * c->d.n_ctx + sp.second] = 1;
+  HIP_TRY(c, hipMemcpy(c->dbg_mask, c->dbg_host.data(), c->dbg_host.size(), hipMemcpyHostToDevice));
+  const unsigned long long init[8] = {0, 0, ~0ull, ~0ull, ~0ull, ~0ull, ~0ull, ~0ull};
+  HIP_TRY(c, hipMemcpy(c->dbg, init, sizeof(init), hipMemcpyHostToDevice));
+  debug_scan_kv(c, c->dbg + 0, c->dbg + 6, c->dbg + 7, st);
+  HIP_TRY(c, hipGetLastError());
+  return QWEN2_OK;
+}
+
+int debug_end(qwen2_ctx *c, const float *logits, int logit_rows, hipStream_t st) {
+  const Dims &d = c->d;
+  debug_scan_kv(c, c->dbg + 1, c->dbg + 2, c->dbg + 3, st);
+  if (logits) q2::debug_nonfinite(logits, (size_t)logit_rows * d.V, c->dbg + 4, st);
+  if (c->last_h) q2::debug_nonfinite(c->last_h, (size_t)c->last_rows * d.H, c->dbg + 5, st);
+  HIP_TRY(c, hipGetLastError());
+  HIP_TRY(c, hipStreamSynchronize(st));
+  unsigned long long r[8];
+  HIP_TRY(c, hipMemcpy(r, c->dbg, sizeof(r), hipMemcpyDeviceToHost));
+  auto value = [&](const float *base, unsigned long long i, float *v) -> int {
+    HIP_TRY(c, hipMemcpy(v, base + i, 4, hipMemcpyDeviceToHost));
+    return QWEN2_OK;
+  };
+  char buf[256];
+  if (r[0] != r[1])
+    return set_err(c, QWEN2_E_DEBUG, "debug check: the KV cache changed outside this call's slots");
+  for (int kv = 0; kv < 2; ++kv) {
+    const unsigned long long w = r[2 + kv];
+    if (w == ~0ull) continue;
+    float v = 0.f;
+    if (value(kv ? c->vc : c->kc, w, &v)) return QWEN2_E_HIP;
+    const unsigned long long slot = w / d.hd;
+    const int dim = (int)(w % d.hd), pos = (int)(slot % d.n_ctx);
+    const int g = (int)((slot / d.n_ctx) % d.nkv), sq = (int)((slot / ((size_t)d.n_ctx * d.nkv)) % d.n_seq);
+    const int l = (int)(slot / ((size_t)d.n_ctx * d.nkv * d.n_seq));
+    snprintf(buf, sizeof(buf), "debug check: non-finite %s at layer %d, sequence %d, KV head %d, "
+             "position %d, dim %d: %g", kv ? "V" : "K", l, sq, g, pos, dim, (double)v);
+    return set_err(c, QWEN2_E_DEBUG, buf);
+  }
+  if (r[4] != ~0ull) {
+    float v = 0.f;
+    if (value(logits, r[4], &v)) return QWEN2_E_HIP;
+    snprintf(buf, sizeof(buf), "debug check: non-finite logit at row %d, id %d: %g",
+             (int)(r[4] / d.V), (int)(r[4] % d.V), (double)v);
+    return set_err(c, QWEN2_E_DEBUG, buf);
+  }
+  if (r[5] != ~0ull) {
+    float v = 0.f;
+    if (value(c->last_h, r[5], &v)) return QWEN2_E_HIP;
+    snprintf(buf, sizeof(buf), "debug check: non-finite hidden state at read-out row %d, dim %d: %g",
+             (int)(r[5] / d.H), (int)(r[5] % d.H), (double)v);
+    return set_err(c, QWEN2_E_DEBUG, buf);
+  }
+  return QWEN2_OK;
+}
+
 }  // namespace
 
 extern "C" {
@@ -634,6 +729,11 @@ int qwen2_prefill(qwen2_ctx *c, int32_t seq, const int32_t *tokens, const int32_
   int rc = q2::check_prefill(&c->hp, seq, tokens, positions, n, &msg);
   if (rc) return set_err(c, rc, msg);
   hipStream_t st = (hipStream_t)stream;
+  if (c->debug) {
+    std::vector<std::pair<int, int>> ds;
+    for (int i = 0; i < n; ++i) ds.emplace_back(seq, positions[i]);
+    if ((rc = debug_begin(c, ds, st))) return rc;
+  }
   std::vector<int32_t> seqs(n, seq);
   const int32_t *fields[3] = {tokens, positions, seqs.data()};
   int *df[3];
@@ -646,7 +746,7 @@ int qwen2_prefill(qwen2_ctx *c, int32_t seq, const int32_t *tokens, const int32_
     if (off + M == n) tail_row(c, M - 1, df[1] + off, df[2] + off, positions[n - 1], seq, st);
   }
   HIP_TRY(c, hipGetLastError());
-  return QWEN2_OK;
+  return c->debug ? debug_end(c, logits_dev, 1, st) : QWEN2_OK;
 }
 
 int qwen2_prefill_batch(qwen2_ctx *c, int32_t nb, const int32_t *seq_ids, const int32_t *lens,
@@ -662,6 +762,12 @@ int qwen2_prefill_batch(qwen2_ctx *c, int32_t nb, const int32_t *seq_ids, const 
   std::vector<int> end(nb);  // one past each sequence's last row
   int total = 0;
   for (int b = 0; b < nb; ++b) end[b] = total += lens[b];
+  if (c->debug) {
+    std::vector<std::pair<int, int>> ds;
+    for (int b = 0, r = 0; b < nb; ++b)
+      for (; r < end[b]; ++r) ds.emplace_back(seq_ids[b], positions[r]);
+    if ((rc = debug_begin(c, ds, st))) return rc;
+  }
   // Passes of up to max_rows consecutive rows; a sequence may straddle two.
   // At the end of each pass the residual rows and queries of the sequences
   // whose last row it holds are set aside (normed, o32: row b for sequence
@@ -716,7 +822,7 @@ int qwen2_prefill_batch(qwen2_ctx *c, int32_t nb, const int32_t *seq_ids, const 
   c->last_h = c->h;
   c->last_rows = nb;
   HIP_TRY(c, hipGetLastError());
-  return QWEN2_OK;
+  return c->debug ? debug_end(c, logits_dev, nb, st) : QWEN2_OK;
 }
 
 int qwen2_decode(qwen2_ctx *c, int32_t B, const int32_t *seq_ids, const int32_t *tokens_dev,
@@ -727,6 +833,11 @@ int qwen2_decode(qwen2_ctx *c, int32_t B, const int32_t *seq_ids, const int32_t 
   if (rc) return set_err(c, rc, msg);
   if (!tokens_dev) return set_err(c, QWEN2_E_ARG, "null tokens_dev");
   hipStream_t st = (hipStream_t)stream;
+  if (c->debug) {
+    std::vector<std::pair<int, int>> ds;
+    for (int b = 0; b < B; ++b) ds.emplace_back(seq_ids[b], positions[b]);
+    if ((rc = debug_begin(c, ds, st))) return rc;
+  }
   const int32_t *fields[2] = {positions, seq_ids};
   int *df[2];
   const CallSlots slots{tokens_dev, logits_dev, argmax_dev};
@@ -739,7 +850,7 @@ int qwen2_decode(qwen2_ctx *c, int32_t B, const int32_t *seq_ids, const int32_t 
   if (!c->use_graphs || c->prof_mask) {
     decode_launches(c, B, n_chunks, df[0], df[1], seq1, st);
     HIP_TRY(c, hipGetLastError());
-    return QWEN2_OK;
+    return c->debug ? debug_end(c, logits_dev, B, st) : QWEN2_OK;
   }
   // What the captured launches depend on: the row count; the chunk count
   // (the chunked attention's grid, the one-row fused attention's key bound),
@@ -774,7 +885,7 @@ int qwen2_decode(qwen2_ctx *c, int32_t B, const int32_t *seq_ids, const int32_t 
     c->graphs.splice(c->graphs.begin(), c->graphs, it);
   }
   HIP_TRY(c, hipGraphLaunch(c->graphs.front().second, st));
-  return QWEN2_OK;
+  return c->debug ? debug_end(c, logits_dev, B, st) : QWEN2_OK;
 }
 
 int qwen2_next_token_probs(qwen2_ctx *c, const float *logits_dev, int32_t rows, float *probs_dev,

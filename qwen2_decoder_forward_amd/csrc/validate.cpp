@@ -159,6 +159,7 @@ const char *qwen2_strerror(int code) {
     case QWEN2_E_ORDER: return "positions of one prefill must strictly increase";
     case QWEN2_E_HIP: return "HIP runtime error";
     case QWEN2_E_OOM: return "out of memory";
+    case QWEN2_E_DEBUG: return "a debug check failed (non-finite output or a KV write outside the call's slots)";
     default: return "unknown error";
   }
 }
