@@ -69,11 +69,12 @@ struct QkvEpi {
 // Warming of a later launch's weights in the L2 of the XCD that will read
 // them.  Blocks of a launch are dealt to the 8 XCDs round-robin by linear
 // block id (block b runs on XCD b % 8), and each XCD has its own L2, so a
-// one-row GEMV whose block g reads row group g reads it on XCD g % 8.  A
-// launch that leaves CUs idle (the one-row QKV GEMV, the one-row attention)
-// takes extra producer blocks that read, on each XCD, the groups the later
-// GEMV will read there; that GEMV then finds them in its L2.  Performance
-// only: the producers write nothing, and a group they miss is read from HBM.
+// one-row GEMV whose block g reads row group g reads it on XCD g % 8.  The
+// one-row attention launch, whose head blocks leave HBM mostly idle (their
+// K / V come from L2), takes extra producer blocks that read, on each XCD,
+// the groups the same layer's down GEMV will read there; that GEMV then
+// finds them in its L2.  Performance only: the producers write nothing, and
+// a group they miss is read from HBM.
 struct L2Warm {
   const uint4 *base;   // the later GEMV's matrix: group g starts at base + g * group_u4
   long long total_u4;  // its size in 16-byte units
