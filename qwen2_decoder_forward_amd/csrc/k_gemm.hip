@@ -41,6 +41,11 @@ struct GemmP {
   float *ws;      // split-K: raw partial sums [splits][M][N] (RESID only)
   int k_steps;    // K slices per block (per split)
   int atomic_out; // split-K residual: partial sums added into h with float atomics
+  // RMSNorm fused into the skinny QKV GEMM: A = RMSNorm(hx rows) * gain,
+  // built from the f32 residual rows hx [M, ldhx] (then A is unused)
+  const float *hx, *gain;
+  int ldhx;
+  float eps;
 };
 
 template <int LBM>
@@ -907,9 +912,10 @@ static int launch_large_m(const GemmP &p, const Workspace &wsp, hipStream_t st) 
 // The four partial tiles are summed through LDS, wavefront t finishing
 // tile t.  A block may also take only a share of K (split-K, residual
 // GEMMs only: raw partial sums, folded in by the next RMSNorm).
-template <int EPI, int TM, int NWS = 4>
+template <int EPI, int TM, int NWS = 4, bool NORM = false>
 __global__ __launch_bounds__(64 * NWS) void k_gemm_skinny(GemmP p) {
   constexpr int U = TM >= 4 ? 4 : 8;  // MFMA steps of loads in flight per wavefront
+  static_assert(!NORM || (EPI == G_QKV && TM == 1 && NWS == 8), "fused RMSNorm: QKV, 32 rows");
   __shared__ f16x sRed[NWS][TM][64];
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int hi = lane >> 5, l32 = lane & 31;
@@ -934,7 +940,56 @@ __global__ __launch_bounds__(64 * NWS) void k_gemm_skinny(GemmP p) {
 #pragma unroll
     for (int r = 0; r < 16; ++r) acc[i][r] = 0.f;
 
-  for (int s = s0; s < s1; s += U) {
+  // Fused RMSNorm (K <= 1024: at most U steps per wavefront).  Every load of
+  // the wavefront goes out at once: its steps of the f32 residual row and of
+  // the weights, and the block stages the norm gains in LDS.  The row's sum
+  // of squares is then reduced over the two lane halves and the wavefronts,
+  // and the normed, gained values become the binary16 A fragments, as the
+  // separate RMSNorm kernel would have written them.
+  __shared__ float sSS[NORM ? NWS : 1][32];
+  __shared__ __attribute__((aligned(16))) float sG[NORM ? 1024 : 4];
+  if constexpr (NORM) {
+    const float *Hp = p.hx + (size_t)min(m0 + l32, M - 1) * p.ldhx + hi * 8;
+    f4 hv[U][2];
+    h8 bf[U];
+#pragma unroll
+    for (int u = 0; u < U; ++u) {
+      // (steps past s1 repeat its last, unused; a wavefront without steps
+      // reads step 0)
+      const int k = max(min(s0 + u, s1 - 1), 0) * 16;
+      hv[u][0] = *(const f4 *)(Hp + k);
+      hv[u][1] = *(const f4 *)(Hp + k + 4);
+      bf[u] = *(const h8 *)(Bp + k);
+    }
+    for (int k = tid * 4; k < K; k += 64 * NWS * 4) *(f4 *)(sG + k) = *(const f4 *)(p.gain + k);
+    float ss = 0.f;
+#pragma unroll
+    for (int u = 0; u < U; ++u)
+      if (s0 + u < s1)
+#pragma unroll
+        for (int c = 0; c < 2; ++c)
+          ss += hv[u][c].x * hv[u][c].x + hv[u][c].y * hv[u][c].y + hv[u][c].z * hv[u][c].z +
+                hv[u][c].w * hv[u][c].w;
+    ss += __shfl_xor(ss, 32, 64);
+    if (hi == 0) sSS[wave][l32] = ss;
+    __syncthreads();
+    float tot = 0.f;
+#pragma unroll
+    for (int w = 0; w < NWS; ++w) tot += sSS[w][l32];
+    const float inv = 1.0f / sqrtf(tot / (float)K + p.eps);
+#pragma unroll
+    for (int u = 0; u < U; ++u)
+      if (s0 + u < s1) {
+        const int k = (s0 + u) * 16 + hi * 8;
+        const f4 g0 = *(const f4 *)(sG + k), g1 = *(const f4 *)(sG + k + 4);
+        const f4 x0 = hv[u][0] * inv * g0, x1 = hv[u][1] * inv * g1;
+        const h8 af = {(_Float16)x0.x, (_Float16)x0.y, (_Float16)x0.z, (_Float16)x0.w,
+                       (_Float16)x1.x, (_Float16)x1.y, (_Float16)x1.z, (_Float16)x1.w};
+        acc[0] = __builtin_amdgcn_mfma_f32_32x32x16_f16(af, bf[u], acc[0], 0, 0, 0);
+      }
+  }
+
+  for (int s = s0; s < (NORM ? s0 : s1); s += U) {
     h8 af[U][TM], bf[U];
 #pragma unroll
     for (int u = 0; u < U; ++u) {
@@ -989,10 +1044,11 @@ __global__ __launch_bounds__(64 * NWS) void k_gemm_skinny(GemmP p) {
 // with blocks dealt evenly over 256 CUs, plus a charge per split (the extra
 // adds).
 template <int EPI>
-static int launch_skinny(GemmP p, const Workspace &wsp, hipStream_t st) {
+static void skinny_shape(const GemmP &p, const Workspace &wsp, int &best_tm, int &best_sp) {
   const int steps = p.K / 16;
   const int nt = (p.N + 31) / 32;
-  int best_tm = 1, best_sp = 1;
+  best_tm = 1;
+  best_sp = 1;
   double best_cost = 1e30;
   for (int tm = 4; tm >= 1; tm >>= 1) {
     const int mt = (p.M + 32 * tm - 1) / (32 * tm);
@@ -1010,6 +1066,14 @@ static int launch_skinny(GemmP p, const Workspace &wsp, hipStream_t st) {
       }
     }
   }
+}
+
+template <int EPI>
+static int launch_skinny(GemmP p, const Workspace &wsp, hipStream_t st) {
+  const int steps = p.K / 16;
+  const int nt = (p.N + 31) / 32;
+  int best_tm, best_sp;
+  skinny_shape<EPI>(p, wsp, best_tm, best_sp);
   p.k_steps = (steps + best_sp - 1) / best_sp;
   const int splits = (steps + p.k_steps - 1) / p.k_steps;
   p.ws = splits > 1 ? wsp.buf : nullptr;
@@ -1107,6 +1171,28 @@ void gemm_qkv(const Dims &d, const LayerW &w, const _Float16 *x, int lda, int M,
   p.d = d;
   p.qkv = e;
   launch<G_QKV>(p, ws, st);
+}
+
+bool qkv_fuses_norm(const Dims &d, int M, const Workspace &ws) {
+  GemmP p = base(nullptr, 0, M, nullptr, d.nqkv, d.H);
+  if (M >= kBigM || p.K > 1024 || p.N > 2048) return false;  // (not the skinny kernel)
+  int tm, sp;
+  skinny_shape<G_QKV>(p, ws, tm, sp);
+  return tm == 1;
+}
+
+void gemm_qkv_normed(const Dims &d, const LayerW &w, const float *h, int ldh, int M, float eps,
+                     const QkvEpi &e, hipStream_t st) {
+  GemmP p = base(nullptr, 0, M, w.wqkv, d.nqkv, d.H);
+  p.d = d;
+  p.qkv = e;
+  p.hx = h;
+  p.ldhx = ldh;
+  p.gain = w.attn_norm;
+  p.eps = eps;
+  p.k_steps = p.K / 16;
+  const dim3 grid((p.N + 31) / 32, (M + 31) / 32, 1);
+  hipLaunchKernelGGL((k_gemm_skinny<G_QKV, 1, 8, true>), grid, dim3(512), 0, st, p);
 }
 
 int gemm_resid(const uint16_t *W, int N, int K, const _Float16 *x, int lda, int M, float *h,

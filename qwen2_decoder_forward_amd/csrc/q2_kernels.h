@@ -171,6 +171,14 @@ struct Workspace {
 constexpr int kMaxSplits = 16;  // split-K partial-sum sets a residual GEMM may leave
 void gemm_qkv(const Dims &d, const LayerW &w, const _Float16 *x, int lda, int M,
               const QkvEpi &e, const Workspace &ws, hipStream_t st);
+// The same with the attention RMSNorm fused in: the rows of h [M, ldh] are
+// normed inside the GEMM (no x buffer).  Only where qkv_fuses_norm holds:
+// the projection runs on the skinny kernel with 32-row tiles (fewer than 512
+// rows, K <= 1024, N <= 2048).  The caller must have no split-K partial sums
+// pending in h.
+bool qkv_fuses_norm(const Dims &d, int M, const Workspace &ws);
+void gemm_qkv_normed(const Dims &d, const LayerW &w, const float *h, int ldh, int M, float eps,
+                     const QkvEpi &e, hipStream_t st);
 // Returns the number of split-K partial-sum sets left in ws.buf ([z][M][N]);
 // when nonzero the next rmsnorm_rows_f16 of h must fold them in.
 int gemm_resid(const uint16_t *W, int N, int K, const _Float16 *x, int lda, int M, float *h,

@@ -548,6 +548,8 @@ void prefill_pass(qwen2_ctx *c, int M, int off, const int *pos, const int *seq,
     const q2::QkvEpi e = qkv_epi(c, l, pos, seq);
     if (gemv) {
       TIMED(QWEN2_OP_QKV, q2::gemv_qkv(d, w, c->h, M, e, eps, c->normed, st));
+    } else if (pending == 0 && q2::qkv_fuses_norm(d, M, c->splitk)) {
+      TIMED(QWEN2_OP_QKV, q2::gemm_qkv_normed(d, w, c->h, d.H, M, eps, e, st));
     } else {
       TIMED(QWEN2_OP_NORM, q2::rmsnorm_rows_f16(c->h, d.H, w.attn_norm, d.H, M, eps, c->x16, d.H,
                                                 nullptr, c->splitk.buf, pending, st));
@@ -632,6 +634,8 @@ void decode_launches(qwen2_ctx *c, int B, int n_chunks, const int *dpos, const i
     const q2::QkvEpi e = qkv_epi(c, l, dpos, dseq);
     if (B <= kGemvRows) {
       TIMED(QWEN2_OP_QKV, q2::gemv_qkv(d, w, c->h, B, e, eps, c->normed, st));
+    } else if (pending == 0 && q2::qkv_fuses_norm(d, B, c->splitk)) {
+      TIMED(QWEN2_OP_QKV, q2::gemm_qkv_normed(d, w, c->h, d.H, B, eps, e, st));
     } else {
       TIMED(QWEN2_OP_NORM, q2::rmsnorm_rows_f16(c->h, d.H, w.attn_norm, d.H, B, eps, c->x16, d.H,
                                                 nullptr, c->splitk.buf, pending, st));
