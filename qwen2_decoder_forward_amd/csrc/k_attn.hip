@@ -1002,7 +1002,21 @@ __global__ __launch_bounds__(64 * G * S) void k_attn_prefill(AttnPreP p) {
   for (int t = 0; t < DT; ++t)
 #pragma unroll
     for (int r = 0; r < 16; ++r) o[t][r] = 0.f;
-  float m_run = kNegInf, l_run = 0.f;
+  // Softmax state of the lane's query row.  Scores are taken relative to a
+  // reference m_ref (a binary16 value, subtracted on the matrix core by one
+  // extra MFMA per 32-key half: a column of ones in K against -m_ref in Q).
+  // The reference is raised only when a score exceeds it by more than 10:
+  // then to the row's maximum, rescaling O and the sum.  Otherwise a tile
+  // takes no cross-lane maximum, rescale or cross-lane sum (the weights
+  // 2^(s - m_ref) stay below 2^10, well inside binary16; O and the sum are
+  // normalised once at the end, so any reference below the maximum gives
+  // the same softmax).  `valid` is false while the row has seen no visible
+  // key (m_ref 0).
+  float m_ref = 0.f, l_part = 0.f;
+  bool valid = false;
+  h8 qbias;  // Q-side operand of the reference column: k-slot 0 (lanes 0-31) = -m_ref
+#pragma unroll
+  for (int j = 0; j < 8; ++j) qbias[j] = (_Float16)0.f;
 
   const _Float16 *kg = p.k16 + sg.kv_off + (size_t)g * p.gstride;
   const _Float16 *vg = p.v16t + sg.kv_off + (size_t)g * p.gstride;
@@ -1057,6 +1071,14 @@ __global__ __launch_bounds__(64 * G * S) void k_attn_prefill(AttnPreP p) {
     }
   };
 
+  // the padding chunk of every K row (columns HD .. HD+7, never written by
+  // the tile loads): 1, 0, ..., 0
+  for (int i = tid; i < 2 * KT; i += nthr) {
+    h8 one;
+#pragma unroll
+    for (int j = 0; j < 8; ++j) one[j] = (_Float16)(j == 0 ? 1.f : 0.f);
+    *(h8 *)(&hK[i / KT][(i % KT) * KP + HD]) = one;
+  }
   if (cnt > 0) {
     gload(kt0);
     swrite(0);
@@ -1077,6 +1099,10 @@ __global__ __launch_bounds__(64 * G * S) void k_attn_prefill(AttnPreP p) {
       for (int hf = 0; hf < 2; ++hf) {
 #pragma unroll
         for (int r = 0; r < 16; ++r) s[hf][r] = 0.f;
+        // (K side: the row's padding chunk, 1 then zeros, read by both lane
+        // halves; the upper half's Q side is zero)
+        const h8 one = *(const h8 *)(sk + (hf * 32 + (lane & 31)) * KP + HD);
+        s[hf] = __builtin_amdgcn_mfma_f32_32x32x16_f16(one, qbias, s[hf], 0, 0, 0);  // - m_ref
 #pragma unroll
         for (int st = 0; st < KSTEPS; ++st) {
           const h8 a = *(const h8 *)(sk + (hf * 32 + (lane & 31)) * KP + st * 16 + hi * 8);
@@ -1093,40 +1119,54 @@ __global__ __launch_bounds__(64 * G * S) void k_attn_prefill(AttnPreP p) {
             if (key > qpos) s[hf][r] = kNegInf;
           }
       }
-      float mt = kNegInf;
+      // The reference moves when a score of the tile exceeds it by more
+      // than 10 (a weight above 2^10), or the row had no visible key yet:
+      // then to the row's maximum (rows whose maximum did not move keep it:
+      // shift 0, alpha 1), and the tile's scores are shifted to match.
+      float mx = kNegInf;
 #pragma unroll
       for (int hf = 0; hf < 2; ++hf)
 #pragma unroll
-        for (int r = 0; r < 16; ++r) mt = fmaxf(mt, s[hf][r]);
-      mt = max32(mt);
-      const float m_new = fmaxf(m_run, mt);
-      // (a query that has seen no visible key yet, e.g. in the second half's
-      // keys when its position lies before them, keeps m = -inf: subtract 0
-      // then, so its weights are exp2(-inf) = 0 instead of NaN)
-      const float m_sub = m_new == kNegInf ? 0.f : m_new;
-      // the hardware 2^x (v_exp_f32): every argument is <= 0, and results
-      // below 2^-126 (weights that cannot matter) flush to zero
-      const float alpha = __builtin_amdgcn_exp2f(m_run - m_sub);
-      float ls = 0.f;
+        for (int r = 0; r < 16; ++r) mx = fmaxf(mx, s[hf][r]);
+      if (__any(!valid || mx > 10.f)) {
+        const float mt = max32(mx);  // (relative to m_ref)
+        if (mt != kNegInf) {  // (a row with no visible key yet keeps its zero state)
+          const float m_abs = fminf(fmaxf(m_ref + (valid ? fmaxf(mt, 0.f) : mt), -60000.f), 60000.f);
+          const float m_new = (float)(_Float16)m_abs;
+          const float shift = m_new - m_ref;
+          const float alpha = valid ? __builtin_amdgcn_exp2f(-shift) : 0.f;
+          l_part *= alpha;
+#pragma unroll
+          for (int t = 0; t < DT; ++t)
+#pragma unroll
+            for (int r = 0; r < 16; ++r) o[t][r] *= alpha;
+#pragma unroll
+          for (int hf = 0; hf < 2; ++hf)
+#pragma unroll
+            for (int r = 0; r < 16; ++r) s[hf][r] -= shift;
+          m_ref = m_new;
+          valid = true;
+          qbias[0] = (_Float16)(hi == 0 ? -m_new : 0.f);
+        }
+      }
+      // binary16 weights 2^s (the hardware 2^x, v_exp_f32: every argument
+      // is <= 10, and results below 2^-126 flush to zero) and the lane's sum
+      // of the rounded weights, two at a time in f32 (v_dot2_f32_f16)
       h8 pb[2][2];
 #pragma unroll
       for (int hf = 0; hf < 2; ++hf)
 #pragma unroll
-        for (int r = 0; r < 16; ++r) {
-          const float e = __builtin_amdgcn_exp2f(s[hf][r] - m_sub);
-          ls += e;
-          pb[hf][r >> 3][r & 7] = (_Float16)e;
-        }
-      ls = sum32(ls);
-      l_run = l_run * alpha + ls;
-      m_run = m_new;
-      const bool rescale = __any(alpha != 1.0f);  // (skipped while no maximum moved)
+        for (int r = 0; r < 16; ++r) pb[hf][r >> 3][r & 7] = (_Float16)__builtin_amdgcn_exp2f(s[hf][r]);
+#pragma unroll
+      for (int hf = 0; hf < 2; ++hf)
+#pragma unroll
+        for (int j = 0; j < 2; ++j)
+#pragma unroll
+          for (int k = 0; k < 8; k += 2)
+            l_part = __builtin_amdgcn_fdot2((h2){pb[hf][j][k], pb[hf][j][k + 1]},
+                                            (h2){(_Float16)1.f, (_Float16)1.f}, l_part, false);
 #pragma unroll
       for (int t = 0; t < DT; ++t) {
-        if (rescale) {
-#pragma unroll
-          for (int r = 0; r < 16; ++r) o[t][r] *= alpha;
-        }
         const _Float16 *vr = sv + (t * 32 + (lane & 31)) * VP;
 #pragma unroll
         for (int hf = 0; hf < 2; ++hf) {
@@ -1145,6 +1185,8 @@ __global__ __launch_bounds__(64 * G * S) void k_attn_prefill(AttnPreP p) {
     __syncthreads();
   }
 
+  float m_run = valid ? m_ref : kNegInf;  // (no visible key: an empty state)
+  float l_run = sum32(l_part);
   if constexpr (S == 2) {  // the second half hands its state to the first through LDS
     float *xb = (float *)smem;  // ([hw][field][lane]; the tiles are no longer read)
     if (half == 1) {
