@@ -194,23 +194,30 @@ __device__ __forceinline__ void tile_epilogue(const GemmP &p, const f16x &v, int
     ok[r] = m[r] < M && n < N;
     m[r] = min(m[r], M - 1);
   }
+  // (residual and workspace addresses as 32-bit byte offsets from the
+  // block-uniform base: h holds at most 8192 rows of 8192 floats, the
+  // workspace 64 MB, so the base stays in scalar registers and a row costs
+  // one vector register instead of a 64-bit pointer)
+  char *const hb = (char *)p.h;
   if (EPI == G_RESID && p.ws && p.atomic_out) {
 #pragma unroll
     for (int r = 0; r < 16; ++r)
-      if (ok[r]) atomicAdd(p.h + (size_t)m[r] * p.ldh + n, v[r]);
+      if (ok[r]) atomicAdd((float *)(hb + ((unsigned)m[r] * (unsigned)p.ldh + (unsigned)n) * 4u), v[r]);
   } else if (EPI == G_RESID && p.ws) {
+    char *const wb = (char *)p.ws;
 #pragma unroll
     for (int r = 0; r < 16; ++r)
-      if (ok[r]) p.ws[((size_t)blockIdx.z * M + m[r]) * N + n] = v[r];
+      if (ok[r])
+        *(float *)(wb + (((unsigned)blockIdx.z * (unsigned)M + (unsigned)m[r]) * (unsigned)N + (unsigned)n) * 4u) = v[r];
   } else if (EPI == G_RESID) {
     const int nc = min(n, N - 1);
     float old[16];
 #pragma unroll
-    for (int r = 0; r < 16; ++r) old[r] = p.h[(size_t)m[r] * p.ldh + nc];
+    for (int r = 0; r < 16; ++r) old[r] = *(const float *)(hb + ((unsigned)m[r] * (unsigned)p.ldh + (unsigned)nc) * 4u);
     pin_regs(old);
 #pragma unroll
     for (int r = 0; r < 16; ++r)
-      if (ok[r]) p.h[(size_t)m[r] * p.ldh + n] = old[r] + v[r];
+      if (ok[r]) *(float *)(hb + ((unsigned)m[r] * (unsigned)p.ldh + (unsigned)n) * 4u) = old[r] + v[r];
   } else {
     float a[16], b[16];
 #pragma unroll
