@@ -6,10 +6,12 @@
 // the KV slots 0..p of its own sequence (full causal attention, no window).
 //
 // Which kernels share a KV head's K / V across its query group:
-//  * k_attn_decode (chunked decode attention) and k_attn_prefill (MFMA
-//    prefill attention) load each K / V tile once per KV head and use it for
-//    every query head of the group (k_attn_prefill's short-prompt form runs
-//    one head per block instead, so the group's heads spread over CUs);
+//  * k_attn_decode_mfma (chunked decode attention: the group's heads are
+//    the columns of its score tile) and k_attn_prefill (MFMA prefill
+//    attention: one wavefront per head over K / V tiles staged once in LDS)
+//    load each K / V tile once per KV head and use it for every query head
+//    of the group (k_attn_prefill's short-prompt form runs one head per
+//    block instead, so the group's heads spread over CUs);
 //  * k_attn_wo1 and k_attn_wo (attention fused with WO, short contexts) do
 //    not: a block serves one (WO row chunk, query head) pair and reads that
 //    head's K / V itself.  Their cost is the per-block K / V fetch and the
@@ -21,15 +23,11 @@
 namespace q2 {
 
 // ------------------------------------------------------------------ decode
-// One block per (64-key chunk, KV head, query row), 256 threads.  The chunk's
-// K and V rows are staged in LDS with coalesced loads and shared by the
-// `group` query heads of the KV head.  Scores: thread t takes key t % 64 for
-// heads t / 64 and t / 64 + 4, so each head's 64 scores sit in one wavefront
-// and its max and exp-sum are wave reductions.  P.V: thread (head, d) sums
-// over 4 dims of the chunk's keys.  A single-chunk call writes the
-// normalised output; otherwise every block writes its chunk's (un-normalised
-// output, max, exp-sum) record and k_attn_merge combines the records.  No
-// block waits on another.
+// Chunked decode attention (k_attn_decode_mfma): one wavefront per (64-key
+// chunk, KV head, query row).  A single-chunk call writes the normalised
+// output; otherwise every wavefront writes its chunk's (un-normalised
+// output, maximum, exp-sum) record and k_attn_merge (or k_merge_wo, which
+// also multiplies by WO) combines the records.  No block waits on another.
 struct AttnDecP {
   Dims d;
   int layer;
@@ -44,110 +42,172 @@ struct AttnDecP {
   float scale;
 };
 
+// One wavefront per (64-key chunk, KV head, query row) on the matrix core,
+// reading the binary16 mirror of the cache (K as [pos][d], V transposed as
+// [d][pos]) straight into MFMA operands, every load issued before the
+// first is used.  The group's query
+// heads are the 32 columns of the score tile (columns >= G are zero and
+// unused): S[key][head] = K Q^T over 16-wide d steps, then per head (a
+// lane's 16 keys of each 32-key half, and its partner lane l ^ 32 holding
+// the other 16) the maximum and the base-2 weights, and O^T[d][head] =
+// V^T P with the weights' binary16 key order matched by the V^T reads.
+// Keys past the row's position are masked (score -inf, V zeroed).  The
+// record's maximum is in natural-log units (the merges weight records by
+// e^(m_c - M)).
 template <int HD, int G, bool DIRECT>
-__global__ __launch_bounds__(256) void k_attn_decode(AttnDecP p) {
-  constexpr int C = kChunkKeys;
-  static_assert(C == 64, "one wavefront per head's chunk scores");
-  // padded K row: rows start 4 banks apart, so the 16-byte row walks of 16
-  // consecutive lanes (keys) touch distinct bank groups
-  constexpr int KS = HD + 4;
-  __shared__ __attribute__((aligned(16))) float sK[C * KS];
-  __shared__ __attribute__((aligned(16))) float sV[C * HD];
-  __shared__ __attribute__((aligned(16))) float sQ[G * HD];
-  __shared__ float sP[G * C];
-  __shared__ float sM[G], sL[G];
-
-  const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
+__global__ __launch_bounds__(64) void k_attn_decode_mfma(AttnDecP p) {
+  static_assert(kChunkKeys == 64 && G <= 32, "64-key chunks, at most 32 heads per group");
+  constexpr int KSTEPS = HD / 16;               // 16-wide d steps of Q K^T
+  constexpr int DT = HD >= 32 ? HD / 32 : 1;    // 32-row d tiles of O^T
+  constexpr bool LATE_V = HD > 64;              // (wide heads: V after the scores, fewer registers)
+  const int lane = threadIdx.x, hi = lane >> 5, l32 = lane & 31;
   const int c = blockIdx.x, g = blockIdx.y, m = blockIdx.z;
   const int pos = p.rows.pos[m];
   const int seq = p.rows.seq[m];
-  const int kb = c * C;
-  const int nk = min(C, pos + 1 - kb);
-  if (nk <= 0) return;  // uniform across the block
-  const float *kbase = p.kv.k + p.kv.off(p.d, p.layer, seq, g, kb);
-  const float *vbase = p.kv.v + p.kv.off(p.d, p.layer, seq, g, kb);
-  const float *qrow = p.q + (size_t)m * p.ldq + (size_t)g * G * HD;
+  const int kb = c * kChunkKeys;
+  const int nk = min(kChunkKeys, pos + 1 - kb);
+  if (nk <= 0) return;  // uniform across the wavefront
+  const size_t b16 = p.kv.off16(p.d, p.layer, seq, g);
+  const _Float16 *kg = p.kv.k16 + b16 + (size_t)kb * HD;  // (chunk slots stay inside ldp)
+  const _Float16 *vg = p.kv.v16t + b16 + kb;
+  const int hq = min(l32, G - 1);
+  const float *qp = p.q + (size_t)m * p.ldq + (size_t)(g * G + hq) * HD;
+  const int vrow = min(l32, HD - 1);  // (d rows HD..31 of a 16-wide head: zeroed below)
 
-  // the q loads, then every K / V load of the thread, in flight at once
-  // (elements past the chunk's nk keys re-read its last key, never used)
-  constexpr int QPT = (G * HD + 255) / 256;
-  float qr[QPT];
+  f4 qv[KSTEPS][2];
 #pragma unroll
-  for (int u = 0; u < QPT; ++u) qr[u] = qrow[min(tid + 256 * u, G * HD - 1)];
-  constexpr int LPT = (C * HD + 1023) / 1024;  // 16-byte loads per thread and tensor
-  f4 kr[LPT], vr[LPT];
-#pragma unroll
-  for (int u = 0; u < LPT; ++u) {
-    const int i = min(tid * 4 + 1024 * u, nk * HD - 4);
-    kr[u] = *(const f4 *)(kbase + i);
-    vr[u] = *(const f4 *)(vbase + i);
+  for (int st = 0; st < KSTEPS; ++st) {
+    qv[st][0] = *(const f4 *)(qp + st * 16 + hi * 8);
+    qv[st][1] = *(const f4 *)(qp + st * 16 + hi * 8 + 4);
   }
-  __builtin_amdgcn_sched_barrier(0);  // (all loads issued before the first LDS write)
+  h8 kf[2][KSTEPS];
 #pragma unroll
-  for (int u = 0; u < LPT; ++u) {
-    const int i = tid * 4 + 1024 * u;
-    if (i < C * HD) {
-      const int r = i / HD, cc = i - r * HD;
-      *(f4 *)(sK + r * KS + cc) = kr[u];
-      *(f4 *)(sV + i) = vr[u];
+  for (int hf = 0; hf < 2; ++hf)
+#pragma unroll
+    for (int st = 0; st < KSTEPS; ++st)
+      kf[hf][st] = *(const h8 *)(kg + (size_t)(hf * 32 + l32) * HD + st * 16 + hi * 8);
+  h4 vf[DT][2][4];
+  auto vload = [&]() {
+#pragma unroll
+    for (int t = 0; t < DT; ++t)
+#pragma unroll
+      for (int hf = 0; hf < 2; ++hf)
+#pragma unroll
+        for (int j = 0; j < 4; ++j)
+          vf[t][hf][j] = *(const h4 *)(vg + (size_t)(t * 32 + vrow) * p.kv.ldp + hf * 32 + 8 * j + 4 * hi);
+  };
+  if (!LATE_V) vload();
+  __builtin_amdgcn_sched_barrier(0);  // (every load in flight before the first is used)
+
+  // Q operand: column l32 = head g*G + l32, scaled by head_dim^-0.5 log2(e)
+  const float qs = l32 < G ? p.scale * 1.4426950408889634f : 0.f;
+  h8 qf[KSTEPS];
+#pragma unroll
+  for (int st = 0; st < KSTEPS; ++st)
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+      qf[st][j] = (_Float16)(qv[st][0][j] * qs);
+      qf[st][4 + j] = (_Float16)(qv[st][1][j] * qs);
+    }
+  f16x s[2];
+#pragma unroll
+  for (int hf = 0; hf < 2; ++hf) {
+#pragma unroll
+    for (int r = 0; r < 16; ++r) s[hf][r] = 0.f;
+#pragma unroll
+    for (int st = 0; st < KSTEPS; ++st)
+      s[hf] = __builtin_amdgcn_mfma_f32_32x32x16_f16(kf[hf][st], qf[st], s[hf], 0, 0, 0);
+  }
+  if (LATE_V) vload();
+  if (nk < kChunkKeys) {  // (the row's last chunk; uniform)
+#pragma unroll
+    for (int hf = 0; hf < 2; ++hf)
+#pragma unroll
+      for (int r = 0; r < 16; ++r)
+        if (hf * 32 + 8 * (r >> 2) + 4 * hi + (r & 3) >= nk) s[hf][r] = kNegInf;
+#pragma unroll
+    for (int t = 0; t < DT; ++t)
+#pragma unroll
+      for (int hf = 0; hf < 2; ++hf)
+#pragma unroll
+        for (int j = 0; j < 4; ++j)
+#pragma unroll
+          for (int e = 0; e < 4; ++e)
+            if (hf * 32 + 8 * j + 4 * hi + e >= nk) vf[t][hf][j][e] = (_Float16)0.f;
+  }
+  if (HD < 32 && l32 >= HD) {
+#pragma unroll
+    for (int hf = 0; hf < 2; ++hf)
+#pragma unroll
+      for (int j = 0; j < 4; ++j) vf[0][hf][j] = (h4){0, 0, 0, 0};
+  }
+  float mx = kNegInf;
+#pragma unroll
+  for (int hf = 0; hf < 2; ++hf)
+#pragma unroll
+    for (int r = 0; r < 16; ++r) mx = fmaxf(mx, s[hf][r]);
+  mx = max32(mx);  // (key 0 of the chunk is always visible: finite)
+  h8 pb[2][2];
+  float l = 0.f;
+#pragma unroll
+  for (int hf = 0; hf < 2; ++hf)
+#pragma unroll
+    for (int r = 0; r < 16; ++r) pb[hf][r >> 3][r & 7] = (_Float16)__builtin_amdgcn_exp2f(s[hf][r] - mx);
+#pragma unroll
+  for (int hf = 0; hf < 2; ++hf)
+#pragma unroll
+    for (int j = 0; j < 2; ++j)
+#pragma unroll
+      for (int k = 0; k < 8; k += 2)
+        l = __builtin_amdgcn_fdot2((h2){pb[hf][j][k], pb[hf][j][k + 1]}, (h2){(_Float16)1.f, (_Float16)1.f}, l,
+                                   false);
+  l = sum32(l);
+  f16x o[DT];
+#pragma unroll
+  for (int t = 0; t < DT; ++t) {
+#pragma unroll
+    for (int r = 0; r < 16; ++r) o[t][r] = 0.f;
+#pragma unroll
+    for (int hf = 0; hf < 2; ++hf) {
+      const h8 a0 = (h8){vf[t][hf][0][0], vf[t][hf][0][1], vf[t][hf][0][2], vf[t][hf][0][3],
+                         vf[t][hf][1][0], vf[t][hf][1][1], vf[t][hf][1][2], vf[t][hf][1][3]};
+      const h8 a1 = (h8){vf[t][hf][2][0], vf[t][hf][2][1], vf[t][hf][2][2], vf[t][hf][2][3],
+                         vf[t][hf][3][0], vf[t][hf][3][1], vf[t][hf][3][2], vf[t][hf][3][3]};
+      o[t] = __builtin_amdgcn_mfma_f32_32x32x16_f16(a0, pb[hf][0], o[t], 0, 0, 0);
+      o[t] = __builtin_amdgcn_mfma_f32_32x32x16_f16(a1, pb[hf][1], o[t], 0, 0, 0);
     }
   }
+  if (l32 >= G) return;
+  // lane: head l32, dims t*32 + 8 rq + 4 hi + 0..3
+  if (DIRECT) {
+    const float inv = 1.0f / l;
+    const size_t ob = (size_t)m * p.ldo + (size_t)(g * G + l32) * HD;
 #pragma unroll
-  for (int u = 0; u < QPT; ++u)
-    if (tid + 256 * u < G * HD) sQ[tid + 256 * u] = qr[u] * p.scale;
-  __syncthreads();
-
-  const int j = lane;
+    for (int t = 0; t < DT; ++t)
 #pragma unroll
-  for (int hi = 0; hi < (G + 3) / 4; ++hi) {
-    const int h = w + 4 * hi;
-    if (h < G) {  // uniform across the wave
-      float a = 0.f;
-      if (j < nk) {
-#pragma unroll
-        for (int d4 = 0; d4 < HD; d4 += 4) {
-          const f4 qq = *(const f4 *)(sQ + h * HD + d4);
-          const f4 kk = *(const f4 *)(sK + j * KS + d4);
-          a = fmaf(qq.x, kk.x, a);
-          a = fmaf(qq.y, kk.y, a);
-          a = fmaf(qq.z, kk.z, a);
-          a = fmaf(qq.w, kk.w, a);
+      for (int rq = 0; rq < 4; ++rq) {
+        const int d0 = t * 32 + 8 * rq + 4 * hi;
+        if (d0 < HD) {
+          const f4 v = {o[t][4 * rq] * inv, o[t][4 * rq + 1] * inv, o[t][4 * rq + 2] * inv, o[t][4 * rq + 3] * inv};
+          if (p.o32) *(f4 *)(p.o32 + ob + d0) = v;
+          if (p.o16) *(h4 *)(p.o16 + ob + d0) = (h4){(_Float16)v.x, (_Float16)v.y, (_Float16)v.z, (_Float16)v.w};
         }
       }
-      const float s = j < nk ? a : kNegInf;
-      const float mx = wave_max(s);
-      const float e = j < nk ? __expf(s - mx) : 0.f;
-      const float sum = wave_sum(e);
-      sP[h * C + j] = e;
-      if (lane == 0) {
-        sM[h] = mx;
-        sL[h] = sum;
+  } else {
+    constexpr int rec = attn_rec_floats(G, HD);
+    float *part = p.part.buf + (((size_t)m * p.d.nkv + g) * p.part.n_chunks + c) * rec;
+#pragma unroll
+    for (int t = 0; t < DT; ++t)
+#pragma unroll
+      for (int rq = 0; rq < 4; ++rq) {
+        const int d0 = t * 32 + 8 * rq + 4 * hi;
+        if (d0 < HD)
+          *(f4 *)(part + l32 * HD + d0) = (f4){o[t][4 * rq], o[t][4 * rq + 1], o[t][4 * rq + 2], o[t][4 * rq + 3]};
       }
+    if (hi == 0) {
+      part[G * HD + l32] = mx * 0.6931471805599453f;  // (natural-log units, as the merges expect)
+      part[G * HD + G + l32] = l;
     }
-  }
-  __syncthreads();
-
-  constexpr int rec = attn_rec_floats(G, HD);
-  float *part = p.part.buf + (((size_t)m * p.d.nkv + g) * p.part.n_chunks + c) * rec;
-  // P.V: thread (head, 4 dims), 16-byte V reads
-  for (int idx = tid; idx < G * HD / 4; idx += 256) {
-    const int h = idx / (HD / 4), d4 = 4 * (idx - h * (HD / 4));
-    f4 acc = {0.f, 0.f, 0.f, 0.f};
-#pragma unroll 8
-    for (int jj = 0; jj < nk; ++jj) acc += sP[h * C + jj] * *(const f4 *)(sV + jj * HD + d4);
-    const int o = h * HD + d4;
-    if (DIRECT) {
-      const f4 v = acc / sL[h];
-      const size_t oi = (size_t)m * p.ldo + (size_t)g * G * HD + o;
-      if (p.o32) *(f4 *)(p.o32 + oi) = v;
-      if (p.o16) *(h4 *)(p.o16 + oi) = (h4){(_Float16)v.x, (_Float16)v.y, (_Float16)v.z, (_Float16)v.w};
-    } else {
-      *(f4 *)(part + o) = acc;
-    }
-  }
-  if (!DIRECT && tid < G) {
-    part[G * HD + tid] = sM[tid];
-    part[G * HD + G + tid] = sL[tid];
   }
 }
 
@@ -645,7 +705,7 @@ void attn_wo_fused(const Dims &d, int layer, const KVCache &kv, const float *q, 
 }
 
 // ------------------------------------- chunk-record merge fused with WO
-// Longer contexts on the decode path: after k_attn_decode has left its
+// Longer contexts on the decode path: after k_attn_decode_mfma has left its
 // chunk records, one block per (WO row chunk, query head) merges the head's
 // records into its attention output (as k_attn_merge does) and multiplies it
 // by its slice of WO, adding the partial row sums into the residual with
@@ -792,9 +852,9 @@ void merge_wo(const Dims &d, const AttnPartials &part, RowInfo rows, int M, cons
 template <int HD, int G>
 static void attn_decode_g(const AttnDecP &p, int M, int n_chunks, bool merge, hipStream_t st) {
   if (n_chunks <= 1) {
-    hipLaunchKernelGGL((k_attn_decode<HD, G, true>), dim3(1, p.d.nkv, M), dim3(256), 0, st, p);
+    hipLaunchKernelGGL((k_attn_decode_mfma<HD, G, true>), dim3(1, p.d.nkv, M), dim3(64), 0, st, p);
   } else {
-    hipLaunchKernelGGL((k_attn_decode<HD, G, false>), dim3(n_chunks, p.d.nkv, M), dim3(256), 0,
+    hipLaunchKernelGGL((k_attn_decode_mfma<HD, G, false>), dim3(n_chunks, p.d.nkv, M), dim3(64), 0,
                        st, p);
     if (merge) hipLaunchKernelGGL((k_attn_merge<HD>), dim3(p.d.nh, M), dim3(256), 0, st, p);
   }
