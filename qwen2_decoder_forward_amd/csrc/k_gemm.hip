@@ -1137,9 +1137,12 @@ static int launch_tiles(GemmP p, const Workspace &wsp, hipStream_t st) {
     if (p.M <= 128) return launch_ring<EPI, 128, 64, 4, 2, 1, 8>(p, 1, wsp, st);
   }
   const int nk = p.K / kBK2;
+  // (up to 64 rows: 64 x 64 tiles, so a block reads no clamped rows and
+  // half the activation slice of a 128 x 32 tile per output column)
+  const bool m64 = p.M <= 64;
   int splits = 1;
   if (EPI == G_RESID && p.K >= 2048 && wsp.buf) {
-    const int blocks = ((p.N + 31) / 32) * ((p.M + 127) / 128);
+    const int blocks = m64 ? (p.N + 63) / 64 : ((p.N + 31) / 32) * ((p.M + 127) / 128);
     splits = max(1, 256 / blocks);
     splits = min(splits, min(kMaxSplits, nk));
     const size_t per = (size_t)p.M * p.N * 4;
@@ -1148,7 +1151,10 @@ static int launch_tiles(GemmP p, const Workspace &wsp, hipStream_t st) {
   }
   p.ws = splits > 1 ? wsp.buf : nullptr;
   p.atomic_out = 1;  // (few rows: the split sums go straight into h)
-  launch_big<EPI, 128, 32, 4>(p, splits, st);
+  if (m64)
+    launch_big<EPI, 64, 64, 2>(p, splits, st);
+  else
+    launch_big<EPI, 128, 32, 4>(p, splits, st);
   return 0;
 }
 
