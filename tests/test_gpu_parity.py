@@ -448,6 +448,47 @@ def test_graph_replay_matches_direct_launches(tiny_w, monkeypatch):
     check(lg_graph, lg_direct, 1e-6, "graph vs direct logits")
 
 
+def test_attention_reference_moves_mid_row(tiny_w):
+    """Keys planted in the cache (qwen2_kv_write on the GPU, directly on the
+    oracle side) at positions 0..127, those of the second 64-key tile 20
+    times larger than the first's: their scores exceed the first tile's
+    maximum by far more than the 2^10 (base-2) margin within which the
+    prefill attention keeps its per-row reference maximum, so the reference
+    moves in the middle of each row and the output accumulated so far is
+    rescaled.  A 40-row continuation prefill at positions 128..167 (MFMA
+    attention), then one 12-row decode step over 12 sequences with the same
+    planted keys (chunked decode attention, its chunk records merged), each
+    against the oracle."""
+    n_seq = 12
+    p = Pair(TINY, tiny_w, n_ctx=256, n_seq=n_seq)
+    nkv, hd, L = TINY.n_head_kv, TINY.head_dim, TINY.n_layer
+    rng = np.random.default_rng(11)
+    k = rng.standard_normal((nkv, 128, hd)).astype(np.float32)
+    k[:, 64:] *= 20.0
+    v = rng.standard_normal((nkv, 128, hd)).astype(np.float32)
+    kd, vd = torch.from_numpy(k).to(DEV), torch.from_numpy(v).to(DEV)
+    for s_ in range(n_seq):
+        Kc, Vc = p.o._cache(s_)
+        for l in range(L):
+            p.m.kv_write(l, s_, 0, 128, kd, vd)
+            Kc[l][:, :128] = k
+            Vc[l][:, :128] = v
+    torch.cuda.synchronize()
+    lg, gid, r = p.prefill(0, syn.make_prompt(TINY, 40, 12), np.arange(128, 168))
+    check(lg, r.logits[0], TOL, "40-row prefill over planted keys")
+    check(p.hidden(0, 1), r.layer_output, TOL, "40-row prefill layer_output")
+    check_id(gid, r.logits[0], r.argmax[0], "40-row prefill over planted keys")
+    for s_ in range(1, n_seq):
+        p.prefill(s_, syn.make_prompt(TINY, 3, 60 + s_), np.arange(128, 131))
+    seqs = list(range(n_seq))
+    toks = [int(t) for t in syn.make_prompt(TINY, n_seq, 13)]
+    lg, ids, r = p.decode(seqs, toks, [168] + [131] * (n_seq - 1))
+    for b in range(n_seq):
+        check(lg[b], r.logits[b], TOL, f"12-row decode over planted keys, row {b}")
+        check_id(ids[b], r.logits[b], r.argmax[b], f"12-row decode over planted keys, row {b}")
+    p.close()
+
+
 def test_one_row_decode_across_slots_and_graph_eviction(tiny_w):
     """One-row decode steps address their slot's K/V from the host, and each
     (slot, chunk count) gets its own captured step: 40 slots decoded one row
