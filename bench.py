@@ -66,13 +66,27 @@ def streamed_f16(shape, wb: dict, rows: int) -> int:
     return wb["f16"] - table + rows * shape.n_embd * 2
 
 
+# Decode positions from which one row's attention runs chunked, reading the
+# binary16 mirror of the cache (below it: the fused kernel reads the f32 cache)
+FUSED_KEYS = 512
+
+
+def kv_read_bytes(shape, positions: int, rows: int, chunked: bool) -> int:
+    """K/V bytes an attention reads for `rows` rows over `positions` slots
+    each: binary16 mirror on the chunked path, f32 cache on the fused one."""
+    el = 2 if chunked else 4
+    return rows * positions * shape.n_layer * 2 * shape.n_head_kv * shape.head_dim * el
+
+
 def decode_bytes(shape, pos: int, wb: dict) -> int:
-    """Algorithmic bytes of one batch-1 decode token at position `pos`: every
-    streamed weight once (f16 matrices incl. the lm_head, the token's
-    embedding row, f32 biases and norms) plus the K/V of positions 0..pos
-    read and one position written (f32)."""
-    kv_pos = shape.n_layer * 2 * shape.n_head_kv * shape.head_dim * 4
-    return streamed_f16(shape, wb, 1) + wb["f32"] + kv_pos * (pos + 1) + kv_pos
+    """Bytes of one batch-1 decode token at position `pos`: every streamed
+    weight once (f16 matrices incl. the lm_head, the token's embedding row,
+    f32 biases and norms), the K/V of positions 0..pos as the attention reads
+    them (f32 cache below FUSED_KEYS positions, binary16 mirror from there),
+    and one position written (f32 cache and binary16 mirror)."""
+    kv_w = shape.n_layer * 2 * shape.n_head_kv * shape.head_dim * (4 + 2)
+    chunked = pos + 1 > FUSED_KEYS
+    return streamed_f16(shape, wb, 1) + wb["f32"] + kv_read_bytes(shape, pos + 1, 1, chunked) + kv_w
 
 
 def gateup_bytes(shape) -> int:
@@ -402,10 +416,11 @@ def main():
     if model.sync_status() != 0:
         raise RuntimeError("device-side error flag set during the benchmark")
 
-    kv_pos = shape.n_layer * 2 * shape.n_head_kv * shape.head_dim * 4
-    if batched:
+    if batched:  # (more than 8 rows: the chunked attention over the binary16 mirror)
         dec_tokens = n_seq
-        dec_bytes = streamed_f16(shape, wb, n_seq) + wb["f32"] + n_seq * kv_pos * (n + 2)
+        kv_w = shape.n_layer * 2 * shape.n_head_kv * shape.head_dim * (4 + 2)
+        dec_bytes = (streamed_f16(shape, wb, n_seq) + wb["f32"] +
+                     kv_read_bytes(shape, n + 1, n_seq, True) + n_seq * kv_w)
     else:
         dec_tokens = steps_dec
         dec_bytes = sum(decode_bytes(shape, n + s, wb) for s in range(steps_dec))
@@ -453,7 +468,9 @@ def main():
 
     fl = prefill_gemm_flops(shape, n)
     prefill_flops = sum(fl.values()) + attn_prefill_flops(shape, n)
-    prefill_bytes = streamed_f16(shape, wb, n) + wb["f32"] + n * kv_pos
+    # (weights once, the prompt's K/V written: f32 cache and binary16 mirror)
+    prefill_bytes = (streamed_f16(shape, wb, n) + wb["f32"] +
+                     n * shape.n_layer * 2 * shape.n_head_kv * shape.head_dim * (4 + 2))
 
     desc = (f"{wl.description}; model {shape.name}: {shape.n_layer} layers, hidden "
             f"{shape.n_embd}, {shape.n_head}/{shape.n_head_kv} heads, hd {shape.head_dim}, "
@@ -470,8 +487,11 @@ def main():
         "scaling": "weak",
         "vs_baseline": None,
         "dtype": ("f16 weights; decode (rows <= 8): f32 activations, accumulation and KV "
-                  "cache; prefill (rows > 8): f16 activation, K/V-mirror and softmax-weight "
-                  "MFMA operands with f32 accumulation, f32 residual stream and KV cache"),
+                  "cache, except that attention from position 512 on reads the binary16 K/V "
+                  "mirror (binary16 query and softmax-weight MFMA operands, f32 accumulation); "
+                  "prefill and batched decode (rows > 8): f16 activation, K/V-mirror and "
+                  "softmax-weight MFMA operands with f32 accumulation, f32 residual stream and "
+                  "KV cache"),
         "data": "synthetic",
         "config": {"workload": desc, "prompt": n, "decode_steps": steps_dec, "n_ctx": n_ctx,
                    "batch": n_seq},
