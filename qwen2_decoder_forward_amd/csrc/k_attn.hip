@@ -983,8 +983,17 @@ struct AttnPreP {
 // own LDS buffers, and their online-softmax states (max, sum, output) are
 // merged through LDS at the end.  This doubles the wavefronts a CU runs
 // (the grid has about one block per CU) and halves the longest block.
+// Groups of 7 add one loader wavefront per half (16 wavefronts at two
+// halves, 8 at one): it alone moves the half's K / V^T tiles from global
+// memory into LDS, in a loop of its own with the same barriers, so the
+// compute wavefronts skip that phase and every SIMD holds the same number
+// of wavefronts.
+template <int G, int S>
+constexpr int prefill_loaders() { return G == 7 ? S : 0; }
+
 template <int HD, int G, int S>
-__global__ __launch_bounds__(64 * G * S) void k_attn_prefill(AttnPreP p) {
+__global__ __launch_bounds__(64 * (G * S + prefill_loaders<G, S>())) void k_attn_prefill(AttnPreP p) {
+  constexpr int NL = prefill_loaders<G, S>();  // loader wavefronts (one per half, or none)
   constexpr int KSTEPS = (HD + 15) / 16;
   constexpr int DT = HD >= 32 ? HD / 32 : 1;  // 32-row d tiles of O^T
   constexpr int DV = DT * 32;
@@ -1006,7 +1015,8 @@ __global__ __launch_bounds__(64 * G * S) void k_attn_prefill(AttnPreP p) {
   VTile *sV = (VTile *)(smem + (size_t)S * 2 * KT * KP * sizeof(_Float16));  // [S]
 
   const int lane = threadIdx.x & 63, w = threadIdx.x >> 6;
-  const int half = w / G, hw = w - half * G;
+  const bool loader = NL > 0 && w >= G * S;  // (wave-uniform)
+  const int half = loader ? w - G * S : w / G, hw = loader ? 0 : w - (w / G) * G;
   const int tid = threadIdx.x - half * NTHR, nthr = NTHR;  // index within the half
   // longest work first: the split tiles' two pieces (descending tiles),
   // then the whole tiles (descending)
@@ -1041,10 +1051,80 @@ __global__ __launch_bounds__(64 * G * S) void k_attn_prefill(AttnPreP p) {
   _Float16(&hK)[2][KT * KP] = sK[half];
   _Float16(&hV)[2][DV * VP] = sV[half];
 
-  if (HD < 32) {  // d rows HD .. 31 of V^T (never loaded) stay zero
+  if (HD < 32 && NL == 0) {  // d rows HD .. 31 of V^T (never loaded) stay zero
     for (int i = tid; i < 2 * (DV - HD) * VP; i += nthr) {
       const int b = i / ((DV - HD) * VP), j = i - b * (DV - HD) * VP;
       hV[b][HD * VP + j] = (_Float16)0.f;
+    }
+  }
+
+  if constexpr (NL > 0) {
+    if (loader) {
+      const _Float16 *kgl = p.k16 + sg.kv_off + (size_t)g * p.gstride;
+      const _Float16 *vgl = p.v16t + sg.kv_off + (size_t)g * p.gstride;
+      const int ntl = kmax / KT + 1;
+      int kbl = 0, kel = ntl;
+      if (piece >= 0) {
+        const int ph = (ntl + 1) / 2;
+        kbl = piece ? ph : 0;
+        kel = piece ? ntl : ph;
+      }
+      const int n0l = (kel - kbl + S - 1) / S;
+      const int kt0l = kbl + half * n0l;
+      const int cntl = max(0, min(kel, kt0l + n0l) - kt0l);
+      // chunk c = lane + 64 i: K at byte 16 c of the tile (its rows of HD
+      // halves are contiguous in the mirror); V^T d row c / 8, keys
+      // 8 (c % 8) .. +8
+      constexpr int LPT = KCH / 64;
+      const char *kb8 = (const char *)kgl, *vb8 = (const char *)vgl;
+      const unsigned kl = (unsigned)lane * 16u;
+      const unsigned vl = (unsigned)(((lane >> 3) * p.ldp + (lane & 7) * 8) * 2);
+      const unsigned vstep = (unsigned)(8 * p.ldp * 2);
+      h8 lk[LPT], lv[LPT];
+      auto lload = [&](int kt) {
+        const unsigned kadv = (unsigned)(kt * KT * HD * 2) + kl, vadv = (unsigned)(kt * KT * 2) + vl;
+#pragma unroll
+        for (int i = 0; i < LPT; ++i) {
+          lk[i] = *(const h8 *)(kb8 + (kadv + (unsigned)i * 1024u));
+          lv[i] = *(const h8 *)(vb8 + (vadv + (unsigned)i * vstep));
+        }
+      };
+      auto lwrite = [&](int buf) {
+#pragma unroll
+        for (int i = 0; i < LPT; ++i) {
+          const int c = lane + 64 * i;
+          const int kk = c / (HD / 8), kc = c - kk * (HD / 8);
+          *(h8 *)(&sK[half][buf][kk * KP + kc * 8]) = lk[i];
+          *(h8 *)(&sV[half][buf][(c >> 3) * VP + (c & 7) * 8]) = lv[i];
+        }
+      };
+      if (HD < 32) {  // d rows HD .. 31 of V^T (never loaded) stay zero
+        for (int i = lane; i < 2 * (DV - HD) * VP; i += 64) {
+          const int bb = i / ((DV - HD) * VP), j = i - bb * (DV - HD) * VP;
+          sV[half][bb][HD * VP + j] = (_Float16)0.f;
+        }
+      }
+      // the padding chunk of every K row (columns HD .. HD+7, never written
+      // by the tile loads): 1, 0, ..., 0
+      for (int i = lane; i < 2 * KT; i += 64) {
+        h8 one;
+#pragma unroll
+        for (int j = 0; j < 8; ++j) one[j] = (_Float16)(j == 0 ? 1.f : 0.f);
+        *(h8 *)(&sK[half][i / KT][(i % KT) * KP + HD]) = one;
+      }
+      if (cntl > 0) {
+        lload(kt0l);
+        lwrite(0);
+        if (cntl > 1) lload(kt0l + 1);
+      }
+      __syncthreads();
+      for (int it = 0; it < n0l; ++it) {  // (the compute wavefronts' barriers, one for one)
+        if (it + 1 < cntl) lwrite((it + 1) & 1);  // its buffer was last read in it - 1
+        if (it + 2 < cntl) lload(kt0l + it + 2);
+        __syncthreads();
+      }
+      if constexpr (S == 2) __syncthreads();  // (the halves' merge)
+      return;
     }
   }
 
@@ -1133,23 +1213,27 @@ __global__ __launch_bounds__(64 * G * S) void k_attn_prefill(AttnPreP p) {
 
   // the padding chunk of every K row (columns HD .. HD+7, never written by
   // the tile loads): 1, 0, ..., 0
-  for (int i = tid; i < 2 * KT; i += nthr) {
-    h8 one;
+  if constexpr (NL == 0) {
+    for (int i = tid; i < 2 * KT; i += nthr) {
+      h8 one;
 #pragma unroll
-    for (int j = 0; j < 8; ++j) one[j] = (_Float16)(j == 0 ? 1.f : 0.f);
-    *(h8 *)(&hK[i / KT][(i % KT) * KP + HD]) = one;
-  }
-  if (cnt > 0) {
-    gload(kt0);
-    swrite(0);
-    if (cnt > 1) gload(kt0 + 1);
+      for (int j = 0; j < 8; ++j) one[j] = (_Float16)(j == 0 ? 1.f : 0.f);
+      *(h8 *)(&hK[i / KT][(i % KT) * KP + HD]) = one;
+    }
+    if (cnt > 0) {
+      gload(kt0);
+      swrite(0);
+      if (cnt > 1) gload(kt0 + 1);
+    }
   }
   __syncthreads();
   for (int it = 0; it < n0; ++it) {  // (every half runs n0 iterations: the barriers match)
     const int buf = it & 1;
     const bool live = it < cnt;
-    if (it + 1 < cnt) swrite(buf ^ 1);  // its buffer was last read in it - 1
-    if (it + 2 < cnt) gload(kt0 + it + 2);
+    if constexpr (NL == 0) {
+      if (it + 1 < cnt) swrite(buf ^ 1);  // its buffer was last read in it - 1
+      if (it + 2 < cnt) gload(kt0 + it + 2);
+    }
     if (live) {
       const _Float16 *sk = hK[buf];
       const _Float16 *sv = hV[buf];
@@ -1333,7 +1417,8 @@ __global__ __launch_bounds__(256) void k_attn_prefill_merge(AttnPreP p) {
 template <int HD, int G>
 static void attn_prefill_g(const AttnPreP &p, dim3 grid, hipStream_t st) {
   constexpr int S = HD <= 64 ? 2 : 1;  // (hd 128 needs more registers than 2 halves allow)
-  hipLaunchKernelGGL((k_attn_prefill<HD, G, S>), grid, dim3(64 * G * S), 0, st, p);
+  hipLaunchKernelGGL((k_attn_prefill<HD, G, S>), grid, dim3(64 * (G * S + prefill_loaders<G, S>())), 0,
+                     st, p);
 }
 
 template <int HD>
