@@ -1243,15 +1243,21 @@ __global__ __launch_bounds__(64 * (G * S + prefill_loaders<G, S>())) void k_attn
       for (int hf = 0; hf < 2; ++hf) {
 #pragma unroll
         for (int r = 0; r < 16; ++r) s[hf][r] = 0.f;
-        // (K side: the row's padding chunk, 1 then zeros, read by both lane
-        // halves; the upper half's Q side is zero)
-        const h8 one = *(const h8 *)(sk + (hf * 32 + (lane & 31)) * KP + HD);
+        // the half's fragments read together, then multiplied (one LDS wait
+        // instead of one per MFMA; with loader wavefronts the registers are
+        // there).  (K side of the reference column: the row's padding chunk,
+        // 1 then zeros, read by both lane halves; the upper half's Q side is
+        // zero.)
+        const _Float16 *kr = sk + (hf * 32 + (lane & 31)) * KP;
+        const h8 one = *(const h8 *)(kr + HD);
+        h8 a[KSTEPS];
+#pragma unroll
+        for (int st = 0; st < KSTEPS; ++st) a[st] = *(const h8 *)(kr + st * 16 + hi * 8);
+        if (NL > 0) __builtin_amdgcn_sched_barrier(0);
         s[hf] = __builtin_amdgcn_mfma_f32_32x32x16_f16(one, qbias, s[hf], 0, 0, 0);  // - m_ref
 #pragma unroll
-        for (int st = 0; st < KSTEPS; ++st) {
-          const h8 a = *(const h8 *)(sk + (hf * 32 + (lane & 31)) * KP + st * 16 + hi * 8);
-          s[hf] = __builtin_amdgcn_mfma_f32_32x32x16_f16(a, qf[st], s[hf], 0, 0, 0);
-        }
+        for (int st = 0; st < KSTEPS; ++st)
+          s[hf] = __builtin_amdgcn_mfma_f32_32x32x16_f16(a[st], qf[st], s[hf], 0, 0, 0);
       }
       // causal mask (only tiles that reach past the first row's position)
       if (key0 + KT - 1 > qpos_min) {
