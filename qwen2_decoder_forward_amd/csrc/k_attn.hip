@@ -957,8 +957,58 @@ struct PreSeg {
   // each (first / second half of their key tiles) whose softmax states go to
   // part (from split record part0 on) and are combined by k_attn_prefill_merge
   int n_tiles, split_from, part0;
+  int p0;         // position of row r0 when the rows' positions are p0, p0+1, ...; else -1
   size_t kv_off;  // element offset of the sequence's KV head 0 in either mirror
 };
+
+// First query tile of a segment with positions p0 .. p0+M-1 (T tiles of 32
+// rows) whose key-tile count (p0 + min(32 t + 31, M - 1)) / 64 + 1 is at
+// least u; T if none.
+__device__ __forceinline__ int tile_reaching(int p0, int M, int T, int u) {
+  const int X = kPreKeys * (u - 1) - p0;  // the row the tile's last row must reach
+  if (X > M - 1) return T;
+  return X <= 0 ? 0 : X / 32;
+}
+
+// Work item wi of a segment with contiguous positions, taking the items in
+// descending order of key tiles (longest first over whole tiles and split
+// pieces together, the list-scheduling order that keeps the CUs' finishing
+// times close): the item's tile and piece (-1: whole tile; 0 / 1: the
+// first / second part of a split tile's key tiles, ceil / floor of half).
+// Items with at least v key tiles are counted in closed form, the work
+// value of item wi is found by bisection, and within one value whole tiles,
+// first pieces and second pieces follow each other, each in descending
+// tile order.
+__device__ inline void prefill_item_lpt(const PreSeg &sg, int wi, int &tile, int &piece) {
+  const int p0 = sg.p0, M = sg.M, T = sg.n_tiles, sf = sg.split_from;
+  auto first = [&](int u) { return tile_reaching(p0, M, T, u); };
+  auto count_ge = [&](int v) {
+    return max(0, sf - first(v)) + (T - max(sf, first(2 * v - 1))) + (T - max(sf, first(2 * v)));
+  };
+  int lo = 1, hi = (p0 + M - 1) / kPreKeys + 2;  // count_ge(lo) > wi >= count_ge(hi)
+  while (hi - lo > 1) {
+    const int mid = (lo + hi) >> 1;
+    if (count_ge(mid) > wi) lo = mid;
+    else hi = mid;
+  }
+  int r = wi - count_ge(lo + 1);  // rank among the items of exactly lo key tiles
+  const int w_hi = min(first(lo + 1), sf), w_n = w_hi - min(first(lo), sf);
+  if (r < w_n) {
+    tile = w_hi - 1 - r;
+    piece = -1;
+    return;
+  }
+  r -= w_n;
+  const int a_hi = max(sf, first(2 * lo + 1)), a_n = a_hi - max(sf, first(2 * lo - 1));
+  if (r < a_n) {
+    tile = a_hi - 1 - r;
+    piece = 0;
+    return;
+  }
+  r -= a_n;
+  tile = max(sf, first(2 * lo + 2)) - 1 - r;
+  piece = 1;
+}
 constexpr int kPreSegs = 8;  // sequences per launch
 
 struct AttnPreP {
@@ -1018,8 +1068,9 @@ __global__ __launch_bounds__(64 * (G * S + prefill_loaders<G, S>())) void k_attn
   const bool loader = NL > 0 && w >= G * S;  // (wave-uniform)
   const int half = loader ? w - G * S : w / G, hw = loader ? 0 : w - (w / G) * G;
   const int tid = threadIdx.x - half * NTHR, nthr = NTHR;  // index within the half
-  // longest work first: the split tiles' two pieces (descending tiles),
-  // then the whole tiles (descending)
+  // longest work first: with contiguous positions in descending order of
+  // key tiles over all items; otherwise the split tiles' two pieces
+  // (descending tiles), then the whole tiles (descending)
   // (the KV head is the grid's fastest index, so the dispatch order is
   // longest-first across the KV heads too)
   // (the sequences of the launch interleave, so equal work ranks of all
@@ -1029,7 +1080,9 @@ __global__ __launch_bounds__(64 * (G * S + prefill_loaders<G, S>())) void k_attn
   const int n_split = sg.n_tiles - sg.split_from;
   if (wi >= sg.n_tiles + n_split) return;  // (a shorter sequence: no work)
   int tile, piece;
-  if (wi < 2 * n_split) {
+  if (sg.p0 >= 0) {
+    prefill_item_lpt(sg, wi, tile, piece);
+  } else if (wi < 2 * n_split) {
     tile = sg.n_tiles - 1 - wi / 2;
     piece = wi & 1;
   } else {
@@ -1483,9 +1536,13 @@ static void attn_prefill_launch(const Dims &d, int layer, const KVCache &kv, con
   p.part = ws.buf;
   p.n_seg = n;
   // Causal balance: with one block per (query tile, KV head) the last tile's
-  // block has the most key tiles; tiles with more than half of the largest
-  // count over the launch (and at least 8 key tiles) are split in two, so no
-  // block has more than about half of the longest tile's work.  Positions
+  // block has the most key tiles; tiles with more than a third of the
+  // largest count over the launch (and at least 8 key tiles) are split in
+  // two, so no block has more than about half of the longest tile's work,
+  // and the blocks, dispatched longest first, even out the CUs' finishing
+  // times (0.5B 4096-token attention 1.61 -> 1.44 ms per prefill, hd-128
+  // 2048 tokens 2.10 -> 1.92 ms, from splitting above half of the largest
+  // count with the pieces dispatched before the whole tiles).  Positions
   // increase within a sequence, so the key-tile count grows with the tile
   // index and a sequence's split tiles are its last ones.  With 512 or more
   // blocks (two per CU) the CUs already balance long and short tiles, and
@@ -1502,11 +1559,14 @@ static void attn_prefill_launch(const Dims &d, int layer, const KVCache &kv, con
     sg.M = segs[i].n;
     sg.n_tiles = sg.split_from = T;
     sg.kv_off = kv.off16(d, layer, segs[i].seq, 0) - b16;
+    sg.p0 = host_pos[sg.r0];
+    for (int r = 1; r < sg.M && sg.p0 >= 0; ++r)
+      if (host_pos[sg.r0 + r] != sg.p0 + r) sg.p0 = -1;
     total_tiles += T;
     kmax = std::max(kmax, ntiles(segs[i], T - 1));
   }
   if (total_tiles * d.nkv >= 128 && total_tiles * d.nkv < 512 && kmax >= 8) {
-    const int lim = (kmax + 1) / 2;
+    const int lim = (kmax + 2) / 3;
     int n_split = 0;
     for (int i = 0; i < n; ++i) {
       int sf = p.seg[i].n_tiles;
