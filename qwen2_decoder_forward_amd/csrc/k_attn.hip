@@ -314,7 +314,8 @@ struct AttnWoP {
   // n_ctx), known on the host; the position itself is read on the device.
   const float *kb1, *vb1;
   int nk1;
-  L2Warm warm;  // one-row calls: producer blocks in grid rows y >= nh
+  L2Warm warm;   // one-row calls: producer blocks in grid rows y >= nh (the down projection)
+  L2Warm warm2;  // ... and after them (the next layer's QKV projection)
 };
 
 template <int N>
@@ -551,7 +552,11 @@ __global__ __launch_bounds__(256) void k_attn_wo1(AttnWoP p) {
                  "s"(p.rows_per_block), "s"(p.scale));
   }
   if (head >= p.d.nh) {  // an L2 warming producer (grid rows past the heads)
-    l2_warm<kWarmStepsAttn>(p.warm, rc + head * (int)gridDim.x);
+    const int id = rc + head * (int)gridDim.x;
+    if (id < p.warm.p0 + p.warm.n_prod)
+      l2_warm<kWarmStepsAttn>(p.warm, id);
+    else
+      l2_warm<kWarmStepsAttn>(p.warm2, id);
     return;
   }
   const unsigned pos = vload(p.rows.pos, 0);
@@ -675,7 +680,7 @@ template <int HD>
 static void attn_wo_hd(const AttnWoP &p, int grid_x, hipStream_t st) {
   dim3 grid(grid_x, p.d.nh);
   if (p.M <= 1) {
-    grid.y += p.warm.n_prod / grid_x;  // (n_prod: whole grid rows)
+    grid.y += (p.warm.n_prod + p.warm2.n_prod) / grid_x;  // (n_prod: whole grid rows)
     hipLaunchKernelGGL((k_attn_wo1<HD>), grid, dim3(256), 0, st, p);
   } else {
     hipLaunchKernelGGL((k_attn_wo<HD, 8>), grid, dim3(256), 0, st, p);
@@ -684,10 +689,10 @@ static void attn_wo_hd(const AttnWoP &p, int grid_x, hipStream_t st) {
 
 void attn_wo_fused(const Dims &d, int layer, const KVCache &kv, const float *q, int ldq,
                    RowInfo rows, int M, int seq1, int nk1, const uint16_t *wo, float *h, int ldh,
-                   const uint16_t *warm_wd, hipStream_t st) {
+                   const uint16_t *warm_wd, const uint16_t *warm_wqkv, hipStream_t st) {
   const int rpb = 4 * wo_loads_fused(d.hd) * (64 / (d.hd / 8));  // WO rows per block
   AttnWoP p{d, layer, kv, q, ldq, rows, M, (const _Float16 *)wo, h, ldh, rpb,
-            1.0f / sqrtf((float)d.hd), nullptr, nullptr, 0, L2Warm{}};
+            1.0f / sqrtf((float)d.hd), nullptr, nullptr, 0, L2Warm{}, L2Warm{}};
   const int gx = (d.H + rpb - 1) / rpb;
   if (M <= 1) {
     p.kb1 = kv.k + kv.off(d, layer, seq1, 0, 0);
@@ -696,6 +701,9 @@ void attn_wo_fused(const Dims &d, int layer, const KVCache &kv, const float *q, 
     if (warm_wd)  // whole grid rows of producers after the heads' rows
       p.warm = warm_gemv1(warm_wd, d.H, d.I_pad, down_rows1(d.I_pad), gx * d.nh,
                           kWarmProdAttn / gx * gx, kWarmStepsAttn);
+    if (warm_wqkv)  // then the next layer's QKV rows (its one-row GEMV: 2 rows per wave)
+      p.warm2 = warm_gemv1(warm_wqkv, d.nqkv, d.H, 2, gx * d.nh + p.warm.n_prod,
+                           kWarmProdQkv / gx * gx, kWarmStepsAttn);
   }
   switch (d.hd) {
     case 16: attn_wo_hd<16>(p, gx, st); break;

@@ -87,6 +87,7 @@ struct L2Warm {
 // producers than idle CUs keep each one's share small: a CU pulls only about
 // 26 KB per microsecond from HBM (outstanding misses over the latency).
 constexpr int kWarmProdAttn = 256, kWarmStepsAttn = 16;
+constexpr int kWarmProdQkv = 64;  // producers for the next layer's QKV rows
 // n_prod producers for a later one-row GEMV over W [N, K] with R rows per
 // wave, hosted by a launch whose producer block ids start at p0; none (n_prod
 // = 0 in the result) when it does not pay (weights too large for the L2s)
@@ -237,11 +238,12 @@ void attn_decode(const Dims &d, int layer, const KVCache &kv, const float *q, in
 constexpr int kFusedKeys = 512;
 constexpr int wo_loads_per_wave(int hd) { return hd == 64 ? 2 : 8; }
 constexpr int wo_loads_fused(int hd) { return hd == 64 ? 2 : 8; }  // (attn_wo_fused's blocks)
-// warm_wd: the down projection of the same layer, warmed by producer blocks
-// of the one-row kernel (null: none).
+// warm_wd: the down projection of the same layer, warm_wqkv: the QKV
+// projection of the next layer, warmed by producer blocks of the one-row
+// kernel (null: none).
 void attn_wo_fused(const Dims &d, int layer, const KVCache &kv, const float *q, int ldq,
                    RowInfo rows, int M, int seq1, int nk1, const uint16_t *wo, float *h, int ldh,
-                   const uint16_t *warm_wd, hipStream_t st);
+                   const uint16_t *warm_wd, const uint16_t *warm_wqkv, hipStream_t st);
 // The chunk records of attn_decode (merge = false) of M <= 8 rows merged
 // and multiplied by WO, the partial row sums added into h with float
 // atomics: per (WO row chunk, query head) block as in attn_wo_fused.

@@ -481,8 +481,9 @@ void attn_wo_gemv(qwen2_ctx *c, int l, const float *q, q2::RowInfo rows, int M, 
   if (n_chunks * q2::kChunkKeys <= q2::kFusedKeys) {
     // one row: its slot and a key bound past its position, from the host
     const int nk1 = std::min(n_chunks * q2::kChunkKeys, d.n_ctx);
+    const uint16_t *next_qkv = l + 1 < d.L ? c->layers[l + 1].wqkv : nullptr;
     TIMED(QWEN2_OP_ATTN, q2::attn_wo_fused(d, l, kv, q, nhd, rows, M, seq1, nk1, w.wo, h, d.H,
-                                           w.wd, st));
+                                           w.wd, next_qkv, st));
     return;
   }
   TIMED(QWEN2_OP_ATTN, q2::attn_decode(d, l, kv, q, nhd, rows, M, n_chunks, false, c->part,
