@@ -75,7 +75,7 @@ int main() {
 @pytest.mark.skipif(shutil.which("g++") is None, reason="needs a host C++ compiler")
 def test_prefill_lpt_order_is_a_descending_bijection(tmp_path):
     s = open(SRC).read()
-    a, b = s.index("struct PreSeg {"), s.index("constexpr int kPreSegs")
+    a, b = s.index("struct PreSeg {"), s.index("struct AttnPreP {")
     code = s[a:b].replace("__device__ __forceinline__", "static inline").replace("__device__ inline",
                                                                                   "static inline")
     assert "prefill_item_lpt" in code and "tile_reaching" in code
