@@ -1461,23 +1461,45 @@ __global__ __launch_bounds__(64 * (G * S + prefill_loaders<G, S>())) void k_attn
 // in base 2).  One block per (split tile, query head).
 template <int HD>
 __global__ __launch_bounds__(256) void k_attn_prefill_merge(AttnPreP p) {
+  constexpr int C = HD / 4;                 // 4-wide chunks of a row
+  constexpr int IT = (32 * C + 255) / 256;  // chunks per thread
   const int u = blockIdx.x, h = blockIdx.y;  // (u: split record, over all sequences)
   int si = 0;
   while (si + 1 < p.n_seg && u >= p.seg[si + 1].part0) ++si;
   const PreSeg &sg = p.seg[si];
   const int r0 = (sg.split_from + u - sg.part0) * 32;
+  const int nq = min(32, sg.M - r0);  // (rows past M come last)
   const float *a = p.part + (((size_t)u * 2 + 0) * p.d.nh + h) * 32 * (HD + 4);
   const float *b = p.part + (((size_t)u * 2 + 1) * p.d.nh + h) * 32 * (HD + 4);
-  for (int idx = threadIdx.x; idx < 32 * HD; idx += 256) {
-    const int q = idx / HD, dd = idx - q * HD;
-    if (r0 + q >= sg.M) break;  // (rows past M come last)
+  // every load first, at clamped rows (a load tied to a condition is waited
+  // for on the spot), then the combination
+  f4 xa[IT], xb[IT];
+  float ma[IT], mb[IT], la[IT], lb[IT];
+#pragma unroll
+  for (int i = 0; i < IT; ++i) {
+    const int idx = min((int)threadIdx.x + 256 * i, 32 * C - 1);
+    const int q = min(idx / C, nq - 1), c = idx % C;
     const float *x = a + q * (HD + 4), *y = b + q * (HD + 4);
-    const float m0 = x[HD], m1 = y[HD];
-    const float mm = fmaxf(m0, m1);
+    xa[i] = *(const f4 *)(x + 4 * c);
+    xb[i] = *(const f4 *)(y + 4 * c);
+    ma[i] = x[HD];
+    mb[i] = y[HD];
+    la[i] = x[HD + 1];
+    lb[i] = y[HD + 1];
+  }
+#pragma unroll
+  for (int i = 0; i < IT; ++i) {
+    const int idx = (int)threadIdx.x + 256 * i;
+    const int q = idx / C, c = idx % C;
+    if (idx >= 32 * C || q >= nq) continue;
+    const float mm = fmaxf(ma[i], mb[i]);
     const float sub = mm == kNegInf ? 0.f : mm;
-    const float w0 = exp2f(m0 - sub), w1 = exp2f(m1 - sub);
-    const float o = (x[dd] * w0 + y[dd] * w1) / (x[HD + 1] * w0 + y[HD + 1] * w1);
-    p.o16[(size_t)(sg.r0 + r0 + q) * p.ldo + (size_t)h * HD + dd] = (_Float16)o;
+    const float w0 = exp2f(ma[i] - sub), w1 = exp2f(mb[i] - sub);
+    const float den = la[i] * w0 + lb[i] * w1;
+    h4 v;
+#pragma unroll
+    for (int e = 0; e < 4; ++e) v[e] = (_Float16)((xa[i][e] * w0 + xb[i][e] * w1) / den);
+    *(h4 *)(p.o16 + (size_t)(sg.r0 + r0 + q) * p.ldo + (size_t)h * HD + 4 * c) = v;
   }
 }
 
