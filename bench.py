@@ -299,6 +299,44 @@ def pmc_pass(torch, q, syn):
         f"of {gateup_bytes(shape)} algorithmic bytes")
 
 
+def library_gemms(torch, syn, wl_name: str) -> None:
+    """For comparison only: the prefill projections of a workload as plain
+    library products (torch.matmul through hipBLASLt, f16 operands, no fused
+    bias / RoPE / SwiGLU / residual epilogues), timed with HIP events; prints
+    each shape's time and its share of the 2.5 PFLOP/s dense f16 peak."""
+    wl = syn.WORKLOADS[wl_name]
+    shape = syn.MODELS[wl.model]
+    M, H, I = wl.prompt_len, shape.n_embd, shape.n_ff
+    nq, nkv = shape.n_head * shape.head_dim, shape.n_head_kv * shape.head_dim
+    shapes = {"qkv": (M, nq + 2 * nkv, H), "wo": (M, H, nq), "gateup": (M, 2 * I, H), "down": (M, H, I)}
+    torch.cuda.set_device(0)
+    g = torch.Generator(device="cuda").manual_seed(0)
+    tot_fl = tot_us = 0.0
+    for name, (m, n, k) in shapes.items():
+        a = torch.randn(m, k, device="cuda", dtype=torch.float16, generator=g)
+        w = torch.randn(n, k, device="cuda", dtype=torch.float16, generator=g)
+        wt = w.t()
+        for _ in range(3):
+            c = a @ wt
+        torch.cuda.synchronize()
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        reps = 20
+        e0.record()
+        for _ in range(reps):
+            c = a @ wt
+        e1.record()
+        torch.cuda.synchronize()
+        us = e0.elapsed_time(e1) / reps * 1e3
+        fl = 2.0 * m * n * k
+        tot_fl += fl
+        tot_us += us
+        log(f"[{wl_name}] library {name} {m} x {n} x {k}: {us:.1f} us, "
+            f"{fl / us / 1e6:.0f} TFLOP/s = {100 * fl / us / 1e6 / MFMA_F16_PEAK_TFS:.1f} % of peak")
+        del a, w, wt, c
+    log(f"[{wl_name}] library projections together: {tot_us:.1f} us, "
+        f"{100 * tot_fl / tot_us / 1e6 / MFMA_F16_PEAK_TFS:.1f} % of peak")
+
+
 def main():
     ap = argparse.ArgumentParser(description=__doc__)
     ap.add_argument("--gpus", type=int, default=1)
@@ -312,6 +350,9 @@ def main():
                     help="summarise a rocprofv3 kernel trace of this script (no GPU use)")
     ap.add_argument("--counter-summary", metavar="CSV",
                     help="summarise a rocprofv3 --pmc counter CSV of this script (no GPU use)")
+    ap.add_argument("--library-gemms", action="store_true",
+                    help="only time the workload's prefill projections as plain torch.matmul "
+                         "products (hipBLASLt), for comparison")
     ap.add_argument("--pmc-pass", action="store_true",
                     help="only the launches a rocprofv3 --pmc counter pass reads: a plain 256 MiB "
                          "device copy (calibration), then 48 launches of the gate/up GEMV")
@@ -334,6 +375,9 @@ def main():
 
     if args.pmc_pass:
         pmc_pass(torch, q, syn)
+        return
+    if args.library_gemms:
+        library_gemms(torch, syn, args.workload)
         return
 
     wl = syn.WORKLOADS[args.workload]
