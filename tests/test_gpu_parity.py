@@ -170,6 +170,28 @@ def test_multi_pass_prefill(tiny_w):
     p.close()
 
 
+@pytest.mark.parametrize("case", ["continuation", "gapped"])
+def test_split_prefill_dispatch_orders(tiny_w, case):
+    """A 2048-row pass splits its longest query tiles (64 tiles x 2 KV heads:
+    128 blocks before the split) and dispatches its work longest first.
+    continuation: the rows follow a 100-row prefill (positions 100..2147), so
+    the closed-form item order starts at position 100; gapped: positions
+    0..1023 and 1124..2147, not contiguous, so the pieces-first order serves
+    (the gap's slots are unwritten and read as zero on both sides)."""
+    p = Pair(TINY, tiny_w, n_ctx=4096)
+    if case == "continuation":
+        p.prefill(0, syn.make_prompt(TINY, 100, 8), np.arange(100))
+        pos = np.arange(100, 2148)
+    else:
+        pos = np.concatenate([np.arange(1024), np.arange(1124, 2148)])
+    lg, gid, r = p.prefill(0, syn.make_prompt(TINY, 2048, 9), pos)
+    check(lg, r.logits[0], TOL, f"split prefill ({case}) logits")
+    check_id(gid, r.logits[0], r.argmax[0], f"split prefill ({case})")
+    h = p.hidden(0, 1)
+    check(h[0], r.layer_output[-1], TOL, f"split prefill ({case}) last hidden row")
+    p.close()
+
+
 def _check_batch(p, seqs, toks, poss, tol, what):
     lg, ids, rs = p.prefill_batch(seqs, toks, poss)
     h = p.hidden(0, len(seqs))
