@@ -35,8 +35,8 @@ MFMA_F16_PEAK_TFS = 2500.0  # MI355X dense f16 MFMA
 # WRITE_SIZE passes, scaled by what the counters read for a 256 MiB copy
 # (profiles/qwen2.5-0.5b_gateup_gemv_hbm_traffic.md); valid only while the
 # kernel source is the one the counters were taken on.
-GATEUP_TRAFFIC_BYTES = 17580563
-GATEUP_TRAFFIC_SRC_SHA = "9566d4c069df358e"
+GATEUP_TRAFFIC_BYTES = 17580542
+GATEUP_TRAFFIC_SRC_SHA = "be3c455c616ec489"
 
 
 def gateup_traffic(shape):
