@@ -1138,11 +1138,13 @@ template <int EPI>
 static int launch_tiles(GemmP p, const Workspace &wsp, hipStream_t st) {
   if (p.M >= kBigM) return launch_large_m<EPI>(p, wsp, st);
   if (p.K <= 1024 && p.N <= 2048) return launch_skinny<EPI>(p, wsp, st);
-  // gate/up of up to 128 rows: a ring of two K slices in flight and the
-  // next step's LDS fragments read ahead (measured on the 0.5B gate/up
-  // GEMM: 64 rows 12.6 -> 9.2 us, 128 rows 13.0 -> 10.9 us)
+  // gate/up of up to 128 rows: a ring of K slices in flight and the next
+  // step's LDS fragments read ahead (measured on the 0.5B gate/up GEMM: two
+  // slices, 64 rows 12.6 -> 9.2 us, 128 rows 13.0 -> 10.9 us; four slices
+  // at up to 64 rows, 64-sequence decode step 1.475 -> 1.460 ms, no gain at
+  // 128 rows)
   if constexpr (EPI == G_SWIGLU) {
-    if (p.M <= 64) return launch_ring<EPI, 64, 64, 2, 2, 1, 4>(p, 1, wsp, st);
+    if (p.M <= 64) return launch_ring<EPI, 64, 64, 2, 4, 1, 4>(p, 1, wsp, st);
     if (p.M <= 128) return launch_ring<EPI, 128, 64, 4, 2, 1, 8>(p, 1, wsp, st);
   }
   const int nk = p.K / kBK2;
