@@ -1021,8 +1021,18 @@ __global__ __launch_bounds__(64 * NWS) void k_gemm_skinny(GemmP p) {
         for (int i = 0; i < TM; ++i)
           acc[i] = __builtin_amdgcn_mfma_f32_32x32x16_f16(af[u][i], bf[u], acc[i], 0, 0, 0);
   }
+  // (QKV: the partial sums go to LDS as [wavefront][accumulator row][lane],
+  // so the reads below, one accumulator row across the lanes, fall on
+  // consecutive banks; read as one 64-byte vector per lane, the same row
+  // was a 16-way bank conflict for each of the eight wavefronts, 1.8 us)
+  float *const sT = (float *)sRed;
+  if constexpr (EPI == G_QKV && TM == 1 && NWS == 8) {
 #pragma unroll
-  for (int i = 0; i < TM; ++i) sRed[wave][i][lane] = acc[i];
+    for (int r = 0; r < 16; ++r) sT[(wave * 16 + r) * 64 + lane] = acc[0][r];
+  } else {
+#pragma unroll
+    for (int i = 0; i < TM; ++i) sRed[wave][i][lane] = acc[i];
+  }
   __syncthreads();
   if constexpr (EPI == G_QKV && TM == 1 && NWS == 8) {
     // every wavefront finishes two of the tile's 16 accumulator rows, so the
@@ -1034,9 +1044,9 @@ __global__ __launch_bounds__(64 * NWS) void k_gemm_skinny(GemmP p) {
 #pragma unroll
     for (int u = 0; u < 2; ++u) {
       const int r = 2 * wave + u;
-      float x = sRed[0][0][lane][r];
+      float x = sT[r * 64 + lane];
 #pragma unroll
-      for (int w = 1; w < NWS; ++w) x += sRed[w][0][lane][r];
+      for (int w = 1; w < NWS; ++w) x += sT[(w * 16 + r) * 64 + lane];
       a[u] = x;
       b[u] = __shfl_xor(x, 1, 64);  // the pair partner (column n + 1)
       const int mm = m0 + 8 * (r >> 2) + 4 * hi + (r & 3);
