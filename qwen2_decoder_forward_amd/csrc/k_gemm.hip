@@ -1021,18 +1021,17 @@ __global__ __launch_bounds__(64 * NWS) void k_gemm_skinny(GemmP p) {
         for (int i = 0; i < TM; ++i)
           acc[i] = __builtin_amdgcn_mfma_f32_32x32x16_f16(af[u][i], bf[u], acc[i], 0, 0, 0);
   }
-  // (QKV: the partial sums go to LDS as [wavefront][accumulator row][lane],
-  // so the reads below, one accumulator row across the lanes, fall on
-  // consecutive banks; read as one 64-byte vector per lane, the same row
-  // was a 16-way bank conflict for each of the eight wavefronts, 1.8 us)
+  // The partial sums go to LDS as [wavefront][row tile][accumulator row]
+  // [lane], so every read below (one accumulator row across the lanes)
+  // falls on consecutive banks; stored as one 64-byte vector per lane, the
+  // same reads were 16-way bank conflicts (QKV: 1.8 us for its eight
+  // wavefronts; in the residual GEMMs, where one to four wavefronts read,
+  // the conflicts took 3/4 of the LDS time but no measurable kernel time).
   float *const sT = (float *)sRed;
-  if constexpr (EPI == G_QKV && TM == 1 && NWS == 8) {
 #pragma unroll
-    for (int r = 0; r < 16; ++r) sT[(wave * 16 + r) * 64 + lane] = acc[0][r];
-  } else {
+  for (int i = 0; i < TM; ++i)
 #pragma unroll
-    for (int i = 0; i < TM; ++i) sRed[wave][i][lane] = acc[i];
-  }
+    for (int r = 0; r < 16; ++r) sT[((wave * TM + i) * 16 + r) * 64 + lane] = acc[i][r];
   __syncthreads();
   if constexpr (EPI == G_QKV && TM == 1 && NWS == 8) {
     // every wavefront finishes two of the tile's 16 accumulator rows, so the
@@ -1046,7 +1045,7 @@ __global__ __launch_bounds__(64 * NWS) void k_gemm_skinny(GemmP p) {
       const int r = 2 * wave + u;
       float x = sT[r * 64 + lane];
 #pragma unroll
-      for (int w = 1; w < NWS; ++w) x += sT[(w * 16 + r) * 64 + lane];
+      for (int w = 1; w < NWS; ++w) x += sT[(w * 16 + r) * 64 + lane];  // (TM = 1)
       a[u] = x;
       b[u] = __shfl_xor(x, 1, 64);  // the pair partner (column n + 1)
       const int mm = m0 + 8 * (r >> 2) + 4 * hi + (r & 3);
@@ -1057,9 +1056,14 @@ __global__ __launch_bounds__(64 * NWS) void k_gemm_skinny(GemmP p) {
     return;
   }
   if (wave >= TM) return;
-  f16x v = sRed[0][wave][lane];
+  f16x v;
 #pragma unroll
-  for (int w = 1; w < NWS; ++w) v += sRed[w][wave][lane];
+  for (int r = 0; r < 16; ++r) {
+    float x = sT[(wave * 16 + r) * 64 + lane];
+#pragma unroll
+    for (int w = 1; w < NWS; ++w) x += sT[((w * TM + wave) * 16 + r) * 64 + lane];
+    v[r] = x;
+  }
 
   tile_epilogue<EPI>(p, v, m0 + wave * 32, n0 + l32);
 }
