@@ -579,6 +579,35 @@ __global__ __launch_bounds__(64 * NW) void k_gemm_big(GemmP p) {
         }
     __syncthreads();
     qkv_epilogue_lds<BMT, BNT, NT>(p, T, m0, n0);
+  } else if constexpr (EPI == G_SWIGLU && BMT >= 128) {
+    // the block's SwiGLU outputs (BMT x BNT / 2 halves) go through LDS (the
+    // operand buffers, free after the last barrier), so the stores are
+    // 16-byte row pieces instead of each lane's 16 single halves down a
+    // column (gate/up of 128 and 4096 rows -3 %; with 64-row tiles the two
+    // extra barriers cost more than the stores gain)
+    _Float16 *T = sAB;  // [BMT][BNT / 2]
+    static_assert(BMT * BNT / 2 <= 2 * (BMT + BNT) * kBK2, "output tile fits the operand buffers");
+    __syncthreads();  // (every wavefront is past its last operand read)
+#pragma unroll
+    for (int i = 0; i < TM; ++i)
+#pragma unroll
+      for (int j = 0; j < TN; ++j)
+#pragma unroll
+        for (int r = 0; r < 16; ++r) {
+          const float a = acc[i][j][r];
+          const float b = __shfl_xor(a, 1, 64);  // (the pair partner: column + 1)
+          const int row = wm * WTM + i * 32 + 8 * (r >> 2) + 4 * hi + (r & 3);
+          const int col = wn * WTN + j * 32 + l32;
+          if ((col & 1) == 0) T[row * (BNT / 2) + (col >> 1)] = (_Float16)(silu(a) * b);
+        }
+    __syncthreads();
+    constexpr int CPR = BNT / 16;  // 16-byte pieces of an output row
+#pragma unroll
+    for (int idx = tid; idx < BMT * CPR; idx += NT) {
+      const int row = idx / CPR, ch = idx - row * CPR;
+      const int m = m0 + row, col = (n0 >> 1) + ch * 8;
+      if (m < M && col < (N >> 1)) *(h8 *)(p.a16 + (size_t)m * p.ld_a + col) = *(const h8 *)(T + row * (BNT / 2) + ch * 8);
+    }
   } else {
     // epilogue, one 32 x 32 tile at a time
 #pragma unroll
