@@ -892,7 +892,10 @@ static int launch_large_m(const GemmP &p, const Workspace &wsp, hipStream_t st) 
     // Measured: 0.5B 4096 rows (288 tiles of 128): 0.78 -> 0.67 ms per
     // prefill on 64-row tiles; 1.5B head layout, 512 rows x 2048 (64 tiles
     // of 128): 0.86 -> 0.66 ms on 32-row tiles; hd-128 2048 rows stays on
-    // 128 (32-row tiles: 3.36 -> 4.29 ms).
+    // 128 (32-row tiles: 3.36 -> 4.29 ms).  With long K (>= 2048) the
+    // 128-row tiles keep two K slices in flight in register sets (hd-128
+    // 2048-row QKV 3.30 -> 3.19 ms per prefill; three sets 3.29; at K = 896
+    // the ring was slower).
     const int nt = (p.N + 127) / 128;
     const int rows[3] = {128, 64, 32};
     const double rate[3] = {1.0, 0.83, 0.59};
@@ -906,7 +909,9 @@ static int launch_large_m(const GemmP &p, const Workspace &wsp, hipStream_t st) 
         best = i;
       }
     }
-    if (best == 0)
+    if (best == 0 && p.K >= 2048)
+      launch_big<EPI, 128, 128, 2, 0, 8, 2>(p, 1, st);
+    else if (best == 0)
       launch_big<EPI, 128, 128, 2, 0, 8>(p, 1, st);
     else if (best == 1)
       launch_big<EPI, 64, 128, 2, 0, 8>(p, 1, st);
