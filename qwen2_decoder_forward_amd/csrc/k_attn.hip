@@ -1030,10 +1030,16 @@ struct AttnPreP {
   _Float16 *o16;
   int ldo;
   float qscale;  // head_dim^-0.5 * log2(e): scores in base 2
-  float *part;   // [split record][piece][query head][32 rows][hd + 4]: o, max, sum (base 2), pad
+  float *part;   // [split record][piece][query head][32 rows] records of pre_rec_bytes(hd):
+                 // o / sum as hd binary16, then max and sum (f32, base 2), pad to 16 bytes
   int n_seg;     // sequences in this launch; block row y is work item y / n_seg of sequence y % n_seg
   PreSeg seg[kPreSegs];
 };
+
+// Bytes of one query row's record in the split pieces' workspace: the
+// normalised output as hd binary16, the maximum and the sum as f32, padded
+// to 16 bytes (hd 64: 144 bytes against 272 for an f32 output).
+__host__ __device__ constexpr int pre_rec_bytes(int hd) { return hd * 2 + 16; }
 
 
 // S = 2 (head_dim <= 64): two wavefronts per query head; the block's two
@@ -1424,20 +1430,22 @@ __global__ __launch_bounds__(64 * (G * S + prefill_loaders<G, S>())) void k_attn
       for (int r = 0; r < 16; ++r) o[t][r] = o[t][r] * a0 + x[(2 + t * 16 + r) * 64] * a1;
   }
 
-  if (piece >= 0) {  // a split piece: its (un-normalised) state for the merge
-    float *pr = p.part + ((((size_t)(sg.part0 + tile - sg.split_from) * 2 + piece) * p.d.nh + h) * 32 +
-                          (lane & 31)) * (HD + 4);
+  if (piece >= 0) {  // a split piece: its normalised output, maximum and sum for the merge
+    char *pr = (char *)p.part + ((((size_t)(sg.part0 + tile - sg.split_from) * 2 + piece) * p.d.nh + h) * 32 +
+                                 (lane & 31)) * pre_rec_bytes(HD);
+    const float inv = l_run > 0.f ? 1.0f / l_run : 0.f;  // (a piece with no visible key: zeros)
 #pragma unroll
     for (int t = 0; t < DT; ++t)
 #pragma unroll
       for (int rq = 0; rq < 4; ++rq) {
         const int d0 = t * 32 + 8 * rq + 4 * hi;
-        if (d0 < HD) *(f4 *)(pr + d0) = (f4){o[t][4 * rq], o[t][4 * rq + 1], o[t][4 * rq + 2], o[t][4 * rq + 3]};
+        if (d0 < HD) {
+          h4 v = {(_Float16)(o[t][4 * rq + 0] * inv), (_Float16)(o[t][4 * rq + 1] * inv),
+                  (_Float16)(o[t][4 * rq + 2] * inv), (_Float16)(o[t][4 * rq + 3] * inv)};
+          *(h4 *)(pr + 2 * d0) = v;
+        }
       }
-    if (hi == 0) {
-      pr[HD] = m_run;
-      pr[HD + 1] = l_run;
-    }
+    if (hi == 0) *(float2 *)(pr + 2 * HD) = make_float2(m_run, l_run);
     return;
   }
   if (!qvalid) return;
@@ -1456,9 +1464,11 @@ __global__ __launch_bounds__(64 * (G * S + prefill_loaders<G, S>())) void k_attn
     }
 }
 
-// Combines the two pieces of each split query tile: O = (e^(m0-M) o0 +
-// e^(m1-M) o1) / (e^(m0-M) l0 + e^(m1-M) l1), M the larger maximum (states
-// in base 2).  One block per (split tile, query head).
+// Combines the two pieces of each split query tile: with each piece's
+// normalised output o_i / l_i stored, O = (e^(m0-M) o0 + e^(m1-M) o1) /
+// (e^(m0-M) l0 + e^(m1-M) l1) is the mean of the two weighted by
+// e^(mi-M) li, M the larger maximum (states in base 2).  One block per
+// (split tile, query head).
 template <int HD>
 __global__ __launch_bounds__(256) void k_attn_prefill_merge(AttnPreP p) {
   constexpr int C = HD / 4;                 // 4-wide chunks of a row
@@ -1469,36 +1479,35 @@ __global__ __launch_bounds__(256) void k_attn_prefill_merge(AttnPreP p) {
   const PreSeg &sg = p.seg[si];
   const int r0 = (sg.split_from + u - sg.part0) * 32;
   const int nq = min(32, sg.M - r0);  // (rows past M come last)
-  const float *a = p.part + (((size_t)u * 2 + 0) * p.d.nh + h) * 32 * (HD + 4);
-  const float *b = p.part + (((size_t)u * 2 + 1) * p.d.nh + h) * 32 * (HD + 4);
+  constexpr int REC = pre_rec_bytes(HD);
+  const char *a = (const char *)p.part + (((size_t)u * 2 + 0) * p.d.nh + h) * 32 * REC;
+  const char *b = (const char *)p.part + (((size_t)u * 2 + 1) * p.d.nh + h) * 32 * REC;
   // every load first, at clamped rows (a load tied to a condition is waited
   // for on the spot), then the combination
-  f4 xa[IT], xb[IT];
-  float ma[IT], mb[IT], la[IT], lb[IT];
+  h4 xa[IT], xb[IT];
+  float2 sa[IT], sb[IT];  // (max, sum) of either piece
 #pragma unroll
   for (int i = 0; i < IT; ++i) {
     const int idx = min((int)threadIdx.x + 256 * i, 32 * C - 1);
     const int q = min(idx / C, nq - 1), c = idx % C;
-    const float *x = a + q * (HD + 4), *y = b + q * (HD + 4);
-    xa[i] = *(const f4 *)(x + 4 * c);
-    xb[i] = *(const f4 *)(y + 4 * c);
-    ma[i] = x[HD];
-    mb[i] = y[HD];
-    la[i] = x[HD + 1];
-    lb[i] = y[HD + 1];
+    const char *x = a + q * REC, *y = b + q * REC;
+    xa[i] = *(const h4 *)(x + 8 * c);
+    xb[i] = *(const h4 *)(y + 8 * c);
+    sa[i] = *(const float2 *)(x + 2 * HD);
+    sb[i] = *(const float2 *)(y + 2 * HD);
   }
 #pragma unroll
   for (int i = 0; i < IT; ++i) {
     const int idx = (int)threadIdx.x + 256 * i;
     const int q = idx / C, c = idx % C;
     if (idx >= 32 * C || q >= nq) continue;
-    const float mm = fmaxf(ma[i], mb[i]);
+    const float mm = fmaxf(sa[i].x, sb[i].x);
     const float sub = mm == kNegInf ? 0.f : mm;
-    const float w0 = exp2f(ma[i] - sub), w1 = exp2f(mb[i] - sub);
-    const float den = la[i] * w0 + lb[i] * w1;
+    const float w0 = exp2f(sa[i].x - sub) * sa[i].y, w1 = exp2f(sb[i].x - sub) * sb[i].y;
+    const float den = w0 + w1;
     h4 v;
 #pragma unroll
-    for (int e = 0; e < 4; ++e) v[e] = (_Float16)((xa[i][e] * w0 + xb[i][e] * w1) / den);
+    for (int e = 0; e < 4; ++e) v[e] = (_Float16)(((float)xa[i][e] * w0 + (float)xb[i][e] * w1) / den);
     *(h4 *)(p.o16 + (size_t)(sg.r0 + r0 + q) * p.ldo + (size_t)h * HD + 4 * c) = v;
   }
 }
@@ -1603,7 +1612,7 @@ static void attn_prefill_launch(const Dims &d, int layer, const KVCache &kv, con
       while (sf > 0 && ntiles(segs[i], sf - 1) > lim) --sf;
       n_split += p.seg[i].n_tiles - sf;
     }
-    const size_t need = (size_t)n_split * 2 * d.nh * 32 * (d.hd + 4) * sizeof(float);
+    const size_t need = (size_t)n_split * 2 * d.nh * 32 * pre_rec_bytes(d.hd);
     if (ws.buf && need <= ws.bytes)
       for (int i = 0; i < n; ++i) {
         int sf = p.seg[i].n_tiles;
