@@ -37,6 +37,14 @@ struct GemvP {
   unsigned long long *best;  // LMHEAD: per-row packed maxima
   float *const *logits;      // LMHEAD: device-resident pointer to [M, V] logits (may hold null)
   float *normed_out;         // LMHEAD: f32 copy of the normed rows [M, K]
+  // k_gemv1_emb: the row is the embedding of token (*emb_tok)[emb_off]
+  // (row 0 and *emb_bad = 1 for an id outside [0, emb_V)), written to
+  // emb_h as f32 by block 0
+  const int *const *emb_tok;
+  int emb_off, emb_V;
+  const uint16_t *emb_E;
+  float *emb_h;
+  unsigned int *emb_bad;
 };
 
 template <int MT, int R, int KB, int EPI>
@@ -248,9 +256,10 @@ __device__ __forceinline__ int xs_slot(int k) {  // LDS slot of element k of a b
   return (c << 9) + (((r >> 2) & 1) << 8) + ((r >> 3) << 2) + (r & 3);
 }
 
-template <int R, int KB, int EPI>
-__global__ __launch_bounds__(256) void k_gemv1(GemvP p) {
+template <int R, int KB, int EPI, bool EMB>
+__device__ __forceinline__ void gemv1_body(const GemvP &p) {
   static_assert(KB % 2 == 0, "KB / 2 pieces per thread");
+  static_assert(!EMB || EPI == EPI_QKV, "the embedding gather feeds the first QKV projection");
   constexpr int XP = KB / 2;  // 16-byte activation pieces per thread and batch
   __shared__ __attribute__((aligned(16))) float sx[KB * 512];
   __shared__ float sRed[4];
@@ -287,38 +296,74 @@ __global__ __launch_bounds__(256) void k_gemv1(GemvP p) {
     // (do-while: K > 0, and a loop-entry test would wait for K before the
     // pointers are loaded)
     int kb0 = 0;
+    int tok = 0;  // (EMB: the token id as read)
     do {
       const bool first = kb0 == 0;
       // 1. this thread's pieces of the activation row (and gains)
       f4 xp[XP], gp[XP];
-#pragma unroll
-      for (int i = 0; i < XP; ++i) {
-        const int k = kb0 + 4 * (tid + 256 * i);
-        const int kc = k < K ? k : K - 4;
-        const f4 a = *(const f4 *)(xg + kc);
-        xp[i] = k < K ? a : (f4){0.f, 0.f, 0.f, 0.f};
-        if (norm && first) {
-          const f4 g = *(const f4 *)(gw + kc);
-          gp[i] = k < K ? g : (f4){0.f, 0.f, 0.f, 0.f};
+      auto load_x = [&]() {
+        const _Float16 *er = nullptr;
+        if constexpr (EMB) {
+          tok = (*p.emb_tok)[p.emb_off];
+          er = (const _Float16 *)p.emb_E + (size_t)(tok < 0 || tok >= p.emb_V ? 0 : tok) * K;
         }
-      }
+#pragma unroll
+        for (int i = 0; i < XP; ++i) {
+          const int k = kb0 + 4 * (tid + 256 * i);
+          const int kc = k < K ? k : K - 4;
+          f4 a;
+          if constexpr (EMB) {
+            const h4 e = *(const h4 *)(er + kc);
+            a = (f4){(float)e[0], (float)e[1], (float)e[2], (float)e[3]};
+          } else {
+            a = *(const f4 *)(xg + kc);
+          }
+          xp[i] = k < K ? a : (f4){0.f, 0.f, 0.f, 0.f};
+          if (norm && first) {
+            const f4 g = *(const f4 *)(gw + kc);
+            gp[i] = k < K ? g : (f4){0.f, 0.f, 0.f, 0.f};
+          }
+        }
+      };
       // 2. the weight stream
       h8 wv[KB][R];
+      auto load_w = [&]() {
 #pragma unroll
-      for (int c = 0; c < KB; ++c) {
-        const int k = kb0 + c * 512 + lane * 8;
-        const bool kin = k < K;
-        const int kc = kin ? k : K - 8;
+        for (int c = 0; c < KB; ++c) {
+          const int k = kb0 + c * 512 + lane * 8;
+          const bool kin = k < K;
+          const int kc = kin ? k : K - 8;
 #pragma unroll
-        for (int r = 0; r < R; ++r) {
-          const int n = row0 + r;
-          const int nc = n < N ? n : N - 1;
-          const h8 w = __builtin_nontemporal_load((const h8 *)(Wp + (size_t)nc * K + kc));
-          wv[c][r] = kin && n < N ? w : (h8){0, 0, 0, 0, 0, 0, 0, 0};
+          for (int r = 0; r < R; ++r) {
+            const int n = row0 + r;
+            const int nc = n < N ? n : N - 1;
+            const h8 w = __builtin_nontemporal_load((const h8 *)(Wp + (size_t)nc * K + kc));
+            wv[c][r] = kin && n < N ? w : (h8){0, 0, 0, 0, 0, 0, 0, 0};
+          }
         }
+      };
+      // (the embedded row waits for two dependent reads, the token's pointer
+      // and the token: its weights are requested first)
+      if constexpr (EMB) {
+        load_w();
+        load_x();
+      } else {
+        load_x();
+        load_w();
       }
       if (EPI == EPI_QKV && first)
         e_pair = qkv_pair_end(p.d, p.qkv, 0, en & ~1, e_pos, e_seq, e_ba, e_bb);
+      if constexpr (EMB) {
+        if (blockIdx.x == 0) {  // the residual stream's row, and the id check
+          // (after the epilogue's loads are requested)
+#pragma unroll
+          for (int i = 0; i < XP; ++i) {
+            const int k = kb0 + 4 * (tid + 256 * i);
+            if (k < K) *(f4 *)(p.emb_h + k) = xp[i];
+          }
+          if (tid == 0 && (tok < 0 || tok >= p.emb_V)) *p.emb_bad = 1u;
+        }
+      }
       // 3. RMS of the row over the block (normed variants: one batch)
       if (norm && first) {
         float ss = 0.f;
@@ -366,6 +411,18 @@ __global__ __launch_bounds__(256) void k_gemv1(GemvP p) {
         if (lane == r && row0 + r < N) qkv_pair_store(e_pair, acc[r], acc[r + 1]);
     }
   }
+}
+
+template <int R, int KB, int EPI>
+__global__ __launch_bounds__(256) void k_gemv1(GemvP p) {
+  gemv1_body<R, KB, EPI, false>(p);
+}
+
+// The first layer's QKV projection of a one-row decode step with the
+// embedding gather folded in (one launch fewer per token).
+template <int R, int KB>
+__global__ __launch_bounds__(256) void k_gemv1_emb(GemvP p) {
+  gemv1_body<R, KB, EPI_QKV, true>(p);
 }
 
 // lm_head of the GEMV path: logits = W_lm RMSNorm(h) w_out, and each row's
@@ -580,10 +637,31 @@ static GemvP base(const uint16_t *W, int N, int K, const float *x, int ldx, int 
 }
 
 void gemv_qkv(const Dims &d, const LayerW &w, const float *h, int M, const QkvEpi &e,
-              float eps, float *normed, hipStream_t st) {
+              float eps, float *normed, hipStream_t st, const EmbedSrc *emb) {
   GemvP p = base(w.wqkv, d.nqkv, d.H, h, d.H, M);
   p.d = d;
   p.qkv = e;
+  if (emb) {  // (callers pass it only where gemv_qkv_embeds holds)
+    p.norm_w = w.attn_norm;
+    p.eps = eps;
+    p.emb_tok = emb->tokens;
+    p.emb_off = emb->off;
+    p.emb_V = emb->V;
+    p.emb_E = emb->E;
+    p.emb_h = const_cast<float *>(h);
+    p.emb_bad = emb->bad;
+    p.n_groups = (p.N + 4 * 2 - 1) / (4 * 2);
+    const int kc = (p.K + 511) / 512;
+    if (kc <= 2)
+      hipLaunchKernelGGL((k_gemv1_emb<2, 2>), dim3(p.n_groups), dim3(256), 0, st, p);
+    else if (kc <= 4)
+      hipLaunchKernelGGL((k_gemv1_emb<2, 4>), dim3(p.n_groups), dim3(256), 0, st, p);
+    else if (kc <= 8)
+      hipLaunchKernelGGL((k_gemv1_emb<2, 8>), dim3(p.n_groups), dim3(256), 0, st, p);
+    else
+      hipLaunchKernelGGL((k_gemv1_emb<2, 10>), dim3(p.n_groups), dim3(256), 0, st, p);
+    return;
+  }
   if (d.H > kGemvNormCols) {  // wide rows: norm first, then the multi-batch GEMV
     rmsnorm_rows_f16(const_cast<float *>(h), d.H, w.attn_norm, d.H, M, eps, nullptr, 0, normed,
                      nullptr, 0, st);

@@ -134,8 +134,19 @@ constexpr int kMaxStopIds = 8;
 // kGemvNormCols are normed first by k_rmsnorm_rows into `normed` ([M, H]
 // f32 scratch), then multiplied by the GEMV without its norm prologue.
 constexpr int kGemvNormCols = 10 * 512;
+// The embedding gather folded into the first QKV projection (one row,
+// rows up to kGemvNormCols): h = f32(E[(*tokens)[off]]), written by the
+// same launch; an id outside [0, V) reads row 0 and sets *bad.
+struct EmbedSrc {
+  const uint16_t *E;
+  int V;
+  const int *const *tokens;
+  int off;
+  unsigned int *bad;
+};
+inline bool gemv_qkv_embeds(const Dims &d, int M) { return M == 1 && d.H <= kGemvNormCols; }
 void gemv_qkv(const Dims &d, const LayerW &w, const float *h, int M, const QkvEpi &e,
-              float eps, float *normed, hipStream_t st);
+              float eps, float *normed, hipStream_t st, const EmbedSrc *emb = nullptr);
 void gemv_resid(const uint16_t *W, int N, int K, const float *x, int ldx, int M, float *h,
                 int ldh, hipStream_t st);
 void gemv_swiglu(const Dims &d, const LayerW &w, const float *h, int M, float *a, int lda,

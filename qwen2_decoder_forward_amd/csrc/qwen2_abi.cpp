@@ -627,14 +627,19 @@ void decode_launches(qwen2_ctx *c, int B, int n_chunks, const int *dpos, const i
   const Dims &d = c->d;
   const float eps = c->hp.rms_eps;
   const q2::RowInfo rows{dpos, dseq};
-  TIMED(QWEN2_OP_EMBED, q2::embed_rows(c->tok_embd, d.H, d.V, &dev_slots(c)->tokens, 0, B, c->h,
-                                       c->bad_flag, st));
+  // (one row: the gather is folded into the first QKV projection)
+  const q2::EmbedSrc emb{c->tok_embd, d.V, &dev_slots(c)->tokens, 0, c->bad_flag};
+  const bool emb_fused = q2::gemv_qkv_embeds(d, B);
+  if (!emb_fused)
+    TIMED(QWEN2_OP_EMBED, q2::embed_rows(c->tok_embd, d.H, d.V, &dev_slots(c)->tokens, 0, B, c->h,
+                                         c->bad_flag, st));
   int pending = 0;  // split-K partial sums of the last residual GEMM not yet in h
   for (int l = 0; l < d.L; ++l) {
     const LayerW &w = c->layers[l];
     const q2::QkvEpi e = qkv_epi(c, l, dpos, dseq);
     if (B <= kGemvRows) {
-      TIMED(QWEN2_OP_QKV, q2::gemv_qkv(d, w, c->h, B, e, eps, c->normed, st));
+      TIMED(QWEN2_OP_QKV, q2::gemv_qkv(d, w, c->h, B, e, eps, c->normed, st,
+                                       l == 0 && emb_fused ? &emb : nullptr));
     } else if (pending == 0 && q2::qkv_fuses_norm(d, B, c->splitk)) {
       TIMED(QWEN2_OP_QKV, q2::gemm_qkv_normed(d, w, c->h, d.H, B, eps, e, st));
     } else {
