@@ -36,7 +36,7 @@ MFMA_F16_PEAK_TFS = 2500.0  # MI355X dense f16 MFMA
 # (profiles/qwen2.5-0.5b_gateup_gemv_hbm_traffic.md); valid only while the
 # kernel source is the one the counters were taken on.
 GATEUP_TRAFFIC_BYTES = 17580542
-GATEUP_TRAFFIC_SRC_SHA = "be3c455c616ec489"
+GATEUP_TRAFFIC_SRC_SHA = "27ab86829299411f"
 
 
 def gateup_traffic(shape):
